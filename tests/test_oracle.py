@@ -1,0 +1,402 @@
+"""Pins for the fp64 oracle, against things other than itself (CPU only).
+
+* a dense KKT solve by LU, assembled from the QP's definition;
+* the dense Schur complement C G^-1 C' and c + C G^-1 g;
+* closed forms (N = 1, A = 0, gamma = 0, exact-step merit, feasible merit);
+* invariants (symmetry, positive definiteness, linearised dynamics, stationarity,
+  merit monotone in the step on convex instances, M(0) = mu ||c||_1);
+* a library PCG (scipy) on the same operators for the iteration count;
+* hand-derived worked examples in tests/golden/.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.sparse.linalg as spla
+
+import oracle
+from block_tridiagonal_pcg_amd import synth
+from dense_kkt import assemble, btd_dense, kkt_solve, merit_dense, x_index
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ALPHAS = synth.ALPHAS.astype(np.float64)
+
+
+def _form(batch, rho=None):
+    return oracle.form_schur(*synth.inputs(batch), rho=rho)
+
+
+def _pcg(batch, fs, eps=1e-12, max_iters=5000, lambda0=None):
+    return oracle.pcg_solve(fs["S"], fs["Pinv"], fs["gamma"], fs["Qinv"], fs["Rinv"], batch["A"],
+                            batch["Bu"], batch["q"], batch["r"], eps, max_iters, lambda0=lambda0)
+
+
+# ---------------------------------------------------------------- generators
+
+
+def test_generator_deterministic_and_prefix():
+    a = synth.make_batch(2, 3)
+    b = synth.make_batch(2, 3)
+    c = synth.make_batch(2, 1, first=2)
+    for f in synth.FIELDS:
+        assert a[f].dtype == np.float32
+        assert np.array_equal(a[f], b[f])
+        assert np.array_equal(a[f][2:3], c[f])
+
+
+def test_generator_shapes_and_distributions():
+    bt = synth.make_batch(3, 2)
+    n, m, N, B = bt["dims"]
+    assert bt["Q"].shape == (B, N, n, n) and bt["R"].shape == (B, N - 1, m, m)
+    assert bt["A"].shape == (B, N - 1, n, n) and bt["Bu"].shape == (B, N - 1, n, m)
+    rad = max(np.max(np.abs(np.linalg.eigvals(bt["A"][0, k].astype(np.float64)))) for k in range(N - 1))
+    assert abs(rad - 0.95) < 1e-5
+    assert np.std(bt["e"]) < 0.05  # e ~ N(0, 0.01) on the headline configuration
+    d = np.diagonal(synth.make_batch(5, 1)["Q"][0], axis1=1, axis2=2)
+    assert d.min() >= 1e-3 * 0.999 and d.max() <= 1e3 * 1.001
+
+
+# ---------------------------------------------------------------- golden
+
+
+def _golden_cases():
+    with open(os.path.join(HERE, "golden", "scalar_lq.json")) as fh:
+        return json.load(fh)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_golden_worked_example(case):
+    arr = {k: np.asarray(case[k], dtype=np.float64)[None] for k in synth.FIELDS}
+    fs = oracle.form_schur(*[arr[k] for k in synth.FIELDS], rho=None)
+    np.testing.assert_allclose(fs["S"][0], case["S"], atol=1e-14)
+    np.testing.assert_allclose(fs["Pinv"][0], case["Pinv"], atol=1e-14)
+    np.testing.assert_allclose(fs["gamma"][0], case["gamma"], atol=1e-14)
+    res = oracle.sqp_step(*[arr[k] for k in synth.FIELDS], None, 1e-12, 10,
+                          np.array([float(a) for a in case["merit_at"]]), case["mu"])
+    np.testing.assert_allclose(res["lam"][0], case["lambda"], atol=1e-13)
+    np.testing.assert_allclose(res["dz"][0], case["dz"], atol=1e-13)
+    assert res["iters"][0] == case["pcg_iters"]
+    np.testing.assert_allclose(res["merit0"][0], case["merit0"], atol=1e-13)
+    np.testing.assert_allclose(res["merit"][0], list(case["merit_at"].values()), atol=1e-13)
+    assert res["best"][0] == case["best"]
+    assert res["flags"][0] == 0
+
+
+# ---------------------------------------------------------------- stage 1
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+@pytest.mark.parametrize("rho", [0.0, 0.5])
+def test_schur_matches_dense_definition(cid, rho):
+    bt = synth.make_batch(cid, 1)
+    n, m, N, _ = bt["dims"]
+    fs = _form(bt, rho=np.array([rho]))
+    d = assemble(bt, 0, rho)
+    Gi = np.linalg.inv(d["G"])
+    S_dense = d["C"] @ Gi @ d["C"].T
+    gam_dense = d["c"] + d["C"] @ Gi @ d["g"]
+    np.testing.assert_allclose(btd_dense(fs["S"][0]), S_dense, atol=1e-12 * np.abs(S_dense).max())
+    np.testing.assert_allclose(fs["gamma"][0].ravel(), gam_dense, atol=1e-12 * np.abs(gam_dense).max())
+    # the G^-1 blocks
+    for k in range(N):
+        i = x_index(k, n, m)
+        np.testing.assert_allclose(fs["Qinv"][0, k], Gi[i:i + n, i:i + n], atol=1e-12)
+    assert fs["flags"][0] == 0
+
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_schur_and_preconditioner_symmetric_spd(cid):
+    bt = synth.make_batch(cid, 1)
+    fs = _form(bt)
+    S = btd_dense(fs["S"][0])
+    P = btd_dense(fs["Pinv"][0])
+    np.testing.assert_allclose(S, S.T, atol=1e-12 * np.abs(S).max())
+    np.testing.assert_allclose(P, P.T, atol=1e-10 * np.abs(P).max())
+    assert np.linalg.eigvalsh(S).min() > 0
+    assert np.linalg.eigvalsh(0.5 * (P + P.T)).min() > 0
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_preconditioner_closed_form(cid):
+    """Phi^-1 = D^-1 J S J D^-1 with D = blkdiag(D_k), J = blkdiag((-1)^k I)."""
+    bt = synth.make_batch(cid, 1)
+    n, m, N, _ = bt["dims"]
+    fs = _form(bt)
+    S = btd_dense(fs["S"][0])
+    Dinv = np.zeros_like(S)
+    J = np.zeros_like(S)
+    for k in range(N):
+        sl = slice(k * n, (k + 1) * n)
+        Dinv[sl, sl] = np.linalg.inv(S[sl, sl])
+        J[sl, sl] = (-1) ** k * np.eye(n)
+    P_closed = Dinv @ J @ S @ J @ Dinv
+    P = btd_dense(fs["Pinv"][0])
+    np.testing.assert_allclose(P, P_closed, atol=1e-10 * np.abs(P_closed).max())
+
+
+def test_form_flags_non_spd():
+    bt = synth.make_batch(1, 3)
+    bt["Q"][1, 3] = -np.eye(bt["dims"][0], dtype=np.float32)
+    bt["R"][2, 0] = np.diag([1.0, -0.5]).astype(np.float32)
+    fs = _form(bt)
+    assert fs["flags"][0] == 0
+    assert fs["flags"][1] & oracle.FLAG_Q_NOT_SPD
+    assert fs["flags"][2] & oracle.FLAG_R_NOT_SPD and not fs["flags"][2] & oracle.FLAG_Q_NOT_SPD
+
+
+def test_form_flags_schur_block_not_spd():
+    """D_k is SPD whenever Q~ and R are; a strongly negative Q~ at the last knot makes
+    D_{N-1} = Q~_{N-1}^-1 + (PSD terms) indefinite, so both flags are raised."""
+    bt = synth.make_batch(1, 1)
+    N = bt["dims"][2]
+    bt["Q"][0, N - 1] = -np.eye(bt["dims"][0], dtype=np.float32) * 1e-3
+    fs = _form(bt)
+    assert fs["flags"][0] & oracle.FLAG_Q_NOT_SPD
+    assert fs["flags"][0] & oracle.FLAG_S_NOT_SPD
+
+
+# ---------------------------------------------------------------- stage 2
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_dz_matches_dense_kkt(cid):
+    bt = synth.make_batch(cid, 1)
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-12)
+    d = assemble(bt, 0)
+    dz_ref, lam_ref = kkt_solve(d["G"], d["g"], d["C"], d["c"])
+    err = np.linalg.norm(res["dz"][0] - dz_ref) / np.linalg.norm(dz_ref)
+    assert err < 1e-9, err
+    lerr = np.linalg.norm(res["lam"][0].ravel() - lam_ref) / np.linalg.norm(lam_ref)
+    assert lerr < 1e-9, lerr
+    assert res["flags"][0] == 0
+
+
+@pytest.mark.slow
+def test_dz_matches_dense_kkt_ill_conditioned():
+    bt = synth.make_batch(5, 1)
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-12, max_iters=20000)
+    d = assemble(bt, 0)
+    dz_ref, _ = kkt_solve(d["G"], d["g"], d["C"], d["c"])
+    err = np.linalg.norm(res["dz"][0] - dz_ref) / np.linalg.norm(dz_ref)
+    assert err < 1e-7, err
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_pcg_residual_and_dynamics_invariants(cid):
+    """||S lam - gamma|| / ||gamma|| <= 1e-8, C dz = c to 1e-9, G dz + g - C' lam = 0."""
+    bt = synth.make_batch(cid, 2)
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-8, max_iters=10 * bt["dims"][0] * bt["dims"][2])
+    tight = _pcg(bt, fs, eps=1e-12, max_iters=10 * bt["dims"][0] * bt["dims"][2])
+    for b in range(2):
+        S = btd_dense(fs["S"][b])
+        gam = fs["gamma"][b].ravel()
+        lam = res["lam"][b].ravel()
+        assert np.linalg.norm(S @ lam - gam) / np.linalg.norm(gam) <= 1e-8
+        assert res["relres"][b] <= 1e-8
+        d = assemble(bt, b)
+        # C dz - c is S lam - gamma, so the 1e-9 bound needs a tightly converged solve
+        dz = tight["dz"][b]
+        lt = tight["lam"][b].ravel()
+        assert np.abs(d["C"] @ dz - d["c"]).max() <= 1e-9
+        assert np.abs(d["G"] @ dz + d["g"] - d["C"].T @ lt).max() <= 1e-9
+        # stationarity holds for any lambda (dz is built from it)
+        assert np.abs(d["G"] @ res["dz"][b] + d["g"] - d["C"].T @ lam).max() <= 1e-9
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_pcg_matches_direct_block_cholesky(cid):
+    bt = synth.make_batch(cid, 2)
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-12)
+    dr = oracle.direct_solve(fs["S"], fs["gamma"])
+    assert (dr["flags"] == 0).all()
+    for b in range(2):
+        lam_np = np.linalg.solve(btd_dense(fs["S"][b]), fs["gamma"][b].ravel())
+        np.testing.assert_allclose(dr["lam"][b].ravel(), lam_np, rtol=0, atol=1e-10 * np.abs(lam_np).max())
+        np.testing.assert_allclose(res["lam"][b].ravel(), lam_np, rtol=0, atol=1e-9 * np.abs(lam_np).max())
+
+
+@pytest.mark.parametrize("cid,eps", [(1, 1e-6), (2, 1e-6), (3, 1e-6), (4, 1e-8)])
+def test_pcg_iterations_match_library_pcg(cid, eps):
+    """scipy's preconditioned CG on the same S, Phi^-1, gamma stops after the same number of
+    iterations (its test is ||r|| <= eps ||b|| as well, starting from zero)."""
+    bt = synth.make_batch(cid, 2)
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=eps)
+    for b in range(2):
+        S = btd_dense(fs["S"][b])
+        P = btd_dense(fs["Pinv"][b])
+        count = [0]
+
+        def cb(_x):
+            count[0] += 1
+
+        x, info = spla.cg(S, fs["gamma"][b].ravel(), rtol=eps, atol=0.0, maxiter=10000,
+                          M=spla.aslinearoperator(P), callback=cb)
+        assert info == 0
+        assert abs(int(res["iters"][b]) - count[0]) <= 1, (res["iters"][b], count[0])
+        np.testing.assert_allclose(res["lam"][b].ravel(), x, atol=10 * eps * np.abs(x).max())
+
+
+def test_special_case_single_knot():
+    """N = 1: S = Q~_0^-1 = Phi, so PCG stops after one iteration with lambda = Q~ x0 + q,
+    dx_0 = x0."""
+    bt = synth.make_batch(2, 3, N=1)
+    fs = _form(bt, rho=np.full(3, 0.25))
+    res = _pcg(bt, fs, eps=1e-12)
+    for b in range(3):
+        Qt = bt["Q"][b, 0].astype(np.float64) + 0.25 * np.eye(bt["dims"][0])
+        lam = Qt @ bt["x0"][b].astype(np.float64) + bt["q"][b, 0]
+        np.testing.assert_allclose(res["lam"][b, 0], lam, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["dz"][b], bt["x0"][b], rtol=1e-12, atol=1e-12)
+        assert res["iters"][b] == 1
+
+
+def test_special_case_zero_dynamics_jacobian():
+    """A_k = 0 makes S block diagonal, the preconditioner exact, and PCG one iteration long."""
+    bt = synth.make_batch(3, 2)
+    bt["A"][:] = 0
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-10)
+    assert (res["iters"] == 1).all()
+    d = assemble(bt, 1)
+    dz_ref, _ = kkt_solve(d["G"], d["g"], d["C"], d["c"])
+    np.testing.assert_allclose(res["dz"][1], dz_ref, atol=1e-10)
+
+
+def test_special_case_zero_rhs():
+    bt = synth.make_batch(1, 1)
+    for f in ("q", "r", "e", "x0"):
+        bt[f][:] = 0
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-6, lambda0=np.ones((1, 8, 4)))
+    assert res["iters"][0] == 0 and np.all(res["lam"] == 0) and np.all(res["dz"] == 0)
+
+
+def test_pcg_flags_maxiter_and_nonfinite():
+    bt = synth.make_batch(2, 2)
+    bt["e"][1, 5, 2] = np.nan
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-6, max_iters=1)
+    assert res["flags"][0] & oracle.FLAG_PCG_MAXITER and res["iters"][0] == 1
+    assert res["flags"][1] & oracle.FLAG_NONFINITE
+
+
+def test_pcg_warm_start_converges_to_same_answer():
+    bt = synth.make_batch(2, 1)
+    fs = _form(bt)
+    cold = _pcg(bt, fs, eps=1e-10)
+    warm = _pcg(bt, fs, eps=1e-10, lambda0=cold["lam"] * (1 + 1e-3))
+    assert warm["iters"][0] < cold["iters"][0]
+    np.testing.assert_allclose(warm["dz"], cold["dz"], atol=1e-8)
+
+
+# ---------------------------------------------------------------- stage 3
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_merit_matches_dense_form_any_step(cid):
+    """The merit of an arbitrary (not optimal) step equals its matrix form."""
+    bt = synth.make_batch(cid, 2)
+    n, m, N, _ = bt["dims"]
+    rng = np.random.default_rng(7)
+    dz = rng.standard_normal((2, N * n + (N - 1) * m))
+    mu = 1.7
+    res = oracle.merit_eval(*synth.inputs(bt), dz, ALPHAS, mu)
+    for b in range(2):
+        d = assemble(bt, b)
+        for i, a in enumerate(ALPHAS):
+            ref = merit_dense(d["G0"], d["g"], d["C"], d["c"], dz[b], a, mu)
+            assert abs(res["merit"][b, i] - ref) <= 1e-12 * max(1.0, abs(ref))
+        assert abs(res["merit0"][b] - mu * np.abs(d["c"]).sum()) <= 1e-12 * res["merit0"][b]
+
+
+@pytest.mark.parametrize("cid", [1, 3])
+def test_merit_closed_form_at_exact_step(cid):
+    """With the exact step the linearised defect is (1 - a) c, so
+    M(a) = a g'dz + a^2/2 dz'G dz + mu (1 - a) ||c||_1."""
+    bt = synth.make_batch(cid, 1)
+    d = assemble(bt, 0)
+    dz, lam = kkt_solve(d["G"], d["g"], d["C"], d["c"])
+    mu = 1.0
+    res = oracle.merit_eval(*synth.inputs(bt), dz[None], ALPHAS, mu)
+    c1 = np.abs(d["c"]).sum()
+    for i, a in enumerate(ALPHAS):
+        ref = a * d["g"] @ dz + 0.5 * a * a * dz @ d["G0"] @ dz + mu * (1 - a) * c1
+        assert abs(res["merit"][0, i] - ref) <= 1e-10 * max(1.0, abs(ref))
+
+
+def test_merit_feasible_instance_closed_form_and_monotone():
+    """x0 = 0, e = 0: M(a) = -a (1 - a/2) dz'G dz for any mu; decreasing on (0, 1]."""
+    bt = synth.make_batch(2, 1)
+    bt["x0"][:] = 0
+    bt["e"][:] = 0
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-12)
+    mer = oracle.merit_eval(*synth.inputs(bt), res["dz"], ALPHAS, 5.0)
+    d = assemble(bt, 0)
+    quad = res["dz"][0] @ d["G0"] @ res["dz"][0]
+    for i, a in enumerate(ALPHAS):
+        ref = -a * (1 - a / 2) * quad
+        assert abs(mer["merit"][0, i] - ref) <= 1e-9 * abs(ref)
+    assert np.all(np.diff(mer["merit"][0]) > 0)  # alphas decrease, merit rises
+    assert mer["best"][0] == 0 and mer["merit0"][0] == 0
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_merit_monotone_with_exact_penalty(cid):
+    """mu >= ||lambda||_inf gives dM/da <= 0 on [0, 1]: merit non-increasing in a."""
+    bt = synth.make_batch(cid, 2)
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-12)
+    for b in range(2):
+        mu = 1.01 * np.abs(res["lam"][b]).max()
+        mer = oracle.merit_eval(*[x[b:b + 1] for x in synth.inputs(bt)], res["dz"][b:b + 1], ALPHAS, mu)
+        assert np.all(np.diff(mer["merit"][0]) >= -1e-12 * np.abs(mer["merit"][0]).max())
+        assert mer["best"][0] == 0
+        assert mer["merit"][0, 0] < mer["merit0"][0]
+
+
+def test_merit_line_search_failure_flag():
+    """An ascent direction (negated step) fails every candidate: best = -1 and the flag."""
+    bt = synth.make_batch(2, 1)
+    bt["x0"][:] = 0
+    bt["e"][:] = 0
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-10)
+    mer = oracle.merit_eval(*synth.inputs(bt), -res["dz"], ALPHAS, 1.0)
+    assert mer["best"][0] == -1 and mer["flags"][0] & oracle.FLAG_LS_FAILED
+
+
+def test_merit_ties_go_to_larger_step():
+    bt = synth.make_batch(1, 1)
+    for f in ("x0", "e", "q", "r"):
+        bt[f][:] = 0
+    dz = np.zeros((1, 8 * 4 + 7 * 2))
+    mer = oracle.merit_eval(*synth.inputs(bt), dz, ALPHAS, 1.0)
+    # all candidates tie at M0 = 0, none is below it
+    assert mer["best"][0] == -1
+    # a step that is exactly 0 everywhere except a knot-free term: every merit equal but below M0
+    bt["e"][0, 0, 0] = 1.0
+    dz2 = np.zeros_like(dz)
+    mer2 = oracle.merit_eval(*synth.inputs(bt), dz2, np.array([1.0, 1.0, 0.5]), 1.0)
+    assert mer2["best"][0] == -1
+
+
+# ---------------------------------------------------------------- whole step
+
+
+def test_sqp_step_equals_stages():
+    bt = synth.make_batch(2, 3)
+    fs = _form(bt)
+    res = _pcg(bt, fs, eps=1e-6, max_iters=200)
+    mer = oracle.merit_eval(*synth.inputs(bt), res["dz"], ALPHAS, 1.0)
+    full = oracle.sqp_step(*synth.inputs(bt), None, 1e-6, 200, ALPHAS, 1.0)
+    np.testing.assert_array_equal(full["dz"], res["dz"])
+    np.testing.assert_array_equal(full["merit"], mer["merit"])
+    np.testing.assert_array_equal(full["iters"], res["iters"])
+    np.testing.assert_array_equal(full["best"], mer["best"])
