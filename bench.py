@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of one SQP iteration's linear-algebra core on one MI355X.
+
+A step is gato_sqp_step over the whole batch: form S, gamma and the stair
+preconditioner, PCG to eps = 1e-6, recover dz, merit at 8 step sizes and
+select (GATO paper Sec. III, Fig. 2 steps a-c), cold-started: lambda is reset
+to zero before every step, so no step reuses the previous step's solution.
+Inputs are seeded synthetic batches (block_tridiagonal_pcg_amd.synth) already
+resident in device memory when the timed region starts.
+
+Prints one JSON line.  Options: --steps K --warmup W --gpus N (N must be 1)
+--config C --batch B --no-cpu-baseline --profile-copy (adds a 256 MiB device
+copy, the reference kernel for scaling rocprofv3 byte counters).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+EPS = 1e-6
+MU = 1.0
+CAPS = {1: 200, 2: 200, 3: 200, 4: 200, 5: 2000}
+KERNEL = "k_sqp_fused"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-copy", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+
+def form_flops(n, m, N):
+    """Dense-block operation count of stage 1 per solve.
+
+    Per knot: SPD inverses of Q~ (n^3) and R (m^3) [Cholesky n^3/3 + triangular
+    inverse n^3/3 + product n^3/3]; A Q~^-1 and A Q~^-1 A' (2 n^3 each); B R^-1 (2 n m^2)
+    and B R^-1 B' (2 n^2 m); D^-1 (n^3); -D_k^-1 S_{k,k+1} D_{k+1}^-1 (4 n^3); gamma
+    (Q~^-1 q, A Q~^-1 q, B R^-1 r: 2 n^2 + 2 n^2 + 2 n m) and the D sum (2 n^2).
+    """
+    per_dyn = 2 * n ** 3 + 2 * n ** 3 + 2 * n * m * m + 2 * n * n * m + m ** 3 + 4 * n ** 3 + 4 * n * n + 2 * n * m
+    per_knot = n ** 3 + n ** 3 + 2 * n * n
+    return N * per_knot + (N - 1) * per_dyn
+
+
+def pcg_iter_flops(n, N):
+    """Per PCG iteration per solve: S p and Phi^-1 r over (3N-2) n x n blocks (2 flops per
+    entry each), three dot products and three axpys over N n entries."""
+    return 2 * 2 * (3 * N - 2) * n * n + 3 * 2 * N * n + 3 * 2 * N * n
+
+
+def pcg_iter_bytes(n, N):
+    """Unique fp32 entries of S and Phi^-1 read per iteration per solve (symmetric diagonal
+    blocks counted once per triangle, off-diagonal blocks once)."""
+    return 4 * 2 * (N * n * (n + 1) // 2 + (N - 1) * n * n)
+
+
+def recover_flops(n, m, N):
+    return N * 2 * n * n + (N - 1) * (2 * n * n + 2 * n * m + 2 * m * m) + 4 * N * n
+
+
+def merit_flops(n, m, N, n_alpha):
+    """Per solve: Q dx, R du, A dx + B du computed once per knot (2 flops per entry),
+    the linear/quadratic terms, and per step size |e + a d| (3 per entry) plus the sums."""
+    per_knot = 2 * n * n + 2 * m * m + 2 * n * n + 2 * n * m + 4 * n + 4 * m
+    return N * per_knot + (n_alpha + 1) * (N * 3 * n + 5 * N)
+
+
+def input_bytes(n, m, N):
+    return 4 * (N * n * n + N * n + (N - 1) * (m * m + m + n * n + n * m + n) + n)
+
+
+def output_bytes(n, m, N, n_alpha):
+    return 4 * (N * n + N * n + (N - 1) * m + n_alpha + 4)
+
+
+# ---------------------------------------------------------------- measured traffic
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_tridiagonal_pcg_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".inc")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources and this workload; else None."""
+    path = os.path.join(ROOT, "profiles", "k_sqp_fused_cfg3_B128_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != source_digest() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline(batch, n_alpha, seconds):
+    import numpy as np
+
+    import oracle
+
+    al = np.array([2.0 ** -i for i in range(n_alpha)])
+    cap = CAPS[batch["cid"]]
+    args = [batch[f] for f in ("Q", "q", "R", "r", "A", "Bu", "e", "x0")]
+    t0 = time.perf_counter()
+    oracle.sqp_step(*args, None, EPS, cap, al, MU)
+    one = time.perf_counter() - t0
+    reps = max(1, min(200, int(math.ceil(seconds / max(one, 1e-6)))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.sqp_step(*args, None, EPS, cap, al, MU)
+    wall = time.perf_counter() - t0
+    B = batch["dims"][3]
+    return {"value": B * reps / wall, "unit": "solves/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "the full %d-solve batch of the timed workload, %d repeats (%.1f s wall), fp64, "
+                      "OpenMP over solves" % (B, reps, wall)}
+
+
+# ---------------------------------------------------------------- main
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from block_tridiagonal_pcg_amd import ops, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[a.config]
+    batch = synth.make_batch(a.config, a.batch)
+    batch["cid"] = a.config
+    n, m, N, B = batch["dims"]
+    n_alpha = 8
+    alphas = synth.ALPHAS
+    cap = CAPS[a.config]
+    dims = batch["dims"]
+    dev = ops.to_device(batch)
+    out = ops.alloc_outputs(dims, n_alpha)
+    ws = ops.workspace_for(dims, n_alpha)
+    stream = torch.cuda.current_stream()
+
+    if a.profile_copy:
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # pre-marshalled call: argument checks once, then only the C call per step
+    step = ops.prepared_sqp_step(dims, *[dev[f] for f in synth.FIELDS], None, EPS, cap, alphas, MU, out["lam"],
+                                 out["dz"], out["merit"], out["merit0"], out["best"], out["iters"], out["relres"],
+                                 out["flags"], workspace=ws, stream=stream)
+    lam = out["lam"]
+    for _ in range(a.warmup):
+        lam.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        lam.zero_()
+        starts[k].record(stream)
+        step()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    kern_med_s = float(np.median(kern_ms)) / 1e3
+
+    iters = out["iters"].cpu().numpy()
+    flags = out["flags"].cpu().numpy()
+    if (flags & ~ops.F_LS_FAILED).any():
+        print("warning: solves flagged: %s" % np.unique(flags), file=sys.stderr)
+
+    # algorithmic work of one launch (the whole batch)
+    flops = B * (form_flops(n, m, N) + recover_flops(n, m, N) + merit_flops(n, m, N, n_alpha)) + \
+        float(iters.sum()) * pcg_iter_flops(n, N)
+    achieved_tflops = flops / kern_avg_s / 1e12
+    fused = ops.gato_workspace_bytes(dims, n_alpha) == 0
+    workload = "%s, B=%d" % (cfg.name, B)
+    traffic = measured_traffic(workload) if fused else None
+
+    # per-stage device times with the three standalone calls (events on the same stream)
+    stage_us = ops.stage_times(dims, dev, EPS, cap, alphas, MU, reps=max(3, min(20, a.steps // 10)))
+    pcg_bytes = float(iters.sum()) * pcg_iter_bytes(n, N)
+    pcg_equiv_gbps = pcg_bytes / (stage_us["linsys_us"] * 1e-6) / 1e9 if stage_us["linsys_us"] > 0 else None
+
+    value = B * a.steps / wall
+    rec = {
+        "metric": "batched SQP-step solves/sec (n=14,m=7,N=64,B=128) + % HBM roofline",
+        "value": value,
+        "unit": "solves/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": wall / a.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "n": n, "m": m, "N": N, "B": B, "eps": EPS, "max_iters": cap,
+                   "n_alpha": n_alpha, "mu": MU, "lambda0": "zero (cold start every step)",
+                   "path": "fused single kernel" if fused else "form + streamed PCG + merit"},
+        "roofline": {
+            "bound": "alu",
+            "kernel": KERNEL if fused else "k_pcg_stream",
+            "achieved": achieved_tflops,
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": traffic,
+            "flops_per_launch": flops,
+            "launch_avg_us": kern_avg_s * 1e6,
+            "launch_median_us": kern_med_s * 1e6,
+        },
+        "pcg_iters": {"min": int(iters.min()), "median": float(np.median(iters)), "max": int(iters.max())},
+        "stage_us_unfused": stage_us,
+        "pcg_hbm_equivalent": {
+            "algorithmic_bytes": pcg_bytes,
+            "achieved_GBps": pcg_equiv_gbps,
+            "frac_of_hbm_peak": (pcg_equiv_gbps / HBM_PEAK_GBPS) if pcg_equiv_gbps else None,
+            "note": "S and Phi^-1 are register-resident in the PCG kernel; this is the rate the "
+                    "same iterations would need from HBM, not HBM traffic",
+        },
+        "source_sha": source_digest(),
+    }
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(batch, n_alpha, a.cpu_seconds)
+        rec["cpu_baseline"]["gpu_over_cpu"] = value / rec["cpu_baseline"]["value"]
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,629 @@
+// gato.hip -- kernels and C ABI of libgato.so (gfx950).
+//
+// Kernels (one workgroup per solve unless noted):
+//   k_sqp_fused   form -> PCG -> recovery -> merit -> selection, everything in
+//                 registers and LDS; used when a workgroup holds the horizon.
+//   k_form        stage 1 alone, one workgroup per window of knots (any N).
+//   k_pcg_res     stage 2 alone with S and Phi^-1 rows loaded once into registers.
+//   k_pcg_stream  stage 2 alone for horizons longer than a workgroup holds:
+//                 C knots per lane group, rows re-read from memory per product.
+//   k_merit       stage 3 alone; any workgroup size gives identical bits.
+#include "gato_stages.h"
+
+#include <cstdlib>
+#include <cstring>
+
+namespace gato {
+
+// ------------------------------------------------------------------ fused step
+
+template <class SH, typename RT>
+struct FusedLds {
+    float parkQ[SH::SLOTS][SH::NC][SH::NC];  // Q~_k^-1 rows, kept for the recovery
+    float parkR[SH::SLOTS][SH::MC][SH::MC];  // R_k^-1 rows
+    union {
+        FormLds<SH> form;
+        PcgLds<SH, RT, 1> pcg;
+        float mer[(GATO_MAX_ALPHA + 1) * 64];
+    } u;
+    int flags;
+};
+
+template <class SH, typename RT>
+__global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, SL = SH::SLOTS;
+    __shared__ FusedLds<SH, RT> L;
+    const Ix ix{p.n, p.m, p.N};
+    const int b = blockIdx.x;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP, k = s;
+    const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < p.n;
+    if (threadIdx.x == 0) L.flags = 0;
+
+    Rows<SH> rw;
+    int fl = 0;
+    form<SH>(
+        p, b, 0, p.N, L.u.form, rw, fl,
+        [&](const float* qi) {
+            if (i < NC)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) L.parkQ[s][i][c] = qi[c];
+        },
+        [&](const float* ri) {
+            if (i < MC)
+#pragma unroll
+                for (int c = 0; c < MC; ++c) L.parkR[s][i][c] = ri[c];
+        });
+    if (fl && i == 0) atomicOr(&L.flags, fl);
+
+    float lam = rowv ? p.lambda[ix.vn(b, k, i)] : 0.0f;
+    int it = 0, pfl = 0;
+    float rel = 0.0f;
+    const RegMat<SH> M{&rw};
+    pcg<SH, RT, 1>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
+
+    // recovery of dz
+    L.u.pcg.xv[s][i] = lam;
+    __syncthreads();
+    const float lamn = (s + 1 < SL) ? L.u.pcg.xv[s + 1][i] : 0.0f;
+    float qi[NC], ri[MC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qi[c] = (i < NC) ? L.parkQ[s][i][c] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < MC; ++c) ri[c] = (i < MC) ? L.parkR[s][i][c] : 0.0f;
+    __syncthreads();
+    float dx, du;
+    recover<SH>(p, b, k, i, lam, lamn, qi, ri, dx, du);
+    if (rowv) {
+        p.lambda[ix.vn(b, k, i)] = lam;
+        p.dz[ix.dx(b, k, i)] = dx;
+    }
+    if (hn && i < p.m) p.dz[ix.du(b, k, i)] = du;
+
+    // merit at every step size, then the selection
+    L.u.pcg.xv[s][i] = dx;
+    __syncthreads();
+    const float dxn = (s + 1 < SL) ? L.u.pcg.xv[s + 1][i] : 0.0f;
+    __syncthreads();
+    for (int t = threadIdx.x; t < (GATO_MAX_ALPHA + 1) * 64; t += blockDim.x) L.u.mer[t] = 0.0f;
+    __syncthreads();
+    merit_knot<SH>(p, b, k, i, dx, du, dxn, L.u.mer + k, 64);
+    __syncthreads();
+    int32_t best;
+    int lsfail;
+    merit_select<4>(p, b, L.u.mer, 64, best, lsfail);
+    if (threadIdx.x == 0) {
+        p.iters[b] = it;
+        p.relres[b] = rel;
+        p.best[b] = best;
+        p.flags[b] = L.flags | pfl | (lsfail ? GATO_F_LS_FAILED : 0);
+    }
+}
+
+// ------------------------------------------------------------------ stage 1 alone
+
+__global__ void k_zero_i32(int32_t* x, int count)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < count) x[t] = 0;
+}
+
+template <class SH>
+__global__ __launch_bounds__(SH::THREADS) void k_form(Params p)
+{
+    constexpr int NP = SH::NP;
+    __shared__ FormLds<SH> L;
+    const Ix ix{p.n, p.m, p.N};
+    const int n = p.n, m = p.m, N = p.N;
+    const int b = blockIdx.x, w = blockIdx.y;
+    int w0, o0, o1;
+    if (p.win_own <= 0) {
+        w0 = 0;
+        o0 = 0;
+        o1 = N;
+    } else {
+        o0 = w * p.win_own;
+        o1 = min(o0 + p.win_own, N);
+        w0 = max(o0 - 2, 0);  // two knots of halo before, one after
+    }
+    const int nslot = min(o1 + 1, N) - w0;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP, k = w0 + s;
+    const bool own = s < nslot && k >= o0 && k < o1;
+    Rows<SH> rw;
+    int fl = 0;
+    form<SH>(
+        p, b, w0, nslot, L, rw, fl,
+        [&](const float* qi) {
+            if (own && i < n)
+#pragma unroll
+                for (int c = 0; c < SH::NC; ++c)
+                    if (c < n) p.Qinv[ix.Q(b, k, i, c)] = qi[c];
+        },
+        [&](const float* ri) {
+            if (own && k < N - 1 && i < m)
+#pragma unroll
+                for (int c = 0; c < SH::MC; ++c)
+                    if (c < m) p.Rinv[ix.R(b, k, i, c)] = ri[c];
+        });
+    if (own && i < n) {
+#pragma unroll
+        for (int c = 0; c < SH::NC; ++c) {
+            if (c < n) {
+                p.S[ix.blk(b, k, 0, i, c)] = rw.slo[c];
+                p.S[ix.blk(b, k, 1, i, c)] = rw.sd[c];
+                p.S[ix.blk(b, k, 2, i, c)] = rw.sup[c];
+                p.Pinv[ix.blk(b, k, 0, i, c)] = rw.plo[c];
+                p.Pinv[ix.blk(b, k, 1, i, c)] = rw.pd[c];
+                p.Pinv[ix.blk(b, k, 2, i, c)] = rw.pup[c];
+            }
+        }
+        p.gamma[ix.vn(b, k, i)] = rw.gam;
+    }
+    if (own && i == 0 && fl) atomicOr(p.flags + b, fl);
+}
+
+// ------------------------------------------------------------------ stage 2 alone
+
+template <class SH, typename RT, int C, class MAT>
+__device__ __forceinline__ void pcg_and_recover(const Params& p, const MAT& M, PcgLds<SH, RT, C>& L,
+                                                const float* gam, float* lam)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, SL = SH::SLOTS, KK = PcgLds<SH, RT, C>::K;
+    const Ix ix{p.n, p.m, p.N};
+    const int b = blockIdx.x;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP;
+    int it = 0, pfl = 0;
+    float rel = 0.0f;
+    pcg<SH, RT, C>(p, M, gam, lam, L, it, rel, pfl);
+#pragma unroll
+    for (int c = 0; c < C; ++c) L.xv[c * SL + s][i] = lam[c];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int k = c * SL + s;
+        const float lamn = (k + 1 < KK) ? L.xv[k + 1][i] : 0.0f;
+        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < p.n;
+        float qi[NC], ri[MC];
+#pragma unroll
+        for (int t = 0; t < NC; ++t) qi[t] = (rowv && t < p.n) ? p.Qinv[ix.Q(b, k, i, t)] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < MC; ++t) ri[t] = (hn && i < p.m && t < p.m) ? p.Rinv[ix.R(b, k, i, t)] : 0.0f;
+        float dx, du;
+        recover<SH>(p, b, k, i, lam[c], lamn, qi, ri, dx, du);
+        if (rowv) {
+            p.lambda[ix.vn(b, k, i)] = lam[c];
+            p.dz[ix.dx(b, k, i)] = dx;
+        }
+        if (hn && i < p.m) p.dz[ix.du(b, k, i)] = du;
+    }
+    if (threadIdx.x == 0) {
+        p.iters[b] = it;
+        p.relres[b] = rel;
+        if (pfl) p.flags[b] |= pfl;
+    }
+}
+
+template <class SH, typename RT>
+__global__ __launch_bounds__(SH::THREADS) void k_pcg_res(Params p)
+{
+    constexpr int NP = SH::NP, NC = SH::NC;
+    __shared__ PcgLds<SH, RT, 1> L;
+    const Ix ix{p.n, p.m, p.N};
+    const int b = blockIdx.x;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP, k = s;
+    const bool rowv = k < p.N && i < p.n;
+    Rows<SH> rw;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const bool v = rowv && c < p.n;
+        rw.slo[c] = v ? p.S[ix.blk(b, k, 0, i, c)] : 0.0f;
+        rw.sd[c] = v ? p.S[ix.blk(b, k, 1, i, c)] : 0.0f;
+        rw.sup[c] = v ? p.S[ix.blk(b, k, 2, i, c)] : 0.0f;
+        rw.plo[c] = v ? p.Pinv[ix.blk(b, k, 0, i, c)] : 0.0f;
+        rw.pd[c] = v ? p.Pinv[ix.blk(b, k, 1, i, c)] : 0.0f;
+        rw.pup[c] = v ? p.Pinv[ix.blk(b, k, 2, i, c)] : 0.0f;
+    }
+    rw.gam = rowv ? p.gamma[ix.vn(b, k, i)] : 0.0f;
+    float lam = rowv ? p.lambda[ix.vn(b, k, i)] : 0.0f;
+    const RegMat<SH> M{&rw};
+    pcg_and_recover<SH, RT, 1>(p, M, L, &rw.gam, &lam);
+}
+
+template <class SH, typename RT, int C>
+__global__ __launch_bounds__(SH::THREADS) void k_pcg_stream(Params p)
+{
+    constexpr int NP = SH::NP, SL = SH::SLOTS;
+    __shared__ PcgLds<SH, RT, C> L;
+    const Ix ix{p.n, p.m, p.N};
+    const int b = blockIdx.x;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP;
+    float gam[C], lam[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int k = c * SL + s;
+        const bool rowv = k < p.N && i < p.n;
+        gam[c] = rowv ? p.gamma[ix.vn(b, k, i)] : 0.0f;
+        lam[c] = rowv ? p.lambda[ix.vn(b, k, i)] : 0.0f;
+    }
+    const GlobalMat<SH> M{p.S, p.Pinv, ix, b, i};
+    pcg_and_recover<SH, RT, C>(p, M, L, gam, lam);
+}
+
+// ------------------------------------------------------------------ stage 3 alone
+
+template <class SH, int LPL>
+__global__ __launch_bounds__(1024) void k_merit(Params p)
+{
+    constexpr int NP = SH::NP, P = 16 * LPL;
+    __shared__ float mer[(GATO_MAX_ALPHA + 1) * P];
+    const Ix ix{p.n, p.m, p.N};
+    const int b = blockIdx.x;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP;
+    const int ks = blockDim.x / NP;
+    for (int t = threadIdx.x; t < (p.n_alpha + 1) * P; t += blockDim.x) mer[t] = 0.0f;
+    __syncthreads();
+    for (int c0 = 0; c0 < p.N; c0 += ks) {
+        const int k = c0 + s;
+        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < p.n;
+        const float dx = rowv ? p.dz[ix.dx(b, k, i)] : 0.0f;
+        const float du = (hn && i < p.m) ? p.dz[ix.du(b, k, i)] : 0.0f;
+        const float dxn = (hn && i < p.n) ? p.dz[ix.dx(b, k + 1, i)] : 0.0f;
+        merit_knot<SH>(p, b, k, i, dx, du, dxn, mer + (kv ? k : 0), P);
+    }
+    __syncthreads();
+    int32_t best;
+    int lsfail;
+    merit_select<LPL>(p, b, mer, P, best, lsfail);
+    if (threadIdx.x == 0) {
+        p.best[b] = best;
+        if (lsfail) p.flags[b] |= GATO_F_LS_FAILED;
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+using PcgRT = float;
+
+static int merit_waves_default(int N, int kpw)
+{
+    const char* env = std::getenv("GATO_MERIT_WAVES");
+    if (env) {
+        const int w = std::atoi(env);
+        if (w >= 1 && w <= 16) return w;
+    }
+    int w = (N + kpw - 1) / kpw;
+    return w < 1 ? 1 : (w > 16 ? 16 : w);
+}
+
+template <class SH>
+struct Ops {
+    static constexpr int SL = SH::SLOTS, KPW = SH::KPW;
+    static int threads_for(int knots) { return ((knots + KPW - 1) / KPW) * 64; }
+    static bool fused_ok(int N) { return N <= SL; }
+    static int stream_chunks(int N) { return N <= SL ? 1 : (N <= 2 * SL ? 2 : (N <= 4 * SL ? 4 : 0)); }
+
+    static hipError_t form(const Params& p, hipStream_t st)
+    {
+        Params q = p;
+        if (p.N <= SL) {
+            q.win_own = 0;
+        } else {
+            q.win_own = SL - 3;
+        }
+        const int nwin = q.win_own ? (p.N + q.win_own - 1) / q.win_own : 1;
+        const int threads = q.win_own ? SH::THREADS : threads_for(p.N);
+        hipLaunchKernelGGL(k_zero_i32, dim3((p.B + 255) / 256), dim3(256), 0, st, p.flags, p.B);
+        hipLaunchKernelGGL((k_form<SH>), dim3(p.B, nwin), dim3(threads), 0, st, q);
+        return hipGetLastError();
+    }
+    static hipError_t pcg(const Params& p, hipStream_t st)
+    {
+        const int C = stream_chunks(p.N);
+        if (C == 1) {
+            hipLaunchKernelGGL((k_pcg_res<SH, PcgRT>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
+        } else if (C == 2) {
+            hipLaunchKernelGGL((k_pcg_stream<SH, PcgRT, 2>), dim3(p.B), dim3(SH::THREADS), 0, st, p);
+        } else if (C == 4) {
+            hipLaunchKernelGGL((k_pcg_stream<SH, PcgRT, 4>), dim3(p.B), dim3(SH::THREADS), 0, st, p);
+        } else {
+            return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    static hipError_t merit(const Params& p, hipStream_t st)
+    {
+        const int P = leaves_for(p.N);
+        const int waves = merit_waves_default(p.N, KPW);
+        const dim3 g(p.B), blk(waves * 64);
+        switch (P / 16) {
+            case 4: hipLaunchKernelGGL((k_merit<SH, 4>), g, blk, 0, st, p); break;
+            case 8: hipLaunchKernelGGL((k_merit<SH, 8>), g, blk, 0, st, p); break;
+            case 16: hipLaunchKernelGGL((k_merit<SH, 16>), g, blk, 0, st, p); break;
+            case 32: hipLaunchKernelGGL((k_merit<SH, 32>), g, blk, 0, st, p); break;
+            case 64: hipLaunchKernelGGL((k_merit<SH, 64>), g, blk, 0, st, p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    static hipError_t fused(const Params& p, hipStream_t st)
+    {
+        hipLaunchKernelGGL((k_sqp_fused<SH, PcgRT>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
+        return hipGetLastError();
+    }
+    static bool supported(int N)
+    {
+        return N >= 1 && stream_chunks(N) != 0 && leaves_for(N) <= 1024;
+    }
+};
+
+// Shapes with kernels in this build: (n, m) of the configurations the
+// benchmark and tests use, plus n = m = 1 for hand-checkable examples.
+template <class F>
+static int with_shape(int n, int m, F&& f)
+{
+    if (n == 14 && m == 7) return f(Ops<Shape<14, 7>>{});
+    if (n == 12 && m == 6) return f(Ops<Shape<12, 6>>{});
+    if (n == 24 && m == 12) return f(Ops<Shape<24, 12>>{});
+    if (n == 4 && m == 2) return f(Ops<Shape<4, 2>>{});
+    if (n == 1 && m == 1) return f(Ops<Shape<1, 1>>{});
+    return GATO_E_UNSUPPORTED;
+}
+
+static bool aligned4(const void* ptr) { return ((uintptr_t)ptr & 3u) == 0; }
+
+static int check_ptrs(std::initializer_list<const void*> req)
+{
+    for (const void* x : req)
+        if (x == nullptr) return GATO_E_NULL;
+    for (const void* x : req)
+        if (!aligned4(x)) return GATO_E_ALIGN;
+    return GATO_OK;
+}
+
+static int check_dims(const gato_dims_t* d)
+{
+    if (d == nullptr) return GATO_E_NULL;
+    if (d->n < 1 || d->m < 1 || d->N < 1 || d->B < 0) return GATO_E_DIMS;
+    if (!gato_shape_supported(d->n, d->m, d->N)) return GATO_E_UNSUPPORTED;
+    return GATO_OK;
+}
+
+// Arrays indexed by the dynamics (R, r, A, Bu, e, Rinv) are empty when N = 1.
+static const void* dyn(const void* x, const gato_dims_t* d)
+{
+    static const int dummy = 0;
+    return (d->N == 1 && x == nullptr) ? &dummy : x;
+}
+
+static Params make_params(const gato_dims_t* d)
+{
+    Params p;
+    std::memset(&p, 0, sizeof(p));
+    p.n = d->n;
+    p.m = d->m;
+    p.N = d->N;
+    p.B = d->B;
+    return p;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t S, Pinv, gamma, Qinv, Rinv, total;
+};
+
+static WsLayout ws_layout(const gato_dims_t* d)
+{
+    const size_t B = d->B, N = d->N, n = d->n, m = d->m;
+    WsLayout w;
+    size_t off = 0;
+    w.S = off;
+    off += align256(B * N * 3 * n * n * sizeof(float));
+    w.Pinv = off;
+    off += align256(B * N * 3 * n * n * sizeof(float));
+    w.gamma = off;
+    off += align256(B * N * n * sizeof(float));
+    w.Qinv = off;
+    off += align256(B * N * n * n * sizeof(float));
+    w.Rinv = off;
+    off += align256(B * (N > 1 ? N - 1 : 1) * m * m * sizeof(float));
+    w.total = off;
+    return w;
+}
+
+static bool fused_path(const gato_dims_t* d)
+{
+    return with_shape(d->n, d->m, [&](auto ops) { return decltype(ops)::fused_ok(d->N) ? 1 : 0; }) == 1;
+}
+
+}  // namespace gato
+
+using namespace gato;
+
+extern "C" {
+
+int gato_shape_supported(int32_t n, int32_t m, int32_t N)
+{
+    if (n < 1 || m < 1 || N < 1) return 0;
+    const int r = with_shape(n, m, [&](auto ops) { return decltype(ops)::supported(N) ? 1 : 0; });
+    return r == 1;
+}
+
+const char* gato_status_string(int code)
+{
+    switch (code) {
+        case GATO_OK: return "ok";
+        case GATO_E_NULL: return "a required pointer is NULL";
+        case GATO_E_DIMS: return "dimensions out of range";
+        case GATO_E_ALIGN: return "a pointer is not 4-byte aligned";
+        case GATO_E_PARAM: return "a scalar parameter is out of range";
+        case GATO_E_HIP: return "a HIP launch failed";
+        case GATO_E_UNSUPPORTED: return "no kernel for this (n, m, N) in this build";
+        case GATO_E_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status code";
+    }
+}
+
+size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha)
+{
+    (void)n_alpha;
+    if (check_dims(dims) != GATO_OK || dims->B == 0) return 0;
+    if (fused_path(dims)) return 0;
+    return ws_layout(dims).total;
+}
+
+int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                    const float* r, const float* A, const float* Bu, const float* e,
+                    const float* x0, const float* rho, float* S, float* Pinv, float* gamma,
+                    float* Qinv, float* Rinv, int32_t* flags, hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
+    rc = check_ptrs({Q, q, dyn(R, dims), dyn(r, dims), dyn(A, dims), dyn(Bu, dims), dyn(e, dims), x0, S,
+                     Pinv, gamma, Qinv, dyn(Rinv, dims), flags});
+    if (rc) return rc;
+    if (rho && !aligned4(rho)) return GATO_E_ALIGN;
+    Params p = make_params(dims);
+    p.Q = Q; p.q = q; p.R = R; p.r = r; p.A = A; p.Bu = Bu; p.e = e; p.x0 = x0; p.rho = rho;
+    p.S = S; p.Pinv = Pinv; p.gamma = gamma; p.Qinv = Qinv; p.Rinv = Rinv; p.flags = flags;
+    return with_shape(dims->n, dims->m, [&](auto ops) {
+        return decltype(ops)::form(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
+    });
+}
+
+int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
+                   const float* gamma, const float* Qinv, const float* Rinv, const float* A,
+                   const float* Bu, const float* q, const float* r, float eps, int32_t max_iters,
+                   float* lambda, float* dz, int32_t* iters, float* relres, int32_t* flags,
+                   hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
+    rc = check_ptrs({S, Pinv, gamma, Qinv, dyn(Rinv, dims), dyn(A, dims), dyn(Bu, dims), q, dyn(r, dims),
+                     lambda, dz, iters, relres, flags});
+    if (rc) return rc;
+    if (!(eps > 0.0f) || max_iters < 1) return GATO_E_PARAM;
+    Params p = make_params(dims);
+    p.S = const_cast<float*>(S); p.Pinv = const_cast<float*>(Pinv); p.gamma = const_cast<float*>(gamma);
+    p.Qinv = const_cast<float*>(Qinv); p.Rinv = const_cast<float*>(Rinv);
+    p.A = A; p.Bu = Bu; p.q = q; p.r = r;
+    p.eps = eps; p.max_iters = max_iters;
+    p.lambda = lambda; p.dz = dz; p.iters = iters; p.relres = relres; p.flags = flags;
+    return with_shape(dims->n, dims->m, [&](auto ops) {
+        return decltype(ops)::pcg(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
+    });
+}
+
+static int check_alpha(const float* alphas_host, int32_t n_alpha, float mu)
+{
+    if (alphas_host == nullptr) return GATO_E_NULL;
+    if (n_alpha < 1 || n_alpha > GATO_MAX_ALPHA) return GATO_E_PARAM;
+    if (!(mu >= 0.0f)) return GATO_E_PARAM;
+    return GATO_OK;
+}
+
+int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                    const float* r, const float* A, const float* Bu, const float* e,
+                    const float* x0, const float* dz, const float* alphas_host, int32_t n_alpha,
+                    float mu, float* merit, float* merit0, int32_t* best, int32_t* flags,
+                    hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
+    rc = check_ptrs({Q, q, dyn(R, dims), dyn(r, dims), dyn(A, dims), dyn(Bu, dims), dyn(e, dims), x0, dz,
+                     merit, merit0, best, flags});
+    if (rc) return rc;
+    rc = check_alpha(alphas_host, n_alpha, mu);
+    if (rc) return rc;
+    Params p = make_params(dims);
+    p.Q = Q; p.q = q; p.R = R; p.r = r; p.A = A; p.Bu = Bu; p.e = e; p.x0 = x0;
+    p.dz = const_cast<float*>(dz);
+    p.mu = mu; p.n_alpha = n_alpha;
+    for (int j = 0; j < n_alpha; ++j) p.alphas[j] = alphas_host[j];
+    p.merit = merit; p.merit0 = merit0; p.best = best; p.flags = flags;
+    return with_shape(dims->n, dims->m, [&](auto ops) {
+        return decltype(ops)::merit(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
+    });
+}
+
+int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                  const float* r, const float* A, const float* Bu, const float* e,
+                  const float* x0, const float* rho, float eps, int32_t max_iters,
+                  const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
+                  float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
+                  int32_t* flags, void* workspace, size_t workspace_bytes,
+                  gato_stage_times_t* times, hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
+    rc = check_ptrs({Q, q, dyn(R, dims), dyn(r, dims), dyn(A, dims), dyn(Bu, dims), dyn(e, dims), x0, lambda,
+                     dz, merit, merit0, best, iters, relres, flags});
+    if (rc) return rc;
+    if (rho && !aligned4(rho)) return GATO_E_ALIGN;
+    if (!(eps > 0.0f) || max_iters < 1) return GATO_E_PARAM;
+    rc = check_alpha(alphas_host, n_alpha, mu);
+    if (rc) return rc;
+    const bool fused = fused_path(dims);
+    const WsLayout wl = ws_layout(dims);
+    if (!fused && dims->B > 0) {
+        if (workspace == nullptr || workspace_bytes < wl.total) return GATO_E_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return GATO_E_ALIGN;
+    }
+    Params p = make_params(dims);
+    p.Q = Q; p.q = q; p.R = R; p.r = r; p.A = A; p.Bu = Bu; p.e = e; p.x0 = x0; p.rho = rho;
+    p.eps = eps; p.max_iters = max_iters; p.mu = mu; p.n_alpha = n_alpha;
+    for (int j = 0; j < n_alpha; ++j) p.alphas[j] = alphas_host[j];
+    p.lambda = lambda; p.dz = dz; p.merit = merit; p.merit0 = merit0; p.best = best;
+    p.iters = iters; p.relres = relres; p.flags = flags;
+    if (!fused) {
+        char* ws = static_cast<char*>(workspace);
+        p.S = reinterpret_cast<float*>(ws + wl.S);
+        p.Pinv = reinterpret_cast<float*>(ws + wl.Pinv);
+        p.gamma = reinterpret_cast<float*>(ws + wl.gamma);
+        p.Qinv = reinterpret_cast<float*>(ws + wl.Qinv);
+        p.Rinv = reinterpret_cast<float*>(ws + wl.Rinv);
+    }
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    bool ev_ok = true;
+    if (times) {
+        for (auto& x : ev) ev_ok = ev_ok && hipEventCreate(&x) == hipSuccess;
+        ev_ok = ev_ok && hipEventRecord(ev[0], stream) == hipSuccess;
+        if (!ev_ok) {
+            for (auto& x : ev)
+                if (x) (void)hipEventDestroy(x);
+            return GATO_E_HIP;
+        }
+    }
+    rc = with_shape(dims->n, dims->m, [&](auto ops) {
+        using O = decltype(ops);
+        if (fused) return O::fused(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
+        if (O::form(p, stream) != hipSuccess) return GATO_E_HIP;
+        if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
+        if (O::pcg(p, stream) != hipSuccess) return GATO_E_HIP;
+        if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
+        if (O::merit(p, stream) != hipSuccess) return GATO_E_HIP;
+        return GATO_OK;
+    });
+    if (times) {
+        float t = 0.0f;
+        bool ok = rc == GATO_OK && hipEventRecord(ev[3], stream) == hipSuccess &&
+                  hipEventSynchronize(ev[3]) == hipSuccess && hipEventElapsedTime(&t, ev[0], ev[3]) == hipSuccess;
+        times->total_us = ok ? 1000.0f * t : -1.0f;
+        // one fused kernel: the stages are not separable in time
+        times->schur_us = times->linsys_us = times->merit_us = -1.0f;
+        if (ok && !fused) {
+            if (hipEventElapsedTime(&t, ev[0], ev[1]) == hipSuccess) times->schur_us = 1000.0f * t;
+            if (hipEventElapsedTime(&t, ev[1], ev[2]) == hipSuccess) times->linsys_us = 1000.0f * t;
+            if (hipEventElapsedTime(&t, ev[2], ev[3]) == hipSuccess) times->merit_us = 1000.0f * t;
+        }
+        for (auto& x : ev) (void)hipEventDestroy(x);
+        if (rc == GATO_OK && !ok) rc = GATO_E_HIP;
+    }
+    return rc;
+}
+
+}  // extern "C"

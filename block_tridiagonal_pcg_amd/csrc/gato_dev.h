@@ -1,0 +1,268 @@
+// gato_dev.h -- lane-level building blocks for the gfx950 kernels.
+//
+// Data layout inside a workgroup: every knot point owns one group of NP lanes
+// (NP = 16 for n <= 16, NP = 32 for n <= 32); lane i of the group holds row i
+// of that knot's blocks in registers.  A wave64 therefore holds 64/NP knots.
+// Products of the small per-knot blocks broadcast a value of lane l of the
+// group to the whole group with the DPP `row_newbcast` control, folded into the
+// multiply-add (see dpp_asm.inc), so the block-dense linear algebra of one knot
+// needs no LDS traffic.  For NP = 32 a group spans two DPP rows; a broadcast
+// then reads from a copy in which V_PERMLANE16_SWAP has duplicated the lower
+// (or upper) row of the group into both rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gato {
+
+#include "dpp_asm.inc"
+
+// Compile-time shape of one instantiation.
+//   NC, MC: loop bounds for states and controls (runtime n <= NC, m <= MC;
+//           rows/columns beyond n, m are zero and padded diagonals are one).
+//   NP:     lanes per knot; SLOTS: knots one workgroup holds.
+template <int NC_, int MC_>
+struct Shape {
+    static constexpr int NC = NC_;
+    static constexpr int MC = MC_;
+    static constexpr int NP = NC_ <= 16 ? 16 : 32;
+    static constexpr int KPW = 64 / NP;
+    static constexpr int SLOTS = NP == 16 ? 64 : 16;
+    static constexpr int THREADS = SLOTS * NP;
+    static_assert(MC_ <= NC_ || MC_ <= NP, "controls must fit in a knot's lane group");
+};
+
+// ------------------------------------------------------------------ DPP moves
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x)
+{
+    const int lo = __double2loint(x), hi = __double2hiint(x);
+    const int l2 = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false);
+    const int h2 = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false);
+    return __hiloint2double(h2, l2);
+}
+
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp(T x)
+{
+    if constexpr (sizeof(T) == 8) return dpp_d<CTRL>(x);
+    else return dpp_f<CTRL>(x);
+}
+
+constexpr int DPP_QP_1032 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QP_2301 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+
+// Duplicate the even (lo) and odd (hi) 16-lane rows of every 32-lane pair.
+__device__ __forceinline__ void dup_rows(float x, float& lo, float& hi)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ double pair_other(double x, bool upper)
+{
+    // value of the same lane in the other row of the 32-lane pair
+    float lo0, hi0, lo1, hi1;
+    dup_rows(__int_as_float(__double2loint(x)), lo0, hi0);
+    dup_rows(__int_as_float(__double2hiint(x)), lo1, hi1);
+    const float l = upper ? lo0 : hi0, h = upper ? lo1 : hi1;
+    return __hiloint2double(__float_as_int(h), __float_as_int(l));
+}
+
+// Sum over the 16 lanes of each DPP row as the canonical pairwise tree
+// ((x0+x1)+(x2+x3)) + ... ; every lane of the row ends with identical bits
+// (each step adds a lane's value to its partner's, and IEEE addition commutes).
+template <typename T>
+__device__ __forceinline__ T rowsum16(T x)
+{
+    x = x + dpp<DPP_QP_1032>(x);
+    x = x + dpp<DPP_QP_2301>(x);
+    x = x + dpp<DPP_ROW_HALF_MIRROR>(x);
+    x = x + dpp<DPP_ROW_MIRROR>(x);
+    return x;
+}
+
+// Sum over the NP lanes of a knot group (canonical tree over NP leaves).
+template <int NP, typename T>
+__device__ __forceinline__ T groupsum(T x)
+{
+    x = rowsum16(x);
+    if constexpr (NP == 32) {
+        if constexpr (sizeof(T) == 8) {
+            const bool upper = (threadIdx.x & 16) != 0;
+            const T o = pair_other(x, upper);
+            x = upper ? o + x : x + o;  // lower row's sum first, in both rows
+        } else {
+            float lo, hi;
+            dup_rows(x, lo, hi);
+            x = lo + hi;
+        }
+    }
+    return x;
+}
+
+// Canonical pairwise sum of P = 16 * L leaves held in LDS (zero-padded).
+// Lane j of each 16-lane row sums leaves [j L, (j+1) L) as a pairwise tree,
+// then the rows' butterflies combine the 16 partial sums.  The result is the
+// pairwise tree over the P leaves and does not depend on which kernel, block
+// shape or wave computes it; with zero padding it equals the pairwise tree
+// over the smallest power of two >= the number of real leaves.
+template <int L, typename T>
+__device__ __forceinline__ T canon_sum(const T* leaves, int stride = 1)
+{
+    const int j = threadIdx.x & 15;
+    T v[L];
+#pragma unroll
+    for (int t = 0; t < L; ++t) v[t] = leaves[(j * L + t) * stride];
+#pragma unroll
+    for (int w = 1; w < L; w *= 2)
+#pragma unroll
+        for (int t = 0; t < L; t += 2 * w) v[t] = v[t] + v[t + w];
+    return rowsum16(v[0]);
+}
+
+// ------------------------------------------------------------------ broadcast sources
+
+// A value to be broadcast from any lane of a knot group.
+template <int NP>
+struct Bc;
+template <>
+struct Bc<16> {
+    float lo;
+    __device__ __forceinline__ explicit Bc(float x) : lo(x) {}
+};
+template <>
+struct Bc<32> {
+    float lo, hi;
+    __device__ __forceinline__ explicit Bc(float x) { dup_rows(x, lo, hi); }
+};
+
+// acc += sum_{c < K} x(lane c) * row[c]
+template <int NP, int K>
+__device__ __forceinline__ void dotb(float& acc, const Bc<NP>& x, const float* row)
+{
+    if constexpr (NP == 16) {
+        static_assert(K <= 16, "");
+        bcA<K>(acc, x.lo, row);
+    } else {
+        static_assert(K <= 32, "");
+        bcA<(K < 16 ? K : 16)>(acc, x.lo, row);
+        if constexpr (K > 16) bcA<K - 16>(acc, x.hi, row + 16);
+    }
+}
+
+// Row arrays to be broadcast from a fixed lane (one register per column).
+template <int NP, int K>
+struct BcRow;
+template <int K>
+struct BcRow<16, K> {
+    float lo[K];
+    __device__ __forceinline__ explicit BcRow(const float* x)
+    {
+#pragma unroll
+        for (int c = 0; c < K; ++c) lo[c] = x[c];
+    }
+};
+template <int K>
+struct BcRow<32, K> {
+    float lo[K], hi[K];
+    __device__ __forceinline__ explicit BcRow(const float* x)
+    {
+#pragma unroll
+        for (int c = 0; c < K; ++c) dup_rows(x[c], lo[c], hi[c]);
+    }
+};
+
+template <int K, int L>
+__device__ __forceinline__ void bcB_chunks(float* acc, const float* src, float mul)
+{
+    if constexpr (K <= 16) {
+        BcB<K>::template run<L>(acc, src, mul);
+    } else {
+        BcB<16>::template run<L>(acc, src, mul);
+        bcB_chunks<K - 16, L>(acc + 16, src + 16, mul);
+    }
+}
+
+// acc[c] += x[c](lane L) * mul for c < K
+template <int NP, int K, int L>
+__device__ __forceinline__ void axpyb(float* acc, const BcRow<NP, K>& x, float mul)
+{
+    if constexpr (NP == 16) {
+        bcB_chunks<K, L>(acc, x.lo, mul);
+    } else {
+        if constexpr (L < 16) bcB_chunks<K, L>(acc, x.lo, mul);
+        else bcB_chunks<K, L - 16>(acc, x.hi, mul);
+    }
+}
+
+// acc[c] += sum_{l < KL} X[l][c] * mul[l], X's row l held by lane l (outer products).
+template <int NP, int K, int KL, int L = 0>
+__device__ __forceinline__ void gemm_rows(float* acc, const BcRow<NP, K>& x, const float* mul)
+{
+    if constexpr (L < KL) {
+        axpyb<NP, K, L>(acc, x, mul[L]);
+        gemm_rows<NP, K, KL, L + 1>(acc, x, mul);
+    }
+}
+
+// ------------------------------------------------------------------ in-place Gauss-Jordan
+
+// Inverse of the K x K matrix whose row i is held by lane i of the group
+// (rows beyond K are ignored), by Gauss-Jordan elimination without pivoting
+// (the matrices are symmetric positive definite, whose pivots are the positive
+// diagonal entries of their LDL' factor).  `bad` is set when a pivot is not
+// positive or not finite; the elimination then continues with the bad pivot
+// and the result is flagged, not repaired.
+//
+// Step j: every lane i != j subtracts A[i][j]/A[j][j] times row j, the pivot
+// row is scaled by 1/A[j][j], and column j becomes the matching column of the
+// inverse (the classical in-place form).  The pivot lane uses the same fused
+// update with multiplier (1/piv - 1), so all lanes run one instruction stream.
+template <int NP, int K, int J = 0>
+__device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
+{
+    if constexpr (J < K) {
+        float piv;
+        if constexpr (NP == 16 || J < 16) {
+            float lo = a[J];
+            if constexpr (NP == 32) {
+                float hi;
+                dup_rows(a[J], lo, hi);
+            }
+            piv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(lo), 0x150 + (J & 15), 0xF, 0xF, false));
+        } else {
+            float lo, hi;
+            dup_rows(a[J], lo, hi);
+            piv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(hi), 0x150 + (J & 15), 0xF, 0xF, false));
+        }
+        bad |= !(piv > 0.0f) || !__builtin_isfinite(piv);
+        const float inv = 1.0f / piv;
+        const bool me = lane == J;
+        const float f = a[J];
+        const float g = me ? (inv - 1.0f) : -(f * inv);
+        float keep = a[J];
+        if constexpr (NP == 16) {
+            BcBs<(K < 16 ? K : 16)>::template run<J & 15>(a, g);
+        } else {
+            BcRow<32, K> src(a);
+            axpyb<32, K, J>(a, src, g);
+        }
+        // column J of the inverse: -A[i][j]/piv off the pivot row, 1/piv on it
+        a[J] = me ? inv : -(keep * inv);
+        gj_steps<NP, K, J + 1>(a, lane, bad);
+    }
+}
+
+}  // namespace gato

@@ -1,0 +1,321 @@
+"""Thin ctypes binding of libgato.so (argument marshalling only).
+
+The functions carry the C ABI's names and argument order.  Array arguments are
+torch tensors on the GPU (float32 or int32, contiguous, in the layouts of
+include/gato.h); their data pointers and the current HIP stream are passed
+through unchanged.  Every step of the computation runs in the library's
+kernels.  Loading fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from ._build import LIB as _LIB_PATH
+
+GATO_MAX_ALPHA = 16
+
+OK = 0
+E_NULL, E_DIMS, E_ALIGN, E_PARAM, E_HIP, E_UNSUPPORTED, E_WORKSPACE = -1, -2, -3, -4, -5, -6, -7
+
+F_Q_NOT_SPD = 1
+F_R_NOT_SPD = 2
+F_S_NOT_SPD = 4
+F_PCG_MAXITER = 8
+F_PCG_BREAKDOWN = 16
+F_LS_FAILED = 32
+F_NONFINITE = 64
+
+EXPORTS = (
+    "gato_form_schur",
+    "gato_pcg_solve",
+    "gato_merit_eval",
+    "gato_sqp_step",
+    "gato_workspace_bytes",
+    "gato_status_string",
+    "gato_shape_supported",
+)
+
+
+class GatoError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(code), code))
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32), ("N", ctypes.c_int32), ("B", ctypes.c_int32)]
+
+
+class StageTimes(ctypes.Structure):
+    _fields_ = [("schur_us", ctypes.c_float), ("linsys_us", ctypes.c_float), ("merit_us", ctypes.c_float),
+                ("total_us", ctypes.c_float)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgato.so (raises if it is missing: there is no fallback path)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError("libgato.so is not built (%s); run __graft_entry__.build()" % _LIB_PATH)
+            lib = ctypes.CDLL(_LIB_PATH)
+            P, I, F, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+            lib.gato_form_schur.argtypes = [P] * 17
+            lib.gato_pcg_solve.argtypes = [P] * 10 + [F, I] + [P] * 6
+            lib.gato_merit_eval.argtypes = [P] * 11 + [I, F] + [P] * 5
+            lib.gato_sqp_step.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P]
+            lib.gato_workspace_bytes.argtypes = [P, I]
+            lib.gato_workspace_bytes.restype = Z
+            lib.gato_status_string.argtypes = [ctypes.c_int]
+            lib.gato_status_string.restype = ctypes.c_char_p
+            lib.gato_shape_supported.argtypes = [I, I, I]
+            for f in ("gato_form_schur", "gato_pcg_solve", "gato_merit_eval", "gato_sqp_step",
+                      "gato_shape_supported"):
+                getattr(lib, f).restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return load().gato_status_string(int(code)).decode()
+
+
+def _dims(n, m, N, B):
+    return Dims(int(n), int(m), int(N), int(B))
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _chk(t, name, dtype=torch.float32, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _shapes(n, m, N, B):
+    d = max(N - 1, 0)
+    return dict(Q=(B, N, n, n), q=(B, N, n), R=(B, d, m, m), r=(B, d, m), A=(B, d, n, n), Bu=(B, d, n, m),
+                e=(B, d, n), x0=(B, n), rho=(B,), S=(B, N, 3, n, n), Pinv=(B, N, 3, n, n), gamma=(B, N, n),
+                Qinv=(B, N, n, n), Rinv=(B, d, m, m), lam=(B, N, n), dz=(B, N * n + d * m), B_=(B,))
+
+
+def _raise(fn, rc):
+    if rc != OK:
+        raise GatoError(fn, rc)
+    return rc
+
+
+def gato_form_schur(dims, Q, q, R, r, A, Bu, e, x0, rho, S, Pinv, gamma, Qinv, Rinv, flags, stream=None):
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
+                 (rho, "rho"), (S, "S"), (Pinv, "Pinv"), (gamma, "gamma"), (Qinv, "Qinv"), (Rinv, "Rinv")):
+        _chk(t, k, shape=sh[k])
+    _chk(flags, "flags", torch.int32, sh["B_"])
+    d = _dims(n, m, N, B)
+    rc = load().gato_form_schur(ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0),
+                                _p(rho), _p(S), _p(Pinv), _p(gamma), _p(Qinv), _p(Rinv), _p(flags),
+                                _stream(stream))
+    return _raise("gato_form_schur", rc)
+
+
+def gato_pcg_solve(dims, S, Pinv, gamma, Qinv, Rinv, A, Bu, q, r, eps, max_iters, lam, dz, iters, relres,
+                   flags, stream=None):
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    for t, k in ((S, "S"), (Pinv, "Pinv"), (gamma, "gamma"), (Qinv, "Qinv"), (Rinv, "Rinv"), (A, "A"),
+                 (Bu, "Bu"), (q, "q"), (r, "r"), (lam, "lam"), (dz, "dz"), (relres, "B_")):
+        _chk(t, k, shape=sh[k])
+    _chk(iters, "iters", torch.int32, sh["B_"])
+    _chk(flags, "flags", torch.int32, sh["B_"])
+    d = _dims(n, m, N, B)
+    rc = load().gato_pcg_solve(ctypes.byref(d), _p(S), _p(Pinv), _p(gamma), _p(Qinv), _p(Rinv), _p(A), _p(Bu),
+                               _p(q), _p(r), float(eps), int(max_iters), _p(lam), _p(dz), _p(iters),
+                               _p(relres), _p(flags), _stream(stream))
+    return _raise("gato_pcg_solve", rc)
+
+
+def _alphas(alphas):
+    a = [float(x) for x in alphas]
+    arr = (ctypes.c_float * max(len(a), 1))(*a)
+    return arr, len(a)
+
+
+def gato_merit_eval(dims, Q, q, R, r, A, Bu, e, x0, dz, alphas, mu, merit, merit0, best, flags, stream=None):
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
+                 (dz, "dz"), (merit0, "B_")):
+        _chk(t, k, shape=sh[k])
+    arr, na = _alphas(alphas)
+    _chk(merit, "merit", shape=(B, na))
+    _chk(best, "best", torch.int32, sh["B_"])
+    _chk(flags, "flags", torch.int32, sh["B_"])
+    d = _dims(n, m, N, B)
+    rc = load().gato_merit_eval(ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0),
+                                _p(dz), arr, na, float(mu), _p(merit), _p(merit0), _p(best), _p(flags),
+                                _stream(stream))
+    return _raise("gato_merit_eval", rc)
+
+
+def gato_workspace_bytes(dims, n_alpha=8):
+    d = _dims(*dims)
+    return int(load().gato_workspace_bytes(ctypes.byref(d), int(n_alpha)))
+
+
+def gato_shape_supported(n, m, N):
+    return bool(load().gato_shape_supported(int(n), int(m), int(N)))
+
+
+def gato_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas, mu, lam, dz, merit, merit0,
+                  best, iters, relres, flags, workspace=None, times=False, stream=None):
+    """One SQP iteration's core.  `workspace` is a uint8 CUDA tensor (or None when the
+    fused path needs none); with times=True returns a StageTimes (the call synchronises)."""
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
+                 (rho, "rho"), (lam, "lam"), (dz, "dz"), (merit0, "B_"), (relres, "B_")):
+        _chk(t, k, shape=sh[k])
+    arr, na = _alphas(alphas)
+    _chk(merit, "merit", shape=(B, na))
+    for t, k in ((best, "best"), (iters, "iters"), (flags, "flags")):
+        _chk(t, k, torch.int32, sh["B_"])
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _chk(workspace, "workspace", torch.uint8)
+        ws_ptr, ws_bytes = _p(workspace), workspace.numel()
+    st = StageTimes() if times else None
+    d = _dims(n, m, N, B)
+    rc = load().gato_sqp_step(ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0),
+                              _p(rho), float(eps), int(max_iters), arr, na, float(mu), _p(lam), _p(dz),
+                              _p(merit), _p(merit0), _p(best), _p(iters), _p(relres), _p(flags), ws_ptr,
+                              ctypes.c_size_t(ws_bytes), ctypes.byref(st) if st is not None else None,
+                              _stream(stream))
+    _raise("gato_sqp_step", rc)
+    return st
+
+
+# ---------------------------------------------------------------- allocation helpers
+
+
+def to_device(batch, device="cuda"):
+    """Copy a synth batch (numpy float32 arrays) to the GPU as contiguous tensors."""
+    fields = ("Q", "q", "R", "r", "A", "Bu", "e", "x0")
+    out = {k: torch.from_numpy(batch[k]).to(device).contiguous() for k in fields}
+    out["dims"] = batch["dims"]
+    return out
+
+
+def workspace_for(dims, n_alpha=8, device="cuda"):
+    nb = gato_workspace_bytes(dims, n_alpha)
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb > 0 else None
+
+
+def alloc_outputs(dims, n_alpha=8, device="cuda"):
+    n, m, N, B = dims
+    f32, i32 = torch.float32, torch.int32
+    sh = _shapes(n, m, N, B)
+    z = lambda k, dt=f32: torch.zeros(sh[k], dtype=dt, device=device)  # noqa: E731
+    return dict(S=z("S"), Pinv=z("Pinv"), gamma=z("gamma"), Qinv=z("Qinv"), Rinv=z("Rinv"), lam=z("lam"),
+                dz=z("dz"), merit=torch.zeros((B, n_alpha), dtype=f32, device=device), merit0=z("B_"),
+                best=z("B_", i32), iters=z("B_", i32), relres=z("B_"), flags=z("B_", i32))
+
+
+def prepared_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas, mu, lam, dz, merit, merit0,
+                      best, iters, relres, flags, workspace=None, stream=None):
+    """Check and marshal gato_sqp_step's arguments once; return a callable that only
+    makes the C call (for timing loops).  The tensors must stay alive and in place."""
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
+                 (rho, "rho"), (lam, "lam"), (dz, "dz"), (merit0, "B_"), (relres, "B_")):
+        _chk(t, k, shape=sh[k])
+    arr, na = _alphas(alphas)
+    _chk(merit, "merit", shape=(B, na))
+    for t, k in ((best, "best"), (iters, "iters"), (flags, "flags")):
+        _chk(t, k, torch.int32, sh["B_"])
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _chk(workspace, "workspace", torch.uint8)
+        ws_ptr, ws_bytes = _p(workspace), workspace.numel()
+    d = _dims(n, m, N, B)
+    fn = load().gato_sqp_step
+    args = (ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0), _p(rho), float(eps),
+            int(max_iters), arr, na, float(mu), _p(lam), _p(dz), _p(merit), _p(merit0), _p(best), _p(iters),
+            _p(relres), _p(flags), ws_ptr, ctypes.c_size_t(ws_bytes), None, _stream(stream))
+    keep = (d, arr)  # noqa: F841  (kept alive by the closure)
+
+    def call():
+        rc = fn(*args)
+        if rc != OK:
+            raise GatoError("gato_sqp_step", rc)
+        return keep
+
+    return call
+
+
+def stage_times(dims, dev, eps, max_iters, alphas, mu, reps=10, stream=None):
+    """Median device time (us) of the three standalone calls on `dev` (a to_device batch):
+    gato_form_schur, gato_pcg_solve (cold start), gato_merit_eval."""
+    import statistics
+
+    st = torch.cuda.current_stream() if stream is None else stream
+    out = alloc_outputs(dims, len(alphas))
+    fields = ("Q", "q", "R", "r", "A", "Bu", "e", "x0")
+    res = {"schur_us": [], "linsys_us": [], "merit_us": []}
+    for _ in range(reps + 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(st)
+        gato_form_schur(dims, *[dev[f] for f in fields], None, out["S"], out["Pinv"], out["gamma"], out["Qinv"],
+                        out["Rinv"], out["flags"], stream=st)
+        ev[1].record(st)
+        out["lam"].zero_()
+        ev[2].record(st)
+        gato_pcg_solve(dims, out["S"], out["Pinv"], out["gamma"], out["Qinv"], out["Rinv"], dev["A"], dev["Bu"],
+                       dev["q"], dev["r"], eps, max_iters, out["lam"], out["dz"], out["iters"], out["relres"],
+                       out["flags"], stream=st)
+        ev[3].record(st)
+        ev[4].record(st)
+        gato_merit_eval(dims, *[dev[f] for f in fields], out["dz"], alphas, mu, out["merit"], out["merit0"],
+                        out["best"], out["flags"], stream=st)
+        ev[5].record(st)
+        torch.cuda.synchronize()
+        res["schur_us"].append(1e3 * ev[0].elapsed_time(ev[1]))
+        res["linsys_us"].append(1e3 * ev[2].elapsed_time(ev[3]))
+        res["merit_us"].append(1e3 * ev[4].elapsed_time(ev[5]))
+    return {k: statistics.median(v[1:]) for k, v in res.items()}

@@ -1,0 +1,202 @@
+/*
+ * gato.h -- C ABI of libgato.so: one SQP iteration's linear-algebra core over
+ * a batch of independent LQ subproblems, on one AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one "GATO: GPU-Accelerated and Batched Trajectory
+ * Optimization for Scalable Edge Model Predictive Control" (arXiv 2510.07625)
+ * describes in Sec. II-III:
+ *   (1) form the block-tridiagonal Schur complement S, the vector gamma and the
+ *       symmetric stair preconditioner Phi^-1 from the QP data (eqs. 4-6);
+ *   (2) solve S lambda = gamma by preconditioned conjugate gradient, one solve
+ *       per workgroup, and recover the primal step dz;
+ *   (3) evaluate the L1 merit function at the line-search step sizes for every
+ *       knot and solve and reduce them (eqs. 3 and 7).
+ *
+ * ---------------------------------------------------------------- problem
+ * Per solve b (B solves, N knot points, n states, m controls), the QP is
+ *   min  sum_{k<N} 1/2 dx_k'(Q_k + rho_b I)dx_k + q_k'dx_k
+ *      + sum_{k<N-1} 1/2 du_k'R_k du_k + r_k'du_k
+ *   s.t. dx_0 = x0,  dx_{k+1} = A_k dx_k + B_k du_k + e_k   (k < N-1),
+ * with e_k = f(x_k,u_k,h) - x_{k+1} the dynamics defect (GATO paper Sec. II,
+ * Step 1).  The pages number states x_0..x_N; here N counts knot points, so
+ * states are x_0..x_{N-1} and controls u_0..u_{N-2}.
+ *
+ * ---------------------------------------------------------------- layouts
+ * Every array is fp32, row-major, batch-major, contiguous and unpadded
+ * (the dense contiguous packing by batch and knot of the paper's Sec. III):
+ *   Q    [B][N][n][n]      q   [B][N][n]
+ *   R    [B][N-1][m][m]    r   [B][N-1][m]
+ *   A    [B][N-1][n][n]    Bu  [B][N-1][n][m]    e [B][N-1][n]    x0 [B][n]
+ *   rho  [B]  (nullable: no damping)
+ *   S, Pinv [B][N][3][n][n]  block row k = [X_{k,k-1}, X_{k,k}, X_{k,k+1}];
+ *                            out-of-range blocks (k = 0 left, k = N-1 right)
+ *                            are written as zeros
+ *   gamma, lambda [B][N][n]   Qinv [B][N][n][n]   Rinv [B][N-1][m][m]
+ *   dz   [B][N*n + (N-1)*m]  ordered dx_0, du_0, dx_1, du_1, ..., dx_{N-1}
+ *                            (dz_k = [dx_k du_k], the paper's Step 2 ordering)
+ *   merit [B][n_alpha]   merit0 [B]   best [B] (int32)
+ *   iters [B] (int32)    relres [B]   flags [B] (int32, GATO_F_* bits)
+ *
+ * ---------------------------------------------------------------- ownership
+ * All array arguments except alphas_host are device pointers owned by the
+ * caller (e.g. from torch tensors); the library never allocates, frees or
+ * copies host<->device inside a call.  alphas_host is a host array of at most
+ * GATO_MAX_ALPHA floats, copied by value into the launch.  Outputs must not
+ * alias inputs, except lambda, which is read (warm start) and written.
+ *
+ * ---------------------------------------------------------------- streams
+ * Every call only enqueues work on `stream` and returns; outputs are valid
+ * after the stream is synchronised.  Exception: gato_sqp_step with a non-NULL
+ * `times` records events and synchronises the stream before returning.
+ *
+ * ---------------------------------------------------------------- errors
+ * Host-side validation runs before anything is enqueued and returns a
+ * negative GATO_E_* code (nothing enqueued) for: a NULL required pointer,
+ * dims < 1, a shape (n, m, N) this build
+ * has no kernel for (GATO_E_UNSUPPORTED), a pointer not 4-byte aligned,
+ * eps <= 0, max_iters < 1, n_alpha outside [1, GATO_MAX_ALPHA], mu < 0 or a
+ * workspace smaller than gato_workspace_bytes().  B = 0 returns GATO_OK
+ * once the dims are valid, before any pointer is looked at (empty tensors may
+ * have NULL data).  With N = 1 the arrays indexed by the dynamics (R, r, A,
+ * Bu, e, Rinv) are empty and may be NULL.  A failed launch returns
+ * GATO_E_HIP.  Numerical trouble never makes a call fail: it sets per-solve
+ * flag bits and the solve's outputs are still written (a failed pivot is
+ * flagged, not repaired).  gato_form_schur and gato_sqp_step set flags[b];
+ * gato_pcg_solve and gato_merit_eval OR their bits into it.
+ *
+ * The library keeps no global mutable state: calls on different streams or
+ * threads are independent.
+ */
+#ifndef GATO_H
+#define GATO_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GATO_MAX_ALPHA 16
+
+typedef struct {
+    int32_t n; /* states per knot */
+    int32_t m; /* controls per knot */
+    int32_t N; /* knot points (horizon) */
+    int32_t B; /* independent solves in the batch */
+} gato_dims_t;
+
+/* Device time per stage of gato_sqp_step, in microseconds (the stage split
+ * of the GATO docs' solver statistics: schur / linsys / merit). */
+typedef struct {
+    float schur_us;
+    float linsys_us;
+    float merit_us;
+    float total_us;
+} gato_stage_times_t;
+
+enum {
+    GATO_OK = 0,
+    GATO_E_NULL = -1,
+    GATO_E_DIMS = -2,
+    GATO_E_ALIGN = -3,
+    GATO_E_PARAM = -4,
+    GATO_E_HIP = -5,
+    GATO_E_UNSUPPORTED = -6,
+    GATO_E_WORKSPACE = -7
+};
+
+enum {
+    GATO_F_Q_NOT_SPD = 1,       /* a pivot of Q_k + rho I was not positive */
+    GATO_F_R_NOT_SPD = 2,       /* a pivot of R_k was not positive */
+    GATO_F_S_NOT_SPD = 4,       /* a pivot of a diagonal Schur block D_k was not positive */
+    GATO_F_PCG_MAXITER = 8,     /* PCG stopped at max_iters without meeting eps */
+    GATO_F_PCG_BREAKDOWN = 16,  /* p'S p <= 0 in PCG */
+    GATO_F_LS_FAILED = 32,      /* no step size lowered the merit below merit0 */
+    GATO_F_NONFINITE = 64       /* a PCG reduction was not finite */
+};
+
+/*
+ * Stage 1 (GATO paper Sec. II eqs. 4-6; setup kernel of Sec. III).
+ * With Q~_k = Q_k + rho_b I:
+ *   Qinv_k = Q~_k^-1, Rinv_k = R_k^-1;
+ *   D_0 = Q~_0^-1,  D_{k+1} = A_k Q~_k^-1 A_k' + B_k R_k^-1 B_k' + Q~_{k+1}^-1;
+ *   S_{k,k+1} = -Q~_k^-1 A_k' = S_{k+1,k}';
+ *   gamma_0 = x0 + Q~_0^-1 q_0,
+ *   gamma_{k+1} = e_k - A_k Q~_k^-1 q_k - B_k R_k^-1 r_k + Q~_{k+1}^-1 q_{k+1};
+ *   Phi^-1_{k,k} = D_k^-1,  Phi^-1_{k,k+1} = -D_k^-1 S_{k,k+1} D_{k+1}^-1 = Phi^-1_{k+1,k}'.
+ * Writes S, Pinv, gamma, Qinv, Rinv and flags (Q/R/S_NOT_SPD bits).
+ */
+int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                    const float* r, const float* A, const float* Bu, const float* e,
+                    const float* x0, const float* rho, float* S, float* Pinv, float* gamma,
+                    float* Qinv, float* Rinv, int32_t* flags, hipStream_t stream);
+
+/*
+ * Stage 2 (GATO paper Sec. II, PCG on S lambda = gamma; batched solver of
+ * Sec. III, one workgroup per solve).  From lambda (in) as the starting point:
+ *   r = gamma - S lambda; z = Phi^-1 r; p = z; eta = r'z; then per iteration
+ *   v = S p; a = eta / p'v; lambda += a p; r -= a v;
+ *   stop when ||r||_2 <= eps ||gamma||_2;  z = Phi^-1 r; p = z + (r'z / eta) p.
+ * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  Then the step
+ *   dx_k = Qinv_k (lambda_k - A_k' lambda_{k+1} - q_k),  dx_{N-1} = Qinv_{N-1}(lambda_{N-1} - q_{N-1}),
+ *   du_k = Rinv_k (-B_k' lambda_{k+1} - r_k).
+ * Writes lambda, dz, iters (S-products in the loop), relres (recurred
+ * ||r|| / ||gamma||) and ORs PCG_MAXITER / PCG_BREAKDOWN / NONFINITE into flags.
+ */
+int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
+                   const float* gamma, const float* Qinv, const float* Rinv, const float* A,
+                   const float* Bu, const float* q, const float* r, float eps, int32_t max_iters,
+                   float* lambda, float* dz, int32_t* iters, float* relres, int32_t* flags,
+                   hipStream_t stream);
+
+/*
+ * Stage 3 (GATO paper Sec. II eq. 3, Sec. III eq. 7; the merit kernel of the
+ * GATO docs' "Merit launch timing").  For every solve, knot and step size a:
+ *   m_k(a) = a (q_k'dx_k + r_k'du_k) + a^2/2 (dx_k'Q_k dx_k + du_k'R_k du_k)
+ *          + mu ||e_k + a (A_k dx_k + B_k du_k - dx_{k+1})||_1   (k < N-1)
+ *          + [k = 0] mu ||x0 - a dx_0||_1,
+ * (undamped Q: rho regularises the step, not the merit), summed over knots in
+ * a fixed pairwise order that does not depend on the launch shape, so results
+ * are bit-identical for any workgroup size.  merit0 = M(0) = mu ||c||_1.
+ * best = argmin_i merit[i] (ties to the smaller i) if below merit0, else -1
+ * and LS_FAILED is ORed into flags.
+ */
+int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                    const float* r, const float* A, const float* Bu, const float* e,
+                    const float* x0, const float* dz, const float* alphas_host, int32_t n_alpha,
+                    float mu, float* merit, float* merit0, int32_t* best, int32_t* flags,
+                    hipStream_t stream);
+
+/*
+ * The three stages in one call (one SQP iteration's linear-algebra core,
+ * GATO paper Sec. III, Fig. 2 steps a-c).  Outputs are those of the three
+ * calls above; flags[b] is set (not ORed).  Where one workgroup can hold a
+ * whole solve, the stages run fused in one kernel and use no workspace;
+ * otherwise S, Pinv, gamma, Qinv and Rinv go through `workspace`
+ * (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device memory).
+ * times (nullable): per-stage device times; when given, the call synchronises.
+ */
+int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                  const float* r, const float* A, const float* Bu, const float* e,
+                  const float* x0, const float* rho, float eps, int32_t max_iters,
+                  const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
+                  float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
+                  int32_t* flags, void* workspace, size_t workspace_bytes,
+                  gato_stage_times_t* times, hipStream_t stream);
+
+/* Workspace gato_sqp_step needs for these dims (0 when the fused path applies). */
+size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha);
+
+/* Static description of a status code. */
+const char* gato_status_string(int code);
+
+/* Non-zero if this build has kernels for (n, m, N). */
+int gato_shape_supported(int32_t n, int32_t m, int32_t N);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GATO_H */

@@ -1,0 +1,98 @@
+"""Helpers for the GPU tests: run each C-ABI call on seeded inputs and return numpy.
+
+Inputs come from the shared generator module; expected values come from the fp64
+oracle on the same float32 inputs.  Nothing here computes any part of the method.
+"""
+import numpy as np
+import torch
+
+from block_tridiagonal_pcg_amd import ops, synth
+
+ALPHAS = synth.ALPHAS
+CAPS = {1: 200, 2: 200, 3: 200, 4: 200, 5: 2000}
+
+
+def cpu(t):
+    return t.detach().cpu().numpy()
+
+
+def gpu_form(batch, rho=None):
+    dims = batch["dims"]
+    dev = ops.to_device(batch)
+    out = ops.alloc_outputs(dims)
+    rh = None if rho is None else torch.as_tensor(np.asarray(rho, np.float32)).cuda()
+    ops.gato_form_schur(dims, *[dev[f] for f in synth.FIELDS], rh, out["S"], out["Pinv"], out["gamma"],
+                        out["Qinv"], out["Rinv"], out["flags"])
+    torch.cuda.synchronize()
+    return {k: cpu(out[k]) for k in ("S", "Pinv", "gamma", "Qinv", "Rinv", "flags")}
+
+
+def gpu_pcg(batch, form, eps, max_iters, lambda0=None, flags=None):
+    """PCG + recovery fed `form` (any arrays of the stage-1 layouts, rounded to float32)."""
+    dims = batch["dims"]
+    n, m, N, B = dims
+    t = lambda a: torch.as_tensor(np.ascontiguousarray(np.asarray(a, np.float32))).cuda()  # noqa: E731
+    lam = t(np.zeros((B, N, n)) if lambda0 is None else lambda0)
+    dz = torch.zeros((B, N * n + (N - 1) * m), dtype=torch.float32, device="cuda")
+    iters = torch.zeros(B, dtype=torch.int32, device="cuda")
+    relres = torch.zeros(B, dtype=torch.float32, device="cuda")
+    fl = torch.as_tensor(np.zeros(B, np.int32) if flags is None else np.asarray(flags, np.int32)).cuda()
+    ops.gato_pcg_solve(dims, t(form["S"]), t(form["Pinv"]), t(form["gamma"]), t(form["Qinv"]), t(form["Rinv"]),
+                       t(batch["A"]), t(batch["Bu"]), t(batch["q"]), t(batch["r"]), eps, max_iters, lam, dz,
+                       iters, relres, fl)
+    torch.cuda.synchronize()
+    return dict(lam=cpu(lam), dz=cpu(dz), iters=cpu(iters), relres=cpu(relres), flags=cpu(fl))
+
+
+def gpu_merit(batch, dz, mu, alphas=ALPHAS, flags=None):
+    dims = batch["dims"]
+    B = dims[3]
+    dev = ops.to_device(batch)
+    dzt = torch.as_tensor(np.ascontiguousarray(np.asarray(dz, np.float32))).cuda()
+    merit = torch.zeros((B, len(alphas)), dtype=torch.float32, device="cuda")
+    merit0 = torch.zeros(B, dtype=torch.float32, device="cuda")
+    best = torch.zeros(B, dtype=torch.int32, device="cuda")
+    fl = torch.as_tensor(np.zeros(B, np.int32) if flags is None else np.asarray(flags, np.int32)).cuda()
+    ops.gato_merit_eval(dims, *[dev[f] for f in synth.FIELDS], dzt, alphas, mu, merit, merit0, best, fl)
+    torch.cuda.synchronize()
+    return dict(merit=cpu(merit), merit0=cpu(merit0), best=cpu(best), flags=cpu(fl))
+
+
+def gpu_sqp(batch, eps, max_iters, mu=1.0, alphas=ALPHAS, rho=None, lambda0=None, times=False):
+    dims = batch["dims"]
+    n, m, N, B = dims
+    dev = ops.to_device(batch)
+    out = ops.alloc_outputs(dims, len(alphas))
+    if lambda0 is not None:
+        out["lam"].copy_(torch.as_tensor(np.asarray(lambda0, np.float32)))
+    rh = None if rho is None else torch.as_tensor(np.asarray(rho, np.float32)).cuda()
+    st = ops.gato_sqp_step(dims, *[dev[f] for f in synth.FIELDS], rh, eps, max_iters, alphas, mu, out["lam"],
+                           out["dz"], out["merit"], out["merit0"], out["best"], out["iters"], out["relres"],
+                           out["flags"], workspace=ops.workspace_for(dims, len(alphas)), times=times)
+    torch.cuda.synchronize()
+    res = {k: cpu(out[k]) for k in ("lam", "dz", "merit", "merit0", "best", "iters", "relres", "flags")}
+    res["times"] = st
+    return res
+
+
+def rel_rows(a, b):
+    """Per-solve relative 2-norm error of a against reference b."""
+    a = np.asarray(a, np.float64).reshape(a.shape[0], -1)
+    b = np.asarray(b, np.float64).reshape(b.shape[0], -1)
+    den = np.linalg.norm(b, axis=1)
+    den[den == 0] = 1.0
+    return np.linalg.norm(a - b, axis=1) / den
+
+
+def merit_rel(gpu_merit_vals, ref):
+    """Relative merit error with the denominator max(|M_ref(a)|, M0_ref) (avoids near-zero division)."""
+    den = np.maximum(np.abs(ref["merit"]), ref["merit0"][:, None])
+    den[den == 0] = 1.0
+    return np.abs(np.asarray(gpu_merit_vals, np.float64) - ref["merit"]) / den
+
+
+def select(merit, merit0):
+    """The selection rule applied to given merit values (ties to the earlier step)."""
+    best = np.argmin(merit, axis=1).astype(np.int32)
+    ok = merit[np.arange(merit.shape[0]), best] < merit0
+    return np.where(ok, best, -1)

@@ -1,0 +1,302 @@
+"""GPU parity: every C-ABI call against the fp64 oracle on the same seeded inputs.
+
+Tolerances (the GPU computes in fp32):
+  stage 1  S, gamma, Q~^-1, R^-1: <= 1e-5 relative Frobenius per solve; Phi^-1: <= 1e-4
+           (fp32 entries carry ~6e-8 relative rounding; Gauss-Jordan inverses of blocks
+           with condition numbers up to ~5e5 lose a few more digits);
+  stage 2  ||dz_gpu - dz_oracle|| / ||dz_oracle|| <= 1e-3 at a PCG exit tolerance of 1e-6;
+  stage 3  merit <= 1e-4 relative, with the denominator max(|M_oracle(a)|, M0), when both
+           sides evaluate the same step.
+Integer outputs decided by floats (the selected step) are compared with the selection
+rule applied to the GPU's own fp32 merits; flags other than the line-search bit must match.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_tridiagonal_pcg_amd import ops, synth
+from gpu_util import (ALPHAS, CAPS, gpu_form, gpu_merit, gpu_pcg, gpu_sqp, merit_rel, rel_rows, select)
+
+pytestmark = pytest.mark.gpu
+
+A64 = ALPHAS.astype(np.float64)
+SMALL = {1: 1, 2: 8, 3: 16, 4: 16, 5: 4}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    ops.load()
+    oracle.load()
+
+
+def _batch(cid, B, **kw):
+    return synth.make_batch(cid, B, **kw)
+
+
+def _ident(*a):
+    print("case:", *a, flush=True)
+
+
+# ---------------------------------------------------------------- stage 1
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_form_parity(cid):
+    B = SMALL[cid]
+    _ident("form", cid, B)
+    bt = _batch(cid, B)
+    rho = np.linspace(0.0, 0.3, B)
+    g = gpu_form(bt, rho=rho)
+    o = oracle.form_schur(*synth.inputs(bt), rho=rho.astype(np.float32))
+    assert rel_rows(g["S"], o["S"]).max() <= 1e-5
+    assert rel_rows(g["gamma"], o["gamma"]).max() <= 1e-5
+    assert rel_rows(g["Qinv"], o["Qinv"]).max() <= 1e-5
+    if bt["dims"][2] > 1:
+        assert rel_rows(g["Rinv"], o["Rinv"]).max() <= 1e-5
+    assert rel_rows(g["Pinv"], o["Pinv"]).max() <= 1e-4
+    np.testing.assert_array_equal(g["flags"], o["flags"])
+    # out-of-range blocks are written as zeros
+    assert np.all(g["S"][:, 0, 0] == 0) and np.all(g["S"][:, -1, 2] == 0)
+    assert np.all(g["Pinv"][:, 0, 0] == 0) and np.all(g["Pinv"][:, -1, 2] == 0)
+
+
+def test_form_flags_match_oracle():
+    bt = _batch(2, 4)
+    n = bt["dims"][0]
+    bt["Q"][1, 5] = -np.eye(n, dtype=np.float32)
+    bt["R"][2, 7] = -np.eye(bt["dims"][1], dtype=np.float32)
+    bt["Q"][3, -1] = -1e-3 * np.eye(n, dtype=np.float32)
+    g = gpu_form(bt)
+    o = oracle.form_schur(*synth.inputs(bt))
+    # Once a pivot fails the two sides carry different garbage downstream (the oracle's
+    # Cholesky yields NaN, Gauss-Jordan a finite flagged inverse), so the S bit of a solve
+    # whose Q or R failed is not compared.
+    qr = ops.F_Q_NOT_SPD | ops.F_R_NOT_SPD
+    np.testing.assert_array_equal(g["flags"] & qr, o["flags"] & qr)
+    clean = (o["flags"] & qr) == 0
+    np.testing.assert_array_equal(g["flags"][clean], o["flags"][clean])
+    assert g["flags"][0] == 0 and g["flags"][1] & ops.F_Q_NOT_SPD and g["flags"][2] & ops.F_R_NOT_SPD
+    assert g["flags"][3] & ops.F_S_NOT_SPD
+
+
+# ---------------------------------------------------------------- stage 2
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_pcg_parity(cid):
+    B = SMALL[cid]
+    _ident("pcg", cid, B)
+    bt = _batch(cid, B)
+    o_form = oracle.form_schur(*synth.inputs(bt))
+    g = gpu_pcg(bt, o_form, 1e-6, CAPS[cid])
+    o = oracle.pcg_solve(o_form["S"], o_form["Pinv"], o_form["gamma"], o_form["Qinv"], o_form["Rinv"], bt["A"],
+                         bt["Bu"], bt["q"], bt["r"], 1e-6, CAPS[cid])
+    err = rel_rows(g["dz"], o["dz"])
+    print("dz rel err max %.3e; iters gpu %s oracle %s" % (err.max(), g["iters"].tolist(), o["iters"].tolist()))
+    assert err.max() <= 1e-3
+    assert (g["flags"] == 0).all() and (o["flags"] == 0).all()
+    assert (g["relres"] <= 1e-6).all()
+    if cid != 5:
+        assert np.abs(g["iters"] - o["iters"]).max() <= 2
+
+
+def test_pcg_warm_start_and_flags():
+    bt = _batch(3, 4)
+    o_form = oracle.form_schur(*synth.inputs(bt))
+    exact = oracle.direct_solve(o_form["S"], o_form["gamma"])["lam"]
+    warm = gpu_pcg(bt, o_form, 1e-6, 200, lambda0=exact)
+    assert (warm["iters"] <= 1).all()
+    capped = gpu_pcg(bt, o_form, 1e-6, 1)
+    assert (capped["flags"] & ops.F_PCG_MAXITER).all() and (capped["iters"] == 1).all()
+    bad = dict(o_form)
+    bad["gamma"] = o_form["gamma"].copy()
+    bad["gamma"][2, 3, 1] = np.nan
+    res = gpu_pcg(bt, bad, 1e-6, 200, flags=np.array([0, 32, 0, 0]))
+    assert res["flags"][2] & ops.F_NONFINITE
+    assert res["flags"][1] == 32  # ORed into existing bits
+    z = dict(o_form)
+    z["gamma"] = np.zeros_like(o_form["gamma"])
+    zr = gpu_pcg(bt, z, 1e-6, 200, lambda0=np.ones_like(exact))
+    assert (zr["iters"] == 0).all() and np.all(zr["lam"] == 0) and (zr["relres"] == 0).all()
+
+
+# ---------------------------------------------------------------- stage 3
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_merit_parity(cid):
+    B = SMALL[cid]
+    _ident("merit", cid, B)
+    bt = _batch(cid, B)
+    ref_step = oracle.sqp_step(*synth.inputs(bt), None, 1e-6, CAPS[cid], A64, 1.0)
+    dz32 = ref_step["dz"].astype(np.float32)
+    for mu in (1.0, 7.5):
+        g = gpu_merit(bt, dz32, mu)
+        o = oracle.merit_eval(*synth.inputs(bt), dz32.astype(np.float64), A64, mu)
+        assert merit_rel(g["merit"], o).max() <= 1e-4
+        assert (np.abs(g["merit0"] - o["merit0"]) <= 1e-4 * o["merit0"]).all()
+        np.testing.assert_array_equal(g["best"], select(g["merit"], g["merit0"]))
+        np.testing.assert_array_equal(g["flags"] & ops.F_LS_FAILED, np.where(g["best"] < 0, ops.F_LS_FAILED, 0))
+
+
+def test_merit_bit_identical_across_workgroup_sizes():
+    bt = _batch(5, 3)
+    dz = np.random.default_rng(0).standard_normal((3, 128 * 14 + 127 * 7)).astype(np.float32) * 0.1
+    runs = []
+    old = os.environ.get("GATO_MERIT_WAVES")
+    try:
+        for w in ("1", "2", "3", "8", "16"):
+            os.environ["GATO_MERIT_WAVES"] = w
+            runs.append(gpu_merit(bt, dz, 1.3))
+    finally:
+        if old is None:
+            os.environ.pop("GATO_MERIT_WAVES", None)
+        else:
+            os.environ["GATO_MERIT_WAVES"] = old
+    for r in runs[1:]:
+        for k in ("merit", "merit0", "best", "flags"):
+            np.testing.assert_array_equal(r[k], runs[0][k])
+
+
+def test_merit_ascent_direction_fails_line_search():
+    bt = _batch(2, 2)
+    bt["x0"][:] = 0
+    bt["e"][:] = 0
+    ref = oracle.sqp_step(*synth.inputs(bt), None, 1e-8, 400, A64, 1.0)
+    g = gpu_merit(bt, -ref["dz"].astype(np.float32), 1.0)
+    assert (g["best"] == -1).all() and (g["flags"] & ops.F_LS_FAILED).all()
+
+
+# ---------------------------------------------------------------- whole step
+
+
+SQP_CASES = [(1, 1), (2, 1), (2, 8), (2, 16), (3, 1), (3, 8), (3, 16), (3, 64), (3, 128), (4, 16), (4, 64), (4, 256),
+             (5, 512)]
+
+
+@pytest.mark.parametrize("cid,B", SQP_CASES, ids=["cfg%d-B%d" % c for c in SQP_CASES])
+def test_sqp_step_parity(cid, B):
+    _ident("sqp_step", cid, B)
+    bt = _batch(cid, B)
+    g = gpu_sqp(bt, 1e-6, CAPS[cid])
+    # the oracle checks every solve, or an evenly spaced sample of 64 at the largest batch
+    idx = np.arange(B) if B <= 256 else np.linspace(0, B - 1, 64).astype(int)
+    sub = {f: bt[f][idx] for f in synth.FIELDS}
+    o = oracle.sqp_step(*[sub[f] for f in synth.FIELDS], None, 1e-6, CAPS[cid], A64, 1.0)
+    err = rel_rows(g["dz"][idx], o["dz"])
+    print("cfg%d B%d: dz rel err max %.3e median %.3e; iters gpu %d..%d oracle %d..%d" % (
+        cid, B, err.max(), np.median(err), g["iters"].min(), g["iters"].max(), o["iters"].min(), o["iters"].max()))
+    assert err.max() <= 1e-3
+    assert ((g["flags"][idx] & ~ops.F_LS_FAILED) == (o["flags"] & ~ops.F_LS_FAILED)).all()
+    # merit of the GPU's own step, against the oracle's merit of that same step
+    om = oracle.merit_eval(*[sub[f] for f in synth.FIELDS], g["dz"][idx].astype(np.float64), A64, 1.0)
+    assert merit_rel(g["merit"][idx], om).max() <= 1e-4
+    np.testing.assert_array_equal(g["best"], select(g["merit"], g["merit0"]))
+    if cid != 5:
+        assert np.abs(g["iters"][idx] - o["iters"]).max() <= 2
+    else:
+        ratio = g["iters"][idx] / np.maximum(o["iters"], 1)
+        assert 0.7 <= ratio.min() and ratio.max() <= 1.5
+
+
+def test_fused_step_equals_staged_calls():
+    """gato_sqp_step (one fused kernel) and form -> pcg -> merit give identical bits."""
+    bt = _batch(3, 16)
+    fused = gpu_sqp(bt, 1e-6, 200)
+    f = gpu_form(bt)
+    p = gpu_pcg(bt, f, 1e-6, 200)
+    m = gpu_merit(bt, p["dz"], 1.0)
+    np.testing.assert_array_equal(fused["dz"], p["dz"])
+    np.testing.assert_array_equal(fused["lam"], p["lam"])
+    np.testing.assert_array_equal(fused["iters"], p["iters"])
+    np.testing.assert_array_equal(fused["merit"], m["merit"])
+    np.testing.assert_array_equal(fused["merit0"], m["merit0"])
+    np.testing.assert_array_equal(fused["best"], m["best"])
+
+
+def test_solve_independent_of_batch_position():
+    big = _batch(2, 16)
+    g = gpu_sqp(big, 1e-6, 200)
+    for b in (0, 7, 15):
+        one = _batch(2, 1, first=b)
+        h = gpu_sqp(one, 1e-6, 200)
+        np.testing.assert_array_equal(h["dz"][0], g["dz"][b])
+        np.testing.assert_array_equal(h["merit"][0], g["merit"][b])
+
+
+def test_stage_times_reported():
+    g = gpu_sqp(_batch(3, 8), 1e-6, 200, times=True)
+    assert g["times"].total_us > 0
+    g5 = gpu_sqp(_batch(5, 2), 1e-6, 2000, times=True)
+    assert g5["times"].schur_us > 0 and g5["times"].linsys_us > 0 and g5["times"].merit_us > 0
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+@pytest.mark.parametrize("N", [1, 2, 5, 37, 63, 64, 65, 100, 128, 129, 200, 256])
+def test_ragged_and_extreme_horizons(N):
+    """Horizons that leave a wave partly empty, fill a workgroup exactly, or spill into the
+    long-horizon path (windowed formation, streamed PCG)."""
+    _ident("horizon", N)
+    bt = _batch(3, 3, N=N)
+    g = gpu_sqp(bt, 1e-6, 400, rho=np.array([0.0, 0.1, 1.0]))
+    o = oracle.sqp_step(*synth.inputs(bt), np.array([0.0, 0.1, 1.0]), 1e-6, 400, A64, 1.0)
+    assert rel_rows(g["dz"], o["dz"]).max() <= 1e-3
+    om = oracle.merit_eval(*synth.inputs(bt), g["dz"].astype(np.float64), A64, 1.0)
+    assert merit_rel(g["merit"], om).max() <= 1e-4
+    f = gpu_form(bt, rho=np.array([0.0, 0.1, 1.0]))
+    of = oracle.form_schur(*synth.inputs(bt), rho=np.array([0.0, 0.1, 1.0]))
+    assert rel_rows(f["S"], of["S"]).max() <= 1e-5 and rel_rows(f["Pinv"], of["Pinv"]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("cid,N", [(1, 1), (4, 1), (4, 3), (4, 17), (4, 32), (2, 65)])
+def test_other_shapes_edges(cid, N):
+    bt = _batch(cid, 2, N=N)
+    g = gpu_sqp(bt, 1e-6, 400)
+    o = oracle.sqp_step(*synth.inputs(bt), None, 1e-6, 400, A64, 1.0)
+    assert rel_rows(g["dz"], o["dz"]).max() <= 1e-3
+
+
+def test_zero_batch_is_a_no_op():
+    bt = _batch(3, 1)
+    n, m, N, _ = bt["dims"]
+    empty = {f: bt[f][:0] for f in synth.FIELDS}
+    empty["dims"] = (n, m, N, 0)
+    r = gpu_sqp(empty, 1e-6, 200)
+    assert r["dz"].shape == (0, N * n + (N - 1) * m)
+
+
+def test_golden_examples_on_gpu():
+    import json
+
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "scalar_lq.json")))["cases"]
+    for c in cases:
+        bt = {k: np.asarray(c[k], np.float32)[None] for k in synth.FIELDS}
+        bt["dims"] = (1, 1, 2, 1)
+        al = np.array([float(a) for a in c["merit_at"]], np.float32)
+        g = gpu_sqp(bt, 1e-6, 10, mu=c["mu"], alphas=al)
+        np.testing.assert_allclose(g["dz"][0], c["dz"], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(g["lam"][0], c["lambda"], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(g["merit"][0], list(c["merit_at"].values()), rtol=1e-5, atol=1e-6)
+        assert g["iters"][0] == c["pcg_iters"] and g["best"][0] == c["best"]
+        f = gpu_form(bt)
+        np.testing.assert_allclose(f["S"][0], c["S"], rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(f["Pinv"][0], c["Pinv"], rtol=1e-6, atol=1e-7)
+
+
+def test_step_flags_match_oracle():
+    bt = _batch(3, 4)
+    bt["e"][1, 10, 3] = np.nan
+    bt["Q"][2, 20] = -np.eye(14, dtype=np.float32)
+    g = gpu_sqp(bt, 1e-6, 200)
+    o = oracle.sqp_step(*synth.inputs(bt), None, 1e-6, 200, A64, 1.0)
+    for b in (0, 3):
+        assert (g["flags"][b] & ~ops.F_LS_FAILED) == (o["flags"][b] & ~ops.F_LS_FAILED) == 0
+    assert g["flags"][1] & ops.F_NONFINITE and o["flags"][1] & ops.F_NONFINITE
+    assert g["flags"][2] & ops.F_Q_NOT_SPD and o["flags"][2] & ops.F_Q_NOT_SPD
