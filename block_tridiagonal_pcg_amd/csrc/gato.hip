@@ -17,73 +17,61 @@ namespace gato {
 
 // ------------------------------------------------------------------ fused step
 
-template <class SH, typename RT>
+template <class SH>
 struct FusedLds {
-    float parkQ[SH::SLOTS][SH::NC][SH::NC];  // Q~_k^-1 rows, kept for the recovery
-    float parkR[SH::SLOTS][SH::MC][SH::MC];  // R_k^-1 rows
+    Park<SH> park;  // G^-1 rows, kept for the recovery
     union {
         FormLds<SH> form;
-        PcgLds<SH, RT, 1> pcg;
+        PcgLds<SH, 1> pcg;
         float mer[(GATO_MAX_ALPHA + 1) * 64];
     } u;
     int flags;
 };
 
-template <class SH, typename RT>
+template <class SH>
 __global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
 {
-    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, SL = SH::SLOTS;
-    __shared__ FusedLds<SH, RT> L;
-    const Ix ix{p.n, p.m, p.N};
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    __shared__ FusedLds<SH> L;
+    const Ix<SH> ix{p.N};
     const int b = blockIdx.x;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP, k = s;
-    const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < p.n;
+    const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC;
     if (threadIdx.x == 0) L.flags = 0;
 
     Rows<SH> rw;
     int fl = 0;
-    form<SH>(
-        p, b, 0, p.N, L.u.form, rw, fl,
-        [&](const float* qi) {
-            if (i < NC)
-#pragma unroll
-                for (int c = 0; c < NC; ++c) L.parkQ[s][i][c] = qi[c];
-        },
-        [&](const float* ri) {
-            if (i < MC)
-#pragma unroll
-                for (int c = 0; c < MC; ++c) L.parkR[s][i][c] = ri[c];
-        });
+    form<SH>(p, b, 0, p.N, L.u.form, L.park, rw, fl, [](const float*, const float*) {});
     if (fl && i == 0) atomicOr(&L.flags, fl);
 
-    float lam = rowv ? p.lambda[ix.vn(b, k, i)] : 0.0f;
+    float lam = ld1(p.lambda, ix.vn(b, k, i), rowv);
     int it = 0, pfl = 0;
     float rel = 0.0f;
     const RegMat<SH> M{&rw};
-    pcg<SH, RT, 1>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
+    pcg<SH, 1>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
 
-    // recovery of dz
-    L.u.pcg.xv[s][i] = lam;
+    // recovery of dz (exchange rows of the PCG buffers: knot k at row k + 1)
+    L.u.pcg.xv[s + 1][i] = lam;
     __syncthreads();
-    const float lamn = (s + 1 < SL) ? L.u.pcg.xv[s + 1][i] : 0.0f;
+    const float lamn = L.u.pcg.xv[s + 2][i];
     float qi[NC], ri[MC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qi[c] = (i < NC) ? L.parkQ[s][i][c] : 0.0f;
+    for (int c = 0; c < NC; ++c) qi[c] = L.park.Q[s][i < NC ? i : 0][c];
 #pragma unroll
-    for (int c = 0; c < MC; ++c) ri[c] = (i < MC) ? L.parkR[s][i][c] : 0.0f;
-    __syncthreads();
+    for (int c = 0; c < MC; ++c) ri[c] = L.park.R[s][i < MC ? i : 0][c];
     float dx, du;
     recover<SH>(p, b, k, i, lam, lamn, qi, ri, dx, du);
     if (rowv) {
         p.lambda[ix.vn(b, k, i)] = lam;
         p.dz[ix.dx(b, k, i)] = dx;
     }
-    if (hn && i < p.m) p.dz[ix.du(b, k, i)] = du;
+    if (hn && i < MC) p.dz[ix.du(b, k, i)] = du;
+    __syncthreads();
 
     // merit at every step size, then the selection
-    L.u.pcg.xv[s][i] = dx;
+    L.u.pcg.xv[s + 1][i] = dx;
     __syncthreads();
-    const float dxn = (s + 1 < SL) ? L.u.pcg.xv[s + 1][i] : 0.0f;
+    const float dxn = L.u.pcg.xv[s + 2][i];
     __syncthreads();
     for (int t = threadIdx.x; t < (GATO_MAX_ALPHA + 1) * 64; t += blockDim.x) L.u.mer[t] = 0.0f;
     __syncthreads();
@@ -109,12 +97,18 @@ __global__ void k_zero_i32(int32_t* x, int count)
 }
 
 template <class SH>
+struct FormOnlyLds {
+    FormLds<SH> f;
+    Park<SH> park;
+};
+
+template <class SH>
 __global__ __launch_bounds__(SH::THREADS) void k_form(Params p)
 {
-    constexpr int NP = SH::NP;
-    __shared__ FormLds<SH> L;
-    const Ix ix{p.n, p.m, p.N};
-    const int n = p.n, m = p.m, N = p.N;
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    __shared__ FormOnlyLds<SH> L;
+    const Ix<SH> ix{p.N};
+    const int N = p.N;
     const int b = blockIdx.x, w = blockIdx.y;
     int w0, o0, o1;
     if (p.win_own <= 0) {
@@ -131,31 +125,23 @@ __global__ __launch_bounds__(SH::THREADS) void k_form(Params p)
     const bool own = s < nslot && k >= o0 && k < o1;
     Rows<SH> rw;
     int fl = 0;
-    form<SH>(
-        p, b, w0, nslot, L, rw, fl,
-        [&](const float* qi) {
-            if (own && i < n)
+    form<SH>(p, b, w0, nslot, L.f, L.park, rw, fl, [&](const float* qi, const float* ri) {
+        if (own && i < NC)
 #pragma unroll
-                for (int c = 0; c < SH::NC; ++c)
-                    if (c < n) p.Qinv[ix.Q(b, k, i, c)] = qi[c];
-        },
-        [&](const float* ri) {
-            if (own && k < N - 1 && i < m)
+            for (int c = 0; c < NC; ++c) p.Qinv[ix.Q(b, k, i) + c] = qi[c];
+        if (own && k < N - 1 && i < MC)
 #pragma unroll
-                for (int c = 0; c < SH::MC; ++c)
-                    if (c < m) p.Rinv[ix.R(b, k, i, c)] = ri[c];
-        });
-    if (own && i < n) {
+            for (int c = 0; c < MC; ++c) p.Rinv[ix.R(b, k, i) + c] = ri[c];
+    });
+    if (own && i < NC) {
 #pragma unroll
-        for (int c = 0; c < SH::NC; ++c) {
-            if (c < n) {
-                p.S[ix.blk(b, k, 0, i, c)] = rw.slo[c];
-                p.S[ix.blk(b, k, 1, i, c)] = rw.sd[c];
-                p.S[ix.blk(b, k, 2, i, c)] = rw.sup[c];
-                p.Pinv[ix.blk(b, k, 0, i, c)] = rw.plo[c];
-                p.Pinv[ix.blk(b, k, 1, i, c)] = rw.pd[c];
-                p.Pinv[ix.blk(b, k, 2, i, c)] = rw.pup[c];
-            }
+        for (int c = 0; c < NC; ++c) {
+            p.S[ix.blk(b, k, 0, i) + c] = rw.slo[c];
+            p.S[ix.blk(b, k, 1, i) + c] = rw.sd[c];
+            p.S[ix.blk(b, k, 2, i) + c] = rw.sup[c];
+            p.Pinv[ix.blk(b, k, 0, i) + c] = rw.plo[c];
+            p.Pinv[ix.blk(b, k, 1, i) + c] = rw.pd[c];
+            p.Pinv[ix.blk(b, k, 2, i) + c] = rw.pup[c];
         }
         p.gamma[ix.vn(b, k, i)] = rw.gam;
     }
@@ -164,37 +150,35 @@ __global__ __launch_bounds__(SH::THREADS) void k_form(Params p)
 
 // ------------------------------------------------------------------ stage 2 alone
 
-template <class SH, typename RT, int C, class MAT>
-__device__ __forceinline__ void pcg_and_recover(const Params& p, const MAT& M, PcgLds<SH, RT, C>& L,
-                                                const float* gam, float* lam)
+template <class SH, int C, class MAT>
+__device__ __forceinline__ void pcg_and_recover(const Params& p, const MAT& M, PcgLds<SH, C>& L, const float* gam,
+                                                float* lam)
 {
-    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, SL = SH::SLOTS, KK = PcgLds<SH, RT, C>::K;
-    const Ix ix{p.n, p.m, p.N};
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, SL = SH::SLOTS;
+    const Ix<SH> ix{p.N};
     const int b = blockIdx.x;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     int it = 0, pfl = 0;
     float rel = 0.0f;
-    pcg<SH, RT, C>(p, M, gam, lam, L, it, rel, pfl);
+    pcg<SH, C>(p, M, gam, lam, L, it, rel, pfl);
 #pragma unroll
-    for (int c = 0; c < C; ++c) L.xv[c * SL + s][i] = lam[c];
+    for (int c = 0; c < C; ++c) L.xv[c * SL + s + 1][i] = lam[c];
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int k = c * SL + s;
-        const float lamn = (k + 1 < KK) ? L.xv[k + 1][i] : 0.0f;
-        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < p.n;
+        const float lamn = L.xv[k + 2][i];
+        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC;
         float qi[NC], ri[MC];
-#pragma unroll
-        for (int t = 0; t < NC; ++t) qi[t] = (rowv && t < p.n) ? p.Qinv[ix.Q(b, k, i, t)] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < MC; ++t) ri[t] = (hn && i < p.m && t < p.m) ? p.Rinv[ix.R(b, k, i, t)] : 0.0f;
+        ld_row<NC>(p.Qinv, ix.Q(b, k, i), rowv, qi);
+        ld_row<MC>(p.Rinv, ix.R(b, k, i), hn && i < MC, ri);
         float dx, du;
         recover<SH>(p, b, k, i, lam[c], lamn, qi, ri, dx, du);
         if (rowv) {
             p.lambda[ix.vn(b, k, i)] = lam[c];
             p.dz[ix.dx(b, k, i)] = dx;
         }
-        if (hn && i < p.m) p.dz[ix.du(b, k, i)] = du;
+        if (hn && i < MC) p.dz[ix.du(b, k, i)] = du;
     }
     if (threadIdx.x == 0) {
         p.iters[b] = it;
@@ -203,50 +187,46 @@ __device__ __forceinline__ void pcg_and_recover(const Params& p, const MAT& M, P
     }
 }
 
-template <class SH, typename RT>
+template <class SH>
 __global__ __launch_bounds__(SH::THREADS) void k_pcg_res(Params p)
 {
     constexpr int NP = SH::NP, NC = SH::NC;
-    __shared__ PcgLds<SH, RT, 1> L;
-    const Ix ix{p.n, p.m, p.N};
+    __shared__ PcgLds<SH, 1> L;
+    const Ix<SH> ix{p.N};
     const int b = blockIdx.x;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP, k = s;
-    const bool rowv = k < p.N && i < p.n;
+    const bool rowv = k < p.N && i < NC;
     Rows<SH> rw;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const bool v = rowv && c < p.n;
-        rw.slo[c] = v ? p.S[ix.blk(b, k, 0, i, c)] : 0.0f;
-        rw.sd[c] = v ? p.S[ix.blk(b, k, 1, i, c)] : 0.0f;
-        rw.sup[c] = v ? p.S[ix.blk(b, k, 2, i, c)] : 0.0f;
-        rw.plo[c] = v ? p.Pinv[ix.blk(b, k, 0, i, c)] : 0.0f;
-        rw.pd[c] = v ? p.Pinv[ix.blk(b, k, 1, i, c)] : 0.0f;
-        rw.pup[c] = v ? p.Pinv[ix.blk(b, k, 2, i, c)] : 0.0f;
-    }
-    rw.gam = rowv ? p.gamma[ix.vn(b, k, i)] : 0.0f;
-    float lam = rowv ? p.lambda[ix.vn(b, k, i)] : 0.0f;
+    ld_row<NC>(p.S, ix.blk(b, k, 0, i), rowv, rw.slo);
+    ld_row<NC>(p.S, ix.blk(b, k, 1, i), rowv, rw.sd);
+    ld_row<NC>(p.S, ix.blk(b, k, 2, i), rowv, rw.sup);
+    ld_row<NC>(p.Pinv, ix.blk(b, k, 0, i), rowv, rw.plo);
+    ld_row<NC>(p.Pinv, ix.blk(b, k, 1, i), rowv, rw.pd);
+    ld_row<NC>(p.Pinv, ix.blk(b, k, 2, i), rowv, rw.pup);
+    rw.gam = ld1(p.gamma, ix.vn(b, k, i), rowv);
+    float lam = ld1(p.lambda, ix.vn(b, k, i), rowv);
     const RegMat<SH> M{&rw};
-    pcg_and_recover<SH, RT, 1>(p, M, L, &rw.gam, &lam);
+    pcg_and_recover<SH, 1>(p, M, L, &rw.gam, &lam);
 }
 
-template <class SH, typename RT, int C>
+template <class SH, int C>
 __global__ __launch_bounds__(SH::THREADS) void k_pcg_stream(Params p)
 {
-    constexpr int NP = SH::NP, SL = SH::SLOTS;
-    __shared__ PcgLds<SH, RT, C> L;
-    const Ix ix{p.n, p.m, p.N};
+    constexpr int NP = SH::NP, SL = SH::SLOTS, NC = SH::NC;
+    __shared__ PcgLds<SH, C> L;
+    const Ix<SH> ix{p.N};
     const int b = blockIdx.x;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     float gam[C], lam[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int k = c * SL + s;
-        const bool rowv = k < p.N && i < p.n;
-        gam[c] = rowv ? p.gamma[ix.vn(b, k, i)] : 0.0f;
-        lam[c] = rowv ? p.lambda[ix.vn(b, k, i)] : 0.0f;
+        const bool rowv = k < p.N && i < NC;
+        gam[c] = ld1(p.gamma, ix.vn(b, k, i), rowv);
+        lam[c] = ld1(p.lambda, ix.vn(b, k, i), rowv);
     }
     const GlobalMat<SH> M{p.S, p.Pinv, ix, b, i};
-    pcg_and_recover<SH, RT, C>(p, M, L, gam, lam);
+    pcg_and_recover<SH, C>(p, M, L, gam, lam);
 }
 
 // ------------------------------------------------------------------ stage 3 alone
@@ -254,9 +234,9 @@ __global__ __launch_bounds__(SH::THREADS) void k_pcg_stream(Params p)
 template <class SH, int LPL>
 __global__ __launch_bounds__(1024) void k_merit(Params p)
 {
-    constexpr int NP = SH::NP, P = 16 * LPL;
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, P = 16 * LPL;
     __shared__ float mer[(GATO_MAX_ALPHA + 1) * P];
-    const Ix ix{p.n, p.m, p.N};
+    const Ix<SH> ix{p.N};
     const int b = blockIdx.x;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     const int ks = blockDim.x / NP;
@@ -264,10 +244,10 @@ __global__ __launch_bounds__(1024) void k_merit(Params p)
     __syncthreads();
     for (int c0 = 0; c0 < p.N; c0 += ks) {
         const int k = c0 + s;
-        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < p.n;
-        const float dx = rowv ? p.dz[ix.dx(b, k, i)] : 0.0f;
-        const float du = (hn && i < p.m) ? p.dz[ix.du(b, k, i)] : 0.0f;
-        const float dxn = (hn && i < p.n) ? p.dz[ix.dx(b, k + 1, i)] : 0.0f;
+        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC;
+        const float dx = ld1(p.dz, ix.dx(b, k, i), rowv);
+        const float du = ld1(p.dz, ix.du(b, k, i), hn && i < MC);
+        const float dxn = ld1(p.dz, ix.dx(b, k + 1, i), hn && i < NC);
         merit_knot<SH>(p, b, k, i, dx, du, dxn, mer + (kv ? k : 0), P);
     }
     __syncthreads();
@@ -281,8 +261,6 @@ __global__ __launch_bounds__(1024) void k_merit(Params p)
 }
 
 // ------------------------------------------------------------------ host side
-
-using PcgRT = float;
 
 static int merit_waves_default(int N, int kpw)
 {
@@ -320,11 +298,11 @@ struct Ops {
     {
         const int C = stream_chunks(p.N);
         if (C == 1) {
-            hipLaunchKernelGGL((k_pcg_res<SH, PcgRT>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
+            hipLaunchKernelGGL((k_pcg_res<SH>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
         } else if (C == 2) {
-            hipLaunchKernelGGL((k_pcg_stream<SH, PcgRT, 2>), dim3(p.B), dim3(SH::THREADS), 0, st, p);
+            hipLaunchKernelGGL((k_pcg_stream<SH, 2>), dim3(p.B), dim3(SH::THREADS), 0, st, p);
         } else if (C == 4) {
-            hipLaunchKernelGGL((k_pcg_stream<SH, PcgRT, 4>), dim3(p.B), dim3(SH::THREADS), 0, st, p);
+            hipLaunchKernelGGL((k_pcg_stream<SH, 4>), dim3(p.B), dim3(SH::THREADS), 0, st, p);
         } else {
             return hipErrorInvalidValue;
         }
@@ -347,7 +325,7 @@ struct Ops {
     }
     static hipError_t fused(const Params& p, hipStream_t st)
     {
-        hipLaunchKernelGGL((k_sqp_fused<SH, PcgRT>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
+        hipLaunchKernelGGL((k_sqp_fused<SH>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
         return hipGetLastError();
     }
     static bool supported(int N)

@@ -248,7 +248,7 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
             piv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(hi), 0x150 + (J & 15), 0xF, 0xF, false));
         }
         bad |= !(piv > 0.0f) || !__builtin_isfinite(piv);
-        const float inv = 1.0f / piv;
+        const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
         const bool me = lane == J;
         const float f = a[J];
         const float g = me ? (inv - 1.0f) : -(f * inv);

@@ -1,7 +1,10 @@
 // gato_stages.h -- the three stages of the SQP-step core as workgroup-level
 // device functions (GATO paper, Sec. II-III).  Every function is called by all
 // threads of a workgroup in uniform control flow; lane (slot s, row i) holds
-// row i of knot w0 + s.
+// row i of knot w0 + s.  Shapes are compile-time (n = NC, m = MC), so all
+// index arithmetic folds into immediate offsets; loads that may fall outside
+// the problem read a valid dummy address and are masked afterwards, so no
+// load sits behind a branch.
 #pragma once
 
 #include "gato.h"
@@ -26,23 +29,29 @@ struct Params {
     int win_own;  // knots owned by one form workgroup (0: the whole horizon)
 };
 
+// The same value in every lane (the reductions below produce identical bits in
+// all lanes); moving it to a scalar register lets branches on it be scalar.
+__device__ __forceinline__ float uniform(float x)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // ------------------------------------------------------------------ indexing
 
+template <class SH>
 struct Ix {
-    int n, m, N;
+    static constexpr int n = SH::NC, m = SH::MC;
+    int N;
     __device__ __forceinline__ size_t kn(int b, int k) const { return (size_t)b * N + k; }
     __device__ __forceinline__ size_t kd(int b, int k) const { return (size_t)b * (N - 1) + k; }
-    __device__ __forceinline__ size_t Q(int b, int k, int i, int c) const { return (kn(b, k) * n + i) * n + c; }
+    __device__ __forceinline__ size_t Q(int b, int k, int i) const { return (kn(b, k) * n + i) * n; }
     __device__ __forceinline__ size_t vn(int b, int k, int i) const { return kn(b, k) * n + i; }
-    __device__ __forceinline__ size_t R(int b, int k, int i, int c) const { return (kd(b, k) * m + i) * m + c; }
+    __device__ __forceinline__ size_t R(int b, int k, int i) const { return (kd(b, k) * m + i) * m; }
     __device__ __forceinline__ size_t vm(int b, int k, int i) const { return kd(b, k) * m + i; }
-    __device__ __forceinline__ size_t A(int b, int k, int i, int c) const { return (kd(b, k) * n + i) * n + c; }
-    __device__ __forceinline__ size_t Bu(int b, int k, int i, int c) const { return (kd(b, k) * n + i) * m + c; }
+    __device__ __forceinline__ size_t A(int b, int k, int i) const { return (kd(b, k) * n + i) * n; }
+    __device__ __forceinline__ size_t Bu(int b, int k, int i) const { return (kd(b, k) * n + i) * m; }
     __device__ __forceinline__ size_t e(int b, int k, int i) const { return kd(b, k) * n + i; }
-    __device__ __forceinline__ size_t blk(int b, int k, int s, int i, int c) const
-    {
-        return ((kn(b, k) * 3 + s) * n + i) * n + c;
-    }
+    __device__ __forceinline__ size_t blk(int b, int k, int s, int i) const { return ((kn(b, k) * 3 + s) * n + i) * n; }
     __device__ __forceinline__ size_t nz() const { return (size_t)N * n + (size_t)(N - 1) * m; }
     __device__ __forceinline__ size_t dx(int b, int k, int i) const { return (size_t)b * nz() + (size_t)k * (n + m) + i; }
     __device__ __forceinline__ size_t du(int b, int k, int i) const
@@ -50,6 +59,31 @@ struct Ix {
         return (size_t)b * nz() + (size_t)k * (n + m) + n + i;
     }
 };
+
+// Masked loads read this page instead of the problem arrays, which may be
+// absent in a call (NULL) or empty (N = 1).  1024 floats cover the widest
+// strided row read (32 x 32); module globals are zero-initialised.
+__device__ float g_zero_page[1024];
+
+// Load K floats at base[off + j * STRIDE] when ok, else zeros; the address is
+// selected before the loads, which are then unconditional.
+template <int K, int STRIDE = 1>
+__device__ __forceinline__ void ld_row(const float* base, size_t off, bool ok, float* out)
+{
+    static_assert((K - 1) * STRIDE < 1024, "masked row read exceeds the zero page");
+    const float* a = ok ? base + off : g_zero_page;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const float v = a[j * STRIDE];
+        out[j] = ok ? v : 0.0f;
+    }
+}
+
+__device__ __forceinline__ float ld1(const float* base, size_t off, bool ok)
+{
+    const float v = *(ok ? base + off : g_zero_page);
+    return ok ? v : 0.0f;
+}
 
 // Rows of one knot's block rows of S and Phi^-1, and gamma, held by lane i.
 template <class SH>
@@ -59,10 +93,18 @@ struct Rows {
     float gam;
 };
 
+// LDS the formation needs only while it runs (reusable afterwards) ...
 template <class SH>
 struct FormLds {
     float xw[SH::SLOTS][SH::NP][SH::NC + 1];  // one matrix row per lane (+1: bank spread)
     float xg[SH::SLOTS][SH::NP];
+};
+
+// ... and the G^-1 rows it parks, which the fused step keeps for the recovery.
+template <class SH>
+struct Park {
+    float Q[SH::SLOTS][SH::NC][SH::NC];  // Q~_k^-1 rows
+    float R[SH::SLOTS][SH::MC][SH::MC];  // R_k^-1 rows
 };
 
 // ------------------------------------------------------------------ stage 1: form
@@ -75,164 +117,167 @@ struct FormLds {
 // becomes a workgroup barrier because a workgroup holds whole horizons, or a
 // window with two knots of halo before and one after).
 //
-// Returns the lane's rows in `out`; Q~_k^-1 and R_k^-1 rows are handed to the
-// sinks as soon as they exist (parked in LDS or stored), so they are not kept
-// live in registers.  `fl` gets the Q/R/S_NOT_SPD bits of this knot.
-template <class SH, class SinkQ, class SinkR>
-__device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, FormLds<SH>& L,
-                                     Rows<SH>& out, int& fl, SinkQ sinkQ, SinkR sinkR)
+// Q~_k^-1 and R_k^-1 rows are parked in LDS (K; the caller may keep
+// them for the recovery) and handed to `sink` for storing.  `fl` gets the
+// Q/R/S_NOT_SPD bits of this knot.
+template <class SH, class Sink>
+__device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, FormLds<SH>& L, Park<SH>& K,
+                                     Rows<SH>& out, int& fl, Sink sink)
 {
     constexpr int NC = SH::NC, MC = SH::MC, NP = SH::NP, SL = SH::SLOTS;
-    const Ix ix{p.n, p.m, p.N};
-    const int n = p.n, m = p.m, N = p.N;
+    const Ix<SH> ix{p.N};
+    const int N = p.N;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     const int k = w0 + s;
     const bool kv = s < nslot && k < N;
     const bool hn = kv && k < N - 1;
-    const bool rowv = kv && i < n;
+    const bool rowv = kv && i < NC;
+    const bool urow = hn && i < MC;
     const float rh = (p.rho != nullptr) ? p.rho[b] : 0.0f;
+    const int sp = s > 0 ? s - 1 : 0;  // previous slot (clamped)
+    const bool has_prev = s >= 1 && k >= 1;
 
     // Q~_k^-1 (identity rows on lanes/knots outside the problem keep it finite)
-    float qi[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        float v = (rowv && c < n) ? p.Q[ix.Q(b, k, i, c)] : 0.0f;
-        if (c == i) v = rowv ? v + rh : 1.0f;
-        qi[c] = v;
-    }
-    bool badq = false;
-    gj_steps<NP, NC>(qi, i, badq);
-    sinkQ(qi);
-
-    // R_k^-1
-    float ri[MC];
-#pragma unroll
-    for (int c = 0; c < MC; ++c) {
-        float v = (hn && i < m && c < m) ? p.R[ix.R(b, k, i, c)] : 0.0f;
-        if (c == i) v = (hn && i < m) ? v : 1.0f;
-        ri[c] = v;
-    }
-    bool badr = false;
-    gj_steps<NP, MC>(ri, i, badr);
-    sinkR(ri);
-
-    // W = A_k Q~_k^-1 (row i), V = B_k R_k^-1 (row i)
-    float ar[NC], W[NC], br[MC], V[MC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        ar[c] = (hn && i < n && c < n) ? p.A[ix.A(b, k, i, c)] : 0.0f;
-        W[c] = 0.0f;
-    }
-    gemm_rows<NP, NC, NC>(W, BcRow<NP, NC>(qi), ar);
-#pragma unroll
-    for (int c = 0; c < MC; ++c) {
-        br[c] = (hn && i < n && c < m) ? p.Bu[ix.Bu(b, k, i, c)] : 0.0f;
-        V[c] = 0.0f;
-    }
-    gemm_rows<NP, MC, MC>(V, BcRow<NP, MC>(ri), br);
-
-    // gamma pieces: h = (Q~_k^-1 q_k)_i (own knot), g = (e_k - W q_k - V r_k)_i (for knot k+1)
-    const float qv = rowv ? p.q[ix.vn(b, k, i)] : 0.0f;
-    const float rv = (hn && i < m) ? p.r[ix.vm(b, k, i)] : 0.0f;
-    const float ev = (hn && i < n) ? p.e[ix.e(b, k, i)] : 0.0f;
-    float h = 0.0f, t1 = 0.0f, t2 = 0.0f;
+    bool badq = false, badr = false, bads = false;
     {
+        float qi[NC];
+        ld_row<NC>(p.Q, ix.Q(b, k, i), rowv, qi);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
+        gj_steps<NP, NC>(qi, i, badq);
+        if (i < NC)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) K.Q[s][i][c] = qi[c];
+        float ri[MC];
+        ld_row<MC>(p.R, ix.R(b, k, i), urow, ri);
+#pragma unroll
+        for (int c = 0; c < MC; ++c)
+            if (c == i) ri[c] = urow ? ri[c] : 1.0f;
+        gj_steps<NP, MC>(ri, i, badr);
+        if (i < MC)
+#pragma unroll
+            for (int c = 0; c < MC; ++c) K.R[s][i][c] = ri[c];
+        sink(qi, ri);
+    }
+
+    // W = A_k Q~_k^-1 (row i), V = B_k R_k^-1 (row i); gamma pieces
+    //   h = (Q~_k^-1 q_k)_i (own knot), g = (e_k - W q_k - V r_k)_i (for knot k+1)
+    float ar[NC], V[MC], h = 0.0f, g;
+    {
+        float qi[NC], ri[MC], W[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qi[c] = K.Q[s][i < NC ? i : 0][c];
+#pragma unroll
+        for (int c = 0; c < MC; ++c) ri[c] = K.R[s][i < MC ? i : 0][c];
+        ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, ar);
+        float br[MC];
+        ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, br);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) W[c] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MC; ++c) V[c] = 0.0f;
+        gemm_rows<NP, NC, NC>(W, BcRow<NP, NC>(qi), ar);
+        gemm_rows<NP, MC, MC>(V, BcRow<NP, MC>(ri), br);
+        const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
+        const float rv = ld1(p.r, ix.vm(b, k, i), urow);
+        const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
+        float t1 = 0.0f, t2 = 0.0f;
         const Bc<NP> qb(qv);
         dotb<NP, NC>(h, qb, qi);
         dotb<NP, NC>(t1, qb, W);
         dotb<NP, MC>(t2, Bc<NP>(rv), V);
+        g = (ev - t1) - t2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) L.xw[s][i][c] = W[c];
     }
-    const float g = (ev - t1) - t2;
+    __syncthreads();
 
     // O_k = S_{k,k+1} = -W_k' (transpose through LDS); S_{k,k-1} = -W_{k-1}
-    float O[NC], slo[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) L.xw[s][i][c] = W[c];
-    __syncthreads();
+    float O[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        O[c] = (i < NC) ? -L.xw[s][c][i] : 0.0f;
-        slo[c] = (s >= 1 && k >= 1) ? -L.xw[s - 1][i][c] : 0.0f;
+        const float wt = L.xw[s][c][i < NC ? i : 0];
+        O[c] = (i < NC) ? -wt : 0.0f;
+        const float w = L.xw[sp][i][c];
+        out.slo[c] = (has_prev && rowv) ? -w : 0.0f;
     }
     __syncthreads();
 
     // U_k = A_k Q~_k^-1 A_k' + B_k R_k^-1 B_k' = -(A_k O_k) + V_k B_k'
-    float U[NC];
     {
-        float nar[NC];
+        float U[NC], nar[NC], bcol[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             U[c] = 0.0f;
             nar[c] = -ar[c];
         }
         gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(O), nar);
-        float bcol[NC];  // lane i < m holds column i of B_k
-#pragma unroll
-        for (int c = 0; c < NC; ++c) bcol[c] = (hn && i < m && c < n) ? p.Bu[ix.Bu(b, k, c, i)] : 0.0f;
+        // lane i < m holds column i of B_k
+        ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, bcol);
         gemm_rows<NP, NC, MC>(U, BcRow<NP, NC>(bcol), V);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) L.xw[s][i][c] = U[c];
+        L.xg[s][i] = g;
     }
+    __syncthreads();
 
     // D_k = Q~_k^-1 + U_{k-1};  gamma_k = h + g_{k-1}  (gamma_0 = h + x0)
-#pragma unroll
-    for (int c = 0; c < NC; ++c) L.xw[s][i][c] = U[c];
-    L.xg[s][i] = g;
-    __syncthreads();
     float sd[NC];
-    float gprev = 0.0f;
     {
-        const bool pv = s >= 1 && k >= 1;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) sd[c] = pv ? qi[c] + L.xw[s - 1][i][c] : qi[c];
-        gprev = pv ? L.xg[s - 1][i] : 0.0f;
+        for (int c = 0; c < NC; ++c) {
+            const float qv = K.Q[s][i < NC ? i : 0][c];
+            const float u = L.xw[sp][i][c];
+            sd[c] = has_prev ? qv + u : qv;
+        }
+        const float gp = L.xg[sp][i];
+        const float x0v = ld1(p.x0, (size_t)b * NC + i, rowv && k == 0);
+        out.gam = rowv ? ((k >= 1) ? h + gp : h + x0v) : 0.0f;
     }
     __syncthreads();
-    const float x0v = rowv ? p.x0[(size_t)b * n + i] : 0.0f;
-    const float gam = (k >= 1) ? h + gprev : h + x0v;
 
     // D_k^-1
     float di[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) di[c] = sd[c];
-    bool bads = false;
+    for (int c = 0; c < NC; ++c) {
+        di[c] = sd[c];
+        out.sd[c] = rowv ? sd[c] : 0.0f;
+    }
     gj_steps<NP, NC>(di, i, bads);
-
-    // Phi^-1_{k,k+1} = -D_k^-1 O_k D_{k+1}^-1 ; Phi^-1_{k,k-1} = (Phi^-1_{k-1,k})'
 #pragma unroll
     for (int c = 0; c < NC; ++c) L.xw[s][i][c] = di[c];
     __syncthreads();
-    float Z[NC];
+
+    // Phi^-1_{k,k+1} = -D_k^-1 O_k D_{k+1}^-1 ; Phi^-1_{k,k-1} = (Phi^-1_{k-1,k})'
     {
-        float Dn[NC], Y[NC];
+        const int sn = s + 1 < SL ? s + 1 : s;
+        float Dn[NC], Y[NC], Z[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            Dn[c] = (s + 1 < SL) ? L.xw[s + 1][i][c] : 0.0f;
+            const float d = L.xw[sn][i][c];
+            Dn[c] = (s + 1 < SL) ? d : 0.0f;
             Y[c] = 0.0f;
             Z[c] = 0.0f;
         }
         __syncthreads();
         gemm_rows<NP, NC, NC>(Y, BcRow<NP, NC>(O), di);  // Y = D_k^-1 O_k
         gemm_rows<NP, NC, NC>(Z, BcRow<NP, NC>(Dn), Y);  // Z = Y D_{k+1}^-1
-    }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) L.xw[s][i][c] = Z[c];
+        for (int c = 0; c < NC; ++c) {
+            L.xw[s][i][c] = Z[c];
+            out.pup[c] = (rowv && k < N - 1) ? -Z[c] : 0.0f;
+        }
+    }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        out.plo[c] = (s >= 1 && k >= 1 && i < NC) ? -L.xw[s - 1][c][i] : 0.0f;
-        out.pup[c] = (k < N - 1) ? -Z[c] : 0.0f;
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        out.slo[c] = rowv ? slo[c] : 0.0f;
-        out.sd[c] = rowv ? sd[c] : 0.0f;
+        const float z = L.xw[sp][c][i < NC ? i : 0];
+        out.plo[c] = (has_prev && rowv) ? -z : 0.0f;
         out.sup[c] = (rowv && k < N - 1) ? O[c] : 0.0f;
         out.pd[c] = rowv ? di[c] : 0.0f;
-        out.plo[c] = rowv ? out.plo[c] : 0.0f;
-        out.pup[c] = rowv ? out.pup[c] : 0.0f;
     }
-    out.gam = rowv ? gam : 0.0f;
+    __syncthreads();
     fl = 0;
     if (kv) {
         if (badq) fl |= GATO_F_Q_NOT_SPD;
@@ -273,25 +318,20 @@ template <class SH>
 struct GlobalMat {
     const float* Sm;
     const float* Pm;
-    Ix ix;
+    Ix<SH> ix;
     int b, i;
-    __device__ __forceinline__ void row(const float* X, int k, int blk, float* out) const
-    {
-        const bool v = k < ix.N && i < ix.n;
-#pragma unroll
-        for (int c = 0; c < SH::NC; ++c) out[c] = (v && c < ix.n) ? X[ix.blk(b, k, blk, i, c)] : 0.0f;
-    }
     __device__ __forceinline__ float mv(const float* X, int k, float xp, float x, float xn) const
     {
         constexpr int NP = SH::NP, NC = SH::NC;
-        float v = 0.0f, t[NC];
-        row(X, k, 0, t);
-        dotb<NP, NC>(v, Bc<NP>(xp), t);
-        row(X, k, 1, t);
-        dotb<NP, NC>(v, Bc<NP>(x), t);
-        row(X, k, 2, t);
-        dotb<NP, NC>(v, Bc<NP>(xn), t);
-        return v;
+        const bool v = k < ix.N && i < NC;
+        float acc = 0.0f, t[NC];
+        ld_row<NC>(X, ix.blk(b, k, 0, i), v, t);
+        dotb<NP, NC>(acc, Bc<NP>(xp), t);
+        ld_row<NC>(X, ix.blk(b, k, 1, i), v, t);
+        dotb<NP, NC>(acc, Bc<NP>(x), t);
+        ld_row<NC>(X, ix.blk(b, k, 2, i), v, t);
+        dotb<NP, NC>(acc, Bc<NP>(xn), t);
+        return acc;
     }
     __device__ __forceinline__ float S(int k, float xp, float x, float xn) const { return mv(Sm, k, xp, x, xn); }
     __device__ __forceinline__ float P(int k, float xp, float x, float xn) const { return mv(Pm, k, xp, x, xn); }
@@ -305,204 +345,222 @@ __host__ __device__ constexpr int leaves_for(int knots)
     return p;
 }
 
-template <class SH, typename RT, int C>
+template <class SH, int C>
 struct PcgLds {
-    static constexpr int K = SH::SLOTS * C;     // knots held (C per lane group)
-    static constexpr int P = leaves_for(K);     // canonical-sum leaves
-    float xv[K][SH::NP];
-    float xz[K][SH::NP];
-    RT red0[P];
-    RT red12[2 * P];
+    static constexpr int K = SH::SLOTS * C;  // knots held (C per lane group)
+    static constexpr int P = leaves_for(K);  // canonical-sum leaves
+    // exchange rows for knots -1 .. K (index + 1); rows 0 and K + 1 stay zero
+    float xv[K + 2][SH::NP];
+    float xz[K + 2][SH::NP];
+    float red0[P];
+    float red12[2 * P];
 };
 
 // Preconditioned CG on S lambda = gamma for one solve per workgroup (GATO
 // paper Sec. II; the per-block PCG of Sec. III).  Each lane group owns C knots
 // (k = c * SLOTS + s); per-knot partial sums go to LDS and every lane forms the
-// same canonical total, so all waves take identical branches.  Two workgroup
-// barriers per iteration: after v = S p (for p'v and v's neighbours) and after
-// z = Phi^-1 r (for r'r, r'z and z's neighbours).  Each lane keeps copies of the
-// neighbouring knots' entries of r and p (same row), updated with the same
-// arithmetic as their owners, so the products need no further exchange.
-template <class SH, typename RT, int C, class MAT>
-__device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* gam, float* lam,
-                                    PcgLds<SH, RT, C>& L, int& iters, float& relres, int& flags)
+// same canonical total, so all waves take identical (scalar) branches.  Two
+// workgroup barriers per iteration: after v = S p (for p'v and v's neighbours)
+// and after z = Phi^-1 r (for r'r, r'z and z's neighbours).  Each lane keeps
+// copies of the neighbouring knots' entries of r and p (same row), updated with
+// the same arithmetic as their owners, so the products need no more exchange.
+// lambda is accumulated in fp64: on ill-conditioned solves it sums hundreds of
+// small steps, and in fp32 that sum alone would cost ~1e-3 in dz.
+template <class SH, int C, class MAT>
+__device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* gam, float* lam, PcgLds<SH, C>& L,
+                                    int& iters_out, float& relres, int& flags_out)
 {
-    constexpr int NP = SH::NP, SL = SH::SLOTS, KK = PcgLds<SH, RT, C>::K, P = PcgLds<SH, RT, C>::P;
+    constexpr int NP = SH::NP, SL = SH::SLOTS, KK = PcgLds<SH, C>::K, P = PcgLds<SH, C>::P;
     constexpr int LPL = P / 16;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     const bool lead = i == 0;
     const int nth = blockDim.x;
 
     for (int t = threadIdx.x; t < P; t += nth) {
-        L.red0[t] = RT(0);
-        L.red12[2 * t] = RT(0);
-        L.red12[2 * t + 1] = RT(0);
+        L.red0[t] = 0.0f;
+        L.red12[2 * t] = 0.0f;
+        L.red12[2 * t + 1] = 0.0f;
+    }
+    for (int t = threadIdx.x; t < NP; t += nth) {
+        L.xv[0][t] = L.xv[KK + 1][t] = 0.0f;
+        L.xz[0][t] = L.xz[KK + 1][t] = 0.0f;
     }
     __syncthreads();
 
-    auto kidx = [&](int c) { return c * SL + s; };
-    auto nbr = [&](float(*buf)[NP], int c, float& xp, float& xn) {
-        const int kk = kidx(c);
-        xp = (kk >= 1) ? buf[kk - 1][i] : 0.0f;
-        xn = (kk + 1 < KK) ? buf[kk + 1][i] : 0.0f;
-    };
+    auto row = [&](int c) { return c * SL + s + 1; };  // exchange row of chunk c
 
     // ||gamma||^2 and the neighbours of lambda
-    RT gg = RT(0);
-    {
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const RT t = groupsum<NP>(RT(gam[c]) * RT(gam[c]));
-            if (lead) L.red0[kidx(c)] = t;
-            L.xv[kidx(c)][i] = lam[c];
-        }
-        __syncthreads();
-        gg = canon_sum<LPL>(L.red0);
+    for (int c = 0; c < C; ++c) {
+        const float t = groupsum<NP>(gam[c] * gam[c]);
+        if (lead) L.red0[row(c) - 1] = t;
+        L.xv[row(c)][i] = lam[c];
     }
+    __syncthreads();
+    const float gg = uniform(canon_sum<LPL>(L.red0));
     float lp[C], ln[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) nbr(L.xv, c, lp[c], ln[c]);
+    for (int c = 0; c < C; ++c) {
+        lp[c] = L.xv[row(c) - 1][i];
+        ln[c] = L.xv[row(c) + 1][i];
+    }
     __syncthreads();
 
-    iters = 0;
-    flags = 0;
+    int iters = 0, flags = 0;
     if (!__builtin_isfinite(gg)) {
-        flags = GATO_F_NONFINITE;
+        iters_out = 0;
+        flags_out = GATO_F_NONFINITE;
         relres = __builtin_nanf("");
         return;
     }
-    if (gg == RT(0)) {
+    if (gg == 0.0f) {
 #pragma unroll
         for (int c = 0; c < C; ++c) lam[c] = 0.0f;
+        iters_out = 0;
+        flags_out = 0;
         relres = 0.0f;
         return;
     }
-    const RT gnorm = sqrt(gg);
-    const RT tol = RT(p.eps) * gnorm;
-    // lambda accumulates hundreds of small steps on ill-conditioned solves; in
-    // fp32 that sum alone would cost ~1e-3 of relative accuracy in dz, so it is
-    // kept in fp64 (one fp64 FMA per lane per iteration) and rounded at the end.
-    double lamd[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) lamd[c] = (double)lam[c];
+    // ||r|| <= eps ||gamma||  <=>  r'r <= eps^2 gamma'gamma (both sides non-negative)
+    const float tol2 = (p.eps * p.eps) * gg;
 
     // r = gamma - S lambda, and its neighbours
     float r[C], rp[C], rn[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        r[c] = gam[c] - M.S(kidx(c), lp[c], lam[c], ln[c]);
-        L.xz[kidx(c)][i] = r[c];
+        r[c] = gam[c] - M.S(row(c) - 1, lp[c], lam[c], ln[c]);
+        L.xz[row(c)][i] = r[c];
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < C; ++c) nbr(L.xz, c, rp[c], rn[c]);
+    for (int c = 0; c < C; ++c) {
+        rp[c] = L.xz[row(c) - 1][i];
+        rn[c] = L.xz[row(c) + 1][i];
+    }
     __syncthreads();
 
+    double lamd[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) lamd[c] = (double)lam[c];
+
     // z = Phi^-1 r; r'r and r'z; neighbours of z
-    float z[C], pv_[C], pp[C], pn[C];
-    RT rr, rz;
+    float pv[C], pp[C], pn[C];
+    float rr, eta;
     {
+        float z[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            z[c] = M.P(kidx(c), rp[c], r[c], rn[c]);
-            const RT a = groupsum<NP>(RT(r[c]) * RT(r[c]));
-            const RT bb = groupsum<NP>(RT(r[c]) * RT(z[c]));
+            z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
+            const float a = groupsum<NP>(r[c] * r[c]);
+            const float bb = groupsum<NP>(r[c] * z[c]);
             if (lead) {
-                L.red12[2 * kidx(c)] = a;
-                L.red12[2 * kidx(c) + 1] = bb;
+                L.red12[2 * (row(c) - 1)] = a;
+                L.red12[2 * (row(c) - 1) + 1] = bb;
             }
-            L.xv[kidx(c)][i] = z[c];
+            L.xv[row(c)][i] = z[c];
         }
         __syncthreads();
-        rr = canon_sum<LPL>(L.red12, 2);
-        rz = canon_sum<LPL>(L.red12 + 1, 2);
+        rr = uniform(canon_sum<LPL>(L.red12, 2));
+        eta = uniform(canon_sum<LPL>(L.red12 + 1, 2));
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            nbr(L.xv, c, pp[c], pn[c]);
-            pv_[c] = z[c];
+            pp[c] = L.xv[row(c) - 1][i];
+            pn[c] = L.xv[row(c) + 1][i];
+            pv[c] = z[c];
         }
         __syncthreads();
     }
-    bool conv = sqrt(rr) <= tol;
+    bool conv = rr <= tol2;
     if (!__builtin_isfinite(rr)) flags |= GATO_F_NONFINITE;
-    RT eta = rz;
-    if (!conv && !(flags & GATO_F_NONFINITE)) {
-        while (iters < p.max_iters) {
+    if (!conv && !flags) {
+        for (;;) {
+            if (iters >= p.max_iters) {
+                flags |= GATO_F_PCG_MAXITER;
+                break;
+            }
             // v = S p ; p'v ; v to neighbours
             float v[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                v[c] = M.S(kidx(c), pp[c], pv_[c], pn[c]);
-                const RT t = groupsum<NP>(RT(pv_[c]) * RT(v[c]));
-                if (lead) L.red0[kidx(c)] = t;
-                L.xv[kidx(c)][i] = v[c];
+                v[c] = M.S(row(c) - 1, pp[c], pv[c], pn[c]);
+                const float t = groupsum<NP>(pv[c] * v[c]);
+                if (lead) L.red0[row(c) - 1] = t;
+                L.xv[row(c)][i] = v[c];
             }
             __syncthreads();
-            const RT pSp = canon_sum<LPL>(L.red0);
+            const float pSp = uniform(canon_sum<LPL>(L.red0));
             float vp[C], vn[C];
 #pragma unroll
-            for (int c = 0; c < C; ++c) nbr(L.xv, c, vp[c], vn[c]);
+            for (int c = 0; c < C; ++c) {
+                vp[c] = L.xv[row(c) - 1][i];
+                vn[c] = L.xv[row(c) + 1][i];
+            }
             if (!__builtin_isfinite(pSp)) {
                 flags |= GATO_F_NONFINITE;
                 break;
             }
-            if (!(pSp > RT(0))) {
+            if (!(pSp > 0.0f)) {
                 flags |= GATO_F_PCG_BREAKDOWN;
                 break;
             }
-            const float a = (float)(eta / pSp);
+            const float a = uniform(eta * __builtin_amdgcn_rcpf(pSp));
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                lamd[c] = fma((double)a, (double)pv_[c], lamd[c]);
+                lamd[c] = fma((double)a, (double)pv[c], lamd[c]);
                 r[c] = fmaf(-a, v[c], r[c]);
                 rp[c] = fmaf(-a, vp[c], rp[c]);
                 rn[c] = fmaf(-a, vn[c], rn[c]);
             }
             ++iters;
             // z = Phi^-1 r ; r'r, r'z ; z to neighbours
+            float z[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                z[c] = M.P(kidx(c), rp[c], r[c], rn[c]);
-                const RT ta = groupsum<NP>(RT(r[c]) * RT(r[c]));
-                const RT tb = groupsum<NP>(RT(r[c]) * RT(z[c]));
+                z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
+                const float ta = groupsum<NP>(r[c] * r[c]);
+                const float tb = groupsum<NP>(r[c] * z[c]);
                 if (lead) {
-                    L.red12[2 * kidx(c)] = ta;
-                    L.red12[2 * kidx(c) + 1] = tb;
+                    L.red12[2 * (row(c) - 1)] = ta;
+                    L.red12[2 * (row(c) - 1) + 1] = tb;
                 }
-                L.xz[kidx(c)][i] = z[c];
+                L.xz[row(c)][i] = z[c];
             }
             __syncthreads();
-            rr = canon_sum<LPL>(L.red12, 2);
-            const RT rz1 = canon_sum<LPL>(L.red12 + 1, 2);
+            rr = uniform(canon_sum<LPL>(L.red12, 2));
+            const float rz = uniform(canon_sum<LPL>(L.red12 + 1, 2));
             float zp[C], zn[C];
 #pragma unroll
-            for (int c = 0; c < C; ++c) nbr(L.xz, c, zp[c], zn[c]);
+            for (int c = 0; c < C; ++c) {
+                zp[c] = L.xz[row(c) - 1][i];
+                zn[c] = L.xz[row(c) + 1][i];
+            }
             if (!__builtin_isfinite(rr)) {
                 flags |= GATO_F_NONFINITE;
                 break;
             }
-            if (sqrt(rr) <= tol) {
+            if (rr <= tol2) {
                 conv = true;
                 break;
             }
-            if (!__builtin_isfinite(rz1)) {
+            if (!__builtin_isfinite(rz)) {
                 flags |= GATO_F_NONFINITE;
                 break;
             }
-            const float be = (float)(rz1 / eta);
-            eta = rz1;
+            const float be = uniform(rz * __builtin_amdgcn_rcpf(eta));
+            eta = rz;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                pv_[c] = fmaf(be, pv_[c], z[c]);
+                pv[c] = fmaf(be, pv[c], z[c]);
                 pp[c] = fmaf(be, pp[c], zp[c]);
                 pn[c] = fmaf(be, pn[c], zn[c]);
             }
         }
-        if (!conv && !(flags & (GATO_F_NONFINITE | GATO_F_PCG_BREAKDOWN))) flags |= GATO_F_PCG_MAXITER;
     }
 #pragma unroll
     for (int c = 0; c < C; ++c) lam[c] = (float)lamd[c];
-    relres = (float)(sqrt(rr) / gnorm);
+    iters_out = iters;
+    flags_out = flags;
+    relres = sqrtf(rr / gg);
     // The loop's barriers order every LDS access above; one more before the
     // caller reuses the buffers.
     __syncthreads();
@@ -517,30 +575,28 @@ __device__ __forceinline__ void recover(const Params& p, int b, int k, int i, fl
                                         const float* qi, const float* ri, float& dx, float& du)
 {
     constexpr int NC = SH::NC, MC = SH::MC, NP = SH::NP;
-    const Ix ix{p.n, p.m, p.N};
-    const int n = p.n, m = p.m, N = p.N;
+    const Ix<SH> ix{p.N};
+    const int N = p.N;
     const bool kv = k < N;
     const bool hn = kv && k < N - 1;
-    const bool rowv = kv && i < n;
+    const bool rowv = kv && i < NC;
+    const bool urow = hn && i < MC;
     float acol[NC], bcol[NC];
-#pragma unroll
-    for (int l = 0; l < NC; ++l) {
-        acol[l] = (hn && i < n && l < n) ? p.A[ix.A(b, k, l, i)] : 0.0f;
-        bcol[l] = (hn && i < m && l < n) ? p.Bu[ix.Bu(b, k, l, i)] : 0.0f;
-    }
+    ld_row<NC, NC>(p.A, ix.A(b, k, 0) + i, hn && i < NC, acol);  // column i of A_k
+    ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, bcol);        // column i of B_k
     const Bc<NP> lnb(lamn);
     float t = 0.0f, tb = 0.0f;
     dotb<NP, NC>(t, lnb, acol);
     dotb<NP, NC>(tb, lnb, bcol);
-    const float qv = rowv ? p.q[ix.vn(b, k, i)] : 0.0f;
-    const float rv = (hn && i < m) ? p.r[ix.vm(b, k, i)] : 0.0f;
+    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
+    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
     const float w = rowv ? (lam - qv) - t : 0.0f;
-    const float u = (hn && i < m) ? -tb - rv : 0.0f;
+    const float u = urow ? -tb - rv : 0.0f;
     float x = 0.0f, y = 0.0f;
     dotb<NP, NC>(x, Bc<NP>(w), qi);
     dotb<NP, MC>(y, Bc<NP>(u), ri);
     dx = rowv ? x : 0.0f;
-    du = (hn && i < m) ? y : 0.0f;
+    du = urow ? y : 0.0f;
 }
 
 // ------------------------------------------------------------------ stage 3: merit
@@ -558,27 +614,21 @@ __device__ __forceinline__ void merit_knot(const Params& p, int b, int k, int i,
                                            float dxn, float* out, int stride)
 {
     constexpr int NC = SH::NC, MC = SH::MC, NP = SH::NP;
-    const Ix ix{p.n, p.m, p.N};
-    const int n = p.n, m = p.m, N = p.N;
+    const Ix<SH> ix{p.N};
+    const int N = p.N;
     const bool kv = k < N;
     const bool hn = kv && k < N - 1;
-    const bool rowv = kv && i < n;
-    const bool urow = hn && i < m;
+    const bool rowv = kv && i < NC;
+    const bool urow = hn && i < MC;
     float Qr[NC], Ar[NC], Rr[MC], Br[MC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        Qr[c] = (rowv && c < n) ? p.Q[ix.Q(b, k, i, c)] : 0.0f;
-        Ar[c] = (hn && i < n && c < n) ? p.A[ix.A(b, k, i, c)] : 0.0f;
-    }
-#pragma unroll
-    for (int c = 0; c < MC; ++c) {
-        Rr[c] = (urow && c < m) ? p.R[ix.R(b, k, i, c)] : 0.0f;
-        Br[c] = (hn && i < n && c < m) ? p.Bu[ix.Bu(b, k, i, c)] : 0.0f;
-    }
-    const float qv = rowv ? p.q[ix.vn(b, k, i)] : 0.0f;
-    const float rv = urow ? p.r[ix.vm(b, k, i)] : 0.0f;
-    const float ev = (hn && i < n) ? p.e[ix.e(b, k, i)] : 0.0f;
-    const float x0v = (rowv && k == 0) ? p.x0[(size_t)b * n + i] : 0.0f;
+    ld_row<NC>(p.Q, ix.Q(b, k, i), rowv, Qr);
+    ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, Ar);
+    ld_row<MC>(p.R, ix.R(b, k, i), urow, Rr);
+    ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, Br);
+    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
+    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
+    const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
+    const float x0v = ld1(p.x0, (size_t)b * NC + i, rowv && k == 0);
 
     const Bc<NP> xb(dx), ub(du);
     float Qdx = 0.0f, Rdu = 0.0f, d = 0.0f;
@@ -606,11 +656,11 @@ template <int LPL>
 __device__ __forceinline__ void merit_select(const Params& p, int b, const float* vals, int P, int32_t& best,
                                              int& lsfail)
 {
-    float M0 = canon_sum<LPL>(vals);
+    const float M0 = uniform(canon_sum<LPL>(vals));
     float bv = 0.0f;
     int bi = 0;
     for (int j = 1; j <= p.n_alpha; ++j) {
-        const float v = canon_sum<LPL>(vals + j * P);
+        const float v = uniform(canon_sum<LPL>(vals + j * P));
         if (threadIdx.x == 0) p.merit[(size_t)b * p.n_alpha + (j - 1)] = v;
         if (j == 1 || v < bv) {
             bv = v;
