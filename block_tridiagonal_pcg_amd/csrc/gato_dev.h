@@ -112,24 +112,35 @@ __device__ __forceinline__ T groupsum(T x)
     return x;
 }
 
-// Canonical pairwise sum of P = 16 * L leaves held in LDS (zero-padded).
-// Lane j of each 16-lane row sums leaves [j L, (j+1) L) as a pairwise tree,
-// then the rows' butterflies combine the 16 partial sums.  The result is the
-// pairwise tree over the P leaves and does not depend on which kernel, block
-// shape or wave computes it; with zero padding it equals the pairwise tree
-// over the smallest power of two >= the number of real leaves.
-template <int L, typename T>
-__device__ __forceinline__ T canon_sum(const T* leaves, int stride = 1)
+// Canonical pairwise sum of P = 64 * L leaves held in LDS (zero-padded), in
+// every lane of the wave: lane t reads its L contiguous leaves (conflict-free
+// LDS access) and sums them pairwise, the 16-lane butterfly combines the lanes
+// of each row, and two swap-adds combine rows 0+1, 2+3 and then the halves.
+// Every node of the tree adds two equal-sized contiguous halves, so the result
+// is the pairwise tree over the P leaves whatever kernel or block shape
+// computes it, and with zero padding it equals the tree over the smallest
+// power of two >= the number of real leaves.
+template <int L>
+__device__ __forceinline__ float canon_wave(const float* leaves)
 {
-    const int j = threadIdx.x & 15;
-    T v[L];
+    const int t = threadIdx.x & 63;
+    float v[L];
 #pragma unroll
-    for (int t = 0; t < L; ++t) v[t] = leaves[(j * L + t) * stride];
+    for (int q = 0; q < L; ++q) v[q] = leaves[t * L + q];
 #pragma unroll
     for (int w = 1; w < L; w *= 2)
 #pragma unroll
-        for (int t = 0; t < L; t += 2 * w) v[t] = v[t] + v[t + w];
-    return rowsum16(v[0]);
+        for (int q = 0; q < L; q += 2 * w) v[q] = v[q] + v[q + w];
+    float x = rowsum16(v[0]);
+    {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // rows 0+1, 2+3
+    }
+    {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // lanes 0-31 + lanes 32-63
+    }
+    return x;
 }
 
 // ------------------------------------------------------------------ broadcast sources

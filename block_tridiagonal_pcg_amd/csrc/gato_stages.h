@@ -36,6 +36,14 @@ __device__ __forceinline__ float uniform(float x)
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
+// A flag taken through a wave ballot right where it is computed: the ballot
+// is convergent and cannot be moved, so the pivot tests it depends on run in
+// place instead of keeping every pivot alive until the flag is finally read.
+__device__ __forceinline__ bool lane_bit(uint64_t mask)
+{
+    return (mask >> (threadIdx.x & 63)) & 1u;
+}
+
 // ------------------------------------------------------------------ indexing
 
 template <class SH>
@@ -146,6 +154,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         for (int c = 0; c < NC; ++c)
             if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
         gj_steps<NP, NC>(qi, i, badq);
+        badq = lane_bit(__builtin_amdgcn_ballot_w64(badq));
         if (i < NC)
 #pragma unroll
             for (int c = 0; c < NC; ++c) K.Q[s][i][c] = qi[c];
@@ -155,6 +164,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         for (int c = 0; c < MC; ++c)
             if (c == i) ri[c] = urow ? ri[c] : 1.0f;
         gj_steps<NP, MC>(ri, i, badr);
+        badr = lane_bit(__builtin_amdgcn_ballot_w64(badr));
         if (i < MC)
 #pragma unroll
             for (int c = 0; c < MC; ++c) K.R[s][i][c] = ri[c];
@@ -245,6 +255,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         out.sd[c] = rowv ? sd[c] : 0.0f;
     }
     gj_steps<NP, NC>(di, i, bads);
+    bads = lane_bit(__builtin_amdgcn_ballot_w64(bads));
 #pragma unroll
     for (int c = 0; c < NC; ++c) L.xw[s][i][c] = di[c];
     __syncthreads();
@@ -352,8 +363,9 @@ struct PcgLds {
     // exchange rows for knots -1 .. K (index + 1); rows 0 and K + 1 stay zero
     float xv[K + 2][SH::NP];
     float xz[K + 2][SH::NP];
-    float red0[P];
-    float red12[2 * P];
+    float red0[P];  // per-knot partial sums: p'v
+    float red1[P];  //                        r'r
+    float red2[P];  //                        r'z
 };
 
 // Preconditioned CG on S lambda = gamma for one solve per workgroup (GATO
@@ -371,15 +383,15 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                                     int& iters_out, float& relres, int& flags_out)
 {
     constexpr int NP = SH::NP, SL = SH::SLOTS, KK = PcgLds<SH, C>::K, P = PcgLds<SH, C>::P;
-    constexpr int LPL = P / 16;
+    constexpr int LPW = P / 64;  // leaves per lane of the canonical sum
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     const bool lead = i == 0;
     const int nth = blockDim.x;
 
     for (int t = threadIdx.x; t < P; t += nth) {
         L.red0[t] = 0.0f;
-        L.red12[2 * t] = 0.0f;
-        L.red12[2 * t + 1] = 0.0f;
+        L.red1[t] = 0.0f;
+        L.red2[t] = 0.0f;
     }
     for (int t = threadIdx.x; t < NP; t += nth) {
         L.xv[0][t] = L.xv[KK + 1][t] = 0.0f;
@@ -397,7 +409,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         L.xv[row(c)][i] = lam[c];
     }
     __syncthreads();
-    const float gg = uniform(canon_sum<LPL>(L.red0));
+    const float gg = uniform(canon_wave<LPW>(L.red0));
     float lp[C], ln[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -454,14 +466,14 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             const float a = groupsum<NP>(r[c] * r[c]);
             const float bb = groupsum<NP>(r[c] * z[c]);
             if (lead) {
-                L.red12[2 * (row(c) - 1)] = a;
-                L.red12[2 * (row(c) - 1) + 1] = bb;
+                L.red1[row(c) - 1] = a;
+                L.red2[row(c) - 1] = bb;
             }
             L.xv[row(c)][i] = z[c];
         }
         __syncthreads();
-        rr = uniform(canon_sum<LPL>(L.red12, 2));
-        eta = uniform(canon_sum<LPL>(L.red12 + 1, 2));
+        rr = uniform(canon_wave<LPW>(L.red1));
+        eta = uniform(canon_wave<LPW>(L.red2));
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             pp[c] = L.xv[row(c) - 1][i];
@@ -488,7 +500,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 L.xv[row(c)][i] = v[c];
             }
             __syncthreads();
-            const float pSp = uniform(canon_sum<LPL>(L.red0));
+            const float pSp = uniform(canon_wave<LPW>(L.red0));
             float vp[C], vn[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -520,14 +532,14 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 const float ta = groupsum<NP>(r[c] * r[c]);
                 const float tb = groupsum<NP>(r[c] * z[c]);
                 if (lead) {
-                    L.red12[2 * (row(c) - 1)] = ta;
-                    L.red12[2 * (row(c) - 1) + 1] = tb;
+                    L.red1[row(c) - 1] = ta;
+                    L.red2[row(c) - 1] = tb;
                 }
                 L.xz[row(c)][i] = z[c];
             }
             __syncthreads();
-            rr = uniform(canon_sum<LPL>(L.red12, 2));
-            const float rz = uniform(canon_sum<LPL>(L.red12 + 1, 2));
+            rr = uniform(canon_wave<LPW>(L.red1));
+            const float rz = uniform(canon_wave<LPW>(L.red2));
             float zp[C], zn[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -652,15 +664,15 @@ __device__ __forceinline__ void merit_knot(const Params& p, int b, int k, int i,
 
 // Canonical sums of the per-knot merit values and the step selection
 // (argmin, ties to the earlier step; accepted only below merit0).
-template <int LPL>
+template <int LPW>
 __device__ __forceinline__ void merit_select(const Params& p, int b, const float* vals, int P, int32_t& best,
                                              int& lsfail)
 {
-    const float M0 = uniform(canon_sum<LPL>(vals));
+    const float M0 = uniform(canon_wave<LPW>(vals));
     float bv = 0.0f;
     int bi = 0;
     for (int j = 1; j <= p.n_alpha; ++j) {
-        const float v = uniform(canon_sum<LPL>(vals + j * P));
+        const float v = uniform(canon_wave<LPW>(vals + j * P));
         if (threadIdx.x == 0) p.merit[(size_t)b * p.n_alpha + (j - 1)] = v;
         if (j == 1 || v < bv) {
             bv = v;
