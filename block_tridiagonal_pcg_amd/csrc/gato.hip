@@ -23,7 +23,7 @@ struct FusedLds {
     union {
         FormLds<SH> form;
         PcgLds<SH, 1> pcg;
-        float mer[(GATO_MAX_ALPHA + 1) * 64];
+        alignas(16) float mer[(GATO_MAX_ALPHA + 1) * 64];
     } u;
     int flags;
 };
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
     __syncthreads();
     int32_t best;
     int lsfail;
-    merit_select<1>(p, b, L.u.mer, 64, best, lsfail);
+    merit_select<4>(p, b, L.u.mer, 64, best, lsfail);
     if (threadIdx.x == 0) {
         p.iters[b] = it;
         p.relres[b] = rel;
@@ -231,11 +231,11 @@ __global__ __launch_bounds__(SH::THREADS) void k_pcg_stream(Params p)
 
 // ------------------------------------------------------------------ stage 3 alone
 
-template <class SH, int LPW>
+template <class SH, int LPL>
 __global__ __launch_bounds__(1024) void k_merit(Params p)
 {
-    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, P = 64 * LPW;
-    __shared__ float mer[(GATO_MAX_ALPHA + 1) * P];
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, P = 16 * LPL;
+    __shared__ __align__(16) float mer[(GATO_MAX_ALPHA + 1) * P];
     const Ix<SH> ix{p.N};
     const int b = blockIdx.x;
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(1024) void k_merit(Params p)
     __syncthreads();
     int32_t best;
     int lsfail;
-    merit_select<LPW>(p, b, mer, P, best, lsfail);
+    merit_select<LPL>(p, b, mer, P, best, lsfail);
     if (threadIdx.x == 0) {
         p.best[b] = best;
         if (lsfail) p.flags[b] |= GATO_F_LS_FAILED;
@@ -313,12 +313,12 @@ struct Ops {
         const int P = leaves_for(p.N);
         const int waves = merit_waves_default(p.N, KPW);
         const dim3 g(p.B), blk(waves * 64);
-        switch (P / 64) {
-            case 1: hipLaunchKernelGGL((k_merit<SH, 1>), g, blk, 0, st, p); break;
-            case 2: hipLaunchKernelGGL((k_merit<SH, 2>), g, blk, 0, st, p); break;
+        switch (P / 16) {
             case 4: hipLaunchKernelGGL((k_merit<SH, 4>), g, blk, 0, st, p); break;
             case 8: hipLaunchKernelGGL((k_merit<SH, 8>), g, blk, 0, st, p); break;
             case 16: hipLaunchKernelGGL((k_merit<SH, 16>), g, blk, 0, st, p); break;
+            case 32: hipLaunchKernelGGL((k_merit<SH, 32>), g, blk, 0, st, p); break;
+            case 64: hipLaunchKernelGGL((k_merit<SH, 64>), g, blk, 0, st, p); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();

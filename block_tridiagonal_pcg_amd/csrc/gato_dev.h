@@ -112,35 +112,68 @@ __device__ __forceinline__ T groupsum(T x)
     return x;
 }
 
-// Canonical pairwise sum of P = 64 * L leaves held in LDS (zero-padded), in
-// every lane of the wave: lane t reads its L contiguous leaves (conflict-free
-// LDS access) and sums them pairwise, the 16-lane butterfly combines the lanes
-// of each row, and two swap-adds combine rows 0+1, 2+3 and then the halves.
-// Every node of the tree adds two equal-sized contiguous halves, so the result
-// is the pairwise tree over the P leaves whatever kernel or block shape
-// computes it, and with zero padding it equals the tree over the smallest
-// power of two >= the number of real leaves.
+// Canonical pairwise sum of P = 16 * L leaves held in LDS (zero-padded, 16-byte
+// aligned, L a multiple of 4), in every lane: lane j of each 16-lane row reads
+// leaves [j L, (j+1) L) with 16-byte loads and sums them pairwise, and the row
+// butterfly combines the 16 partial sums.  Every node of the tree adds two
+// equal-sized contiguous halves, so the result is the pairwise tree over the P
+// leaves whatever kernel or block shape computes it, and with zero padding it
+// equals the tree over the smallest power of two >= the number of real leaves.
 template <int L>
-__device__ __forceinline__ float canon_wave(const float* leaves)
+__device__ __forceinline__ void canon_leaves(const float* leaves, float (&v)[L])
 {
-    const int t = threadIdx.x & 63;
-    float v[L];
+    static_assert(L % 4 == 0, "leaves are read four at a time");
+    const float4* q = reinterpret_cast<const float4*>(leaves) + (threadIdx.x & 15) * (L / 4);
 #pragma unroll
-    for (int q = 0; q < L; ++q) v[q] = leaves[t * L + q];
+    for (int t = 0; t < L / 4; ++t) {
+        const float4 f = q[t];
+        v[4 * t] = f.x;
+        v[4 * t + 1] = f.y;
+        v[4 * t + 2] = f.z;
+        v[4 * t + 3] = f.w;
+    }
+}
+
+template <int L>
+__device__ __forceinline__ float canon_tree(float (&v)[L])
+{
 #pragma unroll
     for (int w = 1; w < L; w *= 2)
 #pragma unroll
-        for (int q = 0; q < L; q += 2 * w) v[q] = v[q] + v[q + w];
-    float x = rowsum16(v[0]);
-    {
-        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // rows 0+1, 2+3
-    }
-    {
-        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // lanes 0-31 + lanes 32-63
-    }
-    return x;
+        for (int t = 0; t < L; t += 2 * w) v[t] = v[t] + v[t + w];
+    return rowsum16(v[0]);
+}
+
+template <int L>
+__device__ __forceinline__ float canon_sum(const float* leaves)
+{
+    float v[L];
+    canon_leaves<L>(leaves, v);
+    return canon_tree<L>(v);
+}
+
+// Two canonical sums with their loads issued together.
+template <int L>
+__device__ __forceinline__ void canon_sum2(const float* la, const float* lb, float& a, float& b)
+{
+    float va[L], vb[L];
+    canon_leaves<L>(la, va);
+    canon_leaves<L>(lb, vb);
+#pragma unroll
+    for (int w = 1; w < L; w *= 2)
+#pragma unroll
+        for (int t = 0; t < L; t += 2 * w) {
+            va[t] = va[t] + va[t + w];
+            vb[t] = vb[t] + vb[t + w];
+        }
+    a = va[0] + dpp<DPP_QP_1032>(va[0]);
+    b = vb[0] + dpp<DPP_QP_1032>(vb[0]);
+    a = a + dpp<DPP_QP_2301>(a);
+    b = b + dpp<DPP_QP_2301>(b);
+    a = a + dpp<DPP_ROW_HALF_MIRROR>(a);
+    b = b + dpp<DPP_ROW_HALF_MIRROR>(b);
+    a = a + dpp<DPP_ROW_MIRROR>(a);
+    b = b + dpp<DPP_ROW_MIRROR>(b);
 }
 
 // ------------------------------------------------------------------ broadcast sources

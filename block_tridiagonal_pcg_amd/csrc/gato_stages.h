@@ -31,6 +31,10 @@ struct Params {
 
 // The same value in every lane (the reductions below produce identical bits in
 // all lanes); moving it to a scalar register lets branches on it be scalar.
+// Materialise x in a register here, so that a load feeding it is issued and
+// waited for at this point rather than sunk past a later branch.
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+
 __device__ __forceinline__ float uniform(float x)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -363,9 +367,9 @@ struct PcgLds {
     // exchange rows for knots -1 .. K (index + 1); rows 0 and K + 1 stay zero
     float xv[K + 2][SH::NP];
     float xz[K + 2][SH::NP];
-    float red0[P];  // per-knot partial sums: p'v
-    float red1[P];  //                        r'r
-    float red2[P];  //                        r'z
+    alignas(16) float red0[P];  // per-knot partial sums: p'v
+    alignas(16) float red1[P];  //                        r'r
+    alignas(16) float red2[P];  //                        r'z
 };
 
 // Preconditioned CG on S lambda = gamma for one solve per workgroup (GATO
@@ -383,7 +387,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                                     int& iters_out, float& relres, int& flags_out)
 {
     constexpr int NP = SH::NP, SL = SH::SLOTS, KK = PcgLds<SH, C>::K, P = PcgLds<SH, C>::P;
-    constexpr int LPW = P / 64;  // leaves per lane of the canonical sum
+    constexpr int LPL = P / 16;  // leaves per lane of the canonical sum
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     const bool lead = i == 0;
     const int nth = blockDim.x;
@@ -409,7 +413,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         L.xv[row(c)][i] = lam[c];
     }
     __syncthreads();
-    const float gg = uniform(canon_wave<LPW>(L.red0));
+    const float gg = uniform(canon_sum<LPL>(L.red0));
     float lp[C], ln[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -472,8 +476,9 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             L.xv[row(c)][i] = z[c];
         }
         __syncthreads();
-        rr = uniform(canon_wave<LPW>(L.red1));
-        eta = uniform(canon_wave<LPW>(L.red2));
+        canon_sum2<LPL>(L.red1, L.red2, rr, eta);
+        rr = uniform(rr);
+        eta = uniform(eta);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             pp[c] = L.xv[row(c) - 1][i];
@@ -482,14 +487,13 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         }
         __syncthreads();
     }
-    bool conv = rr <= tol2;
     if (!__builtin_isfinite(rr)) flags |= GATO_F_NONFINITE;
-    if (!conv && !flags) {
+    if (!(rr <= tol2) && !flags && iters >= p.max_iters) flags |= GATO_F_PCG_MAXITER;
+    if (!(rr <= tol2) && !flags) {
+        // One exit, after the second barrier: a breakdown at the first one leaves
+        // lambda, r and the count as they are and only sets the stop code, so every
+        // loop-carried value has a single definition per iteration.
         for (;;) {
-            if (iters >= p.max_iters) {
-                flags |= GATO_F_PCG_MAXITER;
-                break;
-            }
             // v = S p ; p'v ; v to neighbours
             float v[C];
 #pragma unroll
@@ -500,30 +504,32 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 L.xv[row(c)][i] = v[c];
             }
             __syncthreads();
-            const float pSp = uniform(canon_wave<LPW>(L.red0));
             float vp[C], vn[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 vp[c] = L.xv[row(c) - 1][i];
                 vn[c] = L.xv[row(c) + 1][i];
             }
-            if (!__builtin_isfinite(pSp)) {
-                flags |= GATO_F_NONFINITE;
-                break;
+            const float pSp = uniform(canon_sum<LPL>(L.red0));
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                pin(vp[c]);
+                pin(vn[c]);
             }
-            if (!(pSp > 0.0f)) {
-                flags |= GATO_F_PCG_BREAKDOWN;
-                break;
-            }
+            int stop = !__builtin_isfinite(pSp) ? GATO_F_NONFINITE : !(pSp > 0.0f) ? GATO_F_PCG_BREAKDOWN : 0;
             const float a = uniform(eta * __builtin_amdgcn_rcpf(pSp));
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                lamd[c] = fma((double)a, (double)pv[c], lamd[c]);
-                r[c] = fmaf(-a, v[c], r[c]);
-                rp[c] = fmaf(-a, vp[c], rp[c]);
-                rn[c] = fmaf(-a, vn[c], rn[c]);
+                const double l1 = fma((double)a, (double)pv[c], lamd[c]);
+                const float r1 = fmaf(-a, v[c], r[c]);
+                const float rp1 = fmaf(-a, vp[c], rp[c]);
+                const float rn1 = fmaf(-a, vn[c], rn[c]);
+                lamd[c] = stop ? lamd[c] : l1;
+                r[c] = stop ? r[c] : r1;
+                rp[c] = stop ? rp[c] : rp1;
+                rn[c] = stop ? rn[c] : rn1;
             }
-            ++iters;
+            iters += stop ? 0 : 1;
             // z = Phi^-1 r ; r'r, r'z ; z to neighbours
             float z[C];
 #pragma unroll
@@ -538,24 +544,29 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 L.xz[row(c)][i] = z[c];
             }
             __syncthreads();
-            rr = uniform(canon_wave<LPW>(L.red1));
-            const float rz = uniform(canon_wave<LPW>(L.red2));
             float zp[C], zn[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 zp[c] = L.xz[row(c) - 1][i];
                 zn[c] = L.xz[row(c) + 1][i];
             }
-            if (!__builtin_isfinite(rr)) {
-                flags |= GATO_F_NONFINITE;
-                break;
+            float rz;
+            canon_sum2<LPL>(L.red1, L.red2, rr, rz);
+            rr = uniform(rr);
+            rz = uniform(rz);
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                pin(zp[c]);
+                pin(zn[c]);
             }
-            if (rr <= tol2) {
-                conv = true;
-                break;
+            if (!stop) {
+                if (!__builtin_isfinite(rr)) stop = GATO_F_NONFINITE;
+                else if (rr <= tol2) stop = -1;  // converged
+                else if (!__builtin_isfinite(rz)) stop = GATO_F_NONFINITE;
+                else if (iters >= p.max_iters) stop = GATO_F_PCG_MAXITER;
             }
-            if (!__builtin_isfinite(rz)) {
-                flags |= GATO_F_NONFINITE;
+            if (stop) {
+                if (stop > 0) flags |= stop;
                 break;
             }
             const float be = uniform(rz * __builtin_amdgcn_rcpf(eta));
@@ -664,15 +675,15 @@ __device__ __forceinline__ void merit_knot(const Params& p, int b, int k, int i,
 
 // Canonical sums of the per-knot merit values and the step selection
 // (argmin, ties to the earlier step; accepted only below merit0).
-template <int LPW>
+template <int LPL>
 __device__ __forceinline__ void merit_select(const Params& p, int b, const float* vals, int P, int32_t& best,
                                              int& lsfail)
 {
-    const float M0 = uniform(canon_wave<LPW>(vals));
+    const float M0 = uniform(canon_sum<LPL>(vals));
     float bv = 0.0f;
     int bi = 0;
     for (int j = 1; j <= p.n_alpha; ++j) {
-        const float v = uniform(canon_wave<LPW>(vals + j * P));
+        const float v = uniform(canon_sum<LPL>(vals + j * P));
         if (threadIdx.x == 0) p.merit[(size_t)b * p.n_alpha + (j - 1)] = v;
         if (j == 1 || v < bv) {
             bv = v;
