@@ -54,13 +54,16 @@ __global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
     L.u.pcg.xv[s + 1][i] = lam;
     __syncthreads();
     const float lamn = L.u.pcg.xv[s + 2][i];
-    float qi[NC], ri[MC];
+    float qi[NC], ri[MC], bc[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qi[c] = L.park.Q[s][i < NC ? i : 0][c];
+    for (int c = 0; c < NC; ++c) {
+        qi[c] = L.park.Q[s][i < NC ? i : 0][c];
+        bc[c] = L.park.Bt[s][i < MC ? i : 0][c];
+    }
 #pragma unroll
     for (int c = 0; c < MC; ++c) ri[c] = L.park.R[s][i < MC ? i : 0][c];
     float dx, du;
-    recover<SH>(p, b, k, i, lam, lamn, qi, ri, dx, du);
+    recover<SH>(i, rowv, hn && i < MC, lam, lamn, qi, rw.sup, L.park.h[s][i], bc, L.park.rv[s][i], ri, dx, du);
     if (rowv) {
         p.lambda[ix.vn(b, k, i)] = lam;
         p.dz[ix.dx(b, k, i)] = dx;
@@ -169,11 +172,18 @@ __device__ __forceinline__ void pcg_and_recover(const Params& p, const MAT& M, P
         const int k = c * SL + s;
         const float lamn = L.xv[k + 2][i];
         const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC;
-        float qi[NC], ri[MC];
+        const bool urow = hn && i < MC;
+        float qi[NC], ri[MC], bc[NC], sup[NC];
         ld_row<NC>(p.Qinv, ix.Q(b, k, i), rowv, qi);
-        ld_row<MC>(p.Rinv, ix.R(b, k, i), hn && i < MC, ri);
+        ld_row<MC>(p.Rinv, ix.R(b, k, i), urow, ri);
+        ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, bc);  // column i of B_k
+        M.sup(k, sup);
+        const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
+        const float rv = ld1(p.r, ix.vm(b, k, i), urow);
+        float h = 0.0f;  // (Q~_k^-1 q_k)_i, with the formation's arithmetic
+        dotb<NP, NC>(h, Bc<NP>(qv), qi);
         float dx, du;
-        recover<SH>(p, b, k, i, lam[c], lamn, qi, ri, dx, du);
+        recover<SH>(i, rowv, urow, lam[c], lamn, qi, sup, h, bc, rv, ri, dx, du);
         if (rowv) {
             p.lambda[ix.vn(b, k, i)] = lam[c];
             p.dz[ix.dx(b, k, i)] = dx;
@@ -471,7 +481,7 @@ int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, con
 }
 
 int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
-                   const float* gamma, const float* Qinv, const float* Rinv, const float* A,
+                   const float* gamma, const float* Qinv, const float* Rinv,
                    const float* Bu, const float* q, const float* r, float eps, int32_t max_iters,
                    float* lambda, float* dz, int32_t* iters, float* relres, int32_t* flags,
                    hipStream_t stream)
@@ -479,14 +489,14 @@ int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
     int rc = check_dims(dims);
     if (rc) return rc;
     if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
-    rc = check_ptrs({S, Pinv, gamma, Qinv, dyn(Rinv, dims), dyn(A, dims), dyn(Bu, dims), q, dyn(r, dims),
+    rc = check_ptrs({S, Pinv, gamma, Qinv, dyn(Rinv, dims), dyn(Bu, dims), q, dyn(r, dims),
                      lambda, dz, iters, relres, flags});
     if (rc) return rc;
     if (!(eps > 0.0f) || max_iters < 1) return GATO_E_PARAM;
     Params p = make_params(dims);
     p.S = const_cast<float*>(S); p.Pinv = const_cast<float*>(Pinv); p.gamma = const_cast<float*>(gamma);
     p.Qinv = const_cast<float*>(Qinv); p.Rinv = const_cast<float*>(Rinv);
-    p.A = A; p.Bu = Bu; p.q = q; p.r = r;
+    p.Bu = Bu; p.q = q; p.r = r;
     p.eps = eps; p.max_iters = max_iters;
     p.lambda = lambda; p.dz = dz; p.iters = iters; p.relres = relres; p.flags = flags;
     return with_shape(dims->n, dims->m, [&](auto ops) {

@@ -112,11 +112,14 @@ struct FormLds {
     float xg[SH::SLOTS][SH::NP];
 };
 
-// ... and the G^-1 rows it parks, which the fused step keeps for the recovery.
+// ... and what it parks, which the fused step keeps for the recovery.
 template <class SH>
 struct Park {
-    float Q[SH::SLOTS][SH::NC][SH::NC];  // Q~_k^-1 rows
-    float R[SH::SLOTS][SH::MC][SH::MC];  // R_k^-1 rows
+    float Q[SH::SLOTS][SH::NC][SH::NC];   // Q~_k^-1 rows
+    float R[SH::SLOTS][SH::MC][SH::MC];   // R_k^-1 rows
+    float Bt[SH::SLOTS][SH::MC][SH::NC];  // B_k columns (rows of B_k')
+    float h[SH::SLOTS][SH::NP];           // Q~_k^-1 q_k
+    float rv[SH::SLOTS][SH::NP];          // r_k
 };
 
 // ------------------------------------------------------------------ stage 1: form
@@ -129,9 +132,10 @@ struct Park {
 // becomes a workgroup barrier because a workgroup holds whole horizons, or a
 // window with two knots of halo before and one after).
 //
-// Q~_k^-1 and R_k^-1 rows are parked in LDS (K; the caller may keep
-// them for the recovery) and handed to `sink` for storing.  `fl` gets the
-// Q/R/S_NOT_SPD bits of this knot.
+// Q~_k^-1 and R_k^-1 rows, B_k's columns, Q~_k^-1 q_k and r_k are parked in
+// LDS (K; the fused step keeps them for the recovery); the inverse rows are
+// also handed to `sink` for storing.  `fl` gets the Q/R/S_NOT_SPD bits of this
+// knot.
 template <class SH, class Sink>
 __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, FormLds<SH>& L, Park<SH>& K,
                                      Rows<SH>& out, int& fl, Sink sink)
@@ -187,6 +191,9 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, ar);
         float br[MC];
         ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, br);
+        if (i < NC)
+#pragma unroll
+            for (int c = 0; c < MC; ++c) K.Bt[s][c][i] = br[c];  // transpose of B_k
 #pragma unroll
         for (int c = 0; c < NC; ++c) W[c] = 0.0f;
 #pragma unroll
@@ -202,6 +209,8 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         dotb<NP, NC>(t1, qb, W);
         dotb<NP, MC>(t2, Bc<NP>(rv), V);
         g = (ev - t1) - t2;
+        K.h[s][i] = h;
+        K.rv[s][i] = rv;
 #pragma unroll
         for (int c = 0; c < NC; ++c) L.xw[s][i][c] = W[c];
     }
@@ -228,7 +237,11 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         }
         gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(O), nar);
         // lane i < m holds column i of B_k
-        ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, bcol);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float bt = K.Bt[s][i < MC ? i : 0][c];
+            bcol[c] = urow ? bt : 0.0f;
+        }
         gemm_rows<NP, NC, MC>(U, BcRow<NP, NC>(bcol), V);
 #pragma unroll
         for (int c = 0; c < NC; ++c) L.xw[s][i][c] = U[c];
@@ -325,6 +338,11 @@ struct RegMat {
         dotb<NP, NC>(v, Bc<NP>(xn), rw->pup);
         return v;
     }
+    __device__ __forceinline__ void sup(int, float (&out)[SH::NC]) const
+    {
+#pragma unroll
+        for (int c = 0; c < SH::NC; ++c) out[c] = rw->sup[c];
+    }
 };
 
 // Block-tridiagonal rows read from global memory at every product (for
@@ -350,6 +368,10 @@ struct GlobalMat {
     }
     __device__ __forceinline__ float S(int k, float xp, float x, float xn) const { return mv(Sm, k, xp, x, xn); }
     __device__ __forceinline__ float P(int k, float xp, float x, float xn) const { return mv(Pm, k, xp, x, xn); }
+    __device__ __forceinline__ void sup(int k, float (&out)[SH::NC]) const
+    {
+        ld_row<SH::NC>(Sm, ix.blk(b, k, 2, i), k < ix.N && i < SH::NC, out);
+    }
 };
 
 // Leaves of the canonical knot sums: at least 64 and a power of two.
@@ -592,33 +614,26 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
 // ------------------------------------------------------------------ stage 2b: recovery
 
 // dx_k = Q~_k^-1 (lambda_k - A_k' lambda_{k+1} - q_k), du_k = R_k^-1 (-B_k' lambda_{k+1} - r_k)
-// (the back-substitution of the Schur solve, GATO paper Sec. II eq. 4).
+// (the back-substitution of the Schur solve, GATO paper Sec. II eq. 4).  The
+// A_k term is taken from the upper block of S, S_{k,k+1} = -Q~_k^-1 A_k', so
+//   dx_k = Q~_k^-1 lambda_k + S_{k,k+1} lambda_{k+1} - Q~_k^-1 q_k,
+// which needs no A_k.  Lane i holds row i of Q~_k^-1, S_{k,k+1} and R_k^-1,
+// column i of B_k, (Q~_k^-1 q_k)_i as h and (r_k)_i as rv.
 template <class SH>
-__device__ __forceinline__ void recover(const Params& p, int b, int k, int i, float lam, float lamn,
-                                        const float* qi, const float* ri, float& dx, float& du)
+__device__ __forceinline__ void recover(int i, bool rowv, bool urow, float lam, float lamn, const float* qi,
+                                        const float* sup, float h, const float* bcol, float rv, const float* ri,
+                                        float& dx, float& du)
 {
     constexpr int NC = SH::NC, MC = SH::MC, NP = SH::NP;
-    const Ix<SH> ix{p.N};
-    const int N = p.N;
-    const bool kv = k < N;
-    const bool hn = kv && k < N - 1;
-    const bool rowv = kv && i < NC;
-    const bool urow = hn && i < MC;
-    float acol[NC], bcol[NC];
-    ld_row<NC, NC>(p.A, ix.A(b, k, 0) + i, hn && i < NC, acol);  // column i of A_k
-    ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, bcol);        // column i of B_k
     const Bc<NP> lnb(lamn);
-    float t = 0.0f, tb = 0.0f;
-    dotb<NP, NC>(t, lnb, acol);
+    float x = 0.0f, tb = 0.0f;
+    dotb<NP, NC>(x, Bc<NP>(lam), qi);
+    dotb<NP, NC>(x, lnb, sup);
     dotb<NP, NC>(tb, lnb, bcol);
-    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
-    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
-    const float w = rowv ? (lam - qv) - t : 0.0f;
     const float u = urow ? -tb - rv : 0.0f;
-    float x = 0.0f, y = 0.0f;
-    dotb<NP, NC>(x, Bc<NP>(w), qi);
+    float y = 0.0f;
     dotb<NP, MC>(y, Bc<NP>(u), ri);
-    dx = rowv ? x : 0.0f;
+    dx = rowv ? x - h : 0.0f;
     du = urow ? y : 0.0f;
 }
 

@@ -73,7 +73,7 @@ def load():
             lib = ctypes.CDLL(_LIB_PATH)
             P, I, F, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
             lib.gato_form_schur.argtypes = [P] * 17
-            lib.gato_pcg_solve.argtypes = [P] * 10 + [F, I] + [P] * 6
+            lib.gato_pcg_solve.argtypes = [P] * 9 + [F, I] + [P] * 6
             lib.gato_merit_eval.argtypes = [P] * 11 + [I, F] + [P] * 5
             lib.gato_sqp_step.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P]
             lib.gato_workspace_bytes.argtypes = [P, I]
@@ -154,17 +154,17 @@ def gato_form_schur(dims, Q, q, R, r, A, Bu, e, x0, rho, S, Pinv, gamma, Qinv, R
     return _raise("gato_form_schur", rc)
 
 
-def gato_pcg_solve(dims, S, Pinv, gamma, Qinv, Rinv, A, Bu, q, r, eps, max_iters, lam, dz, iters, relres,
+def gato_pcg_solve(dims, S, Pinv, gamma, Qinv, Rinv, Bu, q, r, eps, max_iters, lam, dz, iters, relres,
                    flags, stream=None):
     n, m, N, B = dims
     sh = _shapes(n, m, N, B)
-    for t, k in ((S, "S"), (Pinv, "Pinv"), (gamma, "gamma"), (Qinv, "Qinv"), (Rinv, "Rinv"), (A, "A"),
+    for t, k in ((S, "S"), (Pinv, "Pinv"), (gamma, "gamma"), (Qinv, "Qinv"), (Rinv, "Rinv"),
                  (Bu, "Bu"), (q, "q"), (r, "r"), (lam, "lam"), (dz, "dz"), (relres, "B_")):
         _chk(t, k, shape=sh[k])
     _chk(iters, "iters", torch.int32, sh["B_"])
     _chk(flags, "flags", torch.int32, sh["B_"])
     d = _dims(n, m, N, B)
-    rc = load().gato_pcg_solve(ctypes.byref(d), _p(S), _p(Pinv), _p(gamma), _p(Qinv), _p(Rinv), _p(A), _p(Bu),
+    rc = load().gato_pcg_solve(ctypes.byref(d), _p(S), _p(Pinv), _p(gamma), _p(Qinv), _p(Rinv), _p(Bu),
                                _p(q), _p(r), float(eps), int(max_iters), _p(lam), _p(dz), _p(iters),
                                _p(relres), _p(flags), _stream(stream))
     return _raise("gato_pcg_solve", rc)
@@ -306,7 +306,7 @@ def stage_times(dims, dev, eps, max_iters, alphas, mu, reps=10, stream=None):
         ev[1].record(st)
         out["lam"].zero_()
         ev[2].record(st)
-        gato_pcg_solve(dims, out["S"], out["Pinv"], out["gamma"], out["Qinv"], out["Rinv"], dev["A"], dev["Bu"],
+        gato_pcg_solve(dims, out["S"], out["Pinv"], out["gamma"], out["Qinv"], out["Rinv"], dev["Bu"],
                        dev["q"], dev["r"], eps, max_iters, out["lam"], out["dz"], out["iters"], out["relres"],
                        out["flags"], stream=st)
         ev[3].record(st)

@@ -141,12 +141,15 @@ int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, con
  *   stop when ||r||_2 <= eps ||gamma||_2;  z = Phi^-1 r; p = z + (r'z / eta) p.
  * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  Then the step
  *   dx_k = Qinv_k (lambda_k - A_k' lambda_{k+1} - q_k),  dx_{N-1} = Qinv_{N-1}(lambda_{N-1} - q_{N-1}),
- *   du_k = Rinv_k (-B_k' lambda_{k+1} - r_k).
+ *   du_k = Rinv_k (-B_k' lambda_{k+1} - r_k),
+ * evaluated as dx_k = Qinv_k lambda_k + S_{k,k+1} lambda_{k+1} - Qinv_k q_k, since
+ * S_{k,k+1} = -Q~_k^-1 A_k' (so A is not an argument: S, Qinv, q, Bu, Rinv, r
+ * must be those of one problem, as gato_form_schur writes them).
  * Writes lambda, dz, iters (S-products in the loop), relres (recurred
  * ||r|| / ||gamma||) and ORs PCG_MAXITER / PCG_BREAKDOWN / NONFINITE into flags.
  */
 int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
-                   const float* gamma, const float* Qinv, const float* Rinv, const float* A,
+                   const float* gamma, const float* Qinv, const float* Rinv,
                    const float* Bu, const float* q, const float* r, float eps, int32_t max_iters,
                    float* lambda, float* dz, int32_t* iters, float* relres, int32_t* flags,
                    hipStream_t stream);

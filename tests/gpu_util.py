@@ -38,7 +38,7 @@ def gpu_pcg(batch, form, eps, max_iters, lambda0=None, flags=None):
     relres = torch.zeros(B, dtype=torch.float32, device="cuda")
     fl = torch.as_tensor(np.zeros(B, np.int32) if flags is None else np.asarray(flags, np.int32)).cuda()
     ops.gato_pcg_solve(dims, t(form["S"]), t(form["Pinv"]), t(form["gamma"]), t(form["Qinv"]), t(form["Rinv"]),
-                       t(batch["A"]), t(batch["Bu"]), t(batch["q"]), t(batch["r"]), eps, max_iters, lam, dz,
+                       t(batch["Bu"]), t(batch["q"]), t(batch["r"]), eps, max_iters, lam, dz,
                        iters, relres, fl)
     torch.cuda.synchronize()
     return dict(lam=cpu(lam), dz=cpu(dz), iters=cpu(iters), relres=cpu(relres), flags=cpu(fl))

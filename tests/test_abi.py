@@ -84,9 +84,9 @@ def test_validation_happens_before_any_launch(lib):
     P = [ctypes.c_void_p(4096 * (j + 1)) for j in range(17)]
     f = lib.gato_pcg_solve
     # eps <= 0 and max_iters < 1
-    assert f(ctypes.byref(d), *P[:9], 0.0, 10, *P[9:14], None) == ops.E_PARAM
-    assert f(ctypes.byref(d), *P[:9], 1e-6, 0, *P[9:14], None) == ops.E_PARAM
-    assert f(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:9], 1e-6, 10, *P[9:14], None) == ops.OK
+    assert f(ctypes.byref(d), *P[:8], 0.0, 10, *P[8:13], None) == ops.E_PARAM
+    assert f(ctypes.byref(d), *P[:8], 1e-6, 0, *P[8:13], None) == ops.E_PARAM
+    assert f(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:8], 1e-6, 10, *P[8:13], None) == ops.OK
 
     al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
     g = lib.gato_merit_eval
