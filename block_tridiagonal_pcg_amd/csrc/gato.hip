@@ -78,7 +78,9 @@ __global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
     __syncthreads();
     for (int t = threadIdx.x; t < (GATO_MAX_ALPHA + 1) * 64; t += blockDim.x) L.u.mer[t] = 0.0f;
     __syncthreads();
-    merit_knot<SH>(p, b, k, i, dx, du, dxn, L.u.mer + k, 64);
+    MeritIn<SH> mi;
+    merit_rows<SH>(p, b, k, i, mi);
+    merit_knot<SH>(p, k, i, mi, dx, du, dxn, L.u.mer + k, 64);
     __syncthreads();
     int32_t best;
     int lsfail;
@@ -258,7 +260,9 @@ __global__ __launch_bounds__(1024) void k_merit(Params p)
         const float dx = ld1(p.dz, ix.dx(b, k, i), rowv);
         const float du = ld1(p.dz, ix.du(b, k, i), hn && i < MC);
         const float dxn = ld1(p.dz, ix.dx(b, k + 1, i), hn && i < NC);
-        merit_knot<SH>(p, b, k, i, dx, du, dxn, mer + (kv ? k : 0), P);
+        MeritIn<SH> mi;
+        merit_rows<SH>(p, b, k, i, mi);
+        merit_knot<SH>(p, k, i, mi, dx, du, dxn, mer + (kv ? k : 0), P);
     }
     __syncthreads();
     int32_t best;

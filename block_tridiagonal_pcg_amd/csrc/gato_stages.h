@@ -639,6 +639,31 @@ __device__ __forceinline__ void recover(int i, bool rowv, bool urow, float lam, 
 
 // ------------------------------------------------------------------ stage 3: merit
 
+// The problem rows and entries one lane needs for its knot's merit terms:
+// row i of Q_k, A_k (n wide), R_k and B_k (m wide), and q, r, e, x0 entries;
+// zeros where the row or entry does not exist.
+template <class SH>
+struct MeritIn {
+    float Q[SH::NC], A[SH::NC], R[SH::MC], B[SH::MC];
+    float q, r, e, x0;
+};
+
+template <class SH>
+__device__ __forceinline__ void merit_rows(const Params& p, int b, int k, int i, MeritIn<SH>& in)
+{
+    constexpr int NC = SH::NC, MC = SH::MC;
+    const Ix<SH> ix{p.N};
+    const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC, urow = hn && i < MC;
+    ld_row<NC>(p.Q, ix.Q(b, k, i), rowv, in.Q);
+    ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, in.A);
+    ld_row<MC>(p.R, ix.R(b, k, i), urow, in.R);
+    ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, in.B);
+    in.q = ld1(p.q, ix.vn(b, k, i), rowv);
+    in.r = ld1(p.r, ix.vm(b, k, i), urow);
+    in.e = ld1(p.e, ix.e(b, k, i), hn && i < NC);
+    in.x0 = ld1(p.x0, (size_t)b * NC + i, rowv && k == 0);
+}
+
 // Per-knot merit terms at a = 0 and at every step size (GATO paper Sec. II
 // eq. 3; Sec. III eq. 7):
 //   m_k(a) = a LIN + (a^2/2) QUAD + mu L1(a),
@@ -648,66 +673,78 @@ __device__ __forceinline__ void recover(int i, bool rowv, bool urow, float lam, 
 // is explicit, so a knot's values do not depend on the kernel computing them.
 // The group's lane 0 writes value j (j = 0: a = 0) to out[j * stride].
 template <class SH>
-__device__ __forceinline__ void merit_knot(const Params& p, int b, int k, int i, float dx, float du,
+__device__ __forceinline__ void merit_knot(const Params& p, int k, int i, const MeritIn<SH>& in, float dx, float du,
                                            float dxn, float* out, int stride)
 {
     constexpr int NC = SH::NC, MC = SH::MC, NP = SH::NP;
-    const Ix<SH> ix{p.N};
     const int N = p.N;
     const bool kv = k < N;
     const bool hn = kv && k < N - 1;
-    const bool rowv = kv && i < NC;
-    const bool urow = hn && i < MC;
-    float Qr[NC], Ar[NC], Rr[MC], Br[MC];
-    ld_row<NC>(p.Q, ix.Q(b, k, i), rowv, Qr);
-    ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, Ar);
-    ld_row<MC>(p.R, ix.R(b, k, i), urow, Rr);
-    ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, Br);
-    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
-    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
-    const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
-    const float x0v = ld1(p.x0, (size_t)b * NC + i, rowv && k == 0);
-
     const Bc<NP> xb(dx), ub(du);
     float Qdx = 0.0f, Rdu = 0.0f, d = 0.0f;
-    dotb<NP, NC>(Qdx, xb, Qr);
-    dotb<NP, MC>(Rdu, ub, Rr);
-    dotb<NP, NC>(d, xb, Ar);
-    dotb<NP, MC>(d, ub, Br);
+    dotb<NP, NC>(Qdx, xb, in.Q);
+    dotb<NP, MC>(Rdu, ub, in.R);
+    dotb<NP, NC>(d, xb, in.A);
+    dotb<NP, MC>(d, ub, in.B);
     d = hn ? __fsub_rn(d, dxn) : 0.0f;
-    const float lin = groupsum<NP>(__fadd_rn(__fmul_rn(qv, dx), __fmul_rn(rv, du)));
+    const float lin = groupsum<NP>(__fadd_rn(__fmul_rn(in.q, dx), __fmul_rn(in.r, du)));
     const float quad = groupsum<NP>(__fadd_rn(__fmul_rn(dx, Qdx), __fmul_rn(du, Rdu)));
-    for (int j = 0; j <= p.n_alpha; ++j) {
-        const float a = (j == 0) ? 0.0f : p.alphas[j - 1];
-        float l1 = fabsf(__fmaf_rn(a, d, ev));
-        if (k == 0) l1 = __fadd_rn(l1, fabsf(__fmaf_rn(-a, dx, x0v)));
-        const float L1 = groupsum<NP>(l1);
-        const float val = __fadd_rn(__fadd_rn(__fmul_rn(a, lin), __fmul_rn(__fmul_rn(0.5f, __fmul_rn(a, a)), quad)),
-                                    __fmul_rn(p.mu, L1));
-        if (i == 0 && kv) out[j * stride] = val;
+    const bool k0 = k == 0;
+#pragma unroll 1
+    for (int j = 0; j <= GATO_MAX_ALPHA; ++j) {
+        if (j <= p.n_alpha) {
+            const float a = (j == 0) ? 0.0f : p.alphas[j - 1];
+            float l1 = fabsf(__fmaf_rn(a, d, in.e));
+            const float l0 = __fadd_rn(l1, fabsf(__fmaf_rn(-a, dx, in.x0)));
+            l1 = k0 ? l0 : l1;
+            const float L1 = groupsum<NP>(l1);
+            const float val = __fadd_rn(
+                __fadd_rn(__fmul_rn(a, lin), __fmul_rn(__fmul_rn(0.5f, __fmul_rn(a, a)), quad)), __fmul_rn(p.mu, L1));
+            if (i == 0 && kv) out[j * stride] = val;
+        }
     }
 }
 
 // Canonical sums of the per-knot merit values and the step selection
-// (argmin, ties to the earlier step; accepted only below merit0).
+// (argmin, ties to the earlier step; accepted only below merit0).  Only wave 0
+// takes part: its four 16-lane rows form the sums of different step sizes side
+// by side (row r takes j = r, r + 4, ...), row leaders store them, and every
+// lane of the wave reads them back in j order for the selection.  Returns
+// false in the other waves (best and lsfail are then not set).
 template <int LPL>
-__device__ __forceinline__ void merit_select(const Params& p, int b, const float* vals, int P, int32_t& best,
+__device__ __forceinline__ bool merit_select(const Params& p, int b, const float* vals, int P, int32_t& best,
                                              int& lsfail)
 {
-    const float M0 = uniform(canon_sum<LPL>(vals));
-    float bv = 0.0f;
-    int bi = 0;
-    for (int j = 1; j <= p.n_alpha; ++j) {
-        const float v = uniform(canon_sum<LPL>(vals + j * P));
-        if (threadIdx.x == 0) p.merit[(size_t)b * p.n_alpha + (j - 1)] = v;
-        if (j == 1 || v < bv) {
-            bv = v;
-            bi = j - 1;
+    constexpr int RMAX = (GATO_MAX_ALPHA + 1 + 3) / 4;
+    if (threadIdx.x >= 64) return false;
+    const int r = threadIdx.x >> 4;
+    const int na = p.n_alpha;
+    float sum[RMAX];
+#pragma unroll
+    for (int q = 0; q < RMAX; ++q) {
+        if (4 * q <= na) {
+            const int j = 4 * q + r;
+            sum[q] = canon_sum<LPL>(vals + (j <= na ? j : na) * P);
+            if ((threadIdx.x & 15) == 0 && j >= 1 && j <= na) p.merit[(size_t)b * na + (j - 1)] = sum[q];
         }
     }
+    const float M0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum[0]), 0));
     if (threadIdx.x == 0) p.merit0[b] = M0;
+    float bv = 0.0f;
+    int bi = 0;
+#pragma unroll
+    for (int j = 1; j <= GATO_MAX_ALPHA; ++j) {
+        if (j <= na) {
+            const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum[j / 4]), 16 * (j % 4)));
+            if (j == 1 || v < bv) {
+                bv = v;
+                bi = j - 1;
+            }
+        }
+    }
     lsfail = !(bv < M0);
     best = lsfail ? -1 : bi;
+    return true;
 }
 
 }  // namespace gato
