@@ -153,11 +153,23 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
     const int sp = s > 0 ? s - 1 : 0;  // previous slot (clamped)
     const bool has_prev = s >= 1 && k >= 1;
 
+    // Every input row this knot needs, loaded up front so that the loads for
+    // the products overlap the inversions.
+    float qi0[NC], ri0[MC], ar[NC], br[MC];
+    ld_row<NC>(p.Q, ix.Q(b, k, i), rowv, qi0);
+    ld_row<MC>(p.R, ix.R(b, k, i), urow, ri0);
+    ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, ar);
+    ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, br);
+    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
+    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
+    const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
+
     // Q~_k^-1 (identity rows on lanes/knots outside the problem keep it finite)
     bool badq = false, badr = false, bads = false;
     {
         float qi[NC];
-        ld_row<NC>(p.Q, ix.Q(b, k, i), rowv, qi);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qi[c] = qi0[c];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
@@ -167,10 +179,8 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
             for (int c = 0; c < NC; ++c) K.Q[s][i][c] = qi[c];
         float ri[MC];
-        ld_row<MC>(p.R, ix.R(b, k, i), urow, ri);
 #pragma unroll
-        for (int c = 0; c < MC; ++c)
-            if (c == i) ri[c] = urow ? ri[c] : 1.0f;
+        for (int c = 0; c < MC; ++c) ri[c] = (c == i) ? (urow ? ri0[c] : 1.0f) : ri0[c];
         gj_steps<NP, MC>(ri, i, badr);
         badr = lane_bit(__builtin_amdgcn_ballot_w64(badr));
         if (i < MC)
@@ -181,16 +191,13 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 
     // W = A_k Q~_k^-1 (row i), V = B_k R_k^-1 (row i); gamma pieces
     //   h = (Q~_k^-1 q_k)_i (own knot), g = (e_k - W q_k - V r_k)_i (for knot k+1)
-    float ar[NC], V[MC], h = 0.0f, g;
+    float V[MC], h = 0.0f, g;
     {
         float qi[NC], ri[MC], W[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) qi[c] = K.Q[s][i < NC ? i : 0][c];
 #pragma unroll
         for (int c = 0; c < MC; ++c) ri[c] = K.R[s][i < MC ? i : 0][c];
-        ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, ar);
-        float br[MC];
-        ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, br);
         if (i < NC)
 #pragma unroll
             for (int c = 0; c < MC; ++c) K.Bt[s][c][i] = br[c];  // transpose of B_k
@@ -200,9 +207,6 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         for (int c = 0; c < MC; ++c) V[c] = 0.0f;
         gemm_rows<NP, NC, NC>(W, BcRow<NP, NC>(qi), ar);
         gemm_rows<NP, MC, MC>(V, BcRow<NP, MC>(ri), br);
-        const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
-        const float rv = ld1(p.r, ix.vm(b, k, i), urow);
-        const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
         float t1 = 0.0f, t2 = 0.0f;
         const Bc<NP> qb(qv);
         dotb<NP, NC>(h, qb, qi);
