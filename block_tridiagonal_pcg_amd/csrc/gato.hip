@@ -241,6 +241,18 @@ __global__ __launch_bounds__(SH::THREADS) void k_pcg_stream(Params p)
     pcg_and_recover<SH, C>(p, M, L, gam, lam);
 }
 
+// ------------------------------------------------------------------ stage 2, direct
+
+// One 64-lane workgroup, one solve per lane group (64 / NP solves): the
+// elimination walks the knots in order, so the solves of a wave move in step.
+template <class SH>
+__global__ __launch_bounds__(64) void k_direct(Params p)
+{
+    constexpr int SPW = 64 / SH::NP;
+    const int b = blockIdx.x * SPW + (int)(threadIdx.x / SH::NP);
+    direct_solve<SH>(p, b, b < p.B);
+}
+
 // ------------------------------------------------------------------ stage 3 alone
 
 template <class SH, int LPL>
@@ -337,15 +349,21 @@ struct Ops {
         }
         return hipGetLastError();
     }
+    static hipError_t direct(const Params& p, hipStream_t st)
+    {
+        constexpr int SPW = 64 / SH::NP;
+        hipLaunchKernelGGL((k_direct<SH>), dim3((p.B + SPW - 1) / SPW), dim3(64), 0, st, p);
+        return hipGetLastError();
+    }
     static hipError_t fused(const Params& p, hipStream_t st)
     {
         hipLaunchKernelGGL((k_sqp_fused<SH>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
         return hipGetLastError();
     }
-    static bool supported(int N)
-    {
-        return N >= 1 && stream_chunks(N) != 0 && leaves_for(N) <= 1024;
-    }
+    // formation (windowed), the direct solve and the merit take any N up to the
+    // merit's 1024 leaves; PCG holds at most four knots per lane group
+    static bool supported(int N) { return N >= 1 && leaves_for(N) <= 1024; }
+    static bool pcg_supported(int N) { return N >= 1 && stream_chunks(N) != 0; }
 };
 
 // Shapes with kernels in this build: (n, m) of the configurations the
@@ -401,8 +419,14 @@ static Params make_params(const gato_dims_t* d)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t S, Pinv, gamma, Qinv, Rinv, total;
+    size_t S, Pinv, gamma, Qinv, Rinv, direct, total;
 };
+
+static size_t direct_ws_bytes(const gato_dims_t* d)
+{
+    const size_t B = d->B, N = d->N, n = d->n;
+    return align256(B * N * n * (n + 1) * sizeof(float));
+}
 
 static WsLayout ws_layout(const gato_dims_t* d)
 {
@@ -419,6 +443,8 @@ static WsLayout ws_layout(const gato_dims_t* d)
     off += align256(B * N * n * n * sizeof(float));
     w.Rinv = off;
     off += align256(B * (N > 1 ? N - 1 : 1) * m * m * sizeof(float));
+    w.direct = off;
+    off += direct_ws_bytes(d);
     w.total = off;
     return w;
 }
@@ -497,6 +523,8 @@ int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
                      lambda, dz, iters, relres, flags});
     if (rc) return rc;
     if (!(eps > 0.0f) || max_iters < 1) return GATO_E_PARAM;
+    if (with_shape(dims->n, dims->m, [&](auto ops) { return decltype(ops)::pcg_supported(dims->N) ? 1 : 0; }) != 1)
+        return GATO_E_UNSUPPORTED;
     Params p = make_params(dims);
     p.S = const_cast<float*>(S); p.Pinv = const_cast<float*>(Pinv); p.gamma = const_cast<float*>(gamma);
     p.Qinv = const_cast<float*>(Qinv); p.Rinv = const_cast<float*>(Rinv);
@@ -505,6 +533,34 @@ int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
     p.lambda = lambda; p.dz = dz; p.iters = iters; p.relres = relres; p.flags = flags;
     return with_shape(dims->n, dims->m, [&](auto ops) {
         return decltype(ops)::pcg(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
+    });
+}
+
+size_t gato_direct_workspace_bytes(const gato_dims_t* dims)
+{
+    if (check_dims(dims) != GATO_OK || dims->B == 0) return 0;
+    return direct_ws_bytes(dims);
+}
+
+int gato_direct_solve(const gato_dims_t* dims, const float* S, const float* gamma, const float* Qinv,
+                      const float* Rinv, const float* Bu, const float* q, const float* r, float* lambda,
+                      float* dz, int32_t* flags, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
+    rc = check_ptrs({S, gamma, Qinv, dyn(Rinv, dims), dyn(Bu, dims), q, dyn(r, dims), lambda, dz, flags});
+    if (rc) return rc;
+    if (workspace == nullptr || workspace_bytes < direct_ws_bytes(dims)) return GATO_E_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return GATO_E_ALIGN;
+    Params p = make_params(dims);
+    p.S = const_cast<float*>(S); p.gamma = const_cast<float*>(gamma);
+    p.Qinv = const_cast<float*>(Qinv); p.Rinv = const_cast<float*>(Rinv);
+    p.Bu = Bu; p.q = q; p.r = r;
+    p.lambda = lambda; p.dz = dz; p.flags = flags;
+    p.dws = static_cast<float*>(workspace);
+    return with_shape(dims->n, dims->m, [&](auto ops) {
+        return decltype(ops)::direct(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
     });
 }
 
@@ -578,6 +634,7 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         p.gamma = reinterpret_cast<float*>(ws + wl.gamma);
         p.Qinv = reinterpret_cast<float*>(ws + wl.Qinv);
         p.Rinv = reinterpret_cast<float*>(ws + wl.Rinv);
+        p.dws = reinterpret_cast<float*>(ws + wl.direct);
     }
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     bool ev_ok = true;
@@ -595,7 +652,7 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (fused) return O::fused(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
         if (O::form(p, stream) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
-        if (O::pcg(p, stream) != hipSuccess) return GATO_E_HIP;
+        if (O::direct(p, stream) != hipSuccess) return GATO_E_HIP;  // horizons a workgroup cannot hold
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
         if (O::merit(p, stream) != hipSuccess) return GATO_E_HIP;
         return GATO_OK;

@@ -27,6 +27,7 @@ struct Params {
     int n_alpha;
     float alphas[GATO_MAX_ALPHA];
     int win_own;  // knots owned by one form workgroup (0: the whole horizon)
+    float* dws;   // direct solve: pivot inverses [B][N][n][n], then eliminated right-hand sides [B][N][n]
 };
 
 // The same value in every lane (the reductions below produce identical bits in
@@ -639,6 +640,137 @@ __device__ __forceinline__ void recover(int i, bool rowv, bool urow, float lam, 
     dotb<NP, MC>(y, Bc<NP>(u), ri);
     dx = rowv ? x - h : 0.0f;
     du = urow ? y : 0.0f;
+}
+
+// ------------------------------------------------------------------ stage 2, direct
+
+// Direct solve of S lambda = gamma for block-tridiagonal SPD S by block
+// elimination (block Thomas, the block LDL' factorisation of S), then the
+// recovery of dz.  This is the alternative to PCG that the GATO pages discuss
+// for long horizons (the paper's block-tridiagonal direct solve; Branch's
+// chronological elimination of block-structured KKT systems).
+//   H_0 = D_0,  g_0 = gamma_0;
+//   T_k = S_{k,k-1} H_{k-1}^-1,  H_k = D_k - T_k S_{k-1,k},  g_k = gamma_k - T_k g_{k-1};
+//   lambda_{N-1} = H_{N-1}^-1 g_{N-1},  lambda_k = H_k^-1 (g_k - S_{k,k+1} lambda_{k+1}).
+// Every H_k is SPD when S is (a Schur complement of a leading block of S), so
+// the Gauss-Jordan inversion runs without pivoting; a pivot that is not
+// positive sets S_NOT_SPD.  One lane group holds one solve and walks the knots
+// in order (lane i: row i of every block); H_k^-1 rows and g_k go to the
+// workspace on the way down and are read back on the way up, where each
+// knot's dz is recovered as soon as lambda_k is known.  The next knot's rows
+// are requested before the current knot's arithmetic.
+template <class SH>
+__device__ __forceinline__ void direct_solve(const Params& p, int b, bool bv)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    const Ix<SH> ix{p.N};
+    const int N = p.N;
+    const int i = threadIdx.x % NP;
+    const int bb = bv ? b : 0;  // lane groups without a solve read masked rows of solve 0
+    const bool rowi = bv && i < NC;
+    float* Hw = p.dws;
+    float* Gw = p.dws + (size_t)p.B * N * NC * NC;
+    const size_t hrow = ((size_t)bb * N * NC + i) * NC;  // + k * NC * NC: row i of H_k^-1
+    const size_t grow = (size_t)bb * N * NC + i;         // + k * NC
+
+    // forward elimination
+    bool bad = false;
+    float Hi[NC], Sp[NC], gh = 0.0f;  // row i of H_{k-1}^-1 and S_{k-1,k}; g_{k-1} entry
+    float lo[NC], dd[NC], up[NC], gam;
+    ld_row<NC>(p.S, ix.blk(bb, 0, 0, i), rowi, lo);
+    ld_row<NC>(p.S, ix.blk(bb, 0, 1, i), rowi, dd);
+    ld_row<NC>(p.S, ix.blk(bb, 0, 2, i), rowi, up);
+    gam = ld1(p.gamma, ix.vn(bb, 0, i), rowi);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) Hi[c] = Sp[c] = 0.0f;
+    for (int k = 0; k < N; ++k) {
+        const bool nv = rowi && k + 1 < N;
+        const int kn = k + 1 < N ? k + 1 : k;
+        float nlo[NC], nd[NC], nup[NC];
+        ld_row<NC>(p.S, ix.blk(bb, kn, 0, i), nv, nlo);
+        ld_row<NC>(p.S, ix.blk(bb, kn, 1, i), nv, nd);
+        ld_row<NC>(p.S, ix.blk(bb, kn, 2, i), nv, nup);
+        const float ngam = ld1(p.gamma, ix.vn(bb, kn, i), nv);
+
+        float T[NC], U[NC], H[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) T[c] = U[c] = 0.0f;
+        gemm_rows<NP, NC, NC>(T, BcRow<NP, NC>(Hi), lo);  // T = S_{k,k-1} H_{k-1}^-1 (zero at k = 0)
+        gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(Sp), T);   // U = T S_{k-1,k}
+        float tg = 0.0f;
+        dotb<NP, NC>(tg, Bc<NP>(gh), T);
+        const float gk = gam - tg;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) H[c] = (c == i && !rowi) ? 1.0f : dd[c] - U[c];  // identity rows off the problem
+        bool bk = false;
+        gj_steps<NP, NC>(H, i, bk);
+        bad |= bk;
+        if (rowi) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) Hw[hrow + (size_t)k * NC * NC + c] = H[c];
+            Gw[grow + (size_t)k * NC] = gk;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            Hi[c] = H[c];
+            Sp[c] = up[c];
+            lo[c] = nlo[c];
+            dd[c] = nd[c];
+            up[c] = nup[c];
+        }
+        gh = gk;
+        gam = ngam;
+    }
+
+    // back substitution, with the recovery of each knot's dz
+    bool nonfinite = false;
+    float lamn = 0.0f;  // row i of lambda_{k+1}
+    for (int k = N - 1; k >= 0; --k) {
+        const bool kv = bv;
+        const bool hn = kv && k < N - 1;
+        const bool rowv = rowi;
+        const bool urow = hn && i < MC;
+        float Hk[NC], sup[NC], qi[NC], ri[MC], bc[NC];
+        ld_row<NC>(Hw, hrow + (size_t)k * NC * NC, rowi, Hk);
+        const float gk = ld1(Gw, grow + (size_t)k * NC, rowi);
+        ld_row<NC>(p.S, ix.blk(bb, k, 2, i), rowi, sup);
+        ld_row<NC>(p.Qinv, ix.Q(bb, k, i), rowv, qi);
+        ld_row<MC>(p.Rinv, ix.R(bb, k, i), urow, ri);
+        ld_row<NC, MC>(p.Bu, ix.Bu(bb, k, 0) + i, urow, bc);  // column i of B_k
+        const float qv = ld1(p.q, ix.vn(bb, k, i), rowv);
+        const float rv = ld1(p.r, ix.vm(bb, k, i), urow);
+
+        float t = 0.0f;
+        dotb<NP, NC>(t, Bc<NP>(lamn), sup);
+        t = gk - t;  // g_k - S_{k,k+1} lambda_{k+1}
+        float lam = 0.0f;
+        dotb<NP, NC>(lam, Bc<NP>(t), Hk);
+        lam = rowi ? lam : 0.0f;
+        nonfinite |= rowi && !__builtin_isfinite(lam);
+        float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
+        dotb<NP, NC>(h, Bc<NP>(qv), qi);
+        float dx, du;
+        recover<SH>(i, rowv, urow, lam, lamn, qi, sup, h, bc, rv, ri, dx, du);
+        if (rowv) {
+            p.lambda[ix.vn(bb, k, i)] = lam;
+            p.dz[ix.dx(bb, k, i)] = dx;
+        }
+        if (urow) p.dz[ix.du(bb, k, i)] = du;
+        lamn = lam;
+    }
+
+    // per-solve flags: any lane of the group
+    const uint64_t grp = (NP == 64 ? ~0ull : ((1ull << NP) - 1ull)) << (threadIdx.x & (64 - NP));
+    const bool any_bad = (__builtin_amdgcn_ballot_w64(bad && rowi) & grp) != 0;
+    const bool any_nf = (__builtin_amdgcn_ballot_w64(nonfinite) & grp) != 0;
+    if (bv && i == 0) {
+        int fl = p.flags[b];
+        if (any_bad) fl |= GATO_F_S_NOT_SPD;
+        if (any_nf) fl |= GATO_F_NONFINITE;
+        p.flags[b] = fl;
+        if (p.iters) p.iters[b] = 0;
+        if (p.relres) p.relres[b] = 0.0f;
+    }
 }
 
 // ------------------------------------------------------------------ stage 3: merit

@@ -155,6 +155,29 @@ int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
                    hipStream_t stream);
 
 /*
+ * Stage 2, direct (the block-tridiagonal direct solve the GATO pages weigh
+ * against PCG for long horizons; Branch's chronological elimination of a
+ * block-structured KKT system).  Solves S lambda = gamma exactly (up to
+ * rounding) by block elimination, the block LDL' factorisation of S:
+ *   H_0 = D_0, g_0 = gamma_0;  T_k = S_{k,k-1} H_{k-1}^-1,
+ *   H_k = D_k - T_k S_{k-1,k},  g_k = gamma_k - T_k g_{k-1};
+ *   lambda_{N-1} = H_{N-1}^-1 g_{N-1},  lambda_k = H_k^-1 (g_k - S_{k,k+1} lambda_{k+1}),
+ * then recovers dz exactly as gato_pcg_solve does.  Arguments as in
+ * gato_pcg_solve, without a starting point, tolerance or iteration cap;
+ * lambda and dz are outputs only.  H_k^-1 (Gauss-Jordan, no pivoting: every H_k
+ * of an SPD S is SPD) and g_k are kept in the caller's workspace, of at least
+ * gato_direct_workspace_bytes(dims) bytes, 256-byte aligned.  A pivot that is not
+ * positive ORs S_NOT_SPD into flags, a non-finite lambda NONFINITE.  The knots are
+ * walked in order, so a solve's time grows linearly with N and does not depend
+ * on the conditioning of S.
+ */
+size_t gato_direct_workspace_bytes(const gato_dims_t* dims);
+int gato_direct_solve(const gato_dims_t* dims, const float* S, const float* gamma, const float* Qinv,
+                      const float* Rinv, const float* Bu, const float* q, const float* r, float* lambda,
+                      float* dz, int32_t* flags, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
  * Stage 3 (GATO paper Sec. II eq. 3, Sec. III eq. 7; the merit kernel of the
  * GATO docs' "Merit launch timing").  For every solve, knot and step size a:
  *   m_k(a) = a (q_k'dx_k + r_k'du_k) + a^2/2 (dx_k'Q_k dx_k + du_k'R_k du_k)
@@ -175,10 +198,17 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
 /*
  * The three stages in one call (one SQP iteration's linear-algebra core,
  * GATO paper Sec. III, Fig. 2 steps a-c).  Outputs are those of the three
- * calls above; flags[b] is set (not ORed).  Where one workgroup can hold a
- * whole solve, the stages run fused in one kernel and use no workspace;
- * otherwise S, Pinv, gamma, Qinv and Rinv go through `workspace`
- * (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device memory).
+ * calls above; flags[b] is set (not ORed).  Horizon policy (the GATO pages'
+ * choice between PCG and a block-tridiagonal direct solve by horizon, with the
+ * switch point measured on this device):
+ *  - where one workgroup can hold a whole solve (N <= 64 for n <= 16, N <= 16
+ *    for n <= 32), the stages run fused in one kernel with PCG, and no
+ *    workspace is used;
+ *  - otherwise stage 2 is gato_direct_solve's block elimination: lambda's
+ *    input is not read, iters and relres are written as 0, and eps and
+ *    max_iters are checked but unused.  S, Pinv, gamma, Qinv, Rinv and the
+ *    elimination's rows go through `workspace` (gato_workspace_bytes() bytes,
+ *    256-byte aligned, caller-owned device memory).
  * times (nullable): per-stage device times; when given, the call synchronises.
  */
 int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
@@ -195,7 +225,10 @@ size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha);
 /* Static description of a status code. */
 const char* gato_status_string(int code);
 
-/* Non-zero if this build has kernels for (n, m, N). */
+/* Non-zero if this build has kernels for (n, m, N): (n, m) in {(14,7), (12,6),
+ * (24,12), (4,2), (1,1)} and 1 <= N <= 1024.  gato_pcg_solve alone is further
+ * limited to N <= 256 for n <= 16 and N <= 64 for n <= 32 (four knots per lane
+ * group) and returns GATO_E_UNSUPPORTED beyond. */
 int gato_shape_supported(int32_t n, int32_t m, int32_t N);
 
 #ifdef __cplusplus

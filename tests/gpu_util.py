@@ -44,6 +44,21 @@ def gpu_pcg(batch, form, eps, max_iters, lambda0=None, flags=None):
     return dict(lam=cpu(lam), dz=cpu(dz), iters=cpu(iters), relres=cpu(relres), flags=cpu(fl))
 
 
+def gpu_direct(batch, form, flags=None):
+    """Direct block-tridiagonal solve + recovery fed `form` (stage-1 layouts, rounded to float32)."""
+    dims = batch["dims"]
+    n, m, N, B = dims
+    t = lambda a: torch.as_tensor(np.ascontiguousarray(np.asarray(a, np.float32))).cuda()  # noqa: E731
+    lam = torch.full((B, N, n), float("nan"), dtype=torch.float32, device="cuda")
+    dz = torch.full((B, N * n + (N - 1) * m), float("nan"), dtype=torch.float32, device="cuda")
+    fl = torch.as_tensor(np.zeros(B, np.int32) if flags is None else np.asarray(flags, np.int32)).cuda()
+    ws = ops.direct_workspace_for(dims)
+    ops.gato_direct_solve(dims, t(form["S"]), t(form["gamma"]), t(form["Qinv"]), t(form["Rinv"]), t(batch["Bu"]),
+                          t(batch["q"]), t(batch["r"]), lam, dz, fl, ws)
+    torch.cuda.synchronize()
+    return dict(lam=cpu(lam), dz=cpu(dz), flags=cpu(fl))
+
+
 def gpu_merit(batch, dz, mu, alphas=ALPHAS, flags=None):
     dims = batch["dims"]
     B = dims[3]

@@ -25,8 +25,8 @@ def lib():
 
 def test_header_declares_the_abi():
     assert _declared() == sorted([
-        "gato_form_schur", "gato_merit_eval", "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step",
-        "gato_status_string", "gato_workspace_bytes"])
+        "gato_direct_solve", "gato_direct_workspace_bytes", "gato_form_schur", "gato_merit_eval",
+        "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step", "gato_status_string", "gato_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -48,13 +48,15 @@ def test_status_strings(lib):
 def test_shapes_and_workspace(lib):
     from block_tridiagonal_pcg_amd import ops
 
-    for n, m, N in ((14, 7, 64), (12, 6, 32), (24, 12, 16), (4, 2, 8), (14, 7, 128), (1, 1, 2), (14, 7, 1)):
+    for n, m, N in ((14, 7, 64), (12, 6, 32), (24, 12, 16), (4, 2, 8), (14, 7, 128), (1, 1, 2), (14, 7, 1),
+                    (14, 7, 1024), (24, 12, 200)):
         assert ops.gato_shape_supported(n, m, N), (n, m, N)
-    for n, m, N in ((13, 7, 64), (14, 7, 0), (14, 7, 257), (24, 12, 65)):
+    for n, m, N in ((13, 7, 64), (14, 7, 0), (14, 7, 1025), (24, 12, 1025)):
         assert not ops.gato_shape_supported(n, m, N), (n, m, N)
     assert ops.gato_workspace_bytes((14, 7, 64, 128)) == 0          # fused: no workspace
     ws = ops.gato_workspace_bytes((14, 7, 128, 512))
-    assert ws >= 512 * 128 * (2 * 3 * 14 * 14 + 14 + 14 * 14) * 4
+    # stage-1 outputs plus the direct solve's pivot inverses and right-hand sides
+    assert ws >= 512 * 128 * (2 * 3 * 14 * 14 + 14 + 14 * 14 + 14 * 15) * 4
     assert ops.gato_workspace_bytes((13, 7, 64, 128)) == 0          # unsupported -> 0
 
 
@@ -87,6 +89,20 @@ def test_validation_happens_before_any_launch(lib):
     assert f(ctypes.byref(d), *P[:8], 0.0, 10, *P[8:13], None) == ops.E_PARAM
     assert f(ctypes.byref(d), *P[:8], 1e-6, 0, *P[8:13], None) == ops.E_PARAM
     assert f(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:8], 1e-6, 10, *P[8:13], None) == ops.OK
+    # PCG holds at most four knots per lane group
+    assert f(ctypes.byref(ops.Dims(14, 7, 257, 2)), *P[:8], 1e-6, 10, *P[8:13], None) == ops.E_UNSUPPORTED
+
+    # direct solve: workspace size, alignment and presence are checked on the host
+    dd = lib.gato_direct_solve
+    need = lib.gato_direct_workspace_bytes(ctypes.byref(d))
+    assert need == ((2 * 64 * 14 * 15 * 4 + 255) // 256) * 256  # B=2 N=64 n=14: H^-1 rows and g
+    ws = ctypes.c_void_p(1 << 20)
+    assert dd(ctypes.byref(d), *P[:10], None, ctypes.c_size_t(need), None) == ops.E_WORKSPACE
+    assert dd(ctypes.byref(d), *P[:10], ws, ctypes.c_size_t(need - 1), None) == ops.E_WORKSPACE
+    assert dd(ctypes.byref(d), *P[:10], ctypes.c_void_p((1 << 20) + 4), ctypes.c_size_t(need), None) == ops.E_ALIGN
+    assert dd(ctypes.byref(d), None, *P[1:10], ws, ctypes.c_size_t(need), None) == ops.E_NULL
+    assert dd(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:10], None, ctypes.c_size_t(0), None) == ops.OK
+    assert dd(ctypes.byref(ops.Dims(5, 2, 64, 4)), *P[:10], ws, ctypes.c_size_t(need), None) == ops.E_UNSUPPORTED
 
     al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
     g = lib.gato_merit_eval

@@ -42,6 +42,19 @@ def _ident(*a):
     print("case:", *a, flush=True)
 
 
+def _direct_path(bt):
+    """gato_sqp_step solves S lambda = gamma directly when a workgroup cannot hold the horizon."""
+    n, _, N, _ = bt["dims"]
+    return N > (64 if n <= 16 else 16)
+
+
+def _exact_dz(bt):
+    """The exact step of the oracle: fp64 formation, block Cholesky of S, recovery."""
+    f = oracle.form_schur(*[bt[k] for k in synth.FIELDS])
+    lam = oracle.direct_solve(f["S"], f["gamma"])["lam"]
+    return oracle.recover(f["Qinv"], f["Rinv"], bt["A"], bt["Bu"], bt["q"], bt["r"], lam)
+
+
 # ---------------------------------------------------------------- stage 1
 
 
@@ -188,6 +201,12 @@ def test_sqp_step_parity(cid, B):
     idx = np.arange(B) if B <= 256 else np.linspace(0, B - 1, 64).astype(int)
     sub = {f: bt[f][idx] for f in synth.FIELDS}
     o = oracle.sqp_step(*[sub[f] for f in synth.FIELDS], None, 1e-6, CAPS[cid], A64, 1.0)
+    if _direct_path(bt):
+        # the step comes from the direct solve: compare with the exact step and the
+        # stage-1 flag bits (the oracle's PCG may stop at its cap on these solves)
+        o["dz"] = _exact_dz(sub)
+        assert (g["iters"] == 0).all()
+        o["flags"] = o["flags"] & ~(ops.F_PCG_MAXITER | ops.F_PCG_BREAKDOWN)
     err = rel_rows(g["dz"][idx], o["dz"])
     print("cfg%d B%d: dz rel err max %.3e median %.3e; iters gpu %d..%d oracle %d..%d" % (
         cid, B, err.max(), np.median(err), g["iters"].min(), g["iters"].max(), o["iters"].min(), o["iters"].max()))
@@ -197,11 +216,8 @@ def test_sqp_step_parity(cid, B):
     om = oracle.merit_eval(*[sub[f] for f in synth.FIELDS], g["dz"][idx].astype(np.float64), A64, 1.0)
     assert merit_rel(g["merit"][idx], om).max() <= 1e-4
     np.testing.assert_array_equal(g["best"], select(g["merit"], g["merit0"]))
-    if cid != 5:
+    if not _direct_path(bt):
         assert np.abs(g["iters"][idx] - o["iters"]).max() <= 2
-    else:
-        ratio = g["iters"][idx] / np.maximum(o["iters"], 1)
-        assert 0.7 <= ratio.min() and ratio.max() <= 1.5
 
 
 def test_fused_step_equals_staged_calls():
@@ -242,12 +258,14 @@ def test_stage_times_reported():
 @pytest.mark.parametrize("N", [1, 2, 5, 37, 63, 64, 65, 100, 128, 129, 200, 256])
 def test_ragged_and_extreme_horizons(N):
     """Horizons that leave a wave partly empty, fill a workgroup exactly, or spill into the
-    long-horizon path (windowed formation, streamed PCG)."""
+    long-horizon path (windowed formation, direct block-tridiagonal solve)."""
     _ident("horizon", N)
     bt = _batch(3, 3, N=N)
     g = gpu_sqp(bt, 1e-6, 400, rho=np.array([0.0, 0.1, 1.0]))
     o = oracle.sqp_step(*synth.inputs(bt), np.array([0.0, 0.1, 1.0]), 1e-6, 400, A64, 1.0)
     assert rel_rows(g["dz"], o["dz"]).max() <= 1e-3
+    if _direct_path(bt):
+        assert (g["iters"] == 0).all() and (g["flags"] & ~ops.F_LS_FAILED == 0).all()
     om = oracle.merit_eval(*synth.inputs(bt), g["dz"].astype(np.float64), A64, 1.0)
     assert merit_rel(g["merit"], om).max() <= 1e-4
     f = gpu_form(bt, rho=np.array([0.0, 0.1, 1.0]))
