@@ -107,10 +107,35 @@ struct FormOnlyLds {
     Park<SH> park;
 };
 
-template <class SH>
+// Copy nf floats from LDS to global memory with the threads t = t0, t0 + nt, ...
+// of the caller, 16 bytes per access when both ends allow it.
+__device__ __forceinline__ void lds_to_global(float* dst, const float* src, int nf, int t0, int nt)
+{
+    if (nf <= 0) return;
+    const bool vec = ((reinterpret_cast<size_t>(dst) | reinterpret_cast<size_t>(src)) & 15) == 0;
+    int done = 0;
+    if (vec) {
+        const int n4 = nf / 4;
+        const float4* s4 = reinterpret_cast<const float4*>(src);
+        float4* d4 = reinterpret_cast<float4*>(dst);
+#pragma unroll 4
+        for (int j = t0; j < n4; j += nt) d4[j] = s4[j];
+        done = 4 * n4;
+    }
+    for (int j = done + t0; j < nf; j += nt) dst[j] = src[j];
+}
+
+// Stage 1 alone.  The outputs leave through LDS so that every store is a
+// contiguous 16-byte write: the parked Q~^-1 / R^-1 blocks are already in the
+// output layout, and each wave stages the S (and Phi^-1) block rows of its own
+// knots in a private slice before writing them out.
+template <class SH, bool PRE>
 __global__ __launch_bounds__(SH::THREADS) void k_form(Params p)
 {
-    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, KPW = SH::KPW;
+    constexpr int ROWBLK = 3 * NC * NC;  // one knot's block row
+    static_assert((SH::THREADS / 64) * KPW * ROWBLK * sizeof(float) <= sizeof(FormOnlyLds<SH>),
+                  "the staging slices must fit in the kernel's LDS");
     __shared__ FormOnlyLds<SH> L;
     const Ix<SH> ix{p.N};
     const int N = p.N;
@@ -130,27 +155,40 @@ __global__ __launch_bounds__(SH::THREADS) void k_form(Params p)
     const bool own = s < nslot && k >= o0 && k < o1;
     Rows<SH> rw;
     int fl = 0;
-    form<SH>(p, b, w0, nslot, L.f, L.park, rw, fl, [&](const float* qi, const float* ri) {
-        if (own && i < NC)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) p.Qinv[ix.Q(b, k, i) + c] = qi[c];
-        if (own && k < N - 1 && i < MC)
-#pragma unroll
-            for (int c = 0; c < MC; ++c) p.Rinv[ix.R(b, k, i) + c] = ri[c];
-    });
-    if (own && i < NC) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            p.S[ix.blk(b, k, 0, i) + c] = rw.slo[c];
-            p.S[ix.blk(b, k, 1, i) + c] = rw.sd[c];
-            p.S[ix.blk(b, k, 2, i) + c] = rw.sup[c];
-            p.Pinv[ix.blk(b, k, 0, i) + c] = rw.plo[c];
-            p.Pinv[ix.blk(b, k, 1, i) + c] = rw.pd[c];
-            p.Pinv[ix.blk(b, k, 2, i) + c] = rw.pup[c];
-        }
-        p.gamma[ix.vn(b, k, i)] = rw.gam;
-    }
+    form<SH, PRE>(p, b, w0, nslot, L.f, L.park, rw, fl, [](const float*, const float*) {});
     if (own && i == 0 && fl) atomicOr(p.flags + b, fl);
+    if (own && i < NC) p.gamma[ix.vn(b, k, i)] = rw.gam;
+
+    // Q~^-1 and R^-1 of the owned knots (contiguous in the park and in memory)
+    const int s0 = o0 - w0, s1 = o1 - w0;
+    const int nt = blockDim.x, t0 = threadIdx.x;
+    lds_to_global(p.Qinv + ix.Q(b, o0, 0), &L.park.Q[s0][0][0], (s1 - s0) * NC * NC, t0, nt);
+    const int r1 = min(o1, N - 1);
+    if (r1 > o0) lds_to_global(p.Rinv + ix.R(b, o0, 0), &L.park.R[s0][0][0], (r1 - o0) * MC * MC, t0, nt);
+    __syncthreads();
+
+    // S and Phi^-1 block rows through a wave-private slice (LDS accesses of one
+    // wave complete in order, so no workgroup barrier is needed between them)
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    float* slice = reinterpret_cast<float*>(&L) + (size_t)wave * KPW * ROWBLK;
+    const int sw = s % KPW;                                   // this lane's knot within the wave
+    const int ws0 = max(s0, wave * KPW), ws1 = min(s1, (wave + 1) * KPW);  // owned slots of the wave
+    auto put = [&](float* dst, const float* lo, const float* dg, const float* hi) {
+        if (i < NC)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                slice[(sw * 3 + 0) * NC * NC + i * NC + c] = lo[c];
+                slice[(sw * 3 + 1) * NC * NC + i * NC + c] = dg[c];
+                slice[(sw * 3 + 2) * NC * NC + i * NC + c] = hi[c];
+            }
+        __builtin_amdgcn_wave_barrier();
+        if (ws1 > ws0)
+            lds_to_global(dst + ix.blk(b, w0 + ws0, 0, 0), slice + (ws0 - wave * KPW) * ROWBLK, (ws1 - ws0) * ROWBLK,
+                          lane, 64);
+        __builtin_amdgcn_wave_barrier();
+    };
+    put(p.S, rw.slo, rw.sd, rw.sup);
+    if constexpr (PRE) put(p.Pinv, rw.plo, rw.pd, rw.pup);
 }
 
 // ------------------------------------------------------------------ stage 2 alone
@@ -306,7 +344,7 @@ struct Ops {
     static bool fused_ok(int N) { return N <= SL; }
     static int stream_chunks(int N) { return N <= SL ? 1 : (N <= 2 * SL ? 2 : (N <= 4 * SL ? 4 : 0)); }
 
-    static hipError_t form(const Params& p, hipStream_t st)
+    static hipError_t form(const Params& p, hipStream_t st, bool pre = true)
     {
         Params q = p;
         if (p.N <= SL) {
@@ -317,7 +355,10 @@ struct Ops {
         const int nwin = q.win_own ? (p.N + q.win_own - 1) / q.win_own : 1;
         const int threads = q.win_own ? SH::THREADS : threads_for(p.N);
         hipLaunchKernelGGL(k_zero_i32, dim3((p.B + 255) / 256), dim3(256), 0, st, p.flags, p.B);
-        hipLaunchKernelGGL((k_form<SH>), dim3(p.B, nwin), dim3(threads), 0, st, q);
+        if (pre)
+            hipLaunchKernelGGL((k_form<SH, true>), dim3(p.B, nwin), dim3(threads), 0, st, q);
+        else
+            hipLaunchKernelGGL((k_form<SH, false>), dim3(p.B, nwin), dim3(threads), 0, st, q);
         return hipGetLastError();
     }
     static hipError_t pcg(const Params& p, hipStream_t st)
@@ -650,7 +691,7 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
     rc = with_shape(dims->n, dims->m, [&](auto ops) {
         using O = decltype(ops);
         if (fused) return O::fused(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
-        if (O::form(p, stream) != hipSuccess) return GATO_E_HIP;
+        if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;  // no Phi^-1: the direct solve follows
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
         if (O::direct(p, stream) != hipSuccess) return GATO_E_HIP;  // horizons a workgroup cannot hold
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;

@@ -134,10 +134,12 @@ struct Park {
 // window with two knots of halo before and one after).
 //
 // Q~_k^-1 and R_k^-1 rows, B_k's columns, Q~_k^-1 q_k and r_k are parked in
-// LDS (K; the fused step keeps them for the recovery); the inverse rows are
-// also handed to `sink` for storing.  `fl` gets the Q/R/S_NOT_SPD bits of this
-// knot.
-template <class SH, class Sink>
+// LDS (K; the fused step keeps them for the recovery, the standalone kernel
+// stores the inverses from there); the inverse rows are also handed to `sink`.
+// `fl` gets the Q/R/S_NOT_SPD bits of this knot.  With PRE false the stair
+// preconditioner (D_k^-1 and the Phi^-1 rows) is not formed: the direct solve
+// does not use it, and S_NOT_SPD then comes from the solve's own pivots.
+template <class SH, bool PRE = true, class Sink>
 __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, FormLds<SH>& L, Park<SH>& K,
                                      Rows<SH>& out, int& fl, Sink sink)
 {
@@ -268,6 +270,21 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         out.gam = rowv ? ((k >= 1) ? h + gp : h + x0v) : 0.0f;
     }
     __syncthreads();
+
+    if constexpr (!PRE) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            out.sd[c] = rowv ? sd[c] : 0.0f;
+            out.sup[c] = (rowv && k < N - 1) ? O[c] : 0.0f;
+            out.plo[c] = out.pd[c] = out.pup[c] = 0.0f;
+        }
+        fl = 0;
+        if (kv) {
+            if (badq) fl |= GATO_F_Q_NOT_SPD;
+            if (hn && badr) fl |= GATO_F_R_NOT_SPD;
+        }
+        return;
+    }
 
     // D_k^-1
     float di[NC];
