@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-copy", action="store_true")
+    ap.add_argument("--merit-variants", action="store_true",
+                    help="instead of the step: time the merit call's launch variants (one JSON line)")
     return ap.parse_args()
 
 
@@ -150,6 +152,92 @@ def cpu_baseline(batch, n_alpha, seconds):
                       "OpenMP over solves" % (B, reps, wall)}
 
 
+# ---------------------------------------------------------------- merit launch variants
+
+
+def _hip():
+    """The HIP runtime this process already loaded (torch's and libgato's), for CU-masked streams."""
+    import ctypes
+
+    path = None
+    for line in open("/proc/self/maps"):
+        if "libamdhip64" in line:
+            path = line.split()[-1]
+            break
+    hip = ctypes.CDLL(path or "libamdhip64.so")
+    V, U, P = ctypes.c_void_p, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)
+    hip.hipExtStreamCreateWithCUMask.argtypes = [P, U, ctypes.POINTER(U)]
+    hip.hipStreamDestroy.argtypes = [V]
+    hip.hipEventCreate.argtypes = [P]
+    hip.hipEventRecord.argtypes = [V, V]
+    hip.hipEventSynchronize.argtypes = [V]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), V, V]
+    hip.hipEventDestroy.argtypes = [V]
+    return hip
+
+
+def merit_variants(a):
+    """Device time of gato_merit_eval per launch for each launch variant: the fused per-knot
+    kernel and the candidate-parallel one, at workgroup sizes 64..1024, on the whole GPU and
+    on streams restricted to fewer CUs (the few-SM analogue of the pages' MPS throttle)."""
+    import ctypes
+
+    import torch
+
+    from block_tridiagonal_pcg_amd import ops, synth
+
+    torch.cuda.set_device(0)
+    hip = _hip()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = []
+    for B in (1, 16, 128):
+        batch = synth.make_batch(a.config, B)
+        dims = batch["dims"]
+        dev = ops.to_device(batch)
+        out = ops.alloc_outputs(dims, 8)
+        ws = ops.workspace_for(dims, 8)
+        ops.gato_sqp_step(dims, *[dev[f] for f in synth.FIELDS], None, EPS, CAPS[a.config], synth.ALPHAS, MU,
+                          out["lam"], out["dz"], out["merit"], out["merit0"], out["best"], out["iters"],
+                          out["relres"], out["flags"], workspace=ws)
+        torch.cuda.synchronize()
+        for cus in sorted({8, 32, 128, n_cu}):
+            words = (n_cu + 31) // 32
+            mask = (ctypes.c_uint32 * words)(*[
+                sum(1 << b for b in range(32) if 32 * w + b < cus) for w in range(words)])
+            st = ctypes.c_void_p()
+            if hip.hipExtStreamCreateWithCUMask(ctypes.byref(st), words, mask) != 0:
+                raise RuntimeError("hipExtStreamCreateWithCUMask failed")
+            e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+            hip.hipEventCreate(ctypes.byref(e0))
+            hip.hipEventCreate(ctypes.byref(e1))
+            for variant in ("fused", "candidate"):
+                for waves in (1, 2, 4, 8, 16):
+                    os.environ["GATO_MERIT_VARIANT"] = variant
+                    os.environ["GATO_MERIT_WAVES"] = str(waves)
+                    call = lambda: ops.gato_merit_eval(dims, *[dev[f] for f in synth.FIELDS], out["dz"],  # noqa
+                                                       synth.ALPHAS, MU, out["merit"], out["merit0"], out["best"],
+                                                       out["flags"], stream=st.value)
+                    for _ in range(3):
+                        call()
+                    reps = 20
+                    hip.hipEventRecord(e0, st)
+                    for _ in range(reps):
+                        call()
+                    hip.hipEventRecord(e1, st)
+                    hip.hipEventSynchronize(e1)
+                    ms = ctypes.c_float()
+                    hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1)
+                    rows.append({"B": B, "cus": cus, "variant": variant, "threads": 64 * waves,
+                                 "us": ms.value * 1e3 / reps})
+            hip.hipEventDestroy(e0)
+            hip.hipEventDestroy(e1)
+            hip.hipStreamDestroy(st)
+    os.environ.pop("GATO_MERIT_VARIANT", None)
+    os.environ.pop("GATO_MERIT_WAVES", None)
+    print(json.dumps({"study": "merit launch variants", "workload": synth.CONFIGS[a.config].name,
+                      "unit": "us per launch", "rows": rows}))
+
+
 # ---------------------------------------------------------------- main
 
 
@@ -167,6 +255,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.merit_variants:
+        merit_variants(a)
+        return
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[a.config]
     batch = synth.make_batch(a.config, a.batch)

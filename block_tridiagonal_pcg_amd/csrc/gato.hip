@@ -324,6 +324,65 @@ __global__ __launch_bounds__(1024) void k_merit(Params p)
     }
 }
 
+// Candidate-parallel variant: one workgroup per (solve, step size), each
+// recomputing a knot's step-size-independent products for its own step size
+// (the pages' per-candidate launch, against the fused per-knot evaluation of
+// k_merit).  A knot's value comes from the same arithmetic as in k_merit and
+// the sum over knots from the same pairwise tree, so both give identical bits.
+template <class SH, int LPL>
+__global__ __launch_bounds__(1024) void k_merit_cand(Params p)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC, P = 16 * LPL;
+    __shared__ __align__(16) float mer[P];
+    const Ix<SH> ix{p.N};
+    const int b = blockIdx.x, j = blockIdx.y;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP;
+    const int ks = blockDim.x / NP;
+    for (int t = threadIdx.x; t < P; t += blockDim.x) mer[t] = 0.0f;
+    __syncthreads();
+    for (int c0 = 0; c0 < p.N; c0 += ks) {
+        const int k = c0 + s;
+        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC;
+        const float dx = ld1(p.dz, ix.dx(b, k, i), rowv);
+        const float du = ld1(p.dz, ix.du(b, k, i), hn && i < MC);
+        const float dxn = ld1(p.dz, ix.dx(b, k + 1, i), hn && i < NC);
+        MeritIn<SH> mi;
+        merit_rows<SH>(p, b, k, i, mi);
+        const MeritPrep m = merit_prep<SH>(p, k, mi, dx, du, dxn);
+        const float v = merit_value<SH>(p, k, mi, m, dx, j);
+        if (i == 0 && kv) mer[k] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x >= 64) return;
+    const float tot = canon_sum<LPL>(mer);
+    if (threadIdx.x == 0) {
+        if (j == 0)
+            p.merit0[b] = tot;
+        else
+            p.merit[(size_t)b * p.n_alpha + (j - 1)] = tot;
+    }
+}
+
+// Selection after k_merit_cand (the rule of merit_select), one thread per solve.
+__global__ void k_merit_pick(Params p)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= p.B) return;
+    const float M0 = p.merit0[b];
+    float bv = 0.0f;
+    int bi = 0;
+    for (int j = 1; j <= p.n_alpha; ++j) {
+        const float v = p.merit[(size_t)b * p.n_alpha + (j - 1)];
+        if (j == 1 || v < bv) {
+            bv = v;
+            bi = j - 1;
+        }
+    }
+    const bool lsfail = !(bv < M0);
+    p.best[b] = lsfail ? -1 : bi;
+    if (lsfail) p.flags[b] |= GATO_F_LS_FAILED;
+}
+
 // ------------------------------------------------------------------ host side
 
 static int merit_waves_default(int N, int kpw)
@@ -335,6 +394,15 @@ static int merit_waves_default(int N, int kpw)
     }
     int w = (N + kpw - 1) / kpw;
     return w < 1 ? 1 : (w > 16 ? 16 : w);
+}
+
+// Launch variant of the standalone merit call: GATO_MERIT_VARIANT=candidate
+// selects the candidate-parallel kernels (for measurement; the default, one
+// workgroup per solve evaluating every step size per knot, is faster).
+static bool merit_per_candidate()
+{
+    const char* env = std::getenv("GATO_MERIT_VARIANT");
+    return env && std::strcmp(env, "candidate") == 0;
 }
 
 template <class SH>
@@ -379,7 +447,21 @@ struct Ops {
     {
         const int P = leaves_for(p.N);
         const int waves = merit_waves_default(p.N, KPW);
-        const dim3 g(p.B), blk(waves * 64);
+        const dim3 blk(waves * 64);
+        if (merit_per_candidate()) {
+            const dim3 g(p.B, p.n_alpha + 1);
+            switch (P / 16) {
+                case 4: hipLaunchKernelGGL((k_merit_cand<SH, 4>), g, blk, 0, st, p); break;
+                case 8: hipLaunchKernelGGL((k_merit_cand<SH, 8>), g, blk, 0, st, p); break;
+                case 16: hipLaunchKernelGGL((k_merit_cand<SH, 16>), g, blk, 0, st, p); break;
+                case 32: hipLaunchKernelGGL((k_merit_cand<SH, 32>), g, blk, 0, st, p); break;
+                case 64: hipLaunchKernelGGL((k_merit_cand<SH, 64>), g, blk, 0, st, p); break;
+                default: return hipErrorInvalidValue;
+            }
+            hipLaunchKernelGGL(k_merit_pick, dim3((p.B + 255) / 256), dim3(256), 0, st, p);
+            return hipGetLastError();
+        }
+        const dim3 g(p.B);
         switch (P / 16) {
             case 4: hipLaunchKernelGGL((k_merit<SH, 4>), g, blk, 0, st, p); break;
             case 8: hipLaunchKernelGGL((k_merit<SH, 8>), g, blk, 0, st, p); break;

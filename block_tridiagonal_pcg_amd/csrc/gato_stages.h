@@ -824,35 +824,58 @@ __device__ __forceinline__ void merit_rows(const Params& p, int b, int k, int i,
 //   L1(a) = ||e_k + a (A dx + B du - dx_{k+1})||_1 + [k = 0] ||x0 - a dx_0||_1.
 // Sums over the lanes of a group use the canonical butterfly and every rounding
 // is explicit, so a knot's values do not depend on the kernel computing them.
-// The group's lane 0 writes value j (j = 0: a = 0) to out[j * stride].
+//
+// The step-size-independent part of a knot's merit terms: LIN, QUAD (summed
+// over the knot's lanes) and this lane's entry of A dx + B du - dx_{k+1}.
+struct MeritPrep {
+    float lin, quad, d;
+};
+
 template <class SH>
-__device__ __forceinline__ void merit_knot(const Params& p, int k, int i, const MeritIn<SH>& in, float dx, float du,
-                                           float dxn, float* out, int stride)
+__device__ __forceinline__ MeritPrep merit_prep(const Params& p, int k, const MeritIn<SH>& in, float dx, float du,
+                                                float dxn)
 {
     constexpr int NC = SH::NC, MC = SH::MC, NP = SH::NP;
-    const int N = p.N;
-    const bool kv = k < N;
-    const bool hn = kv && k < N - 1;
+    const bool hn = k < p.N - 1;
     const Bc<NP> xb(dx), ub(du);
     float Qdx = 0.0f, Rdu = 0.0f, d = 0.0f;
     dotb<NP, NC>(Qdx, xb, in.Q);
     dotb<NP, MC>(Rdu, ub, in.R);
     dotb<NP, NC>(d, xb, in.A);
     dotb<NP, MC>(d, ub, in.B);
-    d = hn ? __fsub_rn(d, dxn) : 0.0f;
-    const float lin = groupsum<NP>(__fadd_rn(__fmul_rn(in.q, dx), __fmul_rn(in.r, du)));
-    const float quad = groupsum<NP>(__fadd_rn(__fmul_rn(dx, Qdx), __fmul_rn(du, Rdu)));
-    const bool k0 = k == 0;
+    MeritPrep m;
+    m.d = hn ? __fsub_rn(d, dxn) : 0.0f;
+    m.lin = groupsum<NP>(__fadd_rn(__fmul_rn(in.q, dx), __fmul_rn(in.r, du)));
+    m.quad = groupsum<NP>(__fadd_rn(__fmul_rn(dx, Qdx), __fmul_rn(du, Rdu)));
+    return m;
+}
+
+// A knot's merit term at step size j (j = 0: a = 0), in every lane of the group.
+template <class SH>
+__device__ __forceinline__ float merit_value(const Params& p, int k, const MeritIn<SH>& in, const MeritPrep& m,
+                                             float dx, int j)
+{
+    const float a = (j == 0) ? 0.0f : p.alphas[j - 1];
+    float l1 = fabsf(__fmaf_rn(a, m.d, in.e));
+    const float l0 = __fadd_rn(l1, fabsf(__fmaf_rn(-a, dx, in.x0)));
+    l1 = (k == 0) ? l0 : l1;
+    const float L1 = groupsum<SH::NP>(l1);
+    return __fadd_rn(__fadd_rn(__fmul_rn(a, m.lin), __fmul_rn(__fmul_rn(0.5f, __fmul_rn(a, a)), m.quad)),
+                     __fmul_rn(p.mu, L1));
+}
+
+// All step sizes of one knot: the group's lane 0 writes value j (j = 0: a = 0)
+// to out[j * stride].
+template <class SH>
+__device__ __forceinline__ void merit_knot(const Params& p, int k, int i, const MeritIn<SH>& in, float dx, float du,
+                                           float dxn, float* out, int stride)
+{
+    const bool kv = k < p.N;
+    const MeritPrep m = merit_prep<SH>(p, k, in, dx, du, dxn);
 #pragma unroll 1
     for (int j = 0; j <= GATO_MAX_ALPHA; ++j) {
         if (j <= p.n_alpha) {
-            const float a = (j == 0) ? 0.0f : p.alphas[j - 1];
-            float l1 = fabsf(__fmaf_rn(a, d, in.e));
-            const float l0 = __fadd_rn(l1, fabsf(__fmaf_rn(-a, dx, in.x0)));
-            l1 = k0 ? l0 : l1;
-            const float L1 = groupsum<NP>(l1);
-            const float val = __fadd_rn(
-                __fadd_rn(__fmul_rn(a, lin), __fmul_rn(__fmul_rn(0.5f, __fmul_rn(a, a)), quad)), __fmul_rn(p.mu, L1));
+            const float val = merit_value<SH>(p, k, in, m, dx, j);
             if (i == 0 && kv) out[j * stride] = val;
         }
     }

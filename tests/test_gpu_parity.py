@@ -158,22 +158,28 @@ def test_merit_parity(cid):
 
 
 def test_merit_bit_identical_across_workgroup_sizes():
+    """The bit-identity gate: every launch variant of the merit (workgroup size, and the
+    fused per-knot or candidate-parallel decomposition) gives the same bits."""
     bt = _batch(5, 3)
     dz = np.random.default_rng(0).standard_normal((3, 128 * 14 + 127 * 7)).astype(np.float32) * 0.1
     runs = []
-    old = os.environ.get("GATO_MERIT_WAVES")
+    saved = {k: os.environ.get(k) for k in ("GATO_MERIT_WAVES", "GATO_MERIT_VARIANT")}
     try:
-        for w in ("1", "2", "3", "8", "16"):
-            os.environ["GATO_MERIT_WAVES"] = w
-            runs.append(gpu_merit(bt, dz, 1.3))
+        for variant in ("fused", "candidate"):
+            os.environ["GATO_MERIT_VARIANT"] = variant
+            for w in ("1", "2", "3", "8", "16"):
+                os.environ["GATO_MERIT_WAVES"] = w
+                runs.append(gpu_merit(bt, dz, 1.3, flags=np.array([0, 64, 0], np.int32)))
     finally:
-        if old is None:
-            os.environ.pop("GATO_MERIT_WAVES", None)
-        else:
-            os.environ["GATO_MERIT_WAVES"] = old
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     for r in runs[1:]:
         for k in ("merit", "merit0", "best", "flags"):
             np.testing.assert_array_equal(r[k], runs[0][k])
+    assert runs[0]["flags"][1] & 64  # ORed into the bits already there
 
 
 def test_merit_ascent_direction_fails_line_search():
