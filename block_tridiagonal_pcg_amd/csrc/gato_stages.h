@@ -739,23 +739,40 @@ __device__ __forceinline__ void direct_solve(const Params& p, int b, bool bv)
         gam = ngam;
     }
 
-    // back substitution, with the recovery of each knot's dz
+    // back substitution, with the recovery of each knot's dz; the next knot's
+    // rows are requested before this knot's arithmetic
+    struct Back {
+        float Hk[NC], sup[NC], qi[NC], ri[MC], bc[NC], gk, qv, rv;
+    };
+    auto fetch = [&](int k, Back& f) {
+        const bool kok = rowi && k >= 0;
+        const int kk = k >= 0 ? k : 0;
+        const bool urow = kok && kk < N - 1 && i < MC;
+        ld_row<NC>(Hw, hrow + (size_t)kk * NC * NC, kok, f.Hk);
+        f.gk = ld1(Gw, grow + (size_t)kk * NC, kok);
+        ld_row<NC>(p.S, ix.blk(bb, kk, 2, i), kok, f.sup);
+        ld_row<NC>(p.Qinv, ix.Q(bb, kk, i), kok, f.qi);
+        ld_row<MC>(p.Rinv, ix.R(bb, kk, i), urow, f.ri);
+        ld_row<NC, MC>(p.Bu, ix.Bu(bb, kk, 0) + i, urow, f.bc);  // column i of B_k
+        f.qv = ld1(p.q, ix.vn(bb, kk, i), kok);
+        f.rv = ld1(p.r, ix.vm(bb, kk, i), urow);
+    };
     bool nonfinite = false;
     float lamn = 0.0f;  // row i of lambda_{k+1}
+    Back cur;
+    fetch(N - 1, cur);
     for (int k = N - 1; k >= 0; --k) {
-        const bool kv = bv;
-        const bool hn = kv && k < N - 1;
+        Back nxt;
+        fetch(k - 1, nxt);
+        const bool hn = bv && k < N - 1;
         const bool rowv = rowi;
         const bool urow = hn && i < MC;
-        float Hk[NC], sup[NC], qi[NC], ri[MC], bc[NC];
-        ld_row<NC>(Hw, hrow + (size_t)k * NC * NC, rowi, Hk);
-        const float gk = ld1(Gw, grow + (size_t)k * NC, rowi);
-        ld_row<NC>(p.S, ix.blk(bb, k, 2, i), rowi, sup);
-        ld_row<NC>(p.Qinv, ix.Q(bb, k, i), rowv, qi);
-        ld_row<MC>(p.Rinv, ix.R(bb, k, i), urow, ri);
-        ld_row<NC, MC>(p.Bu, ix.Bu(bb, k, 0) + i, urow, bc);  // column i of B_k
-        const float qv = ld1(p.q, ix.vn(bb, k, i), rowv);
-        const float rv = ld1(p.r, ix.vm(bb, k, i), urow);
+        const float* Hk = cur.Hk;
+        const float* sup = cur.sup;
+        const float* qi = cur.qi;
+        const float* ri = cur.ri;
+        const float* bc = cur.bc;
+        const float gk = cur.gk, qv = cur.qv, rv = cur.rv;
 
         float t = 0.0f;
         dotb<NP, NC>(t, Bc<NP>(lamn), sup);
@@ -774,6 +791,7 @@ __device__ __forceinline__ void direct_solve(const Params& p, int b, bool bv)
         }
         if (urow) p.dz[ix.du(bb, k, i)] = du;
         lamn = lam;
+        cur = nxt;
     }
 
     // per-solve flags: any lane of the group
