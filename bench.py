@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--profile-copy", action="store_true")
     ap.add_argument("--merit-variants", action="store_true",
                     help="instead of the step: time the merit call's launch variants (one JSON line)")
+    ap.add_argument("--sqp-driver", action="store_true",
+                    help="instead of the step: time the multi-iteration SQP driver on the pendulum-chain plant")
     return ap.parse_args()
 
 
@@ -238,6 +240,53 @@ def merit_variants(a):
                       "unit": "us per launch", "rows": rows}))
 
 
+# ---------------------------------------------------------------- SQP driver
+
+
+def sqp_driver(a, iters=10, N=64, dof=7):
+    """SQP iterations per second of the whole driver loop (plant linearisation on the
+    device, gato_sqp_step, step and damping update) on the 7-DoF chain, and the fp64
+    reference driver on the host for a sample of the batch."""
+    import numpy as np
+    import torch
+
+    from block_tridiagonal_pcg_amd import driver, plant
+
+    torch.cuda.set_device(0)
+    P = plant.Chain(dof)
+    B = a.batch
+    xi, xr, rho = plant.seed(P, B)
+    driver.solve(P, xi, xr, rho, N, 2, record=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = driver.solve(P, xi, xr, rho, N, iters, record=False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    again = driver.solve(P, xi, xr, rho, N, iters, step_events=True)
+    hist = again["history"]
+    rec = {"study": "SQP driver", "plant": "pendulum chain, %d DoF (n=%d, m=%d)" % (dof, P.n, P.m), "N": N, "B": B,
+           "iterations": iters, "ms_per_iteration": wall / iters * 1e3,
+           "solve_iterations_per_s": B * iters / wall,
+           "defect_max_first": float(hist[0]["defect"].max()), "defect_max_last": float(hist[-1]["defect"].max()),
+           "pcg_iters_per_iteration": [int(np.median(h["iters"])) for h in hist],
+           "sqp_step_us_per_iteration": [round(x, 1) for x in again["step_us"]]}
+    del res
+    if not a.no_cpu_baseline:
+        import oracle
+        from oracle import driver_ref
+
+        from block_tridiagonal_pcg_amd import synth
+
+        oracle.load()
+        Bs = min(B, 16)
+        t0 = time.perf_counter()
+        driver_ref.solve(P, xi[:Bs], xr[:Bs], rho[:Bs], N, 2, synth.ALPHAS)
+        cw = time.perf_counter() - t0
+        rec["cpu_reference"] = {"solve_iterations_per_s": Bs * 2 / cw, "sample": "%d solves x 2 iterations" % Bs,
+                                "cores": oracle.num_threads(), "kind": "oracle"}
+    print(json.dumps(rec))
+
+
 # ---------------------------------------------------------------- main
 
 
@@ -257,6 +306,9 @@ def main():
         sys.exit(1)
     if a.merit_variants:
         merit_variants(a)
+        return
+    if a.sqp_driver:
+        sqp_driver(a)
         return
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[a.config]

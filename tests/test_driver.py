@@ -1,0 +1,108 @@
+"""The multi-iteration SQP driver (the outer loop around gato_sqp_step) and its plant.
+
+CPU: the plant's Jacobians against central differences, the reference driver's
+convergence and its damping rule.  GPU: the device driver against the fp64
+reference driver on the same seeded batch.  Tolerance: each iteration's step comes
+from an fp32 solve with dz within 1e-3 of the fp64 one, so the trajectories are
+compared after convergence (1e-3 relative for the states, 1e-4 for the cost);
+accept/reject decisions are compared on the first iteration, where both sides see
+the same data, for the solves whose best merit is not tied (within 1e-3 of the
+merit scale) with another candidate: later decisions meet rounding-level ties near
+the fixed point.
+"""
+import numpy as np
+import pytest
+
+from block_tridiagonal_pcg_amd import plant, synth
+
+
+def test_plant_jacobians_match_central_differences():
+    P = plant.Chain(3)
+    rng = np.random.default_rng(5)
+    X = rng.uniform(-0.5, 0.5, (2, 4, P.n))
+    U = rng.uniform(-0.5, 0.5, (2, 3, P.m))
+    A, Bu, e = plant.linearize(P, X, U)
+    h = 1e-6
+    for j in range(P.n):
+        Xp, Xm = X.copy(), X.copy()
+        Xp[..., :-1, j] += h
+        Xm[..., :-1, j] -= h
+        fd = (plant.step(P, Xp, U) - plant.step(P, Xm, U)) / (2 * h)
+        np.testing.assert_allclose(A[..., :, j], fd, atol=1e-8)
+    for j in range(P.m):
+        Up, Um = U.copy(), U.copy()
+        Up[..., j] += h
+        Um[..., j] -= h
+        fd = (plant.step(P, X, Up) - plant.step(P, X, Um)) / (2 * h)
+        np.testing.assert_allclose(Bu[..., :, j], fd, atol=1e-8)
+    np.testing.assert_allclose(e, plant.step(P, X, U) - X[..., 1:, :])
+
+
+def test_plant_cost_terms_are_the_gradient_of_the_cost():
+    P = plant.Chain(2)
+    rng = np.random.default_rng(6)
+    X = rng.uniform(-1, 1, (1, 5, P.n))
+    U = rng.uniform(-1, 1, (1, 4, P.m))
+    xr = rng.uniform(-1, 1, (1, P.n))
+    Q, q, R, r = plant.cost_terms(P, X, U, xr)
+    h = 1e-6
+    Xp = X.copy()
+    Xp[0, 2, 1] += h
+    Xm = X.copy()
+    Xm[0, 2, 1] -= h
+    g = (plant.cost(P, Xp, U, xr) - plant.cost(P, Xm, U, xr)) / (2 * h)
+    assert abs(g[0] - q[0, 2, 1]) < 1e-6
+    assert np.allclose(Q[0, 2], np.diag(np.r_[np.full(2, P.w_theta), np.full(2, P.w_omega)]))
+    assert np.allclose(r, P.w_u * U) and np.allclose(R[0, 0], P.w_u * np.eye(2))
+
+
+def test_reference_driver_converges_and_follows_the_damping_rule():
+    from oracle import driver_ref
+
+    P = plant.Chain(2)
+    xi, xr, rho0 = plant.seed(P, 4)
+    res = driver_ref.solve(P, xi, xr, rho0, 16, 6, synth.ALPHAS)
+    h = res["history"]
+    d0 = plant.defect(P, np.repeat(xi[:, None, :], 16, axis=1), np.zeros((4, 15, 2)), xi)
+    assert (h[-1]["defect"] < 1e-3 * np.maximum(d0, 1e-3)).all()
+    rho = rho0.copy()
+    for step in h:
+        want = np.where(step["best"] == 0, np.maximum(rho / 10, 1e-8),
+                        np.where(step["best"] < 0, np.minimum(rho * 10, 10.0), rho))
+        np.testing.assert_allclose(step["rho"], want)
+        rho = step["rho"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dof,N,B", [(7, 32, 8), (2, 80, 3)])
+def test_device_driver_matches_reference(dof, N, B):
+    """The first iteration (identical data on both sides) takes the same decisions where
+    they are clear, and both drivers converge to the same trajectory."""
+    import torch
+
+    import oracle
+    from block_tridiagonal_pcg_amd import driver, ops
+    from oracle import driver_ref
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    ops.load()
+    oracle.load()
+    print("case: driver", dof, N, B, flush=True)
+    P = plant.Chain(dof)
+    xi, xr, rho0 = plant.seed(P, B)
+    iters = 10
+    g = driver.solve(P, xi, xr, rho0, N, iters)
+    o = driver_ref.solve(P, xi, xr, rho0, N, iters, synth.ALPHAS)
+    hg, ho = g["history"][0], o["history"][0]
+    scale = np.maximum(np.abs(ho["merit"]).max(1), ho["merit0"])
+    sorted_m = np.sort(np.concatenate([ho["merit"], ho["merit0"][:, None]], 1), 1)
+    clear = (sorted_m[:, 1] - sorted_m[:, 0]) > 1e-3 * scale  # best value not tied with another
+    np.testing.assert_array_equal(hg["best"][clear], ho["best"][clear])
+    assert clear.sum() >= B // 2
+    for h in (g["history"][-1], o["history"][-1]):
+        assert (h["defect"] <= 1e-3).all()
+    Xg, Ug = g["X"].cpu().numpy(), g["U"].cpu().numpy()
+    assert np.linalg.norm(Xg - o["X"]) <= 1e-3 * np.linalg.norm(o["X"])
+    assert np.linalg.norm(Ug - o["U"]) <= 1e-2 * max(np.linalg.norm(o["U"]), 1e-6)
+    np.testing.assert_allclose(g["history"][-1]["cost"], o["history"][-1]["cost"], rtol=1e-4)
