@@ -7,9 +7,14 @@
 //   k_pcg_res     stage 2 alone with S and Phi^-1 rows loaded once into registers.
 //   k_pcg_stream  stage 2 alone for horizons longer than a workgroup holds:
 //                 C knots per lane group, rows re-read from memory per product.
+//   k_direct      stage 2 by block Thomas elimination, one lane group per solve.
+//   k_cr_res      stage 2 by block cyclic reduction, log-depth in the horizon,
+//                 the solve held in registers and LDS (n <= 16, N <= 128).
+//   k_cr          the same for any horizon, reduced rows kept in the workspace.
 //   k_merit       stage 3 alone; any workgroup size gives identical bits.
 #include "gato_stages.h"
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -291,6 +296,48 @@ __global__ __launch_bounds__(64) void k_direct(Params p)
     direct_solve<SH>(p, b, b < p.B);
 }
 
+// ------------------------------------------------------------------ stage 2, cyclic reduction
+
+// One workgroup per solve; up to 64 lane groups (32 for n > 16, whose rows
+// are twice as wide) share the eliminations of each level.  A horizon of N
+// knots has at most ceil(N/2) eliminations per level, so shorter horizons
+// get fewer waves.
+template <class SH>
+struct CrLaunch {
+    static constexpr int MAXT = SH::NP == 16 ? 1024 : 512;
+    static int threads(int N)
+    {
+        int cap = MAXT / SH::NP;
+        if (const char* env = std::getenv("GATO_CR_GROUPS")) {  // lane groups per workgroup (measurements)
+            const int gr = std::atoi(env);
+            if (gr >= 1 && gr < cap) cap = gr;
+        }
+        const int want = (N + 1) / 2;
+        const int groups = want < 1 ? 1 : (want < cap ? want : cap);
+        return ((groups + SH::KPW - 1) / SH::KPW) * 64;
+    }
+};
+
+template <class SH>
+__global__ __launch_bounds__(CrLaunch<SH>::MAXT) void k_cr(Params p)
+{
+    cr_solve<SH>(p, blockIdx.x);
+}
+
+// Horizons whose knots fit in one workgroup's registers (n <= 16, N <= 128):
+// two knots per lane group, W blocks exchanged through LDS.
+template <class SH>
+__global__ __launch_bounds__(1024) void k_cr_res(Params p)
+{
+    cr_resident<SH>(p, blockIdx.x);
+}
+
+static bool cr_streaming_forced()  // GATO_CR_VARIANT=stream: the streaming kernel for every N (measurements)
+{
+    const char* env = std::getenv("GATO_CR_VARIANT");
+    return env && std::strcmp(env, "stream") == 0;
+}
+
 // ------------------------------------------------------------------ stage 3 alone
 
 template <class SH, int LPL>
@@ -478,6 +525,18 @@ struct Ops {
         hipLaunchKernelGGL((k_direct<SH>), dim3((p.B + SPW - 1) / SPW), dim3(64), 0, st, p);
         return hipGetLastError();
     }
+    static hipError_t cr(const Params& p, hipStream_t st)
+    {
+        if constexpr (SH::NP == 16) {
+            if (p.N <= 2 * CrResLds<SH>::MAXG && !cr_streaming_forced()) {
+                const int groups = (p.N + 1) / 2;
+                hipLaunchKernelGGL((k_cr_res<SH>), dim3(p.B), dim3(((groups + KPW - 1) / KPW) * 64), 0, st, p);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((k_cr<SH>), dim3(p.B), dim3(CrLaunch<SH>::threads(p.N)), 0, st, p);
+        return hipGetLastError();
+    }
     static hipError_t fused(const Params& p, hipStream_t st)
     {
         hipLaunchKernelGGL((k_sqp_fused<SH>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
@@ -551,6 +610,23 @@ static size_t direct_ws_bytes(const gato_dims_t* d)
     return align256(B * N * n * (n + 1) * sizeof(float));
 }
 
+// Cyclic reduction: one row [L | U | gamma | D] per knot row, padded to float4s.
+static size_t cr_row_floats(int n) { return (size_t)(3 * n + 1 + 3) / 4 * 4; }
+
+static size_t cr_ws_bytes(const gato_dims_t* d)
+{
+    const size_t B = d->B, N = d->N, n = d->n;
+    return align256(B * N * n * cr_row_floats(d->n) * sizeof(float));
+}
+
+// The long-horizon solve of gato_sqp_step: cyclic reduction unless
+// GATO_LONG_SOLVE=thomas asks for the block Thomas solve (for measurements).
+static bool long_solve_thomas()
+{
+    const char* env = std::getenv("GATO_LONG_SOLVE");
+    return env && std::strcmp(env, "thomas") == 0;
+}
+
 static WsLayout ws_layout(const gato_dims_t* d)
 {
     const size_t B = d->B, N = d->N, n = d->n, m = d->m;
@@ -566,8 +642,8 @@ static WsLayout ws_layout(const gato_dims_t* d)
     off += align256(B * N * n * n * sizeof(float));
     w.Rinv = off;
     off += align256(B * (N > 1 ? N - 1 : 1) * m * m * sizeof(float));
-    w.direct = off;
-    off += direct_ws_bytes(d);
+    w.direct = off;  // the block Thomas or the cyclic-reduction solve's workspace
+    off += std::max(direct_ws_bytes(d), cr_ws_bytes(d));
     w.total = off;
     return w;
 }
@@ -687,6 +763,42 @@ int gato_direct_solve(const gato_dims_t* dims, const float* S, const float* gamm
     });
 }
 
+int32_t gato_cr_levels(int32_t N)
+{
+    if (N < 1) return 0;
+    int levels = 1;
+    for (int64_t s = 1; s < N; s *= 2) ++levels;
+    return levels;
+}
+
+size_t gato_cr_workspace_bytes(const gato_dims_t* dims)
+{
+    if (check_dims(dims) != GATO_OK || dims->B == 0) return 0;
+    return cr_ws_bytes(dims);
+}
+
+int gato_cr_solve(const gato_dims_t* dims, const float* S, const float* gamma, const float* Qinv,
+                  const float* Rinv, const float* Bu, const float* q, const float* r, float* lambda, float* dz,
+                  int32_t* flags, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
+    rc = check_ptrs({S, gamma, Qinv, dyn(Rinv, dims), dyn(Bu, dims), q, dyn(r, dims), lambda, dz, flags});
+    if (rc) return rc;
+    if (workspace == nullptr || workspace_bytes < cr_ws_bytes(dims)) return GATO_E_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return GATO_E_ALIGN;
+    Params p = make_params(dims);
+    p.S = const_cast<float*>(S); p.gamma = const_cast<float*>(gamma);
+    p.Qinv = const_cast<float*>(Qinv); p.Rinv = const_cast<float*>(Rinv);
+    p.Bu = Bu; p.q = q; p.r = r;
+    p.lambda = lambda; p.dz = dz; p.flags = flags;
+    p.dws = static_cast<float*>(workspace);
+    return with_shape(dims->n, dims->m, [&](auto ops) {
+        return decltype(ops)::cr(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
+    });
+}
+
 static int check_alpha(const float* alphas_host, int32_t n_alpha, float mu)
 {
     if (alphas_host == nullptr) return GATO_E_NULL;
@@ -775,7 +887,8 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (fused) return O::fused(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
         if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;  // no Phi^-1: the direct solve follows
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
-        if (O::direct(p, stream) != hipSuccess) return GATO_E_HIP;  // horizons a workgroup cannot hold
+        // horizons a workgroup cannot hold
+        if ((long_solve_thomas() ? O::direct(p, stream) : O::cr(p, stream)) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
         if (O::merit(p, stream) != hipSuccess) return GATO_E_HIP;
         return GATO_OK;

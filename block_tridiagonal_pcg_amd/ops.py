@@ -34,6 +34,9 @@ EXPORTS = (
     "gato_pcg_solve",
     "gato_direct_solve",
     "gato_direct_workspace_bytes",
+    "gato_cr_solve",
+    "gato_cr_workspace_bytes",
+    "gato_cr_levels",
     "gato_merit_eval",
     "gato_sqp_step",
     "gato_workspace_bytes",
@@ -79,6 +82,11 @@ def load():
             lib.gato_direct_solve.argtypes = [P] * 12 + [Z, P]
             lib.gato_direct_workspace_bytes.argtypes = [P]
             lib.gato_direct_workspace_bytes.restype = Z
+            lib.gato_cr_solve.argtypes = [P] * 12 + [Z, P]
+            lib.gato_cr_workspace_bytes.argtypes = [P]
+            lib.gato_cr_workspace_bytes.restype = Z
+            lib.gato_cr_levels.argtypes = [I]
+            lib.gato_cr_levels.restype = I
             lib.gato_merit_eval.argtypes = [P] * 11 + [I, F] + [P] * 5
             lib.gato_sqp_step.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P]
             lib.gato_workspace_bytes.argtypes = [P, I]
@@ -86,7 +94,7 @@ def load():
             lib.gato_status_string.argtypes = [ctypes.c_int]
             lib.gato_status_string.restype = ctypes.c_char_p
             lib.gato_shape_supported.argtypes = [I, I, I]
-            for f in ("gato_form_schur", "gato_pcg_solve", "gato_direct_solve", "gato_merit_eval",
+            for f in ("gato_form_schur", "gato_pcg_solve", "gato_direct_solve", "gato_cr_solve", "gato_merit_eval",
                       "gato_sqp_step", "gato_shape_supported"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
@@ -199,6 +207,42 @@ def gato_direct_solve(dims, S, gamma, Qinv, Rinv, Bu, q, r, lam, dz, flags, work
     rc = load().gato_direct_solve(ctypes.byref(d), _p(S), _p(gamma), _p(Qinv), _p(Rinv), _p(Bu), _p(q), _p(r),
                                   _p(lam), _p(dz), _p(flags), ws_ptr, ctypes.c_size_t(ws_bytes), _stream(stream))
     return _raise("gato_direct_solve", rc)
+
+
+def gato_cr_workspace_bytes(dims):
+    return int(load().gato_cr_workspace_bytes(ctypes.byref(_dims(*dims))))
+
+
+def cr_workspace_for(dims, device="cuda"):
+    nb = gato_cr_workspace_bytes(dims)
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb > 0 else None
+
+
+def gato_cr_levels(N):
+    return int(load().gato_cr_levels(int(N)))
+
+
+def gato_cr_solve(dims, S, gamma, Qinv, Rinv, Bu, q, r, lam, dz, flags, workspace, stream=None):
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    for t, k in ((S, "S"), (gamma, "gamma"), (Qinv, "Qinv"), (Rinv, "Rinv"), (Bu, "Bu"), (q, "q"), (r, "r"),
+                 (lam, "lam"), (dz, "dz")):
+        _chk(t, k, shape=sh[k])
+    _chk(flags, "flags", torch.int32, sh["B_"])
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _chk(workspace, "workspace", torch.uint8)
+        ws_ptr, ws_bytes = _p(workspace), workspace.numel()
+    d = _dims(n, m, N, B)
+    rc = load().gato_cr_solve(ctypes.byref(d), _p(S), _p(gamma), _p(Qinv), _p(Rinv), _p(Bu), _p(q), _p(r),
+                              _p(lam), _p(dz), _p(flags), ws_ptr, ctypes.c_size_t(ws_bytes), _stream(stream))
+    return _raise("gato_cr_solve", rc)
+
+
+def long_solve():
+    """The stage-2 solve gato_sqp_step uses beyond the fused horizons: "cr" (block
+    cyclic reduction) unless GATO_LONG_SOLVE=thomas selects the block Thomas solve."""
+    return "thomas" if os.environ.get("GATO_LONG_SOLVE") == "thomas" else "cr"
 
 
 def _alphas(alphas):
@@ -323,13 +367,15 @@ def prepared_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alpha
 def stage_times(dims, dev, eps, max_iters, alphas, mu, reps=10, stream=None):
     """Median device time (us) of the three standalone calls on `dev` (a to_device batch):
     gato_form_schur, stage 2 as gato_sqp_step runs it (gato_pcg_solve from a cold start
-    where the fused path applies, else gato_direct_solve), gato_merit_eval."""
+    where the fused path applies, else gato_cr_solve or gato_direct_solve as long_solve()
+    says), gato_merit_eval."""
     import statistics
 
     st = torch.cuda.current_stream() if stream is None else stream
     out = alloc_outputs(dims, len(alphas))
     direct = gato_workspace_bytes(dims, len(alphas)) > 0
-    dws = direct_workspace_for(dims) if direct else None
+    cr = direct and long_solve() == "cr"
+    dws = (cr_workspace_for(dims) if cr else direct_workspace_for(dims)) if direct else None
     fields = ("Q", "q", "R", "r", "A", "Bu", "e", "x0")
     res = {"schur_us": [], "linsys_us": [], "merit_us": []}
     for _ in range(reps + 1):
@@ -340,7 +386,10 @@ def stage_times(dims, dev, eps, max_iters, alphas, mu, reps=10, stream=None):
         ev[1].record(st)
         out["lam"].zero_()
         ev[2].record(st)
-        if direct:
+        if cr:
+            gato_cr_solve(dims, out["S"], out["gamma"], out["Qinv"], out["Rinv"], dev["Bu"], dev["q"], dev["r"],
+                          out["lam"], out["dz"], out["flags"], dws, stream=st)
+        elif direct:
             gato_direct_solve(dims, out["S"], out["gamma"], out["Qinv"], out["Rinv"], dev["Bu"], dev["q"], dev["r"],
                               out["lam"], out["dz"], out["flags"], dws, stream=st)
         else:

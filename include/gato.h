@@ -178,6 +178,38 @@ int gato_direct_solve(const gato_dims_t* dims, const float* S, const float* gamm
                       hipStream_t stream);
 
 /*
+ * Stage 2, cyclic reduction (the cyclic-frames elimination plan of the Branch
+ * page, "Specializing Robotics Solvers in Warp": its elimination-plan figure
+ * and the cyclic-reduction row of its plans table; the log-depth alternative
+ * to gato_direct_solve for long horizons).  Solves S lambda = gamma exactly (up
+ * to rounding) by block cyclic reduction: level l = 0, 1, ... eliminates the
+ * knots that are odd multiples of s = 2^l from the system on the multiples of
+ * s.  With L_k, U_k the couplings of knot k to knots k - s and k + s there,
+ * an eliminated knot j forms Y1_j = D_j^-1 L_j, Y2_j = D_j^-1 U_j,
+ * y3_j = D_j^-1 gamma_j, and a kept knot i (a multiple of 2s) becomes
+ *   D_i - L_i Y2_{i-s} - U_i Y1_{i+s},  L_i <- -L_i Y1_{i-s},  U_i <- -U_i Y2_{i+s},
+ *   gamma_i - L_i y3_{i-s} - U_i y3_{i+s}.
+ * Knot 0 is left alone after ceil(log2 N) levels and solved directly; the
+ * back substitution lambda_j = y3_j - Y1_j lambda_{j-s} - Y2_j lambda_{j+s}
+ * runs the levels in reverse.  Then dz is recovered exactly as gato_pcg_solve
+ * does.  Arguments as in gato_direct_solve; the reduced rows and the Y blocks
+ * go through the caller's workspace, of at least gato_cr_workspace_bytes(dims)
+ * bytes, 256-byte aligned.  Pivot blocks are inverted by Gauss-Jordan without
+ * pivoting (each is a diagonal block of a Schur complement of an SPD S); a
+ * pivot that is not positive ORs S_NOT_SPD into flags, a non-finite lambda
+ * NONFINITE.  The eliminations of one level run in parallel, so a solve's
+ * depth grows with log2 N rather than N.
+ */
+size_t gato_cr_workspace_bytes(const gato_dims_t* dims);
+int gato_cr_solve(const gato_dims_t* dims, const float* S, const float* gamma, const float* Qinv,
+                  const float* Rinv, const float* Bu, const float* q, const float* r, float* lambda, float* dz,
+                  int32_t* flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Number of levels gato_cr_solve runs for a horizon of N knots:
+ * ceil(log2 N) reduction levels plus the final single-knot solve (0 for N < 1). */
+int32_t gato_cr_levels(int32_t N);
+
+/*
  * Stage 3 (GATO paper Sec. II eq. 3, Sec. III eq. 7; the merit kernel of the
  * GATO docs' "Merit launch timing").  For every solve, knot and step size a:
  *   m_k(a) = a (q_k'dx_k + r_k'du_k) + a^2/2 (dx_k'Q_k dx_k + du_k'R_k du_k)
@@ -204,11 +236,13 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *  - where one workgroup can hold a whole solve (N <= 64 for n <= 16, N <= 16
  *    for n <= 32), the stages run fused in one kernel with PCG, and no
  *    workspace is used;
- *  - otherwise stage 2 is gato_direct_solve's block elimination: lambda's
- *    input is not read, iters and relres are written as 0, and eps and
- *    max_iters are checked but unused.  S, Pinv, gamma, Qinv, Rinv and the
- *    elimination's rows go through `workspace` (gato_workspace_bytes() bytes,
- *    256-byte aligned, caller-owned device memory).
+ *  - otherwise stage 2 is gato_cr_solve's block cyclic reduction (or, with
+ *    the environment variable GATO_LONG_SOLVE=thomas, gato_direct_solve's
+ *    block elimination): lambda's input is not read, iters and relres are
+ *    written as 0, and eps and max_iters are checked but unused.  S, Pinv,
+ *    gamma, Qinv, Rinv and the solve's rows go through `workspace`
+ *    (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device
+ *    memory).
  * times (nullable): per-stage device times; when given, the call synchronises.
  */
 int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,

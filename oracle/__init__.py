@@ -17,6 +17,7 @@ from .ref import (  # noqa: F401
     merit_eval,
     sqp_step,
     direct_solve,
+    cyclic_plan,
     recover,
     FLAG_Q_NOT_SPD,
     FLAG_R_NOT_SPD,

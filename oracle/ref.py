@@ -186,6 +186,25 @@ def direct_solve(S, gamma):
     return dict(lam=lam, flags=fl)
 
 
+def cyclic_plan(T):
+    """The cyclic-frames elimination order for a chain of T frames (Branch page,
+    "Specializing Robotics Solvers in Warp": the elimination-plan figure of "The
+    three descriptions", where cyclic frames eliminate the odd frames first and
+    then every other frame of what remains; the plans table's cyclic-reduction
+    row).  Returns the levels in order, each the list of frames it eliminates;
+    the last level is the one frame left, solved alone.  Integer bookkeeping
+    only: the exact result of any valid order is the block Cholesky solve above.
+    """
+    remaining = list(range(T))
+    levels = []
+    while len(remaining) > 1:
+        levels.append(remaining[1::2])  # the second, fourth, ... frame of the current chain
+        remaining = remaining[0::2]
+    if remaining:
+        levels.append(remaining)
+    return levels
+
+
 def recover(Qinv, Rinv, A, Bu, q, r, lam):
     """dz from lambda (the recovery step alone)."""
     B, N, n, _ = Qinv.shape

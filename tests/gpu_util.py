@@ -44,17 +44,26 @@ def gpu_pcg(batch, form, eps, max_iters, lambda0=None, flags=None):
     return dict(lam=cpu(lam), dz=cpu(dz), iters=cpu(iters), relres=cpu(relres), flags=cpu(fl))
 
 
-def gpu_direct(batch, form, flags=None):
-    """Direct block-tridiagonal solve + recovery fed `form` (stage-1 layouts, rounded to float32)."""
+def gpu_direct(batch, form, flags=None, solver="thomas"):
+    """Direct block-tridiagonal solve + recovery fed `form` (stage-1 layouts, rounded to
+    float32): gato_direct_solve (block Thomas) or, with solver="cr", gato_cr_solve
+    (block cyclic reduction, its workspace filled with NaN beforehand so that a read
+    of a row the solve did not write shows in the result)."""
     dims = batch["dims"]
     n, m, N, B = dims
     t = lambda a: torch.as_tensor(np.ascontiguousarray(np.asarray(a, np.float32))).cuda()  # noqa: E731
     lam = torch.full((B, N, n), float("nan"), dtype=torch.float32, device="cuda")
     dz = torch.full((B, N * n + (N - 1) * m), float("nan"), dtype=torch.float32, device="cuda")
     fl = torch.as_tensor(np.zeros(B, np.int32) if flags is None else np.asarray(flags, np.int32)).cuda()
-    ws = ops.direct_workspace_for(dims)
-    ops.gato_direct_solve(dims, t(form["S"]), t(form["gamma"]), t(form["Qinv"]), t(form["Rinv"]), t(batch["Bu"]),
-                          t(batch["q"]), t(batch["r"]), lam, dz, fl, ws)
+    args = (t(form["S"]), t(form["gamma"]), t(form["Qinv"]), t(form["Rinv"]), t(batch["Bu"]), t(batch["q"]),
+            t(batch["r"]), lam, dz, fl)
+    if solver == "cr":
+        ws = ops.cr_workspace_for(dims)
+        if ws is not None:
+            ws.fill_(255)  # every float NaN
+        ops.gato_cr_solve(dims, *args, ws)
+    else:
+        ops.gato_direct_solve(dims, *args, ops.direct_workspace_for(dims))
     torch.cuda.synchronize()
     return dict(lam=cpu(lam), dz=cpu(dz), flags=cpu(fl))
 

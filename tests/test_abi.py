@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared():
     text = open(os.path.join(ROOT, "include", "gato.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gato_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int32_t|int|size_t|const char\*)\s+(gato_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -25,6 +25,7 @@ def lib():
 
 def test_header_declares_the_abi():
     assert _declared() == sorted([
+        "gato_cr_levels", "gato_cr_solve", "gato_cr_workspace_bytes",
         "gato_direct_solve", "gato_direct_workspace_bytes", "gato_form_schur", "gato_merit_eval",
         "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step", "gato_status_string", "gato_workspace_bytes"])
 
@@ -55,8 +56,8 @@ def test_shapes_and_workspace(lib):
         assert not ops.gato_shape_supported(n, m, N), (n, m, N)
     assert ops.gato_workspace_bytes((14, 7, 64, 128)) == 0          # fused: no workspace
     ws = ops.gato_workspace_bytes((14, 7, 128, 512))
-    # stage-1 outputs plus the direct solve's pivot inverses and right-hand sides
-    assert ws >= 512 * 128 * (2 * 3 * 14 * 14 + 14 + 14 * 14 + 14 * 15) * 4
+    # stage-1 outputs plus the long-horizon solve's rows (cyclic reduction: 44 floats per row)
+    assert ws >= 512 * 128 * (2 * 3 * 14 * 14 + 14 + 14 * 14 + 14 * 44) * 4
     assert ops.gato_workspace_bytes((13, 7, 64, 128)) == 0          # unsupported -> 0
 
 
@@ -104,6 +105,18 @@ def test_validation_happens_before_any_launch(lib):
     assert dd(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:10], None, ctypes.c_size_t(0), None) == ops.OK
     assert dd(ctypes.byref(ops.Dims(5, 2, 64, 4)), *P[:10], ws, ctypes.c_size_t(need), None) == ops.E_UNSUPPORTED
 
+    # cyclic reduction: the same host checks
+    cr = lib.gato_cr_solve
+    need = lib.gato_cr_workspace_bytes(ctypes.byref(d))
+    assert need == ((2 * 64 * 14 * 44 * 4 + 255) // 256) * 256  # B=2 N=64 n=14: [L|U|gamma|D] rows of 44 floats
+    assert cr(ctypes.byref(d), *P[:10], None, ctypes.c_size_t(need), None) == ops.E_WORKSPACE
+    assert cr(ctypes.byref(d), *P[:10], ws, ctypes.c_size_t(need - 1), None) == ops.E_WORKSPACE
+    assert cr(ctypes.byref(d), *P[:10], ctypes.c_void_p((1 << 20) + 4), ctypes.c_size_t(need), None) == ops.E_ALIGN
+    assert cr(ctypes.byref(d), *P[:9], None, ws, ctypes.c_size_t(need), None) == ops.E_NULL
+    assert cr(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:10], None, ctypes.c_size_t(0), None) == ops.OK
+    assert cr(ctypes.byref(ops.Dims(5, 2, 64, 4)), *P[:10], ws, ctypes.c_size_t(need), None) == ops.E_UNSUPPORTED
+    assert cr(ctypes.byref(ops.Dims(14, 7, 1025, 1)), *P[:10], ws, ctypes.c_size_t(1 << 40), None) == ops.E_UNSUPPORTED
+
     al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
     g = lib.gato_merit_eval
     assert g(ctypes.byref(d), *P[:9], al, 0, 1.0, *P[9:13], None) == ops.E_PARAM
@@ -136,3 +149,14 @@ def test_single_knot_allows_empty_dynamics(lib):
     # with dynamics present (N > 1) the NULL arrays are rejected before any launch; the
     # N = 1 acceptance path launches kernels, so it is exercised by the GPU tests
     assert lib.gato_form_schur(ctypes.byref(ops.Dims(14, 7, 2, 1)), *args, None) == ops.E_NULL
+
+
+def test_cyclic_reduction_depth_matches_the_plan(lib):
+    """The library's level count is the oracle's cyclic-frames plan length,
+    ceil(log2 N) + 1, over the whole supported horizon range."""
+    import oracle
+    from block_tridiagonal_pcg_amd import ops
+
+    assert ops.gato_cr_levels(0) == 0
+    for N in list(range(1, 300)) + [511, 512, 513, 1023, 1024]:
+        assert ops.gato_cr_levels(N) == len(oracle.cyclic_plan(N)), N

@@ -1,0 +1,140 @@
+"""GPU parity of the block cyclic-reduction solve (gato_cr_solve) against the fp64
+oracle's block Cholesky of S, on the same seeded float32 inputs.
+
+Tolerance: like the block Thomas solve, the cyclic reduction's only error is fp32
+rounding of S, gamma and the elimination (a Cholesky factorisation of S with its
+knots reordered), so dz against the oracle's exact step is held to the stage-2 bar,
+||dz_gpu - dz_exact|| / ||dz_exact|| <= 1e-3, on every configuration, and to 5e-5 on
+the well-conditioned ones.  An fp32 emulation of the same elimination order gives
+at most 5.1e-6 on those and 5.4e-4 on the ill-conditioned long-horizon workload.
+The workspace is filled with NaN before every call, so a read of a row that the
+solve has not written shows up as a non-finite result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_tridiagonal_pcg_amd import ops, synth
+from gpu_util import gpu_direct, rel_rows
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {1: 1, 2: 8, 3: 16, 4: 16, 5: 4}
+TIGHT = {1: 5e-5, 2: 5e-5, 3: 5e-5, 4: 5e-5, 5: 1e-3}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    ops.load()
+    oracle.load()
+
+
+def _ident(*a):
+    print("case:", *a, flush=True)
+
+
+def _exact(bt, form):
+    """The oracle's exact step: block Cholesky of S, then the recovery."""
+    lam = oracle.direct_solve(form["S"], form["gamma"])["lam"]
+    dz = oracle.recover(form["Qinv"], form["Rinv"], bt["A"], bt["Bu"], bt["q"], bt["r"], lam)
+    return lam, dz
+
+
+def _cr(bt, form, flags=None):
+    return gpu_direct(bt, form, flags=flags, solver="cr")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_cr_parity(cid):
+    B = SMALL[cid]
+    _ident("cr", cid, B)
+    bt = synth.make_batch(cid, B)
+    form = oracle.form_schur(*synth.inputs(bt))
+    g = _cr(bt, form)
+    lam, dz = _exact(bt, form)
+    err = rel_rows(g["dz"], dz)
+    print("dz rel err max %.3e median %.3e; lambda rel err max %.3e" % (err.max(), np.median(err),
+                                                                        rel_rows(g["lam"], lam).max()))
+    assert (g["flags"] == 0).all()
+    assert err.max() <= TIGHT[cid]
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 31, 63, 64, 65, 127, 128, 129, 255, 256, 257, 600, 1023, 1024])
+def test_cr_horizons(N):
+    """Powers of two and their neighbours (a level whose last knot has no right
+    neighbour), one knot, and the largest supported horizon, where each lane group
+    takes several knots per level."""
+    B = 3
+    _ident("cr horizon", N, B)
+    bt = synth.make_batch(3, B, N=N)
+    form = oracle.form_schur(*synth.inputs(bt))
+    g = _cr(bt, form)
+    _, dz = _exact(bt, form)
+    assert (g["flags"] == 0).all()
+    assert rel_rows(g["dz"], dz).max() <= 5e-5
+
+
+@pytest.mark.parametrize("nm,N", [((1, 1), 9), ((4, 2), 33), ((12, 6), 100), ((24, 12), 9), ((24, 12), 70)])
+def test_cr_other_shapes(nm, N):
+    n, m = nm
+    _ident("cr shape", n, m, N)
+    bt = synth.make_batch(2, 3, n=n, m=m, N=N)
+    form = oracle.form_schur(*synth.inputs(bt))
+    g = _cr(bt, form)
+    _, dz = _exact(bt, form)
+    assert (g["flags"] == 0).all()
+    assert rel_rows(g["dz"], dz).max() <= 5e-5
+
+
+def test_cr_independent_of_batch_position():
+    big = synth.make_batch(3, 9, N=100)
+    g = _cr(big, oracle.form_schur(*synth.inputs(big)))
+    for b in (0, 4, 8):
+        one = synth.make_batch(3, 1, N=100, first=b)
+        h = _cr(one, oracle.form_schur(*synth.inputs(one)))
+        np.testing.assert_array_equal(h["dz"][0], g["dz"][b])
+        np.testing.assert_array_equal(h["lam"][0], g["lam"][b])
+
+
+def test_cr_flags():
+    bt = synth.make_batch(3, 4, N=40)
+    form = oracle.form_schur(*synth.inputs(bt))
+    bad = {k: np.array(v, copy=True) for k, v in form.items()}
+    bad["S"][1] = -bad["S"][1]          # negative definite: the first pivot fails
+    bad["gamma"][2, 5, 3] = np.nan      # a non-finite right-hand side
+    g = _cr(bt, bad, flags=np.array([0, 0, 0, 32], np.int32))
+    assert g["flags"][0] == 0
+    assert g["flags"][1] & ops.F_S_NOT_SPD
+    assert g["flags"][2] & ops.F_NONFINITE
+    assert g["flags"][3] == 32  # ORed into the bits already there
+
+
+def test_cr_agrees_with_block_thomas():
+    """Two elimination orders of one SPD system: both within rounding of the exact
+    solve, so within twice the bar of each other."""
+    bt = synth.make_batch(4, 8, N=200)
+    form = oracle.form_schur(*synth.inputs(bt))
+    c = _cr(bt, form)
+    t = gpu_direct(bt, form)
+    assert rel_rows(c["dz"], t["dz"]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("N", [2, 3, 17, 64, 100, 127, 128])
+def test_cr_resident_and_streaming_kernels_agree(N, monkeypatch):
+    """Up to 128 knots (n <= 16) the solve runs with every knot held in registers
+    and LDS; GATO_CR_VARIANT=stream selects the kernel that keeps the reduced
+    rows in the workspace.  Both are held to the oracle, and to each other."""
+    _ident("cr variants", N)
+    bt = synth.make_batch(2, 3, N=N)
+    form = oracle.form_schur(*synth.inputs(bt))
+    _, dz = _exact(bt, form)
+    res = _cr(bt, form)
+    monkeypatch.setenv("GATO_CR_VARIANT", "stream")
+    st = _cr(bt, form)
+    for g in (res, st):
+        assert (g["flags"] == 0).all()
+        assert rel_rows(g["dz"], dz).max() <= 5e-5
+    assert rel_rows(res["dz"], st["dz"]).max() <= 2e-5

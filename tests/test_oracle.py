@@ -400,3 +400,76 @@ def test_sqp_step_equals_stages():
     np.testing.assert_array_equal(full["merit"], mer["merit"])
     np.testing.assert_array_equal(full["iters"], res["iters"])
     np.testing.assert_array_equal(full["best"], mer["best"])
+
+
+# ---------------------------------------------------------------- cyclic-frames plan
+
+
+def test_cyclic_plan_small_cases():
+    assert oracle.cyclic_plan(0) == []
+    assert oracle.cyclic_plan(1) == [[0]]
+    assert oracle.cyclic_plan(2) == [[1], [0]]
+    assert oracle.cyclic_plan(6) == [[1, 3, 5], [2], [4], [0]]
+    assert oracle.cyclic_plan(8) == [[1, 3, 5, 7], [2, 6], [4], [0]]
+
+
+@pytest.mark.parametrize("T", list(range(1, 70)) + [127, 128, 129, 500, 1024])
+def test_cyclic_plan_covers_every_frame_in_ceil_log2_plus_one_levels(T):
+    plan = oracle.cyclic_plan(T)
+    flat = [f for lv in plan for f in lv]
+    assert sorted(flat) == list(range(T))  # each frame eliminated exactly once
+    levels = 1
+    while (1 << (levels - 1)) < T:  # smallest L with 2^(L-1) >= T, i.e. ceil(log2 T) + 1
+        levels += 1
+    assert len(plan) == levels
+    if T > 1:
+        assert plan[0] == list(range(1, T, 2))  # odd frames first
+    assert plan[-1] == [0]
+
+
+@pytest.mark.parametrize("cid,T", [(2, 7), (3, 12), (1, 5)])
+def test_cyclic_plan_is_fill_in_free_and_solves_exactly(cid, T):
+    """Eliminating S's frames in the plan's order by dense Schur complements: each
+    level's frames are pairwise non-adjacent in the current chain, what remains
+    stays block tridiagonal in chain order (no fill-in beyond neighbours), and the
+    back substitution reproduces a dense LU solve."""
+    bt = synth.make_batch(cid, 1, N=T)
+    fs = _form(bt)
+    n = fs["S"].shape[-1]
+    S = btd_dense(fs["S"][0])
+    gam = fs["gamma"][0].ravel().copy()
+    want = np.linalg.solve(S, gam)
+    blk = lambda f: slice(f * n, (f + 1) * n)  # noqa: E731
+    chain = list(range(T))
+    M, g = S.copy(), gam.copy()
+    done = []  # (frame, rows of M and g at its elimination, chain at that level)
+    scale = np.abs(S).max()
+    for lv in oracle.cyclic_plan(T):
+        pos = {f: k for k, f in enumerate(chain)}
+        idx = sorted(pos[f] for f in lv)
+        assert all(b - a > 1 for a, b in zip(idx, idx[1:]))  # independent frames
+        keep = [f for f in chain if f not in lv]
+        e = np.concatenate([np.arange(f * n, (f + 1) * n) for f in lv])
+        k = np.concatenate([np.arange(f * n, (f + 1) * n) for f in keep]) if keep else np.zeros(0, int)
+        for f in lv:
+            done.append((f, M[blk(f)].copy(), g[blk(f)].copy()))
+        if keep:
+            Mee_inv = np.linalg.inv(M[np.ix_(e, e)])
+            Mk = M[np.ix_(k, k)] - M[np.ix_(k, e)] @ Mee_inv @ M[np.ix_(e, k)]
+            gk = g[k] - M[np.ix_(k, e)] @ Mee_inv @ g[e]
+            M = np.zeros_like(M)
+            g = np.zeros_like(g)
+            M[np.ix_(k, k)] = Mk
+            g[k] = gk
+            for a, fa in enumerate(keep):
+                for b, fb in enumerate(keep):
+                    if abs(a - b) > 1:
+                        assert np.abs(M[blk(fa), blk(fb)]).max() <= 1e-12 * scale
+        chain = keep
+    # back substitution, last elimination first: D_f lam_f = g_f - (coupling rows) lam
+    lam = np.zeros(T * n)
+    for f, rows, gf in reversed(done):
+        other = rows.copy()
+        other[:, blk(f)] = 0.0
+        lam[blk(f)] = np.linalg.solve(rows[:, blk(f)], gf - other @ lam)
+    np.testing.assert_allclose(lam, want, rtol=0, atol=1e-9 * np.abs(want).max())
