@@ -525,10 +525,15 @@ struct Ops {
         hipLaunchKernelGGL((k_direct<SH>), dim3((p.B + SPW - 1) / SPW), dim3(64), 0, st, p);
         return hipGetLastError();
     }
+    static bool cr_resident(int N)
+    {
+        if constexpr (SH::NP == 16) return N <= 2 * CrResLds<SH>::MAXG && !cr_streaming_forced();
+        return false;
+    }
     static hipError_t cr(const Params& p, hipStream_t st)
     {
         if constexpr (SH::NP == 16) {
-            if (p.N <= 2 * CrResLds<SH>::MAXG && !cr_streaming_forced()) {
+            if (cr_resident(p.N)) {
                 const int groups = (p.N + 1) / 2;
                 hipLaunchKernelGGL((k_cr_res<SH>), dim3(p.B), dim3(((groups + KPW - 1) / KPW) * 64), 0, st, p);
                 return hipGetLastError();
@@ -619,12 +624,24 @@ static size_t cr_ws_bytes(const gato_dims_t* d)
     return align256(B * N * n * cr_row_floats(d->n) * sizeof(float));
 }
 
-// The long-horizon solve of gato_sqp_step: cyclic reduction unless
-// GATO_LONG_SOLVE=thomas asks for the block Thomas solve (for measurements).
-static bool long_solve_thomas()
+// The long-horizon solve of gato_sqp_step, chosen by a cost model measured on
+// MI355X (knots n = 14): block Thomas walks the knots in order, about 3.0 us
+// per knot whatever the batch until its one lane group per solve fills the
+// chip (about 1.6 ns per knot and solve beyond); cyclic reduction is
+// log-depth but does twice the arithmetic, about 0.35 us per solve with the
+// register-resident kernel (N <= 128, n <= 16) and 4.3 ns per knot and solve
+// with the streaming one once the batch fills the chip.  Cyclic reduction is
+// taken while its batch time stays below the Thomas walk's latency.
+// GATO_LONG_SOLVE=thomas or =cr forces either (for measurements).
+static bool long_solve_cr(const gato_dims_t* d, bool resident)
 {
-    const char* env = std::getenv("GATO_LONG_SOLVE");
-    return env && std::strcmp(env, "thomas") == 0;
+    if (const char* env = std::getenv("GATO_LONG_SOLVE")) {
+        if (std::strcmp(env, "thomas") == 0) return false;
+        if (std::strcmp(env, "cr") == 0) return true;
+    }
+    const double thomas_us = 3.0 * d->N;
+    const double cr_us = d->B * (resident ? 0.35 : 0.0043 * d->N);
+    return cr_us < thomas_us;
 }
 
 static WsLayout ws_layout(const gato_dims_t* d)
@@ -679,6 +696,16 @@ const char* gato_status_string(int code)
         case GATO_E_WORKSPACE: return "workspace missing or too small";
         default: return "unknown status code";
     }
+}
+
+int gato_step_solver(const gato_dims_t* dims)
+{
+    const int rc = check_dims(dims);
+    if (rc) return rc;
+    if (fused_path(dims)) return GATO_SOLVER_FUSED_PCG;
+    const bool resident =
+        with_shape(dims->n, dims->m, [&](auto ops) { return decltype(ops)::cr_resident(dims->N) ? 1 : 0; }) == 1;
+    return long_solve_cr(dims, resident) ? GATO_SOLVER_CR : GATO_SOLVER_THOMAS;
 }
 
 size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha)
@@ -888,7 +915,8 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;  // no Phi^-1: the direct solve follows
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
         // horizons a workgroup cannot hold
-        if ((long_solve_thomas() ? O::direct(p, stream) : O::cr(p, stream)) != hipSuccess) return GATO_E_HIP;
+        const bool cr = long_solve_cr(dims, O::cr_resident(p.N));
+        if ((cr ? O::cr(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
         if (O::merit(p, stream) != hipSuccess) return GATO_E_HIP;
         return GATO_OK;

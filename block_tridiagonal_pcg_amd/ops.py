@@ -40,6 +40,7 @@ EXPORTS = (
     "gato_merit_eval",
     "gato_sqp_step",
     "gato_workspace_bytes",
+    "gato_step_solver",
     "gato_status_string",
     "gato_shape_supported",
 )
@@ -89,6 +90,8 @@ def load():
             lib.gato_cr_levels.restype = I
             lib.gato_merit_eval.argtypes = [P] * 11 + [I, F] + [P] * 5
             lib.gato_sqp_step.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P]
+            lib.gato_step_solver.argtypes = [P]
+            lib.gato_step_solver.restype = ctypes.c_int
             lib.gato_workspace_bytes.argtypes = [P, I]
             lib.gato_workspace_bytes.restype = Z
             lib.gato_status_string.argtypes = [ctypes.c_int]
@@ -239,10 +242,15 @@ def gato_cr_solve(dims, S, gamma, Qinv, Rinv, Bu, q, r, lam, dz, flags, workspac
     return _raise("gato_cr_solve", rc)
 
 
-def long_solve():
-    """The stage-2 solve gato_sqp_step uses beyond the fused horizons: "cr" (block
-    cyclic reduction) unless GATO_LONG_SOLVE=thomas selects the block Thomas solve."""
-    return "thomas" if os.environ.get("GATO_LONG_SOLVE") == "thomas" else "cr"
+SOLVER_FUSED_PCG, SOLVER_THOMAS, SOLVER_CR = 0, 1, 2
+
+
+def gato_step_solver(dims):
+    """The stage-2 solver gato_sqp_step runs for dims (the library's horizon policy)."""
+    rc = int(load().gato_step_solver(ctypes.byref(_dims(*dims))))
+    if rc < 0:
+        raise GatoError("gato_step_solver", rc)
+    return rc
 
 
 def _alphas(alphas):
@@ -367,14 +375,14 @@ def prepared_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alpha
 def stage_times(dims, dev, eps, max_iters, alphas, mu, reps=10, stream=None):
     """Median device time (us) of the three standalone calls on `dev` (a to_device batch):
     gato_form_schur, stage 2 as gato_sqp_step runs it (gato_pcg_solve from a cold start
-    where the fused path applies, else gato_cr_solve or gato_direct_solve as long_solve()
-    says), gato_merit_eval."""
+    where the fused path applies, else gato_cr_solve or gato_direct_solve as
+    gato_step_solver says), gato_merit_eval."""
     import statistics
 
     st = torch.cuda.current_stream() if stream is None else stream
     out = alloc_outputs(dims, len(alphas))
     direct = gato_workspace_bytes(dims, len(alphas)) > 0
-    cr = direct and long_solve() == "cr"
+    cr = direct and gato_step_solver(dims) == SOLVER_CR
     dws = (cr_workspace_for(dims) if cr else direct_workspace_for(dims)) if direct else None
     fields = ("Q", "q", "R", "r", "A", "Bu", "e", "x0")
     res = {"schur_us": [], "linsys_us": [], "merit_us": []}

@@ -236,10 +236,13 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *  - where one workgroup can hold a whole solve (N <= 64 for n <= 16, N <= 16
  *    for n <= 32), the stages run fused in one kernel with PCG, and no
  *    workspace is used;
- *  - otherwise stage 2 is gato_cr_solve's block cyclic reduction (or, with
- *    the environment variable GATO_LONG_SOLVE=thomas, gato_direct_solve's
- *    block elimination): lambda's input is not read, iters and relres are
- *    written as 0, and eps and max_iters are checked but unused.  S, Pinv,
+ *  - otherwise stage 2 is a direct solve: gato_cr_solve's block cyclic
+ *    reduction while the batch is small enough for its log-depth to pay
+ *    (B * 0.35 us < 3 N us for n <= 16 and N <= 128, B < 700 beyond; measured
+ *    switch points), else gato_direct_solve's block Thomas elimination (the
+ *    environment variable GATO_LONG_SOLVE=thomas or =cr forces either).
+ *    lambda's input is not read, iters and relres are written as 0, and eps
+ *    and max_iters are checked but unused.  S, Pinv,
  *    gamma, Qinv, Rinv and the solve's rows go through `workspace`
  *    (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device
  *    memory).
@@ -252,6 +255,14 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
                   float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
                   int32_t* flags, void* workspace, size_t workspace_bytes,
                   gato_stage_times_t* times, hipStream_t stream);
+
+/* The stage-2 solver gato_sqp_step runs for these dims (horizon policy above),
+ * in the calling process's environment: GATO_SOLVER_FUSED_PCG, GATO_SOLVER_THOMAS
+ * or GATO_SOLVER_CR; a negative status for invalid or unsupported dims. */
+#define GATO_SOLVER_FUSED_PCG 0
+#define GATO_SOLVER_THOMAS 1
+#define GATO_SOLVER_CR 2
+int gato_step_solver(const gato_dims_t* dims);
 
 /* Workspace gato_sqp_step needs for these dims (0 when the fused path applies). */
 size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha);

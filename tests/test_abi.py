@@ -27,7 +27,8 @@ def test_header_declares_the_abi():
     assert _declared() == sorted([
         "gato_cr_levels", "gato_cr_solve", "gato_cr_workspace_bytes",
         "gato_direct_solve", "gato_direct_workspace_bytes", "gato_form_schur", "gato_merit_eval",
-        "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step", "gato_status_string", "gato_workspace_bytes"])
+        "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step", "gato_status_string", "gato_step_solver",
+        "gato_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -160,3 +161,27 @@ def test_cyclic_reduction_depth_matches_the_plan(lib):
     assert ops.gato_cr_levels(0) == 0
     for N in list(range(1, 300)) + [511, 512, 513, 1023, 1024]:
         assert ops.gato_cr_levels(N) == len(oracle.cyclic_plan(N)), N
+
+
+def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
+    """Fused PCG where a workgroup holds the horizon; beyond, cyclic reduction while
+    its batch time (0.35 us per solve resident, 4.3 ns per knot and solve streaming)
+    stays below the block Thomas walk's 3 us per knot, else block Thomas."""
+    from block_tridiagonal_pcg_amd import ops
+
+    monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
+    monkeypatch.delenv("GATO_CR_VARIANT", raising=False)
+    F, T, C = ops.SOLVER_FUSED_PCG, ops.SOLVER_THOMAS, ops.SOLVER_CR
+    cases = {(14, 7, 64, 128): F, (24, 12, 16, 4): F, (14, 7, 65, 512): C, (14, 7, 65, 1024): T,
+             (14, 7, 128, 512): C, (14, 7, 128, 1024): C, (14, 7, 128, 2048): T,
+             (14, 7, 256, 512): C, (14, 7, 256, 1024): T, (14, 7, 1024, 64): C, (14, 7, 1024, 1024): T,
+             (24, 12, 100, 8): C}
+    for dims, want in cases.items():
+        assert ops.gato_step_solver(dims) == want, dims
+    monkeypatch.setenv("GATO_LONG_SOLVE", "thomas")
+    assert ops.gato_step_solver((14, 7, 128, 16)) == T
+    assert ops.gato_step_solver((14, 7, 64, 16)) == F  # the fused path is not affected
+    monkeypatch.setenv("GATO_LONG_SOLVE", "cr")
+    assert ops.gato_step_solver((14, 7, 1024, 4096)) == C
+    with pytest.raises(ops.GatoError):
+        ops.gato_step_solver((13, 7, 128, 16))

@@ -138,3 +138,22 @@ def test_cr_resident_and_streaming_kernels_agree(N, monkeypatch):
         assert (g["flags"] == 0).all()
         assert rel_rows(g["dz"], dz).max() <= 5e-5
     assert rel_rows(res["dz"], st["dz"]).max() <= 2e-5
+
+
+@pytest.mark.parametrize("solver", ["cr", "thomas", None])
+def test_sqp_step_long_horizon_with_either_solver(solver, monkeypatch):
+    """gato_sqp_step beyond the fused horizons, with the policy's choice and with
+    each solver forced: the step is the oracle's exact step within the bar."""
+    from gpu_util import gpu_sqp
+
+    if solver:
+        monkeypatch.setenv("GATO_LONG_SOLVE", solver)
+    else:
+        monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
+    _ident("sqp long horizon", solver)
+    bt = synth.make_batch(3, 6, N=150)
+    g = gpu_sqp(bt, 1e-6, 200)
+    form = oracle.form_schur(*synth.inputs(bt))
+    _, dz = _exact(bt, form)
+    assert (g["iters"] == 0).all()
+    assert rel_rows(g["dz"], dz).max() <= 5e-5
