@@ -8,10 +8,9 @@
 //   k_pcg_stream  stage 2 alone for horizons longer than a workgroup holds:
 //                 C knots per lane group, rows re-read from memory per product.
 //   k_direct      stage 2 by block Thomas elimination, one lane group per solve.
-//   k_cr_res      stage 2 by block cyclic reduction, log-depth in the horizon,
-//                 the solve held in registers and LDS (n <= 16, N <= 128).
-//   k_cr          the same for any horizon, reduced rows kept in the workspace.
+// Stage 2 by block cyclic reduction (k_cr, k_cr_res) is in gato_cr.hip.
 //   k_merit       stage 3 alone; any workgroup size gives identical bits.
+#include "gato_internal.h"
 #include "gato_stages.h"
 
 #include <algorithm>
@@ -296,48 +295,6 @@ __global__ __launch_bounds__(64) void k_direct(Params p)
     direct_solve<SH>(p, b, b < p.B);
 }
 
-// ------------------------------------------------------------------ stage 2, cyclic reduction
-
-// One workgroup per solve; up to 64 lane groups (32 for n > 16, whose rows
-// are twice as wide) share the eliminations of each level.  A horizon of N
-// knots has at most ceil(N/2) eliminations per level, so shorter horizons
-// get fewer waves.
-template <class SH>
-struct CrLaunch {
-    static constexpr int MAXT = SH::NP == 16 ? 1024 : 512;
-    static int threads(int N)
-    {
-        int cap = MAXT / SH::NP;
-        if (const char* env = std::getenv("GATO_CR_GROUPS")) {  // lane groups per workgroup (measurements)
-            const int gr = std::atoi(env);
-            if (gr >= 1 && gr < cap) cap = gr;
-        }
-        const int want = (N + 1) / 2;
-        const int groups = want < 1 ? 1 : (want < cap ? want : cap);
-        return ((groups + SH::KPW - 1) / SH::KPW) * 64;
-    }
-};
-
-template <class SH>
-__global__ __launch_bounds__(CrLaunch<SH>::MAXT) void k_cr(Params p)
-{
-    cr_solve<SH>(p, blockIdx.x);
-}
-
-// Horizons whose knots fit in one workgroup's registers (n <= 16, N <= 128):
-// two knots per lane group, W blocks exchanged through LDS.
-template <class SH>
-__global__ __launch_bounds__(1024) void k_cr_res(Params p)
-{
-    cr_resident<SH>(p, blockIdx.x);
-}
-
-static bool cr_streaming_forced()  // GATO_CR_VARIANT=stream: the streaming kernel for every N (measurements)
-{
-    const char* env = std::getenv("GATO_CR_VARIANT");
-    return env && std::strcmp(env, "stream") == 0;
-}
-
 // ------------------------------------------------------------------ stage 3 alone
 
 template <class SH, int LPL>
@@ -525,23 +482,6 @@ struct Ops {
         hipLaunchKernelGGL((k_direct<SH>), dim3((p.B + SPW - 1) / SPW), dim3(64), 0, st, p);
         return hipGetLastError();
     }
-    static bool cr_resident(int N)
-    {
-        if constexpr (SH::NP == 16) return N <= 2 * CrResLds<SH>::MAXG && !cr_streaming_forced();
-        return false;
-    }
-    static hipError_t cr(const Params& p, hipStream_t st)
-    {
-        if constexpr (SH::NP == 16) {
-            if (cr_resident(p.N)) {
-                const int groups = (p.N + 1) / 2;
-                hipLaunchKernelGGL((k_cr_res<SH>), dim3(p.B), dim3(((groups + KPW - 1) / KPW) * 64), 0, st, p);
-                return hipGetLastError();
-            }
-        }
-        hipLaunchKernelGGL((k_cr<SH>), dim3(p.B), dim3(CrLaunch<SH>::threads(p.N)), 0, st, p);
-        return hipGetLastError();
-    }
     static hipError_t fused(const Params& p, hipStream_t st)
     {
         hipLaunchKernelGGL((k_sqp_fused<SH>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
@@ -553,16 +493,14 @@ struct Ops {
     static bool pcg_supported(int N) { return N >= 1 && stream_chunks(N) != 0; }
 };
 
-// Shapes with kernels in this build: (n, m) of the configurations the
-// benchmark and tests use, plus n = m = 1 for hand-checkable examples.
+// Shapes with kernels in this build (GATO_FOR_SHAPES).
 template <class F>
 static int with_shape(int n, int m, F&& f)
 {
-    if (n == 14 && m == 7) return f(Ops<Shape<14, 7>>{});
-    if (n == 12 && m == 6) return f(Ops<Shape<12, 6>>{});
-    if (n == 24 && m == 12) return f(Ops<Shape<24, 12>>{});
-    if (n == 4 && m == 2) return f(Ops<Shape<4, 2>>{});
-    if (n == 1 && m == 1) return f(Ops<Shape<1, 1>>{});
+#define GATO_SHAPE(n_, m_) \
+    if (n == n_ && m == m_) return f(Ops<Shape<n_, m_>>{});
+    GATO_FOR_SHAPES(GATO_SHAPE)
+#undef GATO_SHAPE
     return GATO_E_UNSUPPORTED;
 }
 
@@ -613,35 +551,6 @@ static size_t direct_ws_bytes(const gato_dims_t* d)
 {
     const size_t B = d->B, N = d->N, n = d->n;
     return align256(B * N * n * (n + 1) * sizeof(float));
-}
-
-// Cyclic reduction: one row [L | U | gamma | D] per knot row, padded to float4s.
-static size_t cr_row_floats(int n) { return (size_t)(3 * n + 1 + 3) / 4 * 4; }
-
-static size_t cr_ws_bytes(const gato_dims_t* d)
-{
-    const size_t B = d->B, N = d->N, n = d->n;
-    return align256(B * N * n * cr_row_floats(d->n) * sizeof(float));
-}
-
-// The long-horizon solve of gato_sqp_step, chosen by a cost model measured on
-// MI355X (knots n = 14): block Thomas walks the knots in order, about 3.0 us
-// per knot whatever the batch until its one lane group per solve fills the
-// chip (about 1.6 ns per knot and solve beyond); cyclic reduction is
-// log-depth but does twice the arithmetic, about 0.35 us per solve with the
-// register-resident kernel (N <= 128, n <= 16) and 4.3 ns per knot and solve
-// with the streaming one once the batch fills the chip.  Cyclic reduction is
-// taken while its batch time stays below the Thomas walk's latency.
-// GATO_LONG_SOLVE=thomas or =cr forces either (for measurements).
-static bool long_solve_cr(const gato_dims_t* d, bool resident)
-{
-    if (const char* env = std::getenv("GATO_LONG_SOLVE")) {
-        if (std::strcmp(env, "thomas") == 0) return false;
-        if (std::strcmp(env, "cr") == 0) return true;
-    }
-    const double thomas_us = 3.0 * d->N;
-    const double cr_us = d->B * (resident ? 0.35 : 0.0043 * d->N);
-    return cr_us < thomas_us;
 }
 
 static WsLayout ws_layout(const gato_dims_t* d)
@@ -703,9 +612,7 @@ int gato_step_solver(const gato_dims_t* dims)
     const int rc = check_dims(dims);
     if (rc) return rc;
     if (fused_path(dims)) return GATO_SOLVER_FUSED_PCG;
-    const bool resident =
-        with_shape(dims->n, dims->m, [&](auto ops) { return decltype(ops)::cr_resident(dims->N) ? 1 : 0; }) == 1;
-    return long_solve_cr(dims, resident) ? GATO_SOLVER_CR : GATO_SOLVER_THOMAS;
+    return cr_preferred(dims) ? GATO_SOLVER_CR : GATO_SOLVER_THOMAS;
 }
 
 size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha)
@@ -821,9 +728,7 @@ int gato_cr_solve(const gato_dims_t* dims, const float* S, const float* gamma, c
     p.Bu = Bu; p.q = q; p.r = r;
     p.lambda = lambda; p.dz = dz; p.flags = flags;
     p.dws = static_cast<float*>(workspace);
-    return with_shape(dims->n, dims->m, [&](auto ops) {
-        return decltype(ops)::cr(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
-    });
+    return cr_launch(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
 }
 
 static int check_alpha(const float* alphas_host, int32_t n_alpha, float mu)
@@ -915,8 +820,7 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;  // no Phi^-1: the direct solve follows
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
         // horizons a workgroup cannot hold
-        const bool cr = long_solve_cr(dims, O::cr_resident(p.N));
-        if ((cr ? O::cr(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
+        if ((cr_preferred(dims) ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
         if (O::merit(p, stream) != hipSuccess) return GATO_E_HIP;
         return GATO_OK;

@@ -1,0 +1,681 @@
+// gato_cr.h -- block cyclic reduction of S lambda = gamma as workgroup-level
+// device functions: the cyclic-frames elimination plan of the Branch page
+// ("Specializing Robotics Solvers in Warp"), the log-depth alternative to the
+// block Thomas solve for long horizons.  Same lane layout as gato_stages.h
+// (lane i of a knot group holds row i of that knot's blocks).
+#pragma once
+
+#include "gato_stages.h"
+
+namespace gato {
+
+// ------------------------------------------------------------------ stage 2, cyclic reduction
+
+// Float4-wide row transfers for the cyclic-reduction workspace (K a multiple
+// of 4, rows 16-byte aligned); a masked read takes the zero page instead.
+template <int K>
+__device__ __forceinline__ void ld4(const float* base, size_t off, bool ok, float* out)
+{
+    static_assert(K % 4 == 0 && K <= 2048, "");
+    const float4* a = reinterpret_cast<const float4*>(ok ? base + off : g_zero_page);
+#pragma unroll
+    for (int t = 0; t < K / 4; ++t) {
+        const float4 f = a[t];
+        out[4 * t] = ok ? f.x : 0.0f;
+        out[4 * t + 1] = ok ? f.y : 0.0f;
+        out[4 * t + 2] = ok ? f.z : 0.0f;
+        out[4 * t + 3] = ok ? f.w : 0.0f;
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void st4(float* base, size_t off, const float* v)
+{
+    static_assert(K % 4 == 0, "");
+    float4* a = reinterpret_cast<float4*>(base + off);
+#pragma unroll
+    for (int t = 0; t < K / 4; ++t) a[t] = make_float4(v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]);
+}
+
+// Value of lane P of the knot group, in every lane of the group.
+template <int NP, int P>
+__device__ __forceinline__ float bcast(float x)
+{
+    float src = x;
+    if constexpr (NP == 32) {
+        float lo, hi;
+        dup_rows(x, lo, hi);
+        src = P < 16 ? lo : hi;
+    }
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(src), 0x150 + (P & 15), 0xF, 0xF, false));
+}
+
+// acc[c] += acc[c](lane L) * mul for c < K, in place, in chunks of 16 columns.
+template <int K, int L>
+__device__ __forceinline__ void bcBs_chunks(float* acc, float mul)
+{
+    if constexpr (K <= 16) {
+        BcBs<K>::template run<L>(acc, mul);
+    } else {
+        BcBs<16>::template run<L>(acc, mul);
+        bcBs_chunks<K - 16, L>(acc + 16, mul);
+    }
+}
+
+// In-place Cholesky factorisation and lower solve of one row-per-lane block
+// row [D | R] (D: NC x NC symmetric positive definite in columns 0..NC-1,
+// right-hand sides R in columns NC..K-1): afterwards lane i holds row i of
+// [C' | C^-1 R] with D = C C' (C lower triangular); only the entries of C' on
+// and right of the diagonal are meaningful.  Step j eliminates column j from
+// the rows below j (one broadcast multiply-add per remaining column, all lanes
+// running one instruction stream) and leaves row j as it is; each row is
+// scaled by 1/sqrt(its pivot) once at the end.  (Folding that scaling into the
+// step's multiply-add, with multiplier 1/sqrt(pivot) - 1, would cost the row a
+// relative error of about 2^-24 sqrt(pivot), which large pivots make visible.)
+// `bad` is set when a pivot is not positive or not finite; the factorisation
+// then continues, flagged.
+template <int NP, int NC, int K, int J = 0>
+__device__ __forceinline__ void chol_steps(float* a, int lane, bool active, float& rs_own, bool& bad)
+{
+    if constexpr (J < NC) {
+        const float piv = bcast<NP, J>(a[J]);
+        bad |= active && (!(piv > 0.0f) || !__builtin_isfinite(piv));
+        const float rinv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
+        const float g = (active && lane > J) ? -(a[J] * rinv) : 0.0f;
+        rs_own = (active && lane == J) ? __builtin_amdgcn_rsqf(piv) : rs_own;  // v_rsq_f32, 1 ulp
+        if constexpr (NP == 16) {
+            bcBs_chunks<K - J, J>(a + J, g);
+        } else {
+            BcRow<32, K - J> src(a + J);
+            axpyb<32, K - J, J>(a + J, src, g);
+        }
+        chol_steps<NP, NC, K, J + 1>(a, lane, active, rs_own, bad);
+    }
+}
+
+// Groups with `active` false run the same instructions with zero multipliers
+// and a unit scale, which leaves their rows exactly as they were (their own
+// rows are the only broadcast sources they read).
+template <int NP, int NC, int K>
+__device__ __forceinline__ void chol_solve(float* a, int lane, bool& bad, bool active = true)
+{
+    float rs = 1.0f;
+    chol_steps<NP, NC, K>(a, lane, active, rs, bad);
+#pragma unroll
+    for (int c = 0; c < K; ++c) a[c] *= rs;
+}
+
+// Back substitution C' x = v for the factor left by chol_solve: lane i holds
+// row i of C' (ct) and v_i; on return x holds x_i.  Runs from the last row up,
+// one broadcast per row.
+template <int NP, int NC, int P = NC - 1>
+__device__ __forceinline__ void tri_upper_solve(const float* ct, float v, float dinv, int lane, float& x)
+{
+    if constexpr (P >= 0) {
+        const float xp = bcast<NP, P>(v * dinv);
+        if (lane == P) x = xp;
+        v = lane < P ? fmaf(-ct[P], xp, v) : v;
+        tri_upper_solve<NP, NC, P - 1>(ct, v, dinv, lane, x);
+    }
+}
+
+// One knot's row of the reduced system in the workspace, padded to whole
+// float4s.  A knot still in the system keeps [- | U | gamma | D]; when it is
+// eliminated the row becomes [W1 | W2 | w3 | C'] (see cr_solve).
+template <class SH>
+struct CrRow {
+    static constexpr int NC = SH::NC;
+    static constexpr int L = 0, U = NC, G = 2 * NC, D = 2 * NC + 1;
+    static constexpr int W = (3 * NC + 1 + 3) / 4 * 4;
+};
+
+// Block cyclic reduction of S lambda = gamma, then the recovery of dz: the
+// cyclic-frames elimination plan of the Branch page ("Specializing Robotics
+// Solvers in Warp": the elimination-plan figure of "The three descriptions" and
+// the cyclic-reduction row of the plans table), odd knots first, then every
+// other knot of what remains, ceil(log2 N) + 1 levels in all.  Each
+// elimination is the factor step that page describes for its cyclic fronts:
+// an in-place Cholesky factorisation and lower solve, then a Schur-complement
+// update of the neighbours.
+//
+// Level l works on the knots that are multiples of s = 2^l.  With U_k the
+// coupling of knot k to knot k + s in that system (and U_{k-s}' its coupling
+// to k - s), every knot j eliminated at this level (an odd multiple of s)
+// factors D_j = C_j C_j' and forms
+//   W1_j = C_j^-1 U_{j-s}',  W2_j = C_j^-1 U_j,  w3_j = C_j^-1 gamma_j,
+// and every kept knot i (a multiple of 2s) takes the Schur complement of its
+// two eliminated neighbours:
+//   D_i <- D_i - W2_{i-s}' W2_{i-s} - W1_{i+s}' W1_{i+s},   U_i <- -W1_{i+s}' W2_{i+s},
+//   gamma_i <- gamma_i - W2_{i-s}' w3_{i-s} - W1_{i+s}' w3_{i+s},
+// so the kept knots form a system of the same kind on stride 2s, symmetric by
+// construction.  The last level solves knot 0 alone, and the back
+// substitution runs the levels in reverse:
+//   lambda_j = C_j'^-1 (w3_j - W1_j lambda_{j-s} - W2_j lambda_{j+s}).
+// This is the block Cholesky factorisation of S with its knots reordered, so
+// every pivot block is SPD when S is; a pivot that is not positive sets
+// S_NOT_SPD.
+//
+// One workgroup holds one solve; its lane groups (lane i: row i of a block)
+// share each level's eliminations and then its updates, with a workgroup
+// barrier between the two phases.  The products W'W take column i of W (a
+// strided read of the eliminated knot's workspace rows) and broadcast rows of
+// W, so no transpose is formed.  Level 0 reads S and gamma directly; later
+// levels, the factors and the back substitution use the workspace rows.
+// Waves with no knot in a phase skip it.
+template <class SH>
+__device__ __forceinline__ void cr_solve(const Params& p, int b)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    using RW = CrRow<SH>;
+    constexpr int W = RW::W;
+    constexpr int KA = 3 * NC + 1;  // [D | U_{j-s}' | U_j | gamma]
+    const Ix<SH> ix{p.N};
+    const int N = p.N;
+    const int i = threadIdx.x % NP;
+    const int g = threadIdx.x / NP;
+    const int G = blockDim.x / NP;
+    const bool rowi = i < NC;
+    float* ws = p.dws;
+    auto wrow = [&](int k, int r) { return (((size_t)b * N + k) * NC + r) * W; };
+
+    __shared__ int wg_flags;
+    if (threadIdx.x == 0) wg_flags = 0;
+    bool bad = false, nonfinite = false;
+
+    int levels = 0;
+    for (int s = 1; s < N; s *= 2, ++levels) {
+        const bool fromS = s == 1;
+        // eliminate the odd multiples of s
+        const int E = (N + s - 1) / (2 * s);
+        for (int t0 = 0; t0 < E; t0 += G) {
+            const int t = t0 + g;
+            const bool ok = t < E;
+            if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+            const int j = ok ? s * (2 * t + 1) : s;
+            const bool hasU = j + s < N;
+            const bool ld = ok && rowi;
+            float a[KA];
+            float* D = a;
+            float* Lt = a + NC;      // row i of U_{j-s}'
+            float* U = a + 2 * NC;
+            if (fromS) {
+                ld_row<NC>(p.S, ix.blk(b, j, 1, i), ld, D);
+                ld_row<NC>(p.S, ix.blk(b, j, 0, i), ld, Lt);
+                ld_row<NC>(p.S, ix.blk(b, j, 2, i), ld && hasU, U);
+                a[3 * NC] = ld1(p.gamma, ix.vn(b, j, i), ld);
+            } else {
+                float r[W];
+                ld4<W>(ws, wrow(j, i), ld, r);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    D[c] = r[RW::D + c];
+                    U[c] = hasU ? r[RW::U + c] : 0.0f;
+                }
+                a[3 * NC] = r[RW::G];
+                ld_row<NC, W>(ws, wrow(j - s, 0) + RW::U + i, ld, Lt);  // column i of U_{j-s}
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) D[c] = ok ? D[c] : (c == i ? 1.0f : 0.0f);  // absent: identity
+            bool bk = false;
+            chol_solve<NP, NC, KA>(a, i, bk);
+            bad |= bk && ok;
+            if (ld) {
+                float r[W];
+#pragma unroll
+                for (int c = 0; c < W; ++c) r[c] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    r[RW::L + c] = Lt[c];  // W1
+                    r[RW::U + c] = U[c];   // W2
+                    r[RW::D + c] = D[c];   // row i of C'
+                }
+                r[RW::G] = a[3 * NC];  // w3
+                st4<W>(ws, wrow(j, i), r);
+            }
+        }
+        __syncthreads();
+        // update the multiples of 2s from their eliminated neighbours
+        const int K = (N + 2 * s - 1) / (2 * s);
+        for (int t0 = 0; t0 < K; t0 += G) {
+            const int t = t0 + g;
+            const bool ok = t < K;
+            if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+            const int k = ok ? 2 * s * t : 0;
+            const bool hasL = k > 0, hasU = k + s < N;
+            const bool ld = ok && rowi;
+            float D[NC], U[NC], gam;
+            if (fromS) {
+                ld_row<NC>(p.S, ix.blk(b, k, 1, i), ld, D);
+                gam = ld1(p.gamma, ix.vn(b, k, i), ld);
+            } else {
+                float r[W];
+                ld4<W>(ws, wrow(k, i), ld, r);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) D[c] = r[RW::D + c];
+                gam = r[RW::G];
+            }
+            {
+                // knot k - s: D -= W2' W2, gamma -= W2' w3
+                const int km = hasL ? k - s : 0;
+                float col[NC], row[NC];
+                ld_row<NC, W>(ws, wrow(km, 0) + RW::U + i, ld && hasL, col);  // column i of W2
+                ld_row<NC>(ws, wrow(km, i) + RW::U, ld && hasL, row);          // row i of W2
+                const float w3 = ld1(ws, wrow(km, i) + RW::G, ld && hasL);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) col[c] = -col[c];
+                gemm_rows<NP, NC, NC>(D, BcRow<NP, NC>(row), col);
+                dotb<NP, NC>(gam, Bc<NP>(w3), col);
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) U[c] = 0.0f;
+            {
+                // knot k + s: D -= W1' W1, U = -W1' W2, gamma -= W1' w3
+                const int kp = hasU ? k + s : 0;
+                float col[NC], r1[NC], r2[NC];
+                ld_row<NC, W>(ws, wrow(kp, 0) + RW::L + i, ld && hasU, col);  // column i of W1
+                ld_row<NC>(ws, wrow(kp, i) + RW::L, ld && hasU, r1);           // row i of W1
+                ld_row<NC>(ws, wrow(kp, i) + RW::U, ld && hasU, r2);           // row i of W2
+                const float w3 = ld1(ws, wrow(kp, i) + RW::G, ld && hasU);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) col[c] = -col[c];
+                gemm_rows<NP, NC, NC>(D, BcRow<NP, NC>(r1), col);
+                gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(r2), col);
+                dotb<NP, NC>(gam, Bc<NP>(w3), col);
+            }
+            if (ld) {
+                float r[W];
+#pragma unroll
+                for (int c = 0; c < W; ++c) r[c] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    r[RW::U + c] = U[c];
+                    r[RW::D + c] = D[c];
+                }
+                r[RW::G] = gam;
+                st4<W>(ws, wrow(k, i), r);
+            }
+        }
+        __syncthreads();
+    }
+
+    // last level: knot 0 alone, lambda_0 = C_0'^-1 C_0^-1 gamma_0
+    {
+        const bool ok = g == 0;
+        if (__builtin_amdgcn_ballot_w64(ok) != 0) {
+            const bool ld = ok && rowi;
+            float a[NC + 1];
+            if (N == 1) {
+                ld_row<NC>(p.S, ix.blk(b, 0, 1, i), ld, a);
+                a[NC] = ld1(p.gamma, ix.vn(b, 0, i), ld);
+            } else {
+                float r[W];
+                ld4<W>(ws, wrow(0, i), ld, r);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) a[c] = r[RW::D + c];
+                a[NC] = r[RW::G];
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) a[c] = ok ? a[c] : (c == i ? 1.0f : 0.0f);
+            bool bk = false;
+            chol_solve<NP, NC, NC + 1>(a, i, bk);
+            bad |= bk && ok;
+            float dg = 1.0f;  // C_0'[i][i]
+#pragma unroll
+            for (int c = 0; c < NC; ++c) dg = c == i ? a[c] : dg;
+            float lam = 0.0f;
+            tri_upper_solve<NP, NC>(a, a[NC], __builtin_amdgcn_rcpf(ld ? dg : 1.0f), i, lam);
+            nonfinite |= ld && !__builtin_isfinite(lam);
+            if (ld) p.lambda[ix.vn(b, 0, i)] = lam;
+        }
+        __syncthreads();
+    }
+
+    // back substitution, levels in reverse
+    for (int l = levels - 1; l >= 0; --l) {
+        const int s = 1 << l;
+        const int E = (N + s - 1) / (2 * s);
+        for (int t0 = 0; t0 < E; t0 += G) {
+            const int t = t0 + g;
+            const bool ok = t < E;
+            if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+            const int j = ok ? s * (2 * t + 1) : s;
+            const bool hasU = j + s < N;
+            const bool ld = ok && rowi;
+            float r[W];
+            ld4<W>(ws, wrow(j, i), ld, r);
+            const float lm = ld1(p.lambda, ix.vn(b, j - s, i), ld);
+            const float lp = ld1(p.lambda, ix.vn(b, hasU ? j + s : j, i), ld && hasU);
+            float v = r[RW::G];
+            float acc = 0.0f;
+            dotb<NP, NC>(acc, Bc<NP>(lm), r + RW::L);  // W1_j lambda_{j-s}
+            dotb<NP, NC>(acc, Bc<NP>(lp), r + RW::U);  // W2_j lambda_{j+s}
+            v -= acc;
+            float dg = 1.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) dg = c == i ? r[RW::D + c] : dg;
+            float lam = 0.0f;
+            tri_upper_solve<NP, NC>(r + RW::D, v, __builtin_amdgcn_rcpf(ld ? dg : 1.0f), i, lam);
+            nonfinite |= ld && !__builtin_isfinite(lam);
+            if (ld) p.lambda[ix.vn(b, j, i)] = lam;
+        }
+        __syncthreads();
+    }
+
+    // recovery of every knot's dz from lambda_k and lambda_{k+1}
+    for (int t0 = 0; t0 < N; t0 += G) {
+        const int k = t0 + g;
+        const bool ok = k < N;
+        if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+        const int kk = ok ? k : 0;
+        const bool rowv = ok && rowi;
+        const bool urow = ok && kk < N - 1 && i < MC;
+        float qi[NC], sup[NC], ri[MC], bc[NC];
+        ld_row<NC>(p.Qinv, ix.Q(b, kk, i), rowv, qi);
+        ld_row<NC>(p.S, ix.blk(b, kk, 2, i), rowv, sup);
+        ld_row<MC>(p.Rinv, ix.R(b, kk, i), urow, ri);
+        ld_row<NC, MC>(p.Bu, ix.Bu(b, kk, 0) + i, urow, bc);  // column i of B_k
+        const float qv = ld1(p.q, ix.vn(b, kk, i), rowv);
+        const float rv = ld1(p.r, ix.vm(b, kk, i), urow);
+        const float lam = ld1(p.lambda, ix.vn(b, kk, i), rowv);
+        const float lamn = ld1(p.lambda, ix.vn(b, kk + 1 < N ? kk + 1 : kk, i), rowv && kk + 1 < N);
+        float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
+        dotb<NP, NC>(h, Bc<NP>(qv), qi);
+        float dx, du;
+        recover<SH>(i, rowv, urow, lam, lamn, qi, sup, h, bc, rv, ri, dx, du);
+        if (rowv) p.dz[ix.dx(b, kk, i)] = dx;
+        if (urow) p.dz[ix.du(b, kk, i)] = du;
+    }
+
+    // per-solve flags: any lane of the workgroup (an LDS atomic, then one writer)
+    const int fl = (bad ? GATO_F_S_NOT_SPD : 0) | (nonfinite ? GATO_F_NONFINITE : 0);
+    if (fl) atomicOr(&wg_flags, fl);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        p.flags[b] |= wg_flags;
+        if (p.iters) p.iters[b] = 0;
+        if (p.relres) p.relres[b] = 0.0f;
+    }
+}
+
+// ------------------------------------------------------------------ cyclic reduction, register-resident
+
+// The same elimination for horizons whose knots fit in one workgroup's
+// registers (N <= 128, n <= 16): lane group g keeps the odd knot 2g+1 and one
+// even knot for the whole solve, so only the W blocks of eliminated knots move
+// between groups, through LDS, and memory sees S and the recovery's inputs
+// once.  Even knot 2m is eliminated at level 1 + ctz(m) (knot 0 last); the even
+// knots are assigned to groups in order of decreasing level, so each level's
+// eliminations and updates fall on contiguous groups:
+//   group 0: knot 0;  then the knots of the deepest level, ..., then those of
+//   level 1, each level in increasing knot order.
+// With M even knots, c(t) = (M - 1) >> t of m = 1 .. M-1 are multiples of 2^t,
+// and the m with ctz(m) = t occupy groups [1 + c(t+1), 1 + c(t)).
+__host__ __device__ constexpr int cr_mult(int M, int t) { return (M - 1) >> t; }
+
+__host__ __device__ constexpr int cr_even_group(int m, int M)
+{
+    if (m == 0) return 0;
+    int t = 0;
+    while (((m >> t) & 1) == 0) ++t;
+    return 1 + cr_mult(M, t + 1) + ((m >> t) - 1) / 2;
+}
+
+// Inverse of cr_even_group for 0 <= g < M.
+__host__ __device__ constexpr int cr_group_even(int g, int M)
+{
+    if (g <= 0) return 0;
+    for (int t = 0; t < 31; ++t) {
+        const int lo = 1 + cr_mult(M, t + 1), hi = 1 + cr_mult(M, t);
+        if (g >= lo && g < hi) return (2 * (g - lo) + 1) << t;
+    }
+    return 0;
+}
+
+template <class SH>
+struct CrResLds {
+    static constexpr int NC = SH::NC, YW = 2 * NC + 1;
+    static constexpr int MAXG = 64;
+    float os[MAXG][NC][YW];  // [W1 | W2 | w3] rows of the odd knots (level 0), kept to the end
+    union {
+        float es[MAXG / 2][NC][YW];  // [W1 | W2 | w3] rows of the even knots eliminated at one level
+        float lam[2 * MAXG][NC];     // lambda, once the forward sweep is over
+    };
+    int flags;
+};
+
+template <class SH>
+__device__ __forceinline__ void cr_resident(const Params& p, int b)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    static_assert(NP == 16, "one knot row per lane of a 16-lane group");
+    using LDS = CrResLds<SH>;
+    constexpr int YW = LDS::YW;
+    constexpr int KA = 3 * NC + 1;  // [D | L | U | gamma]
+    __shared__ LDS sm;
+    const Ix<SH> ix{p.N};
+    const int N = p.N;
+    const int M = (N + 1) / 2;  // even knots, one per lane group
+    const int i = threadIdx.x % NP;
+    const int g = threadIdx.x / NP;
+    const bool rowi = i < NC;
+    const int ii = rowi ? i : 0;  // LDS row index that stays inside a slot
+    const bool hasG = g < M;
+    int levels = 0;  // reduction levels, ceil(log2 N)
+    for (int s = 1; s < N; s *= 2) ++levels;
+    const int jo = 2 * g + 1;  // this group's odd knot
+    const bool hasO = hasG && jo < N;
+    const int me = hasG ? cr_group_even(g, M) : 0;
+    const int ke = 2 * me;  // this group's even knot
+    const int lev = me == 0 ? levels : 1 + __builtin_ctz(me);  // its elimination level (levels: the last solve)
+
+    if (threadIdx.x == 0) sm.flags = 0;
+    bool bad = false, nonfinite = false;
+
+    // level 0, eliminations: the odd knots; their W rows go to LDS, and their C'
+    // rows, needed only by the last back-substitution step, to the workspace
+    // (16 floats per row, M knots per solve)
+    const size_t ocrow = (((size_t)b * M + (hasO ? g : 0)) * NC + ii) * 16;
+    {
+        const bool ld = hasO && rowi;
+        const int jj = hasO ? jo : 0;
+        float a[KA];
+        ld_row<NC>(p.S, ix.blk(b, jj, 1, i), ld, a);
+        ld_row<NC>(p.S, ix.blk(b, jj, 0, i), ld, a + NC);
+        ld_row<NC>(p.S, ix.blk(b, jj, 2, i), ld && jo + 1 < N, a + 2 * NC);
+        a[3 * NC] = ld1(p.gamma, ix.vn(b, jj, i), ld);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) a[c] = hasO ? a[c] : (c == i ? 1.0f : 0.0f);
+        if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
+            chol_solve<NP, NC, KA>(a, i, bad, hasO);
+            if (ld) {
+#pragma unroll
+                for (int c = 0; c < YW; ++c) sm.os[g][i][c] = a[NC + c];
+                float r[16];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) r[c] = c < NC ? a[c] : 0.0f;
+                st4<16>(p.dws, ocrow, r);
+            }
+        }
+    }
+
+    // even knot: [D | L | U | gamma] until it is eliminated, then [C' | W1 | W2 | w3]
+    float e[KA];
+    {
+        const bool ld = hasG && rowi;
+        ld_row<NC>(p.S, ix.blk(b, ke, 1, i), ld, e);
+        ld_row<NC>(p.S, ix.blk(b, ke, 2, i), ld && ke + 1 < N, e + 2 * NC);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) e[NC + c] = 0.0f;
+        e[3 * NC] = ld1(p.gamma, ix.vn(b, ke, i), ld);
+    }
+    __syncthreads();
+
+    // Schur update of a kept knot from the W rows of its eliminated neighbours
+    // (Wm: knot k - s, Wp: knot k + s; either absent at the ends), and, when the
+    // knot is eliminated at the next level, its coupling to knot k - 2s there.
+    auto update = [&](bool kept, bool hasL, bool hasU, bool needL, const float* Wm, const float* Wp) {
+        // every value read from an absent neighbour's slot is masked to zero
+        // (a slot that no knot wrote may hold any bits)
+        const bool okm = kept && hasL, okp = kept && hasU;
+        float col[NC], row[NC];
+        // D -= W2m' W2m, gamma -= W2m' w3m, and L = -W2m' W1m when needed
+#pragma unroll
+        for (int m = 0; m < NC; ++m) col[m] = (okm && rowi) ? -Wm[m * YW + NC + ii] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) row[c] = okm ? Wm[ii * YW + NC + c] : 0.0f;
+        gemm_rows<NP, NC, NC>(e, BcRow<NP, NC>(row), col);
+        dotb<NP, NC>(e[3 * NC], Bc<NP>(okm ? Wm[ii * YW + 2 * NC] : 0.0f), col);
+        if (__builtin_amdgcn_ballot_w64(needL) != 0) {
+            // the old L is not needed: a kept knot's L only matters at its elimination
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                row[c] = okm ? Wm[ii * YW + c] : 0.0f;
+                e[NC + c] = kept ? 0.0f : e[NC + c];
+            }
+            gemm_rows<NP, NC, NC>(e + NC, BcRow<NP, NC>(row), col);
+        }
+        // D -= W1p' W1p, U = -W1p' W2p, gamma -= W1p' w3p
+#pragma unroll
+        for (int m = 0; m < NC; ++m) col[m] = (okp && rowi) ? -Wp[m * YW + ii] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) row[c] = okp ? Wp[ii * YW + c] : 0.0f;
+        gemm_rows<NP, NC, NC>(e, BcRow<NP, NC>(row), col);
+        // the old U is not needed either (W1p already carries it)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            row[c] = okp ? Wp[ii * YW + NC + c] : 0.0f;
+            e[2 * NC + c] = kept ? 0.0f : e[2 * NC + c];
+        }
+        gemm_rows<NP, NC, NC>(e + 2 * NC, BcRow<NP, NC>(row), col);
+        dotb<NP, NC>(e[3 * NC], Bc<NP>(okp ? Wp[ii * YW + 2 * NC] : 0.0f), col);
+    };
+
+    // level 0, updates: every even knot, from odd knots k - 1 (group m - 1) and k + 1 (group m)
+    {
+        const bool kept = hasG;
+        if (__builtin_amdgcn_ballot_w64(kept) != 0) {
+            const bool hasL = ke > 0, hasU = ke + 1 < N;
+            const float* Wm = &sm.os[hasL ? me - 1 : 0][0][0];
+            const float* Wp = &sm.os[hasU ? me : 0][0][0];
+            update(kept, hasL, hasU, kept && lev == 1, Wm, Wp);
+        }
+    }
+    __syncthreads();
+
+    // levels 1 .. levels-1: the even knots of that level are eliminated, the rest updated
+    for (int l = 1; l < levels; ++l) {
+        const int s = 1 << l;
+        const int first = 1 + cr_mult(M, l);  // groups [first, 1 + c(l-1)) hold this level's knots
+        const bool elim = hasG && lev == l;
+        if (__builtin_amdgcn_ballot_w64(elim) != 0) {
+            chol_solve<NP, NC, KA>(e, i, bad, elim);  // other groups' rows stay as they are
+            if (elim && rowi) {
+#pragma unroll
+                for (int c = 0; c < YW; ++c) sm.es[g - first][i][c] = e[NC + c];
+            }
+        }
+        __syncthreads();
+        const bool kept = hasG && lev > l;
+        if (__builtin_amdgcn_ballot_w64(kept) != 0) {
+            const bool hasL = ke > 0, hasU = ke + s < N;
+            const int gm = hasL ? cr_even_group((ke - s) / 2, M) - first : 0;
+            const int gp = hasU ? cr_even_group((ke + s) / 2, M) - first : 0;
+            update(kept, hasL, hasU, kept && lev == l + 1 && lev < levels, &sm.es[gm][0][0], &sm.es[gp][0][0]);
+        }
+        __syncthreads();
+    }
+
+    // last level: knot 0 alone (group 0); lambda now lives in LDS
+    {
+        const bool last = g == 0;
+        if (__builtin_amdgcn_ballot_w64(last) != 0) {
+            float a[NC + 1];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) a[c] = e[c];
+            a[NC] = e[3 * NC];
+            chol_solve<NP, NC, NC + 1>(a, i, bad, last);
+            float dg = 1.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) dg = c == i ? a[c] : dg;
+            float lam = 0.0f;
+            tri_upper_solve<NP, NC>(a, a[NC], __builtin_amdgcn_rcpf(rowi ? dg : 1.0f), i, lam);
+            nonfinite |= last && rowi && !__builtin_isfinite(lam);
+            if (last && rowi) sm.lam[0][i] = lam;
+        }
+        __syncthreads();
+    }
+
+    // back substitution, levels in reverse: lambda_j = C_j'^-1 (w3 - W1 lambda_{j-s} - W2 lambda_{j+s})
+    auto back = [&](bool act, int k, int s, const float* ct, const float* w1, const float* w2, float w3) {
+        const bool hasU = k + s < N;
+        const float lm = (act && rowi) ? sm.lam[act ? k - s : 0][ii] : 0.0f;
+        const float lp = (act && rowi && hasU) ? sm.lam[hasU ? k + s : 0][ii] : 0.0f;
+        float acc = 0.0f;
+        dotb<NP, NC>(acc, Bc<NP>(lm), w1);
+        dotb<NP, NC>(acc, Bc<NP>(lp), w2);
+        float dg = 1.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dg = c == i ? ct[c] : dg;
+        float lam = 0.0f;
+        tri_upper_solve<NP, NC>(ct, w3 - acc, __builtin_amdgcn_rcpf((act && rowi) ? dg : 1.0f), i, lam);
+        nonfinite |= act && rowi && !__builtin_isfinite(lam);
+        if (act && rowi) sm.lam[k][i] = lam;
+    };
+    for (int l = levels - 1; l >= 1; --l) {
+        const bool act = hasG && lev == l;
+        if (__builtin_amdgcn_ballot_w64(act) != 0) back(act, ke, 1 << l, e, e + NC, e + 2 * NC, e[3 * NC]);
+        __syncthreads();
+    }
+    if (levels >= 1) {
+        if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
+            float w1[NC], w2[NC], oc[16];
+            ld4<16>(p.dws, ocrow, hasO && rowi, oc);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                w1[c] = sm.os[hasO ? g : 0][ii][c];
+                w2[c] = sm.os[hasO ? g : 0][ii][NC + c];
+            }
+            back(hasO, jo, 1, oc, w1, w2, sm.os[hasO ? g : 0][ii][2 * NC]);
+        }
+        __syncthreads();
+    }
+
+    // recovery of this group's knots, and lambda to memory
+#pragma unroll 1
+    for (int w = 0; w < 2; ++w) {
+        const bool ok = w == 0 ? hasG : hasO;
+        if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+        const int kk = ok ? (w == 0 ? ke : jo) : 0;
+        const bool rowv = ok && rowi;
+        const bool urow = ok && kk < N - 1 && i < MC;
+        float qi[NC], sup[NC], ri[MC], bc[NC];
+        ld_row<NC>(p.Qinv, ix.Q(b, kk, i), rowv, qi);
+        ld_row<NC>(p.S, ix.blk(b, kk, 2, i), rowv, sup);
+        ld_row<MC>(p.Rinv, ix.R(b, kk, i), urow, ri);
+        ld_row<NC, MC>(p.Bu, ix.Bu(b, kk, 0) + i, urow, bc);  // column i of B_k
+        const float qv = ld1(p.q, ix.vn(b, kk, i), rowv);
+        const float rv = ld1(p.r, ix.vm(b, kk, i), urow);
+        const float lam = rowv ? sm.lam[kk][ii] : 0.0f;
+        const float lamn = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
+        float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
+        dotb<NP, NC>(h, Bc<NP>(qv), qi);
+        float dx, du;
+        recover<SH>(i, rowv, urow, lam, lamn, qi, sup, h, bc, rv, ri, dx, du);
+        if (rowv) {
+            p.lambda[ix.vn(b, kk, i)] = lam;
+            p.dz[ix.dx(b, kk, i)] = dx;
+        }
+        if (urow) p.dz[ix.du(b, kk, i)] = du;
+    }
+
+    const int fl = (bad ? GATO_F_S_NOT_SPD : 0) | (nonfinite ? GATO_F_NONFINITE : 0);
+    if (fl) atomicOr(&sm.flags, fl);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        p.flags[b] |= sm.flags;
+        if (p.iters) p.iters[b] = 0;
+        if (p.relres) p.relres[b] = 0.0f;
+    }
+}
+
+}  // namespace gato

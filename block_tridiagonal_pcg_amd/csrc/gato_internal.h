@@ -1,0 +1,32 @@
+// gato_internal.h -- host-side interface between the library's translation
+// units: gato.hip (formation, PCG, block Thomas, merit, the C ABI) and
+// gato_cr.hip (block cyclic reduction).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "gato.h"
+
+// (n, m) of the shapes this build has kernels for: those of the configurations
+// the benchmark and tests use, plus n = m = 1 for hand-checkable examples.
+#define GATO_FOR_SHAPES(X) X(14, 7) X(12, 6) X(24, 12) X(4, 2) X(1, 1)
+
+namespace gato {
+
+struct Params;
+
+// Workspace of gato_cr_solve: one float4-padded row [L | U | gamma | D] per
+// knot row of every solve, 256-byte aligned size.
+size_t cr_ws_bytes(const gato_dims_t* d);
+
+// Launches the cyclic reduction for p (shape p.n x p.m, which must be one this
+// build has kernels for): the register-resident kernel where it applies, else
+// the streaming one.
+hipError_t cr_launch(const Params& p, hipStream_t st);
+
+// Whether gato_sqp_step takes cyclic reduction rather than block Thomas
+// beyond the fused horizons, by the measured cost model.
+bool cr_preferred(const gato_dims_t* d);
+
+}  // namespace gato
