@@ -11,8 +11,10 @@ memory when the timed region starts; the timed region is the K launches alone,
 and HIP events on the launch stream around it give the kernel's average time.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (N must be 1)
---config C --batch B --no-cpu-baseline --profile-copy (adds a 256 MiB device
-copy, the reference kernel for scaling rocprofv3 byte counters).
+--config C --batch B --horizon N (the configuration's generators at another
+horizon) --no-cpu-baseline --profile-copy (adds a 256 MiB device copy, the
+reference kernel for scaling rocprofv3 byte counters).  Study modes, each one
+JSON line instead of the step: --merit-variants, --sqp-driver, --solver-sweep.
 """
 import argparse
 import hashlib
@@ -40,6 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--batch", type=int, default=128)
+    ap.add_argument("--horizon", type=int, default=None, help="override the configuration's N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-copy", action="store_true")
@@ -47,6 +50,9 @@ def parse():
                     help="instead of the step: time the merit call's launch variants (one JSON line)")
     ap.add_argument("--sqp-driver", action="store_true",
                     help="instead of the step: time the multi-iteration SQP driver on the pendulum-chain plant")
+    ap.add_argument("--solver-sweep", action="store_true",
+                    help="instead of the step: time the block Thomas and cyclic-reduction solves over horizons "
+                         "and batch sizes (the measurements behind gato_sqp_step's switch)")
     return ap.parse_args()
 
 
@@ -83,6 +89,25 @@ def direct_flops(n, m, N):
     back substitution (two n x n products with a vector, 4 n^2); per dynamics step
     T = S_{k,k-1} H^-1 and T S_{k-1,k} (2 n^3 each) and the right-hand side update."""
     return N * (2 * n ** 3 + 4 * n * n + n) + (N - 1) * (4 * n ** 3 + 3 * n * n)
+
+
+def cr_flops(n, N):
+    """Block cyclic reduction per solve, level by level: each eliminated knot factors its
+    pivot block (n^3/3) and solves it against [L U gamma] (2n+1 columns of n^2); each kept
+    knot takes W2'W2 and W2'w3 from its left neighbour (2 n^3 + 2 n^2) and W1'W1, W1'W2,
+    W1'w3 from its right one (4 n^3 + 2 n^2); the back substitution costs two products with
+    a vector and a triangular solve (5 n^2) per eliminated knot; the last knot is factored
+    and solved alone (n^3/3 + 2 n^2)."""
+    f = 0.0
+    s = 1
+    while s < N:
+        for j in range(s, N, 2 * s):
+            f += n ** 3 / 3 + (2 * n + 1) * n * n + 5 * n * n
+            f += 2 * n ** 3 + 2 * n * n  # into the kept knot j - s
+            if j + s < N:
+                f += 4 * n ** 3 + 2 * n * n  # into the kept knot j + s
+        s *= 2
+    return f + n ** 3 / 3 + 2 * n * n
 
 
 def recover_flops(n, m, N):
@@ -292,6 +317,62 @@ def sqp_driver(a, iters=10, N=64, dof=7):
     print(json.dumps(rec))
 
 
+# ---------------------------------------------------------------- long-horizon solvers
+
+
+def solver_sweep(a):
+    """gato_direct_solve (block Thomas) and gato_cr_solve (block cyclic reduction) on
+    stage-1 outputs of the given configuration's generators, over horizons and batch
+    sizes; the batch is 64 generated solves tiled on the device (the solves' times do
+    not depend on their values).  Also reports gato_step_solver's choice."""
+    import torch
+
+    from block_tridiagonal_pcg_amd import ops, synth
+
+    torch.cuda.set_device(0)
+
+    def timeit(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    rows = []
+    for N in (65, 128, 256, 512, 1024):
+        base = synth.make_batch(a.config, 64, N=N)
+        dev0 = ops.to_device(base)
+        n, m = base["dims"][0], base["dims"][1]
+        for B in (64, 256, 512, 1024, 2048, 4096):
+            if B * N > 2 ** 21:
+                continue
+            dev = {k: v.repeat(B // 64, *([1] * (v.dim() - 1))).contiguous() for k, v in dev0.items() if k != "dims"}
+            dims = (n, m, N, B)
+            out = ops.alloc_outputs(dims)
+            ops.gato_form_schur(dims, *[dev[f] for f in synth.FIELDS], None, out["S"], out["Pinv"], out["gamma"],
+                                out["Qinv"], out["Rinv"], out["flags"])
+            args = (out["S"], out["gamma"], out["Qinv"], out["Rinv"], dev["Bu"], dev["q"], dev["r"], out["lam"],
+                    out["dz"], out["flags"])
+            wd, wc = ops.direct_workspace_for(dims), ops.cr_workspace_for(dims)
+            reps = 3 if B * N >= 2 ** 19 else 6
+            td = timeit(lambda: ops.gato_direct_solve(dims, *args, wd), reps)
+            tc = timeit(lambda: ops.gato_cr_solve(dims, *args, wc), reps)
+            choice = ops.gato_step_solver(dims)
+            rows.append({"N": N, "B": B, "thomas_us": round(td, 1), "cr_us": round(tc, 1),
+                         "faster": "cr" if tc < td else "thomas",
+                         "policy": {ops.SOLVER_CR: "cr", ops.SOLVER_THOMAS: "thomas"}.get(choice, "fused")})
+            print("N=%4d B=%5d thomas %9.1f us  cr %9.1f us  policy %s" % (N, B, td, tc, rows[-1]["policy"]),
+                  file=sys.stderr, flush=True)
+            del out, wd, wc, dev
+            torch.cuda.empty_cache()
+    print(json.dumps({"study": "long-horizon solvers", "workload": synth.CONFIGS[a.config].name,
+                      "unit": "us per call", "rows": rows}))
+
+
 # ---------------------------------------------------------------- main
 
 
@@ -315,9 +396,12 @@ def main():
     if a.sqp_driver:
         sqp_driver(a)
         return
+    if a.solver_sweep:
+        solver_sweep(a)
+        return
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[a.config]
-    batch = synth.make_batch(a.config, a.batch)
+    batch = synth.make_batch(a.config, a.batch, N=a.horizon)
     batch["cid"] = a.config
     n, m, N, B = batch["dims"]
     n_alpha = 8
@@ -366,15 +450,45 @@ def main():
         print("warning: solves flagged: %s" % np.unique(flags), file=sys.stderr)
 
     # algorithmic work of one launch (the whole batch)
-    fused = ops.gato_workspace_bytes(dims, n_alpha) == 0
+    solver = ops.gato_step_solver(dims)
+    fused = solver == ops.SOLVER_FUSED_PCG
+    solve_flops = B * (cr_flops(n, N) if solver == ops.SOLVER_CR else direct_flops(n, m, N))
     flops = B * (form_flops(n, m, N) + recover_flops(n, m, N) + merit_flops(n, m, N, n_alpha)) + \
-        (float(iters.sum()) * pcg_iter_flops(n, N) if fused else B * direct_flops(n, m, N))
-    achieved_tflops = flops / kern_avg_s / 1e12
-    workload = "%s, B=%d" % (cfg.name, B)
+        (float(iters.sum()) * pcg_iter_flops(n, N) if fused else solve_flops)
+    workload = "%s, B=%d" % (cfg.name, B) if a.horizon is None else "%s at N=%d, B=%d" % (cfg.name, N, B)
     traffic = measured_traffic(workload) if fused else None
 
     # per-stage device times with the three standalone calls (events on the same stream)
     stage_us = ops.stage_times(dims, dev, EPS, cap, alphas, MU, reps=max(3, min(20, a.steps // 10)))
+    if fused:
+        # one kernel: the timed launches are the dominant kernel
+        achieved_tflops = flops / kern_avg_s / 1e12
+        kernel, kernel_us = KERNEL, kern_avg_s * 1e6
+    else:
+        # form, direct solve and merit kernels: the roofline is the solve's, timed like the
+        # fused kernel (K back-to-back calls on the step's own stage-1 outputs, HIP events
+        # on the launch stream around them)
+        kernel = "k_cr_res / k_cr (block cyclic reduction)" if solver == ops.SOLVER_CR else \
+            "k_direct (block Thomas)"
+        sw = ops.cr_workspace_for(dims) if solver == ops.SOLVER_CR else ops.direct_workspace_for(dims)
+        solve = ops.gato_cr_solve if solver == ops.SOLVER_CR else ops.gato_direct_solve
+        st1 = ops.alloc_outputs(dims, n_alpha)
+        ops.gato_form_schur(dims, *[dev[f] for f in synth.FIELDS], None, st1["S"], st1["Pinv"], st1["gamma"],
+                            st1["Qinv"], st1["Rinv"], st1["flags"], stream=stream)
+        sargs = (st1["S"], st1["gamma"], st1["Qinv"], st1["Rinv"], dev["Bu"], dev["q"], dev["r"], st1["lam"],
+                 st1["dz"], st1["flags"])
+        for _ in range(3):
+            solve(dims, *sargs, sw, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            solve(dims, *sargs, sw, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kernel_us = e0.elapsed_time(e1) * 1e3 / a.steps
+        achieved_tflops = solve_flops / (kernel_us * 1e-6) / 1e12
+        del st1, sw
     pcg_bytes = float(iters.sum()) * pcg_iter_bytes(n, N)
     pcg_equiv_gbps = pcg_bytes / (stage_us["linsys_us"] * 1e-6) / 1e9 if fused and stage_us["linsys_us"] > 0 else None
 
@@ -394,17 +508,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "n": n, "m": m, "N": N, "B": B, "eps": EPS, "max_iters": cap,
                    "n_alpha": n_alpha, "mu": MU, "lambda0": "zero (cold start: a zeroed buffer per step)",
-                   "path": "fused single kernel" if fused else "form + direct block-tridiagonal solve + merit"},
+                   "path": "fused single kernel" if fused else "form + %s + merit" % (
+                       "block cyclic reduction" if solver == ops.SOLVER_CR else "block Thomas solve")},
         "roofline": {
             "bound": "alu",
-            "kernel": KERNEL if fused else "whole step (k_form, k_direct, k_merit)",
+            "kernel": kernel,
             "achieved": achieved_tflops,
             "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
             "traffic": traffic,
-            "flops_per_launch": flops,
-            "launch_avg_us": kern_avg_s * 1e6,
+            "flops_per_launch": flops if fused else solve_flops,
+            "launch_avg_us": kernel_us,
+            "step_launch_avg_us": kern_avg_s * 1e6,
         },
         "pcg_iters": {"min": int(iters.min()), "median": float(np.median(iters)), "max": int(iters.max())},
         "stage_us_unfused": stage_us,
