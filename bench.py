@@ -294,9 +294,23 @@ def sqp_driver(a, iters=10, N=64, dof=7):
     wall = time.perf_counter() - t0
     again = driver.solve(P, xi, xr, rho, N, iters, step_events=True)
     hist = again["history"]
+    # the same iterations with one iteration captured in a HIP graph and replayed
+    driver.solve(P, xi, xr, rho, N, 2, record=False, graph=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gres = driver.solve(P, xi, xr, rho, N, iters, record=False, graph=True)
+    torch.cuda.synchronize()
+    wall_graph = time.perf_counter() - t0
     rec = {"study": "SQP driver", "plant": "pendulum chain, %d DoF (n=%d, m=%d)" % (dof, P.n, P.m), "N": N, "B": B,
            "iterations": iters, "ms_per_iteration": wall / iters * 1e3,
            "solve_iterations_per_s": B * iters / wall,
+           "graph_ms_per_iteration": wall_graph / iters * 1e3,
+           "graph_solve_iterations_per_s": B * iters / wall_graph,
+           "graph_replay_ms_per_iteration": gres["replay_us"] / 1e3,
+           "graph_replay_solve_iterations_per_s": B / (gres["replay_us"] * 1e-6),
+           "graph_note": "first iteration eager, then one captured iteration replayed; graph_ms_per_iteration "
+                         "is the wall time including the eager iteration and the capture, graph_replay_* the "
+                         "replays alone (HIP events)",
            "defect_max_first": float(hist[0]["defect"].max()), "defect_max_last": float(hist[-1]["defect"].max()),
            "pcg_iters_per_iteration": [int(np.median(h["iters"])) for h in hist],
            "sqp_step_us_per_iteration": [round(x, 1) for x in again["step_us"]]}

@@ -59,13 +59,31 @@ def _cat(parts):
     return np.concatenate(parts, -1)
 
 
+_DEVICE_CONSTS = {}
+
+
 def _const(x, a):
-    """Constant array `a` (numpy) with x's dtype and device."""
+    """Constant array `a` (numpy) with x's dtype and device.  Device copies are made
+    once per (value, dtype, device) and reused, so that the plant's functions launch
+    no host-to-device copy after their first call (and can be captured in a graph)."""
     if _torch(x):
         import torch
 
-        return torch.as_tensor(a, dtype=x.dtype, device=x.device)
+        a = np.ascontiguousarray(a)
+        key = (a.tobytes(), a.shape, str(x.dtype), str(x.device))
+        t = _DEVICE_CONSTS.get(key)
+        if t is None:
+            t = torch.as_tensor(a, dtype=x.dtype, device=x.device)
+            _DEVICE_CONSTS[key] = t
+        return t
     return np.asarray(a, dtype=x.dtype)
+
+
+def _tile(x, small, shape):
+    """The constant `small` (numpy) repeated to `shape`, as a new array like x."""
+    if _torch(x):
+        return _const(x, small).expand(shape).contiguous()
+    return np.broadcast_to(np.asarray(small, dtype=x.dtype), shape).copy()
 
 
 def laplacian_matrix(d):
@@ -111,8 +129,8 @@ def cost_terms(P: Chain, X, U, x_ref):
     """Q_k = W, q_k = W (x_k - x_ref), R_k = Rw, r_k = Rw u_k for the tracking cost."""
     d, n = P.dof, P.n
     w = np.concatenate([np.full(d, P.w_theta), np.full(d, P.w_omega)])
-    Q = _const(X, np.broadcast_to(np.diag(w), tuple(X.shape[:-1]) + (n, n)).copy())
-    R = _const(X, np.broadcast_to(P.w_u * np.eye(d), tuple(U.shape[:-1]) + (d, d)).copy())
+    Q = _tile(X, np.diag(w), tuple(X.shape[:-1]) + (n, n))
+    R = _tile(X, P.w_u * np.eye(d), tuple(U.shape[:-1]) + (d, d))
     q = (X - x_ref[:, None, :]) * _const(X, w)
     r = P.w_u * U
     return Q, q, R, r

@@ -106,3 +106,33 @@ def test_device_driver_matches_reference(dof, N, B):
     assert np.linalg.norm(Xg - o["X"]) <= 1e-3 * np.linalg.norm(o["X"])
     assert np.linalg.norm(Ug - o["U"]) <= 1e-2 * max(np.linalg.norm(o["U"]), 1e-6)
     np.testing.assert_allclose(g["history"][-1]["cost"], o["history"][-1]["cost"], rtol=1e-4)
+
+
+@pytest.mark.gpu
+def test_driver_graph_replays_match_eager_iterations():
+    """The graph-replayed driver (one captured iteration, replayed) against the eager
+    loop: after every iteration (a synchronisation and host copies between replays)
+    the trajectory, damping and selected step agree."""
+    import torch
+
+    from block_tridiagonal_pcg_amd import driver, ops
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    ops.load()
+    print("case: driver graph replay", flush=True)
+    P = plant.Chain(7)
+    xi, xr, rho0 = plant.seed(P, 16)
+
+    def grab(store):
+        return lambda k, st: store.append({f: st[f].cpu().numpy().copy() for f in ("X", "U", "rho", "best")})
+
+    eager, graphed = [], []
+    driver.solve(P, xi, xr, rho0, 32, 6, record=False, on_iteration=grab(eager))
+    driver.solve(P, xi, xr, rho0, 32, 6, record=False, graph=True, on_iteration=grab(graphed))
+    assert len(eager) == len(graphed) == 6
+    for k, (a, b) in enumerate(zip(eager, graphed)):
+        np.testing.assert_array_equal(a["best"], b["best"], err_msg="iteration %d" % k)
+        np.testing.assert_allclose(b["rho"], a["rho"], rtol=1e-6, err_msg="iteration %d" % k)
+        for f in ("X", "U"):
+            np.testing.assert_allclose(b[f], a[f], rtol=1e-5, atol=1e-6, err_msg="%s, iteration %d" % (f, k))
