@@ -640,8 +640,8 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         __syncthreads();
     }
 
-    // recovery of this group's knots, and lambda to memory
-#pragma unroll 1
+    // recovery of this group's knots, and lambda to memory (both knots' loads issued together)
+#pragma unroll
     for (int w = 0; w < 2; ++w) {
         const bool ok = w == 0 ? hasG : hasO;
         if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;

@@ -77,7 +77,8 @@ def test_cr_horizons(N):
     assert rel_rows(g["dz"], dz).max() <= 5e-5
 
 
-@pytest.mark.parametrize("nm,N", [((1, 1), 9), ((4, 2), 33), ((12, 6), 100), ((24, 12), 9), ((24, 12), 70)])
+@pytest.mark.parametrize("nm,N", [((1, 1), 9), ((1, 1), 1000), ((4, 2), 33), ((4, 2), 300), ((12, 6), 100),
+                                  ((12, 6), 129), ((24, 12), 9), ((24, 12), 70), ((24, 12), 257), ((24, 12), 1024)])
 def test_cr_other_shapes(nm, N):
     n, m = nm
     _ident("cr shape", n, m, N)
@@ -152,6 +153,20 @@ def test_sqp_step_long_horizon_with_either_solver(solver, monkeypatch):
         monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
     _ident("sqp long horizon", solver)
     bt = synth.make_batch(3, 6, N=150)
+    g = gpu_sqp(bt, 1e-6, 200)
+    form = oracle.form_schur(*synth.inputs(bt))
+    _, dz = _exact(bt, form)
+    assert (g["iters"] == 0).all()
+    assert rel_rows(g["dz"], dz).max() <= 5e-5
+
+
+def test_sqp_step_long_horizon_wide_knots():
+    """n = 24 (32-lane groups) beyond its fused horizon of 16: the step's direct solve
+    against the oracle's exact step."""
+    from gpu_util import gpu_sqp
+
+    _ident("sqp long horizon n=24")
+    bt = synth.make_batch(4, 3, N=40)
     g = gpu_sqp(bt, 1e-6, 200)
     form = oracle.form_schur(*synth.inputs(bt))
     _, dz = _exact(bt, form)
