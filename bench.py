@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -139,10 +140,21 @@ FUSED_SOURCES = ("block_tridiagonal_pcg_amd/csrc/gato.hip", "block_tridiagonal_p
                  "block_tridiagonal_pcg_amd/csrc/gato_internal.h", "include/gato.h")
 
 
-def source_digest():
+def _code_only(text):
+    """C/C++ source without its comments and with whitespace collapsed: what the
+    compiler sees (the sources hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def source_digest(read=None):
+    """Digest of the fused kernel's sources, comments excluded (a comment cannot
+    change the kernel the counters were taken on)."""
+    read = read or (lambda f: open(os.path.join(ROOT, f)).read())
     h = hashlib.sha256()
     for f in FUSED_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        h.update(_code_only(read(f)).encode())
     return h.hexdigest()[:16]
 
 

@@ -431,6 +431,43 @@ __host__ __device__ constexpr int cr_group_even(int g, int M)
     return 0;
 }
 
+// Nested dissection for horizons beyond one workgroup's registers (n <= 16,
+// N > 128): the knots are cut into ND_CHUNKS contiguous chunks, one per lane
+// group; each chunk's interior knots are eliminated in order (k_nd_reduce),
+// which leaves a block-tridiagonal system on the chunks' first and last knots
+// (2 * ND_CHUNKS of them); that system is reduced cyclically by the
+// register-resident kernel in its "virtual" mode; the interior knots are then
+// back-substituted chunk by chunk (k_nd_back).  Workspace, in floats:
+//   [B][N][n][W]     factor rows [W1 | W2 | w3 | C'] of the interior knots
+//   [B][2C][n][W]    rows [L | U | gamma | D] of the boundary system
+//   [B][C][n][16]    C' rows of the boundary system's odd knots
+// (C = ND_CHUNKS, W = CrRow<SH>::W).
+constexpr int ND_CHUNKS = 64;
+
+__host__ __device__ constexpr int nd_start(int j, int N) { return (int)(((long long)j * N) / ND_CHUNKS); }
+
+// Real knot of boundary-system knot v: chunk v/2's first (v even) or last (v odd) knot.
+__host__ __device__ constexpr int nd_real(int v, int N)
+{
+    return (v & 1) ? nd_start(v / 2 + 1, N) - 1 : nd_start(v / 2, N);
+}
+
+template <class SH>
+struct NdWs {
+    static constexpr int NC = SH::NC, W = CrRow<SH>::W;
+    size_t B, N;
+    __host__ __device__ size_t fac(size_t b, size_t k, size_t i) const { return ((b * N + k) * NC + i) * W; }
+    __host__ __device__ size_t vrow(size_t b, size_t v, size_t i) const
+    {
+        return B * N * NC * W + ((b * 2 * ND_CHUNKS + v) * NC + i) * W;
+    }
+    __host__ __device__ size_t oc(size_t b, size_t g, size_t i) const
+    {
+        return B * (N + 2 * ND_CHUNKS) * NC * W + ((b * ND_CHUNKS + g) * NC + i) * 16;
+    }
+    __host__ __device__ size_t floats() const { return B * (N + 2 * ND_CHUNKS) * NC * W + B * ND_CHUNKS * NC * 16; }
+};
+
 template <class SH>
 struct CrResLds {
     static constexpr int NC = SH::NC, YW = 2 * NC + 1;
@@ -443,7 +480,10 @@ struct CrResLds {
     int flags;
 };
 
-template <class SH>
+// VIRT: solve the boundary system of the nested dissection (2 * ND_CHUNKS knots,
+// rows from the workspace) and write its lambda at the real knots, instead of
+// solving S itself and recovering dz.
+template <class SH, bool VIRT = false>
 __device__ __forceinline__ void cr_resident(const Params& p, int b)
 {
     constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
@@ -451,9 +491,12 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     using LDS = CrResLds<SH>;
     constexpr int YW = LDS::YW;
     constexpr int KA = 3 * NC + 1;  // [D | L | U | gamma]
+    constexpr int W = CrRow<SH>::W;
+    using RW = CrRow<SH>;
     __shared__ LDS sm;
     const Ix<SH> ix{p.N};
-    const int N = p.N;
+    const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
+    const int N = VIRT ? 2 * ND_CHUNKS : p.N;
     const int M = (N + 1) / 2;  // even knots, one per lane group
     const int i = threadIdx.x % NP;
     const int g = threadIdx.x / NP;
@@ -474,15 +517,27 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     // level 0, eliminations: the odd knots; their W rows go to LDS, and their C'
     // rows, needed only by the last back-substitution step, to the workspace
     // (16 floats per row, M knots per solve)
-    const size_t ocrow = (((size_t)b * M + (hasO ? g : 0)) * NC + ii) * 16;
+    const size_t ocrow = VIRT ? nw.oc(b, hasO ? g : 0, ii) : (((size_t)b * M + (hasO ? g : 0)) * NC + ii) * 16;
     {
         const bool ld = hasO && rowi;
         const int jj = hasO ? jo : 0;
         float a[KA];
-        ld_row<NC>(p.S, ix.blk(b, jj, 1, i), ld, a);
-        ld_row<NC>(p.S, ix.blk(b, jj, 0, i), ld, a + NC);
-        ld_row<NC>(p.S, ix.blk(b, jj, 2, i), ld && jo + 1 < N, a + 2 * NC);
-        a[3 * NC] = ld1(p.gamma, ix.vn(b, jj, i), ld);
+        if constexpr (VIRT) {
+            float r[W];
+            ld4<W>(p.dws, nw.vrow(b, jj, ii), ld, r);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                a[c] = r[RW::D + c];
+                a[NC + c] = r[RW::L + c];
+                a[2 * NC + c] = jo + 1 < N ? r[RW::U + c] : 0.0f;
+            }
+            a[3 * NC] = r[RW::G];
+        } else {
+            ld_row<NC>(p.S, ix.blk(b, jj, 1, i), ld, a);
+            ld_row<NC>(p.S, ix.blk(b, jj, 0, i), ld, a + NC);
+            ld_row<NC>(p.S, ix.blk(b, jj, 2, i), ld && jo + 1 < N, a + 2 * NC);
+            a[3 * NC] = ld1(p.gamma, ix.vn(b, jj, i), ld);
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) a[c] = hasO ? a[c] : (c == i ? 1.0f : 0.0f);
         if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
@@ -502,11 +557,22 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     float e[KA];
     {
         const bool ld = hasG && rowi;
-        ld_row<NC>(p.S, ix.blk(b, ke, 1, i), ld, e);
-        ld_row<NC>(p.S, ix.blk(b, ke, 2, i), ld && ke + 1 < N, e + 2 * NC);
+        if constexpr (VIRT) {
+            float r[W];
+            ld4<W>(p.dws, nw.vrow(b, ke, ii), ld, r);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                e[c] = r[RW::D + c];
+                e[2 * NC + c] = ke + 1 < N ? r[RW::U + c] : 0.0f;
+            }
+            e[3 * NC] = r[RW::G];
+        } else {
+            ld_row<NC>(p.S, ix.blk(b, ke, 1, i), ld, e);
+            ld_row<NC>(p.S, ix.blk(b, ke, 2, i), ld && ke + 1 < N, e + 2 * NC);
+            e[3 * NC] = ld1(p.gamma, ix.vn(b, ke, i), ld);
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) e[NC + c] = 0.0f;
-        e[3 * NC] = ld1(p.gamma, ix.vn(b, ke, i), ld);
     }
     __syncthreads();
 
@@ -640,9 +706,18 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         __syncthreads();
     }
 
+    if constexpr (VIRT) {
+        // lambda of the boundary knots, at their real positions
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const bool ok = w == 0 ? hasG : hasO;
+            const int v = w == 0 ? ke : jo;
+            if (ok && rowi) p.lambda[ix.vn(b, nd_real(v, p.N), i)] = sm.lam[v][i];
+        }
+    }
     // recovery of this group's knots, and lambda to memory (both knots' loads issued together)
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < (VIRT ? 0 : 2); ++w) {
         const bool ok = w == 0 ? hasG : hasO;
         if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
         const int kk = ok ? (w == 0 ? ke : jo) : 0;
@@ -676,6 +751,235 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         if (p.iters) p.iters[b] = 0;
         if (p.relres) p.relres[b] = 0.0f;
     }
+}
+
+// ------------------------------------------------------------------ nested dissection, chunk interiors
+
+template <class SH>
+struct NdLds {
+    float t[ND_CHUNKS][SH::NC][SH::NC + 1];  // one transpose tile per lane group (+1: bank spread)
+    int flags;
+};
+
+// Eliminates every chunk's interior knots in order (lane group g: chunk g).
+// The chunk's first knot a stays in registers and collects the Schur
+// complement of the knots eliminated so far, together with its coupling F to
+// the current front knot f; eliminating f (D_f = C C', W1 = C^-1 F', W2 =
+// C^-1 U_f, w3 = C^-1 gamma_f) updates
+//   D_a -= W1'W1, gamma_a -= W1'w3, F <- -W1'W2 (now the coupling a <-> f+1),
+//   D_{f+1} -= W2'W2, gamma_{f+1} -= W2'w3.
+// Each front's factor row goes to the workspace for the back substitution.
+// Afterwards the chunk's first and last knots, with F between them and S's own
+// coupling to the next chunk, are rows of the boundary system.  Transposes go
+// through the group's own LDS tile (no barrier: the tile belongs to one wave).
+template <class SH>
+__device__ __forceinline__ void nd_reduce(const Params& p, int b)
+{
+    constexpr int NP = SH::NP, NC = SH::NC;
+    static_assert(NP == 16, "one knot row per lane of a 16-lane group");
+    constexpr int KA = 3 * NC + 1;
+    using RW = CrRow<SH>;
+    constexpr int W = RW::W;
+    __shared__ NdLds<SH> sm;
+    const Ix<SH> ix{p.N};
+    const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
+    const int N = p.N;
+    const int i = threadIdx.x % NP;
+    const int g = threadIdx.x / NP;  // chunk
+    const bool rowi = i < NC;
+    const int ii = rowi ? i : 0;
+    const int a = nd_start(g, N), bk = nd_start(g + 1, N) - 1;
+    const int nint = bk - a - 1;  // interior knots (chunks hold >= 2 knots)
+    const int maxint = (N + ND_CHUNKS - 1) / ND_CHUNKS - 2;
+    float(*t)[NC + 1] = sm.t[g];
+    if (threadIdx.x == 0) sm.flags = 0;
+    bool bad = false;
+
+    auto transpose = [&](const float* x, float* out) {  // out[c] = X[c][i], X's row i in lane i
+        if (rowi) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) t[i][c] = x[c];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) out[c] = t[c][ii];
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    float Da[NC], F[NC], Dn[NC];
+    ld_row<NC>(p.S, ix.blk(b, a, 1, i), rowi, Da);
+    ld_row<NC>(p.S, ix.blk(b, a, 2, i), rowi, F);  // coupling a <-> a+1
+    ld_row<NC>(p.S, ix.blk(b, a + 1, 1, i), rowi, Dn);
+    float ga = ld1(p.gamma, ix.vn(b, a, i), rowi);
+    float gn = ld1(p.gamma, ix.vn(b, a + 1, i), rowi);
+
+    // One elimination step on front f; groups with act false (their chunk has
+    // one interior knot fewer) run it with zero multipliers and keep their state.
+    auto step = [&](int f, bool act) {
+        float x[KA];  // [D_f | F' | U_f | gamma_f]
+        ld_row<NC>(p.S, ix.blk(b, f, 2, i), act && rowi, x + 2 * NC);  // coupling f <-> f+1
+        transpose(F, x + NC);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) x[c] = Dn[c];
+        x[3 * NC] = gn;
+        chol_solve<NP, NC, KA>(x, i, bad, act);
+        if (act && rowi) {
+            float r[W];
+#pragma unroll
+            for (int c = 0; c < W; ++c) r[c] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                r[RW::L + c] = x[NC + c];
+                r[RW::U + c] = x[2 * NC + c];
+                r[RW::D + c] = x[c];
+            }
+            r[RW::G] = x[3 * NC];
+            st4<W>(p.dws, nw.fac(b, f, i), r);
+        }
+        float c[NC];  // -(column i of W1), then -(column i of W2)
+        transpose(x + NC, c);
+#pragma unroll
+        for (int k = 0; k < NC; ++k) c[k] = (act && rowi) ? -c[k] : 0.0f;
+        // the chunk's first knot; the old F is no longer needed (W1 carries it)
+        gemm_rows<NP, NC, NC>(Da, BcRow<NP, NC>(x + NC), c);
+        dotb<NP, NC>(ga, Bc<NP>(x[3 * NC]), c);
+#pragma unroll
+        for (int k = 0; k < NC; ++k) F[k] = act ? 0.0f : F[k];
+        gemm_rows<NP, NC, NC>(F, BcRow<NP, NC>(x + 2 * NC), c);
+        // the next front (groups that are done keep their last knot's rows)
+        transpose(x + 2 * NC, c);
+        {
+            float Dx[NC];
+            ld_row<NC>(p.S, ix.blk(b, f + 1, 1, i), act && rowi, Dx);
+            const float gx = ld1(p.gamma, ix.vn(b, f + 1, i), act && rowi);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                c[k] = (act && rowi) ? -c[k] : 0.0f;
+                Dn[k] = act ? Dx[k] : Dn[k];
+            }
+            gn = act ? gx : gn;
+        }
+        gemm_rows<NP, NC, NC>(Dn, BcRow<NP, NC>(x + 2 * NC), c);
+        dotb<NP, NC>(gn, Bc<NP>(x[3 * NC]), c);
+    };
+
+    // the steps every chunk has, then the one that the longer chunks have in addition
+    const int minint = N / ND_CHUNKS - 2;
+    for (int st = 0; st < minint; ++st) step(a + 1 + st, true);
+    if (maxint > minint) {
+        const bool act = nint > minint;
+        step(act ? a + 1 + minint : a + 1, act);
+    }
+
+    // rows of the boundary system: knot 2g (= a): [- | F | gamma_a | D_a];
+    // knot 2g+1 (= bk): [F' | S_{bk,bk+1} | gamma_bk | D_bk]
+    float Lb[NC], Ub[NC];
+    transpose(F, Lb);
+    ld_row<NC>(p.S, ix.blk(b, bk, 2, i), rowi && bk + 1 < N, Ub);
+    if (rowi) {
+        float r[W];
+#pragma unroll
+        for (int c = 0; c < W; ++c) r[c] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            r[RW::U + c] = F[c];
+            r[RW::D + c] = Da[c];
+        }
+        r[RW::G] = ga;
+        st4<W>(p.dws, nw.vrow(b, 2 * g, i), r);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            r[RW::L + c] = Lb[c];
+            r[RW::U + c] = Ub[c];
+            r[RW::D + c] = Dn[c];
+        }
+        r[RW::G] = gn;
+        st4<W>(p.dws, nw.vrow(b, 2 * g + 1, i), r);
+    }
+    if (bad) atomicOr(&sm.flags, GATO_F_S_NOT_SPD);
+    __syncthreads();
+    if (threadIdx.x == 0) p.flags[b] |= sm.flags;
+}
+
+// Back substitution of every chunk's interior knots (the chunk's first and last
+// knots have lambda from the boundary system), last interior knot first:
+//   lambda_f = C_f'^-1 (w3_f - W1_f lambda_a - W2_f lambda_{f+1}),
+// then the recovery of dz for every knot, spread over the lane groups.
+template <class SH>
+__device__ __forceinline__ void nd_back(const Params& p, int b)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    using RW = CrRow<SH>;
+    constexpr int W = RW::W;
+    __shared__ int wg_flags;
+    const Ix<SH> ix{p.N};
+    const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
+    const int N = p.N;
+    const int i = threadIdx.x % NP;
+    const int g = threadIdx.x / NP;
+    const bool rowi = i < NC;
+    const int a = nd_start(g, N), bk = nd_start(g + 1, N) - 1;
+    const int maxsz = (N + ND_CHUNKS - 1) / ND_CHUNKS;
+    if (threadIdx.x == 0) wg_flags = 0;
+    bool nonfinite = false;
+
+    // interior lambdas, last interior knot first, the next factor row requested
+    // before this one's arithmetic
+    const float la = ld1(p.lambda, ix.vn(b, a, i), rowi);
+    float lamn = ld1(p.lambda, ix.vn(b, bk, i), rowi);  // lambda of the knot after the front
+    const int maxint = maxsz - 2;
+    float cur[W];
+    ld4<W>(p.dws, nw.fac(b, bk - 1 > a ? bk - 1 : a, i), rowi && bk - 1 > a, cur);
+    for (int st = 0; st < maxint; ++st) {
+        const int k = bk - 1 - st;
+        const bool act = k > a;
+        if (__builtin_amdgcn_ballot_w64(act) == 0) continue;
+        float nxt[W];
+        ld4<W>(p.dws, nw.fac(b, k - 1 > a ? k - 1 : a, i), rowi && k - 1 > a, nxt);
+        float acc = 0.0f;
+        dotb<NP, NC>(acc, Bc<NP>(la), cur + RW::L);
+        dotb<NP, NC>(acc, Bc<NP>(lamn), cur + RW::U);
+        float dg = 1.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dg = c == i ? cur[RW::D + c] : dg;
+        float lin = 0.0f;
+        tri_upper_solve<NP, NC>(cur + RW::D, cur[RW::G] - acc, __builtin_amdgcn_rcpf((act && rowi) ? dg : 1.0f), i,
+                                lin);
+        nonfinite |= act && rowi && !__builtin_isfinite(lin);
+        if (act && rowi) p.lambda[ix.vn(b, k, i)] = lin;
+        lamn = act ? lin : lamn;
+#pragma unroll
+        for (int c = 0; c < W; ++c) cur[c] = nxt[c];
+    }
+    __syncthreads();  // every lambda of the solve is written
+
+    // recovery of every knot's dz, knots spread over the lane groups
+    for (int t0 = 0; t0 < N; t0 += ND_CHUNKS) {
+        const int k = t0 + g;
+        const bool ok = k < N;
+        if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+        const int kk = ok ? k : 0;
+        const bool rowv = ok && rowi;
+        const bool urow = ok && kk < N - 1 && i < MC;
+        float qi[NC], sup[NC], ri[MC], bc[NC];
+        ld_row<NC>(p.Qinv, ix.Q(b, kk, i), rowv, qi);
+        ld_row<NC>(p.S, ix.blk(b, kk, 2, i), rowv, sup);
+        ld_row<MC>(p.Rinv, ix.R(b, kk, i), urow, ri);
+        ld_row<NC, MC>(p.Bu, ix.Bu(b, kk, 0) + i, urow, bc);  // column i of B_k
+        const float qv = ld1(p.q, ix.vn(b, kk, i), rowv);
+        const float rv = ld1(p.r, ix.vm(b, kk, i), urow);
+        const float lam = ld1(p.lambda, ix.vn(b, kk, i), rowv);
+        const float lamk = ld1(p.lambda, ix.vn(b, kk + 1 < N ? kk + 1 : kk, i), rowv && kk + 1 < N);
+        float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
+        dotb<NP, NC>(h, Bc<NP>(qv), qi);
+        float dx, du;
+        recover<SH>(i, rowv, urow, lam, lamk, qi, sup, h, bc, rv, ri, dx, du);
+        if (rowv) p.dz[ix.dx(b, kk, i)] = dx;
+        if (urow) p.dz[ix.du(b, kk, i)] = du;
+    }
+    if (nonfinite) atomicOr(&wg_flags, GATO_F_NONFINITE);
+    __syncthreads();
+    if (threadIdx.x == 0) p.flags[b] |= wg_flags;
 }
 
 }  // namespace gato

@@ -2,11 +2,16 @@
 // long-horizon solve of gato_sqp_step while its log-depth pays).
 //
 // Kernels (one workgroup per solve):
-//   k_cr_res  every knot of the solve held in registers and LDS (n <= 16, N <= 128).
-//   k_cr      any horizon, the reduced rows kept in the workspace.
+//   k_cr_res     every knot of the solve held in registers and LDS (n <= 16, N <= 128).
+//   k_nd_reduce, k_cr_res<VIRT>, k_nd_back
+//                nested dissection for n <= 16, N > 128: chunk interiors eliminated
+//                in order, the chunks' boundary system reduced cyclically, then
+//                the interiors back-substituted.
+//   k_cr         any horizon and shape, the reduced rows kept in the workspace.
 #include "gato_internal.h"
 #include "gato_cr.h"
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -48,6 +53,25 @@ __global__ __launch_bounds__(1024) void k_cr_res(Params p)
     cr_resident<SH>(p, blockIdx.x);
 }
 
+// Nested dissection (n <= 16, N > 128): three launches of 64 lane groups.
+template <class SH>
+__global__ __launch_bounds__(1024) void k_nd_reduce(Params p)
+{
+    nd_reduce<SH>(p, blockIdx.x);
+}
+
+template <class SH>
+__global__ __launch_bounds__(1024) void k_cr_res_virt(Params p)
+{
+    cr_resident<SH, true>(p, blockIdx.x);
+}
+
+template <class SH>
+__global__ __launch_bounds__(1024) void k_nd_back(Params p)
+{
+    nd_back<SH>(p, blockIdx.x);
+}
+
 static bool cr_streaming_forced()  // GATO_CR_VARIANT=stream: the streaming kernel for every N (measurements)
 {
     const char* env = std::getenv("GATO_CR_VARIANT");
@@ -68,6 +92,14 @@ static hipError_t cr_launch_shape(const Params& p, hipStream_t st)
         if (cr_resident<SH>(p.N)) {
             const int groups = (p.N + 1) / 2;
             hipLaunchKernelGGL((k_cr_res<SH>), dim3(p.B), dim3(((groups + SH::KPW - 1) / SH::KPW) * 64), 0, st, p);
+            return hipGetLastError();
+        }
+        if (!cr_streaming_forced()) {  // N > 128: nested dissection
+            static_assert(2 * ND_CHUNKS == 2 * CrResLds<SH>::MAXG, "boundary system = one resident workgroup");
+            const dim3 blk(ND_CHUNKS * SH::NP);
+            hipLaunchKernelGGL((k_nd_reduce<SH>), dim3(p.B), blk, 0, st, p);
+            hipLaunchKernelGGL((k_cr_res_virt<SH>), dim3(p.B), blk, 0, st, p);
+            hipLaunchKernelGGL((k_nd_back<SH>), dim3(p.B), blk, 0, st, p);
             return hipGetLastError();
         }
     }
@@ -102,29 +134,33 @@ static size_t cr_row_floats(int n) { return (size_t)(3 * n + 1 + 3) / 4 * 4; }
 
 size_t cr_ws_bytes(const gato_dims_t* d)
 {
-    const size_t B = d->B, N = d->N, n = d->n;
-    return align256(B * N * n * cr_row_floats(d->n) * sizeof(float));
+    // the largest of the three layouts: the streaming kernel's rows (B N n W), the
+    // resident kernel's parked rows (B ceil(N/2) n 16) and the nested dissection's
+    // (interior factor rows, the boundary system's rows and its parked rows)
+    const size_t B = d->B, N = d->N, n = d->n, W = cr_row_floats(d->n);
+    return align256((B * (N + 2 * ND_CHUNKS) * n * W + B * ND_CHUNKS * n * 16) * sizeof(float));
 }
 
 // The long-horizon solve of gato_sqp_step, chosen by a cost model measured on
 // MI355X (knots n = 14): block Thomas walks the knots in order, about 3.0 us
 // per knot whatever the batch until its one lane group per solve fills the
 // chip (about 1.6 ns per knot and solve beyond); cyclic reduction is
-// log-depth but does twice the arithmetic, about 0.35 us per solve with the
-// register-resident kernel (N <= 128, n <= 16) and 4.3 ns per knot and solve
-// with the streaming one once the batch fills the chip.  Cyclic reduction is
-// taken while its batch time stays below the Thomas walk's latency.
-// GATO_LONG_SOLVE=thomas or =cr forces either (for measurements).
+// log-depth but does more arithmetic: about 0.35 us per solve with the
+// register-resident kernel (N <= 128, n <= 16), 2.7 ns per knot and solve with
+// the nested dissection (N > 128, n <= 16) and 4.3 ns with the streaming
+// kernel (n > 16), once its batch fills the chip.  Cyclic reduction is taken
+// while its batch time stays below block Thomas's.  GATO_LONG_SOLVE=thomas or
+// =cr forces either (for measurements).
 bool cr_preferred(const gato_dims_t* d)
 {
-    const bool resident = with_cr_shape(d->n, d->m, [&](auto sh) { return cr_resident<decltype(sh)>(d->N) ? 1 : 0; }) == 1;
     if (const char* env = std::getenv("GATO_LONG_SOLVE")) {
         if (std::strcmp(env, "thomas") == 0) return false;
         if (std::strcmp(env, "cr") == 0) return true;
     }
-    const double thomas_us = 3.0 * d->N;
-    const double cr_us = d->B * (resident ? 0.35 : 0.0043 * d->N);
-    return cr_us < thomas_us;
+    const bool narrow = d->n <= 16 && !cr_streaming_forced();
+    const double per_solve_us = narrow ? (d->N <= 2 * ND_CHUNKS ? 0.35 : 0.0027 * d->N) : 0.0043 * d->N;
+    const double thomas_us = std::max(3.0 * d->N, 0.0016 * d->N * d->B);
+    return d->B * per_solve_us < thomas_us;
 }
 
 }  // namespace gato

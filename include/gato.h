@@ -192,21 +192,28 @@ int gato_direct_solve(const gato_dims_t* dims, const float* S, const float* gamm
  * Knot 0 is left alone after ceil(log2 N) levels and solved directly; the
  * back substitution lambda_j = y3_j - Y1_j lambda_{j-s} - Y2_j lambda_{j+s}
  * runs the levels in reverse.  Then dz is recovered exactly as gato_pcg_solve
- * does.  Arguments as in gato_direct_solve; the reduced rows and the Y blocks
- * go through the caller's workspace, of at least gato_cr_workspace_bytes(dims)
- * bytes, 256-byte aligned.  Pivot blocks are inverted by Gauss-Jordan without
- * pivoting (each is a diagonal block of a Schur complement of an SPD S); a
- * pivot that is not positive ORs S_NOT_SPD into flags, a non-finite lambda
- * NONFINITE.  The eliminations of one level run in parallel, so a solve's
- * depth grows with log2 N rather than N.
+ * does.  Each elimination is a Cholesky factorisation of the pivot block with
+ * a lower solve of its couplings, D_j = C C', W = C^-1 [L U gamma], followed by
+ * the Schur update of the neighbours (the block Cholesky factorisation of S
+ * with its knots reordered), so every pivot block is SPD when S is; a pivot
+ * that is not positive ORs S_NOT_SPD into flags, a non-finite lambda NONFINITE.
+ * For n <= 16 and N > 128 the order is a nested dissection: the horizon is cut
+ * into 64 chunks whose interior knots are eliminated first, in order (each
+ * chunk in parallel), and the 128 chunk-boundary knots are then reduced
+ * cyclically as above.  Arguments as in gato_direct_solve; the reduced rows
+ * and factors go through the caller's workspace, of at least
+ * gato_cr_workspace_bytes(dims) bytes, 256-byte aligned.  The eliminations of
+ * one level (or chunk step) run in parallel, so a solve's depth grows with
+ * log2 N (plus N/64 chunk steps) rather than N.
  */
 size_t gato_cr_workspace_bytes(const gato_dims_t* dims);
 int gato_cr_solve(const gato_dims_t* dims, const float* S, const float* gamma, const float* Qinv,
                   const float* Rinv, const float* Bu, const float* q, const float* r, float* lambda, float* dz,
                   int32_t* flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Number of levels gato_cr_solve runs for a horizon of N knots:
- * ceil(log2 N) reduction levels plus the final single-knot solve (0 for N < 1). */
+/* Number of levels of the cyclic-frames plan for a chain of N knots: ceil(log2 N)
+ * reduction levels plus the final single-knot solve (0 for N < 1); gato_cr_solve
+ * runs exactly these levels for N <= 128 (n <= 16) or any N (n > 16). */
 int32_t gato_cr_levels(int32_t N);
 
 /*
@@ -238,9 +245,10 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *    workspace is used;
  *  - otherwise stage 2 is a direct solve: gato_cr_solve's block cyclic
  *    reduction while the batch is small enough for its log-depth to pay
- *    (B * 0.35 us < 3 N us for n <= 16 and N <= 128, B < 700 beyond; measured
- *    switch points), else gato_direct_solve's block Thomas elimination (the
- *    environment variable GATO_LONG_SOLVE=thomas or =cr forces either).
+ *    (measured switch points: B * 0.35 us < 3 N us for n <= 16 and N <= 128,
+ *    B < ~1100 for n <= 16 beyond, B < ~700 for n > 16), else
+ *    gato_direct_solve's block Thomas elimination (the environment variable
+ *    GATO_LONG_SOLVE=thomas or =cr forces either).
  *    lambda's input is not read, iters and relres are written as 0, and eps
  *    and max_iters are checked but unused.  S, Pinv,
  *    gamma, Qinv, Rinv and the solve's rows go through `workspace`

@@ -109,7 +109,9 @@ def test_validation_happens_before_any_launch(lib):
     # cyclic reduction: the same host checks
     cr = lib.gato_cr_solve
     need = lib.gato_cr_workspace_bytes(ctypes.byref(d))
-    assert need == ((2 * 64 * 14 * 44 * 4 + 255) // 256) * 256  # B=2 N=64 n=14: [L|U|gamma|D] rows of 44 floats
+    # B=2 N=64 n=14: rows of 44 floats for the N knots and the 128 boundary knots of the
+    # nested dissection, plus that system's parked rows of 16 floats (64 per solve)
+    assert need == ((2 * ((64 + 128) * 14 * 44 + 64 * 14 * 16) * 4 + 255) // 256) * 256
     assert cr(ctypes.byref(d), *P[:10], None, ctypes.c_size_t(need), None) == ops.E_WORKSPACE
     assert cr(ctypes.byref(d), *P[:10], ws, ctypes.c_size_t(need - 1), None) == ops.E_WORKSPACE
     assert cr(ctypes.byref(d), *P[:10], ctypes.c_void_p((1 << 20) + 4), ctypes.c_size_t(need), None) == ops.E_ALIGN
@@ -165,8 +167,9 @@ def test_cyclic_reduction_depth_matches_the_plan(lib):
 
 def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
     """Fused PCG where a workgroup holds the horizon; beyond, cyclic reduction while
-    its batch time (0.35 us per solve resident, 4.3 ns per knot and solve streaming)
-    stays below the block Thomas walk's 3 us per knot, else block Thomas."""
+    its batch time (0.35 us per solve resident, 2.7 ns per knot and solve with the
+    nested dissection, 4.3 ns streaming for n > 16) stays below block Thomas's
+    (3 us per knot, or 1.6 ns per knot and solve once the batch fills the chip)."""
     from block_tridiagonal_pcg_amd import ops
 
     monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
@@ -174,8 +177,8 @@ def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
     F, T, C = ops.SOLVER_FUSED_PCG, ops.SOLVER_THOMAS, ops.SOLVER_CR
     cases = {(14, 7, 64, 128): F, (24, 12, 16, 4): F, (14, 7, 65, 512): C, (14, 7, 65, 1024): T,
              (14, 7, 128, 512): C, (14, 7, 128, 1024): C, (14, 7, 128, 2048): T,
-             (14, 7, 256, 512): C, (14, 7, 256, 1024): T, (14, 7, 1024, 64): C, (14, 7, 1024, 1024): T,
-             (24, 12, 100, 8): C}
+             (14, 7, 256, 512): C, (14, 7, 256, 1024): C, (14, 7, 256, 2048): T, (14, 7, 1024, 64): C,
+             (14, 7, 1024, 1024): C, (14, 7, 1024, 2048): T, (24, 12, 100, 8): C, (24, 12, 100, 1024): T}
     for dims, want in cases.items():
         assert ops.gato_step_solver(dims) == want, dims
     monkeypatch.setenv("GATO_LONG_SOLVE", "thomas")

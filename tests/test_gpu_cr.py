@@ -123,11 +123,13 @@ def test_cr_agrees_with_block_thomas():
     assert rel_rows(c["dz"], t["dz"]).max() <= 1e-4
 
 
-@pytest.mark.parametrize("N", [2, 3, 17, 64, 100, 127, 128])
+@pytest.mark.parametrize("N", [2, 3, 17, 64, 100, 127, 128, 129, 191, 300, 1024])
 def test_cr_resident_and_streaming_kernels_agree(N, monkeypatch):
     """Up to 128 knots (n <= 16) the solve runs with every knot held in registers
-    and LDS; GATO_CR_VARIANT=stream selects the kernel that keeps the reduced
-    rows in the workspace.  Both are held to the oracle, and to each other."""
+    and LDS, beyond that as a nested dissection (chunk interiors, then the
+    boundary system in registers); GATO_CR_VARIANT=stream selects the kernel that
+    keeps the reduced rows in the workspace.  Both are held to the oracle, and to
+    each other."""
     _ident("cr variants", N)
     bt = synth.make_batch(2, 3, N=N)
     form = oracle.form_schur(*synth.inputs(bt))
