@@ -119,6 +119,32 @@ __device__ __forceinline__ void tri_upper_solve(const float* ct, float v, float 
     }
 }
 
+// The recovery of knot k's dz (recover(), the back substitution of the Schur
+// solve) from lambda_k and lambda_{k+1} in lane i's row, with the knot's rows of
+// Q~^-1, S_{k,k+1}, R^-1 and r, q and column i of B_k read here; ok false masks
+// the loads and the stores (k must still be a knot of the horizon).
+template <class SH>
+__device__ __forceinline__ void recover_knot(const Params& p, int b, int k, int i, bool ok, float lam, float lamn)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    const Ix<SH> ix{p.N};
+    const bool rowv = ok && i < NC;
+    const bool urow = ok && k < p.N - 1 && i < MC;
+    float qi[NC], sup[NC], ri[MC], bc[NC];
+    ld_row<NC>(p.Qinv, ix.Q(b, k, i), rowv, qi);
+    ld_row<NC>(p.S, ix.blk(b, k, 2, i), rowv, sup);
+    ld_row<MC>(p.Rinv, ix.R(b, k, i), urow, ri);
+    ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, bc);  // column i of B_k
+    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
+    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
+    float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
+    dotb<NP, NC>(h, Bc<NP>(qv), qi);
+    float dx, du;
+    recover<SH>(i, rowv, urow, rowv ? lam : 0.0f, lamn, qi, sup, h, bc, rv, ri, dx, du);
+    if (rowv) p.dz[ix.dx(b, k, i)] = dx;
+    if (urow) p.dz[ix.du(b, k, i)] = du;
+}
+
 // One knot's row of the reduced system in the workspace, padded to whole
 // float4s.  A knot still in the system keeps [- | U | gamma | D]; when it is
 // eliminated the row becomes [W1 | W2 | w3 | C'] (see cr_solve).
@@ -368,22 +394,9 @@ __device__ __forceinline__ void cr_solve(const Params& p, int b)
         if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
         const int kk = ok ? k : 0;
         const bool rowv = ok && rowi;
-        const bool urow = ok && kk < N - 1 && i < MC;
-        float qi[NC], sup[NC], ri[MC], bc[NC];
-        ld_row<NC>(p.Qinv, ix.Q(b, kk, i), rowv, qi);
-        ld_row<NC>(p.S, ix.blk(b, kk, 2, i), rowv, sup);
-        ld_row<MC>(p.Rinv, ix.R(b, kk, i), urow, ri);
-        ld_row<NC, MC>(p.Bu, ix.Bu(b, kk, 0) + i, urow, bc);  // column i of B_k
-        const float qv = ld1(p.q, ix.vn(b, kk, i), rowv);
-        const float rv = ld1(p.r, ix.vm(b, kk, i), urow);
         const float lam = ld1(p.lambda, ix.vn(b, kk, i), rowv);
         const float lamn = ld1(p.lambda, ix.vn(b, kk + 1 < N ? kk + 1 : kk, i), rowv && kk + 1 < N);
-        float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
-        dotb<NP, NC>(h, Bc<NP>(qv), qi);
-        float dx, du;
-        recover<SH>(i, rowv, urow, lam, lamn, qi, sup, h, bc, rv, ri, dx, du);
-        if (rowv) p.dz[ix.dx(b, kk, i)] = dx;
-        if (urow) p.dz[ix.du(b, kk, i)] = du;
+        recover_knot<SH>(p, b, kk, i, ok, lam, lamn);
     }
 
     // per-solve flags: any lane of the workgroup (an LDS atomic, then one writer)
@@ -722,25 +735,10 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
         const int kk = ok ? (w == 0 ? ke : jo) : 0;
         const bool rowv = ok && rowi;
-        const bool urow = ok && kk < N - 1 && i < MC;
-        float qi[NC], sup[NC], ri[MC], bc[NC];
-        ld_row<NC>(p.Qinv, ix.Q(b, kk, i), rowv, qi);
-        ld_row<NC>(p.S, ix.blk(b, kk, 2, i), rowv, sup);
-        ld_row<MC>(p.Rinv, ix.R(b, kk, i), urow, ri);
-        ld_row<NC, MC>(p.Bu, ix.Bu(b, kk, 0) + i, urow, bc);  // column i of B_k
-        const float qv = ld1(p.q, ix.vn(b, kk, i), rowv);
-        const float rv = ld1(p.r, ix.vm(b, kk, i), urow);
         const float lam = rowv ? sm.lam[kk][ii] : 0.0f;
         const float lamn = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
-        float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
-        dotb<NP, NC>(h, Bc<NP>(qv), qi);
-        float dx, du;
-        recover<SH>(i, rowv, urow, lam, lamn, qi, sup, h, bc, rv, ri, dx, du);
-        if (rowv) {
-            p.lambda[ix.vn(b, kk, i)] = lam;
-            p.dz[ix.dx(b, kk, i)] = dx;
-        }
-        if (urow) p.dz[ix.du(b, kk, i)] = du;
+        if (rowv) p.lambda[ix.vn(b, kk, i)] = lam;
+        recover_knot<SH>(p, b, kk, i, ok, lam, lamn);
     }
 
     const int fl = (bad ? GATO_F_S_NOT_SPD : 0) | (nonfinite ? GATO_F_NONFINITE : 0);
@@ -960,22 +958,9 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
         if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
         const int kk = ok ? k : 0;
         const bool rowv = ok && rowi;
-        const bool urow = ok && kk < N - 1 && i < MC;
-        float qi[NC], sup[NC], ri[MC], bc[NC];
-        ld_row<NC>(p.Qinv, ix.Q(b, kk, i), rowv, qi);
-        ld_row<NC>(p.S, ix.blk(b, kk, 2, i), rowv, sup);
-        ld_row<MC>(p.Rinv, ix.R(b, kk, i), urow, ri);
-        ld_row<NC, MC>(p.Bu, ix.Bu(b, kk, 0) + i, urow, bc);  // column i of B_k
-        const float qv = ld1(p.q, ix.vn(b, kk, i), rowv);
-        const float rv = ld1(p.r, ix.vm(b, kk, i), urow);
         const float lam = ld1(p.lambda, ix.vn(b, kk, i), rowv);
         const float lamk = ld1(p.lambda, ix.vn(b, kk + 1 < N ? kk + 1 : kk, i), rowv && kk + 1 < N);
-        float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
-        dotb<NP, NC>(h, Bc<NP>(qv), qi);
-        float dx, du;
-        recover<SH>(i, rowv, urow, lam, lamk, qi, sup, h, bc, rv, ri, dx, du);
-        if (rowv) p.dz[ix.dx(b, kk, i)] = dx;
-        if (urow) p.dz[ix.du(b, kk, i)] = du;
+        recover_knot<SH>(p, b, kk, i, ok, lam, lamk);
     }
     if (nonfinite) atomicOr(&wg_flags, GATO_F_NONFINITE);
     __syncthreads();
