@@ -416,21 +416,29 @@ struct Ops {
     static bool fused_ok(int N) { return N <= SL; }
     static int stream_chunks(int N) { return N <= SL ? 1 : (N <= 2 * SL ? 2 : (N <= 4 * SL ? 4 : 0)); }
 
+    // Horizons longer than a workgroup are formed in windows.  For n <= 16 the
+    // windows hold 32 knots (512 threads, half the LDS), so that two workgroups
+    // share a CU and one's loads and stores overlap the other's arithmetic.
+    using WinShape = Shape<SH::NC, SH::MC, SH::NP == 16 ? SH::SLOTS / 2 : SH::SLOTS>;
+    template <class FS>
+    static void form_launch(const Params& q, int nwin, int threads, hipStream_t st, bool pre)
+    {
+        if (pre)
+            hipLaunchKernelGGL((k_form<FS, true>), dim3(q.B, nwin), dim3(threads), 0, st, q);
+        else
+            hipLaunchKernelGGL((k_form<FS, false>), dim3(q.B, nwin), dim3(threads), 0, st, q);
+    }
     static hipError_t form(const Params& p, hipStream_t st, bool pre = true)
     {
         Params q = p;
+        hipLaunchKernelGGL(k_zero_i32, dim3((p.B + 255) / 256), dim3(256), 0, st, p.flags, p.B);
         if (p.N <= SL) {
             q.win_own = 0;
+            form_launch<SH>(q, 1, threads_for(p.N), st, pre);
         } else {
-            q.win_own = SL - 3;
+            q.win_own = WinShape::SLOTS - 3;
+            form_launch<WinShape>(q, (p.N + q.win_own - 1) / q.win_own, WinShape::THREADS, st, pre);
         }
-        const int nwin = q.win_own ? (p.N + q.win_own - 1) / q.win_own : 1;
-        const int threads = q.win_own ? SH::THREADS : threads_for(p.N);
-        hipLaunchKernelGGL(k_zero_i32, dim3((p.B + 255) / 256), dim3(256), 0, st, p.flags, p.B);
-        if (pre)
-            hipLaunchKernelGGL((k_form<SH, true>), dim3(p.B, nwin), dim3(threads), 0, st, q);
-        else
-            hipLaunchKernelGGL((k_form<SH, false>), dim3(p.B, nwin), dim3(threads), 0, st, q);
         return hipGetLastError();
     }
     static hipError_t pcg(const Params& p, hipStream_t st)

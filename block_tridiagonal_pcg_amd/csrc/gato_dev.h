@@ -21,14 +21,15 @@ namespace gato {
 // Compile-time shape of one instantiation.
 //   NC, MC: loop bounds for states and controls (runtime n <= NC, m <= MC;
 //           rows/columns beyond n, m are zero and padded diagonals are one).
-//   NP:     lanes per knot; SLOTS: knots one workgroup holds.
-template <int NC_, int MC_>
+//   NP:     lanes per knot; SLOTS: knots one workgroup holds (by default the
+//           most a 1024-thread workgroup holds; fewer for the windowed formation).
+template <int NC_, int MC_, int SLOTS_ = 0>
 struct Shape {
     static constexpr int NC = NC_;
     static constexpr int MC = MC_;
     static constexpr int NP = NC_ <= 16 ? 16 : 32;
     static constexpr int KPW = 64 / NP;
-    static constexpr int SLOTS = NP == 16 ? 64 : 16;
+    static constexpr int SLOTS = SLOTS_ ? SLOTS_ : (NP == 16 ? 64 : 16);
     static constexpr int THREADS = SLOTS * NP;
     static_assert(MC_ <= NC_ || MC_ <= NP, "controls must fit in a knot's lane group");
 };
