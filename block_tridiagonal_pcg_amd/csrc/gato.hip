@@ -43,12 +43,13 @@ __global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
     const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC;
     if (threadIdx.x == 0) L.flags = 0;
 
+    // the starting point, loaded now so that its latency hides behind the formation
+    float lam = ld1(p.lambda, ix.vn(b, k, i), rowv);
     Rows<SH> rw;
     int fl = 0;
     form<SH>(p, b, 0, p.N, L.u.form, L.park, rw, fl, [](const float*, const float*) {});
     if (fl && i == 0) atomicOr(&L.flags, fl);
 
-    float lam = ld1(p.lambda, ix.vn(b, k, i), rowv);
     int it = 0, pfl = 0;
     float rel = 0.0f;
     const RegMat<SH> M{&rw};

@@ -31,6 +31,9 @@ struct Shape {
     static constexpr int KPW = 64 / NP;
     static constexpr int SLOTS = SLOTS_ ? SLOTS_ : (NP == 16 ? 64 : 16);
     static constexpr int THREADS = SLOTS * NP;
+    // Whether the formation's n x n products go to the matrix cores: a
+    // 16x16x1 MFMA step costs as much as ~7 DPP multiply-adds per row.
+    static constexpr bool MMA = NP == 16 && NC_ >= 8;
     static_assert(MC_ <= NC_ || MC_ <= NP, "controls must fit in a knot's lane group");
 };
 
@@ -260,6 +263,63 @@ __device__ __forceinline__ void gemm_rows(float* acc, const BcRow<NP, K>& x, con
         axpyb<NP, K, L>(acc, x, mul[L]);
         gemm_rows<NP, K, KL, L + 1>(acc, x, mul);
     }
+}
+
+// ------------------------------------------------------------------ matrix-core products (NP = 16)
+
+// A product A B' of the wave's four knots at once on the matrix cores, with A,
+// B and the result all in row layout (lane i of a group holds row i).  One
+// V_MFMA_F32_16X16X1_4B_F32 per k: its four 16x16 blocks are the wave's four
+// lane groups, lane i of a group supplies B[i][k] as the first operand and
+// A[i][k] as the second, and each block accumulates D = B A' with D[a][b] in
+// lane 16*(a/4) + b, register 4*group + a%4.  `mma_rows` then moves tile (lane
+// row q, register quartet g) to (lane row g, quartet q) with two rounds of
+// permlane swaps, which leaves lane b of group g holding column b of D_g, i.e.
+// row b of A B'.  Each output element is its own K-term dot product, so
+// garbage in a padding lane's row only reaches that lane's row and column.
+typedef float mma16_t __attribute__((ext_vector_type(16)));
+
+// acc += A B' over columns k < K of the lane's rows a (of A) and b (of B)
+template <int K>
+__device__ __forceinline__ void mma_abt(mma16_t& acc, const float* a, const float* b)
+{
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x1f32(b[k], a[k], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void swap_rows32(float& x, float& y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void swap_rows16(float& x, float& y)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+// r[c] = (A B')[lane][c] for c < NCOL, from an accumulator filled by mma_abt.
+template <int NCOL>
+__device__ __forceinline__ void mma_rows(const mma16_t& acc, float* r)
+{
+    static_assert(NCOL <= 16, "");
+    float t[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) t[v] = acc[v];
+    // rows 2-3 of quartets 0-1 <-> rows 0-1 of quartets 2-3
+#pragma unroll
+    for (int v = 0; v < 8; ++v) swap_rows32(t[v], t[v + 8]);
+    // rows 1, 3 of quartets 0, 2 <-> rows 0, 2 of quartets 1, 3
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        swap_rows16(t[v], t[v + 4]);
+        swap_rows16(t[v + 8], t[v + 12]);
+    }
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) r[c] = t[c];
 }
 
 // ------------------------------------------------------------------ in-place Gauss-Jordan

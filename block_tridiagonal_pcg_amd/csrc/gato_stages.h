@@ -195,7 +195,10 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 
     // W = A_k Q~_k^-1 (row i), V = B_k R_k^-1 (row i); gamma pieces
     //   h = (Q~_k^-1 q_k)_i (own knot), g = (e_k - W q_k - V r_k)_i (for knot k+1)
+    // On the matrix cores U_k = W_k A_k' + V_k B_k' is formed here too, while
+    // W_k's rows are still in registers (the DPP form below takes O_k's rows).
     float V[MC], h = 0.0f, g;
+    float U[NC];
     {
         float qi[NC], ri[MC], W[NC];
 #pragma unroll
@@ -206,11 +209,23 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
             for (int c = 0; c < MC; ++c) K.Bt[s][c][i] = br[c];  // transpose of B_k
 #pragma unroll
-        for (int c = 0; c < NC; ++c) W[c] = 0.0f;
-#pragma unroll
         for (int c = 0; c < MC; ++c) V[c] = 0.0f;
-        gemm_rows<NP, NC, NC>(W, BcRow<NP, NC>(qi), ar);
+        if constexpr (SH::MMA) {
+            mma16_t acc = {};
+            mma_abt<NC>(acc, ar, qi);  // A_k Q~_k^-1' (Q~_k^-1 is symmetric)
+            mma_rows<NC>(acc, W);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) W[c] = 0.0f;
+            gemm_rows<NP, NC, NC>(W, BcRow<NP, NC>(qi), ar);
+        }
         gemm_rows<NP, MC, MC>(V, BcRow<NP, MC>(ri), br);
+        if constexpr (SH::MMA) {
+            mma16_t acc = {};
+            mma_abt<NC>(acc, ar, W);  // A_k W_k' = A_k Q~_k^-1 A_k'
+            mma_abt<MC>(acc, V, br);  // V_k B_k' = B_k R_k^-1 B_k'
+            mma_rows<NC>(acc, U);
+        }
         float t1 = 0.0f, t2 = 0.0f;
         const Bc<NP> qb(qv);
         dotb<NP, NC>(h, qb, qi);
@@ -237,20 +252,22 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 
     // U_k = A_k Q~_k^-1 A_k' + B_k R_k^-1 B_k' = -(A_k O_k) + V_k B_k'
     {
-        float U[NC], nar[NC], bcol[NC];
+        if constexpr (!SH::MMA) {
+            float nar[NC], bcol[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            U[c] = 0.0f;
-            nar[c] = -ar[c];
-        }
-        gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(O), nar);
-        // lane i < m holds column i of B_k
+            for (int c = 0; c < NC; ++c) {
+                U[c] = 0.0f;
+                nar[c] = -ar[c];
+            }
+            gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(O), nar);
+            // lane i < m holds column i of B_k
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const float bt = K.Bt[s][i < MC ? i : 0][c];
-            bcol[c] = urow ? bt : 0.0f;
+            for (int c = 0; c < NC; ++c) {
+                const float bt = K.Bt[s][i < MC ? i : 0][c];
+                bcol[c] = urow ? bt : 0.0f;
+            }
+            gemm_rows<NP, NC, MC>(U, BcRow<NP, NC>(bcol), V);
         }
-        gemm_rows<NP, NC, MC>(U, BcRow<NP, NC>(bcol), V);
 #pragma unroll
         for (int c = 0; c < NC; ++c) L.xw[s][i][c] = U[c];
         L.xg[s][i] = g;
@@ -312,8 +329,18 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
             Z[c] = 0.0f;
         }
         __syncthreads();
-        gemm_rows<NP, NC, NC>(Y, BcRow<NP, NC>(O), di);  // Y = D_k^-1 O_k
-        gemm_rows<NP, NC, NC>(Z, BcRow<NP, NC>(Dn), Y);  // Z = Y D_{k+1}^-1
+        if constexpr (SH::MMA) {
+            // Z = D_k^-1 (O_k D_{k+1}^-1): Y holds the rows of (O_k D_{k+1}^-1)'
+            mma16_t acc = {};
+            mma_abt<NC>(acc, Dn, O);
+            mma_rows<NC>(acc, Y);
+            acc = mma16_t{};
+            mma_abt<NC>(acc, di, Y);
+            mma_rows<NC>(acc, Z);
+        } else {
+            gemm_rows<NP, NC, NC>(Y, BcRow<NP, NC>(O), di);  // Y = D_k^-1 O_k
+            gemm_rows<NP, NC, NC>(Z, BcRow<NP, NC>(Dn), Y);  // Z = Y D_{k+1}^-1
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             L.xw[s][i][c] = Z[c];
@@ -437,16 +464,25 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
     const bool lead = i == 0;
     const int nth = blockDim.x;
 
-    for (int t = threadIdx.x; t < P; t += nth) {
-        L.red0[t] = 0.0f;
-        L.red1[t] = 0.0f;
-        L.red2[t] = 0.0f;
+    // Zero what no lane group writes: the edge rows, the rows and leaves of
+    // slots beyond the groups present (a block of G < SLOTS groups), and the
+    // leaves past the last knot's.  Every other exchange row and leaf is
+    // written by its own group before it is read, so these stores need no
+    // barrier of their own.
+    const int G = nth / NP;
+    for (int t = threadIdx.x; t < P; t += nth)
+        if (t >= KK || t % SL >= G) {
+            L.red0[t] = 0.0f;
+            L.red1[t] = 0.0f;
+            L.red2[t] = 0.0f;
+        }
+    for (int t = threadIdx.x; t < (KK + 2) * NP; t += nth) {
+        const int r = t / NP;
+        if (r == 0 || r == KK + 1 || (r - 1) % SL >= G) {
+            L.xv[r][t % NP] = 0.0f;
+            L.xz[r][t % NP] = 0.0f;
+        }
     }
-    for (int t = threadIdx.x; t < NP; t += nth) {
-        L.xv[0][t] = L.xv[KK + 1][t] = 0.0f;
-        L.xz[0][t] = L.xz[KK + 1][t] = 0.0f;
-    }
-    __syncthreads();
 
     auto row = [&](int c) { return c * SL + s + 1; };  // exchange row of chunk c
 
@@ -465,7 +501,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         lp[c] = L.xv[row(c) - 1][i];
         ln[c] = L.xv[row(c) + 1][i];
     }
-    __syncthreads();
+    // (no barrier: xv is next written after the one that follows r's stores)
 
     int iters = 0, flags = 0;
     if (!__builtin_isfinite(gg)) {
@@ -498,7 +534,8 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         rp[c] = L.xz[row(c) - 1][i];
         rn[c] = L.xz[row(c) + 1][i];
     }
-    __syncthreads();
+    // (no barrier: z goes to xv and the red1/red2 leaves, which nobody reads
+    // between the barriers around this point; xz is next written in the loop)
 
     double lamd[C];
 #pragma unroll
