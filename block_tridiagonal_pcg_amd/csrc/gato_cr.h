@@ -596,6 +596,52 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         // every value read from an absent neighbour's slot is masked to zero
         // (a slot that no knot wrote may hold any bits)
         const bool okm = kept && hasL, okp = kept && hasU;
+        if constexpr (SH::MMA && NC < 16) {
+            // On the matrix cores every product is (columns)' (columns): lane c
+            // reads column c of the W blocks from LDS, and lane n reads w3, so
+            // the sum's column n is the gamma update.  Rows of a group that
+            // sits out come out as zero, and padding lanes keep their rows.
+            const int c2 = i <= NC ? NC + i : 0;   // W2 columns, w3 at lane n
+            const int c1 = i < NC ? i : 2 * NC;    // W1 columns, w3 at lane n
+            const bool cl = i <= NC;
+            float m2[NC], p1[NC], r[NC + 1];
+#pragma unroll
+            for (int l = 0; l < NC; ++l) {
+                m2[l] = (okm && cl) ? Wm[l * YW + c2] : 0.0f;
+                p1[l] = (okp && cl) ? Wp[l * YW + c1] : 0.0f;
+            }
+            // D -= W2m' W2m + W1p' W1p, gamma -= W2m' w3m + W1p' w3p
+            mma16_t acc = {};
+            mma_abt<NC>(acc, m2, m2);
+            mma_abt<NC>(acc, p1, p1);
+            mma_rows<NC + 1>(acc, r);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) e[c] = rowi ? e[c] - r[c] : e[c];
+            e[3 * NC] = rowi ? e[3 * NC] - r[NC] : e[3 * NC];
+            // U = -W1p' W2p (the old U is not needed: W1p already carries it)
+            {
+                float p2[NC];
+#pragma unroll
+                for (int l = 0; l < NC; ++l) p2[l] = (okp && rowi) ? Wp[l * YW + NC + ii] : 0.0f;
+                mma16_t au = {};
+                mma_abt<NC>(au, p1, p2);
+                mma_rows<NC>(au, r);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) e[2 * NC + c] = kept ? (rowi ? 0.0f - r[c] : 0.0f) : e[2 * NC + c];
+            }
+            // L = -W2m' W1m when the knot is eliminated next (the old L is not needed)
+            if (__builtin_amdgcn_ballot_w64(needL) != 0) {
+                float m1[NC];
+#pragma unroll
+                for (int l = 0; l < NC; ++l) m1[l] = (okm && rowi) ? Wm[l * YW + ii] : 0.0f;
+                mma16_t al = {};
+                mma_abt<NC>(al, m2, m1);
+                mma_rows<NC>(al, r);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) e[NC + c] = kept ? (rowi ? 0.0f - r[c] : 0.0f) : e[NC + c];
+            }
+            return;
+        }
         float col[NC], row[NC];
         // D -= W2m' W2m, gamma -= W2m' w3m, and L = -W2m' W1m when needed
 #pragma unroll
@@ -833,6 +879,48 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
             }
             r[RW::G] = x[3 * NC];
             st4<W>(p.dws, nw.fac(b, f, i), r);
+        }
+        if constexpr (SH::MMA && NC < 16) {
+            // (columns)' (columns) on the matrix cores: lane c holds column c
+            // of W1 (then W2), and lane n the column w3, so each sum's column n
+            // is the gamma update.  Groups with act false get zero products.
+            auto columns = [&](const float* w, float* out) {  // out[k] = W[k][lane], w3 at lane n
+                if (rowi) {
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) t[i][c] = w[c];
+                    t[i][NC] = x[3 * NC];
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int k = 0; k < NC; ++k) out[k] = (act && i <= NC) ? t[k][i <= NC ? i : 0] : 0.0f;
+                __builtin_amdgcn_wave_barrier();
+            };
+            float w1[NC], w2[NC], r[NC + 1];
+            columns(x + NC, w1);
+            columns(x + 2 * NC, w2);
+            // the chunk's first knot: D_a -= W1' W1, gamma_a -= W1' w3, F = -W1' W2
+            mma16_t acc = {};
+            mma_abt<NC>(acc, w1, w1);
+            mma_rows<NC + 1>(acc, r);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) Da[k] = rowi ? Da[k] - r[k] : Da[k];
+            ga = rowi ? ga - r[NC] : ga;
+            acc = mma16_t{};
+            mma_abt<NC>(acc, w1, w2);
+            mma_rows<NC>(acc, r);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) F[k] = act ? (rowi ? 0.0f - r[k] : 0.0f) : F[k];
+            // the next front: D_{f+1} -= W2' W2, gamma_{f+1} -= W2' w3
+            float Dx[NC];
+            ld_row<NC>(p.S, ix.blk(b, f + 1, 1, i), act && rowi, Dx);
+            const float gx = ld1(p.gamma, ix.vn(b, f + 1, i), act && rowi);
+            acc = mma16_t{};
+            mma_abt<NC>(acc, w2, w2);
+            mma_rows<NC + 1>(acc, r);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) Dn[k] = act ? (rowi ? Dx[k] - r[k] : Dx[k]) : Dn[k];
+            gn = act ? (rowi ? gx - r[NC] : gx) : gn;
+            return;
         }
         float c[NC];  // -(column i of W1), then -(column i of W2)
         transpose(x + NC, c);
