@@ -456,6 +456,16 @@ __host__ __device__ constexpr int cr_group_even(int g, int M)
 //   [B][C][n][16]    C' rows of the boundary system's odd knots
 // (C = ND_CHUNKS, W = CrRow<SH>::W).
 constexpr int ND_CHUNKS = 64;
+// The chunk kernels spread one solve's chunks over ND_SPLIT workgroups of
+// ND_GPW lane groups each: a batch that holds one solve per CU in the other
+// stages thus fills the device in these (workgroup y of solve b: chunks
+// y*ND_GPW .. (y+1)*ND_GPW - 1).
+#ifndef GATO_ND_SPLIT
+#define GATO_ND_SPLIT 2
+#endif
+constexpr int ND_SPLIT = GATO_ND_SPLIT;
+constexpr int ND_GPW = ND_CHUNKS / ND_SPLIT;
+static_assert(ND_CHUNKS % ND_SPLIT == 0 && ND_GPW % 4 == 0, "whole waves per workgroup");
 
 __host__ __device__ constexpr int nd_start(int j, int N) { return (int)(((long long)j * N) / ND_CHUNKS); }
 
@@ -801,7 +811,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
 
 template <class SH>
 struct NdLds {
-    float t[ND_CHUNKS][SH::NC][SH::NC + 1];  // one transpose tile per lane group (+1: bank spread)
+    float t[ND_GPW][SH::NC][SH::NC + 1];  // one transpose tile per lane group (+1: bank spread)
     int flags;
 };
 
@@ -829,13 +839,13 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
     const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
     const int N = p.N;
     const int i = threadIdx.x % NP;
-    const int g = threadIdx.x / NP;  // chunk
+    const int g = blockIdx.y * ND_GPW + threadIdx.x / NP;  // chunk
     const bool rowi = i < NC;
     const int ii = rowi ? i : 0;
     const int a = nd_start(g, N), bk = nd_start(g + 1, N) - 1;
     const int nint = bk - a - 1;  // interior knots (chunks hold >= 2 knots)
     const int maxint = (N + ND_CHUNKS - 1) / ND_CHUNKS - 2;
-    float(*t)[NC + 1] = sm.t[g];
+    float(*t)[NC + 1] = sm.t[threadIdx.x / NP];
     if (threadIdx.x == 0) sm.flags = 0;
     bool bad = false;
 
@@ -984,7 +994,7 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
     }
     if (bad) atomicOr(&sm.flags, GATO_F_S_NOT_SPD);
     __syncthreads();
-    if (threadIdx.x == 0) p.flags[b] |= sm.flags;
+    if (threadIdx.x == 0 && sm.flags) atomicOr(p.flags + b, sm.flags);  // the solve's other workgroups too
 }
 
 // Back substitution of every chunk's interior knots (the chunk's first and last
@@ -1002,7 +1012,8 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
     const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
     const int N = p.N;
     const int i = threadIdx.x % NP;
-    const int g = threadIdx.x / NP;
+    const int gl = threadIdx.x / NP;
+    const int g = blockIdx.y * ND_GPW + gl;  // chunk
     const bool rowi = i < NC;
     const int a = nd_start(g, N), bk = nd_start(g + 1, N) - 1;
     const int maxsz = (N + ND_CHUNKS - 1) / ND_CHUNKS;
@@ -1037,12 +1048,15 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
 #pragma unroll
         for (int c = 0; c < W; ++c) cur[c] = nxt[c];
     }
-    __syncthreads();  // every lambda of the solve is written
+    __syncthreads();  // every lambda of this workgroup's chunks is written
 
-    // recovery of every knot's dz, knots spread over the lane groups
-    for (int t0 = 0; t0 < N; t0 += ND_CHUNKS) {
-        const int k = t0 + g;
-        const bool ok = k < N;
+    // recovery of dz for the knots of this workgroup's chunks, spread over its
+    // lane groups (the knot after the last one starts the next chunk, whose
+    // lambda came from the boundary system)
+    const int k0 = nd_start(blockIdx.y * ND_GPW, N), k1 = nd_start((blockIdx.y + 1) * ND_GPW, N);
+    for (int t0 = k0; t0 < k1; t0 += ND_GPW) {
+        const int k = t0 + gl;
+        const bool ok = k < k1;
         if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
         const int kk = ok ? k : 0;
         const bool rowv = ok && rowi;
@@ -1052,7 +1066,7 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
     }
     if (nonfinite) atomicOr(&wg_flags, GATO_F_NONFINITE);
     __syncthreads();
-    if (threadIdx.x == 0) p.flags[b] |= wg_flags;
+    if (threadIdx.x == 0 && wg_flags) atomicOr(p.flags + b, wg_flags);
 }
 
 }  // namespace gato

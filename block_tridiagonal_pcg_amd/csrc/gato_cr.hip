@@ -53,9 +53,11 @@ __global__ __launch_bounds__(1024) void k_cr_res(Params p)
     cr_resident<SH>(p, blockIdx.x);
 }
 
-// Nested dissection (n <= 16, N > 128): three launches of 64 lane groups.
+// Nested dissection (n <= 16, N > 128): the chunk kernels take ND_SPLIT
+// workgroups of ND_GPW lane groups per solve, the boundary system one
+// workgroup of 64 lane groups.
 template <class SH>
-__global__ __launch_bounds__(1024) void k_nd_reduce(Params p)
+__global__ __launch_bounds__(ND_GPW * 16) void k_nd_reduce(Params p)
 {
     nd_reduce<SH>(p, blockIdx.x);
 }
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(1024) void k_cr_res_virt(Params p)
 }
 
 template <class SH>
-__global__ __launch_bounds__(1024) void k_nd_back(Params p)
+__global__ __launch_bounds__(ND_GPW * 16) void k_nd_back(Params p)
 {
     nd_back<SH>(p, blockIdx.x);
 }
@@ -96,10 +98,10 @@ static hipError_t cr_launch_shape(const Params& p, hipStream_t st)
         }
         if (!cr_streaming_forced()) {  // N > 128: nested dissection
             static_assert(2 * ND_CHUNKS == 2 * CrResLds<SH>::MAXG, "boundary system = one resident workgroup");
-            const dim3 blk(ND_CHUNKS * SH::NP);
-            hipLaunchKernelGGL((k_nd_reduce<SH>), dim3(p.B), blk, 0, st, p);
-            hipLaunchKernelGGL((k_cr_res_virt<SH>), dim3(p.B), blk, 0, st, p);
-            hipLaunchKernelGGL((k_nd_back<SH>), dim3(p.B), blk, 0, st, p);
+            const dim3 chunks(p.B, ND_SPLIT), blk(ND_GPW * SH::NP);
+            hipLaunchKernelGGL((k_nd_reduce<SH>), chunks, blk, 0, st, p);
+            hipLaunchKernelGGL((k_cr_res_virt<SH>), dim3(p.B), dim3(ND_CHUNKS * SH::NP), 0, st, p);
+            hipLaunchKernelGGL((k_nd_back<SH>), chunks, blk, 0, st, p);
             return hipGetLastError();
         }
     }
