@@ -147,9 +147,9 @@ size_t cr_ws_bytes(const gato_dims_t* d)
 // MI355X (knots n = 14): block Thomas walks the knots in order, about 3.0 us
 // per knot whatever the batch until its one lane group per solve fills the
 // chip (about 1.6 ns per knot and solve beyond); cyclic reduction is
-// log-depth but does more arithmetic: about 0.35 us per solve with the
-// register-resident kernel (N <= 128, n <= 16), 2.7 ns per knot and solve with
-// the nested dissection (N > 128, n <= 16) and 4.3 ns with the streaming
+// log-depth but does more arithmetic: about 0.15 us + 1.05 ns per knot per
+// solve with the register-resident kernel (N <= 128, n <= 16), 2.6 ns per knot
+// and solve with the nested dissection (N > 128, n <= 16) and 4.3 ns with the streaming
 // kernel (n > 16), once its batch fills the chip.  Cyclic reduction is taken
 // while its batch time stays below block Thomas's.  GATO_LONG_SOLVE=thomas or
 // =cr forces either (for measurements).
@@ -160,7 +160,8 @@ bool cr_preferred(const gato_dims_t* d)
         if (std::strcmp(env, "cr") == 0) return true;
     }
     const bool narrow = d->n <= 16 && !cr_streaming_forced();
-    const double per_solve_us = narrow ? (d->N <= 2 * ND_CHUNKS ? 0.35 : 0.0027 * d->N) : 0.0043 * d->N;
+    const double per_solve_us =
+        narrow ? (d->N <= 2 * ND_CHUNKS ? 0.15 + 0.00105 * d->N : 0.0026 * d->N) : 0.0043 * d->N;
     const double thomas_us = std::max(3.0 * d->N, 0.0016 * d->N * d->B);
     return d->B * per_solve_us < thomas_us;
 }

@@ -167,8 +167,8 @@ def test_cyclic_reduction_depth_matches_the_plan(lib):
 
 def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
     """Fused PCG where a workgroup holds the horizon; beyond, cyclic reduction while
-    its batch time (0.35 us per solve resident, 2.7 ns per knot and solve with the
-    nested dissection, 4.3 ns streaming for n > 16) stays below block Thomas's
+    its batch time (0.15 us + 1.05 ns per knot per solve resident, 2.6 ns per knot
+    and solve with the nested dissection, 4.3 ns streaming for n > 16) stays below block Thomas's
     (3 us per knot, or 1.6 ns per knot and solve once the batch fills the chip)."""
     from block_tridiagonal_pcg_amd import ops
 
