@@ -192,7 +192,24 @@ __global__ __launch_bounds__(SH::THREADS) void k_form(Params p)
                           lane, 64);
         __builtin_amdgcn_wave_barrier();
     };
-    put(p.S, rw.slo, rw.sd, rw.sup);
+    // S's diagonal and upper blocks, knot by knot (the lower blocks are not read)
+    auto put_upper = [&](float* dst, const float* dg, const float* hi) {
+        if (i < NC)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                slice[(sw * 3 + 1) * NC * NC + i * NC + c] = dg[c];
+                slice[(sw * 3 + 2) * NC * NC + i * NC + c] = hi[c];
+            }
+        __builtin_amdgcn_wave_barrier();
+        for (int ws = ws0; ws < ws1; ++ws)
+            lds_to_global(dst + ix.blk(b, w0 + ws, 1, 0), slice + (ws - wave * KPW) * ROWBLK + NC * NC, 2 * NC * NC,
+                          lane, 64);
+        __builtin_amdgcn_wave_barrier();
+    };
+    if (!PRE && p.s_upper_only)
+        put_upper(p.S, rw.sd, rw.sup);
+    else
+        put(p.S, rw.slo, rw.sd, rw.sup);
     if constexpr (PRE) put(p.Pinv, rw.plo, rw.pd, rw.pup);
 }
 
@@ -826,10 +843,13 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
     rc = with_shape(dims->n, dims->m, [&](auto ops) {
         using O = decltype(ops);
         if (fused) return O::fused(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
-        if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;  // no Phi^-1: the direct solve follows
+        // horizons a workgroup cannot hold: no Phi^-1, since a direct solve follows, and
+        // no lower blocks of S when that solve reads only the upper ones
+        const bool cr = cr_preferred(dims);
+        p.s_upper_only = cr && !cr_reads_lower(dims);
+        if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
-        // horizons a workgroup cannot hold
-        if ((cr_preferred(dims) ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
+        if ((cr ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
         if (O::merit(p, stream) != hipSuccess) return GATO_E_HIP;
         return GATO_OK;

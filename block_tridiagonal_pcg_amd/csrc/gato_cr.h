@@ -557,7 +557,8 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
             a[3 * NC] = r[RW::G];
         } else {
             ld_row<NC>(p.S, ix.blk(b, jj, 1, i), ld, a);
-            ld_row<NC>(p.S, ix.blk(b, jj, 0, i), ld, a + NC);
+            // L = S_{j,j-1} = S_{j-1,j}': column i of the upper block of knot j - 1
+            ld_row<NC, NC>(p.S, ix.blk(b, jj > 0 ? jj - 1 : 0, 2, 0) + ii, ld, a + NC);
             ld_row<NC>(p.S, ix.blk(b, jj, 2, i), ld && jo + 1 < N, a + 2 * NC);
             a[3 * NC] = ld1(p.gamma, ix.vn(b, jj, i), ld);
         }

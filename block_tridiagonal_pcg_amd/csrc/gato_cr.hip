@@ -143,6 +143,11 @@ size_t cr_ws_bytes(const gato_dims_t* d)
     return align256((B * (N + 2 * ND_CHUNKS) * n * W + B * ND_CHUNKS * n * 16) * sizeof(float));
 }
 
+bool cr_reads_lower(const gato_dims_t* d)
+{
+    return !(d->n <= 16 && !cr_streaming_forced());
+}
+
 // The long-horizon solve of gato_sqp_step, chosen by a cost model measured on
 // MI355X (knots n = 14): block Thomas walks the knots in order, about 3.0 us
 // per knot whatever the batch until its one lane group per solve fills the

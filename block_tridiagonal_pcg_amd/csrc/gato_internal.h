@@ -25,6 +25,11 @@ size_t cr_ws_bytes(const gato_dims_t* d);
 // the streaming one.
 hipError_t cr_launch(const Params& p, hipStream_t st);
 
+// Whether the cyclic reduction cr_launch runs for these dimensions reads the
+// lower blocks S_{k,k-1} (the streaming kernel does; the register-resident
+// kernel and the nested dissection read the upper blocks only).
+bool cr_reads_lower(const gato_dims_t* d);
+
 // Whether gato_sqp_step takes cyclic reduction rather than block Thomas
 // beyond the fused horizons, by the measured cost model.
 bool cr_preferred(const gato_dims_t* d);

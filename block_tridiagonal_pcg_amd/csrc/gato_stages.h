@@ -27,6 +27,7 @@ struct Params {
     int n_alpha;
     float alphas[GATO_MAX_ALPHA];
     int win_own;  // knots owned by one form workgroup (0: the whole horizon)
+    int s_upper_only;  // stage 1 alone: write S's diagonal and upper blocks only (the solve reads no lower block)
     float* dws;   // direct solve: pivot inverses [B][N][n][n], then eliminated right-hand sides [B][N][n]
 };
 

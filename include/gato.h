@@ -200,7 +200,9 @@ int gato_direct_solve(const gato_dims_t* dims, const float* S, const float* gamm
  * For n <= 16 and N > 128 the order is a nested dissection: the horizon is cut
  * into 64 chunks whose interior knots are eliminated first, in order (each
  * chunk in parallel), and the 128 chunk-boundary knots are then reduced
- * cyclically as above.  Arguments as in gato_direct_solve; the reduced rows
+ * cyclically as above.  For n <= 16 only the diagonal and upper blocks of S
+ * are read (S is symmetric: S_{k,k-1} = S_{k-1,k}'); for n > 16 the lower
+ * blocks too.  Arguments as in gato_direct_solve; the reduced rows
  * and factors go through the caller's workspace, of at least
  * gato_cr_workspace_bytes(dims) bytes, 256-byte aligned.  The eliminations of
  * one level (or chunk step) run in parallel, so a solve's depth grows with

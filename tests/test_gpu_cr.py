@@ -174,3 +174,22 @@ def test_sqp_step_long_horizon_wide_knots():
     _, dz = _exact(bt, form)
     assert (g["iters"] == 0).all()
     assert rel_rows(g["dz"], dz).max() <= 5e-5
+
+
+@pytest.mark.parametrize("N", [9, 128, 300])
+def test_cr_reads_no_lower_block(N):
+    """For n <= 16 the solve reads S's diagonal and upper blocks only (the lower ones
+    are their transposes): with every lower block NaN it returns the same bits, for
+    the register-resident kernel (N <= 128) and the nested dissection."""
+    B = 3
+    _ident("cr upper blocks only", N, B)
+    bt = synth.make_batch(3, B, N=N)
+    form = oracle.form_schur(*synth.inputs(bt))
+    g = _cr(bt, form)
+    poisoned = dict(form)
+    S = np.array(form["S"], dtype=np.float32)
+    S[:, :, 0] = np.nan
+    poisoned["S"] = S
+    h = _cr(bt, poisoned)
+    assert (g["flags"] == 0).all() and (h["flags"] == 0).all()
+    assert np.array_equal(g["lam"], h["lam"]) and np.array_equal(g["dz"], h["dz"])
