@@ -569,8 +569,10 @@ static Params make_params(const gato_dims_t* d)
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// gato_sqp_step's workspace beyond the fused horizons.  Only the direct solves
+// run there, so it holds no Phi^-1.
 struct WsLayout {
-    size_t S, Pinv, gamma, Qinv, Rinv, direct, total;
+    size_t S, gamma, Qinv, Rinv, direct, total;
 };
 
 static size_t direct_ws_bytes(const gato_dims_t* d)
@@ -585,8 +587,6 @@ static WsLayout ws_layout(const gato_dims_t* d)
     WsLayout w;
     size_t off = 0;
     w.S = off;
-    off += align256(B * N * 3 * n * n * sizeof(float));
-    w.Pinv = off;
     off += align256(B * N * 3 * n * n * sizeof(float));
     w.gamma = off;
     off += align256(B * N * n * sizeof(float));
@@ -823,7 +823,6 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
     if (!fused) {
         char* ws = static_cast<char*>(workspace);
         p.S = reinterpret_cast<float*>(ws + wl.S);
-        p.Pinv = reinterpret_cast<float*>(ws + wl.Pinv);
         p.gamma = reinterpret_cast<float*>(ws + wl.gamma);
         p.Qinv = reinterpret_cast<float*>(ws + wl.Qinv);
         p.Rinv = reinterpret_cast<float*>(ws + wl.Rinv);

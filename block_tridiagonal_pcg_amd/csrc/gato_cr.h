@@ -741,6 +741,9 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         __syncthreads();
     }
 
+    // From here on, addresses come from a fresh copy of the solve index.
+    const int bl = late(b);
+
     // back substitution, levels in reverse: lambda_j = C_j'^-1 (w3 - W1 lambda_{j-s} - W2 lambda_{j+s})
     auto back = [&](bool act, int k, int s, const float* ct, const float* w1, const float* w2, float w3) {
         const bool hasU = k + s < N;
@@ -765,7 +768,8 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     if (levels >= 1) {
         if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
             float w1[NC], w2[NC], oc[16];
-            ld4<16>(p.dws, ocrow, hasO && rowi, oc);
+            const size_t ocl = VIRT ? nw.oc(bl, hasO ? g : 0, ii) : (((size_t)bl * M + (hasO ? g : 0)) * NC + ii) * 16;
+            ld4<16>(p.dws, ocl, hasO && rowi, oc);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 w1[c] = sm.os[hasO ? g : 0][ii][c];
@@ -782,7 +786,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         for (int w = 0; w < 2; ++w) {
             const bool ok = w == 0 ? hasG : hasO;
             const int v = w == 0 ? ke : jo;
-            if (ok && rowi) p.lambda[ix.vn(b, nd_real(v, p.N), i)] = sm.lam[v][i];
+            if (ok && rowi) p.lambda[ix.vn(bl, nd_real(v, p.N), i)] = sm.lam[v][i];
         }
     }
     // recovery of this group's knots, and lambda to memory (both knots' loads issued together)
@@ -794,17 +798,17 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         const bool rowv = ok && rowi;
         const float lam = rowv ? sm.lam[kk][ii] : 0.0f;
         const float lamn = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
-        if (rowv) p.lambda[ix.vn(b, kk, i)] = lam;
-        recover_knot<SH>(p, b, kk, i, ok, lam, lamn);
+        if (rowv) p.lambda[ix.vn(bl, kk, i)] = lam;
+        recover_knot<SH>(p, bl, kk, i, ok, lam, lamn);
     }
 
     const int fl = (bad ? GATO_F_S_NOT_SPD : 0) | (nonfinite ? GATO_F_NONFINITE : 0);
     if (fl) atomicOr(&sm.flags, fl);
     __syncthreads();
     if (threadIdx.x == 0) {
-        p.flags[b] |= sm.flags;
-        if (p.iters) p.iters[b] = 0;
-        if (p.relres) p.relres[b] = 0.0f;
+        p.flags[bl] |= sm.flags;
+        if (p.iters) p.iters[bl] = 0;
+        if (p.relres) p.relres[bl] = 0.0f;
     }
 }
 

@@ -37,6 +37,15 @@ struct Params {
 // waited for at this point rather than sunk past a later branch.
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
 
+// An opaque copy of a uniform index: addresses formed from it after this point
+// are recomputed there instead of being kept live (or spilled) from an earlier
+// computation of the same expression.
+__device__ __forceinline__ int late(int x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 __device__ __forceinline__ float uniform(float x)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));

@@ -252,8 +252,8 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *    gato_direct_solve's block Thomas elimination (the environment variable
  *    GATO_LONG_SOLVE=thomas or =cr forces either).
  *    lambda's input is not read, iters and relres are written as 0, and eps
- *    and max_iters are checked but unused.  S, Pinv,
- *    gamma, Qinv, Rinv and the solve's rows go through `workspace`
+ *    and max_iters are checked but unused.  S (no Phi^-1: the
+ *    direct solves do not use it), gamma, Qinv, Rinv and the solve's rows go through `workspace`
  *    (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device
  *    memory).
  * times (nullable): per-stage device times; when given, the call synchronises.
