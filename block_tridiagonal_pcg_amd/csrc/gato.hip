@@ -346,6 +346,62 @@ __global__ __launch_bounds__(1024) void k_merit(Params p)
     }
 }
 
+// The per-knot merit values of one solve spread over gridDim.y workgroups
+// (knots y N / Y .. (y + 1) N / Y - 1 in workgroup y), into p.mpart, for
+// batches too small to fill the device with one workgroup per solve; then
+// k_merit_sum forms the same canonical sums as k_merit, so the bits match.
+template <class SH>
+__global__ __launch_bounds__(1024) void k_merit_knots(Params p)
+{
+    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    const Ix<SH> ix{p.N};
+    const int b = blockIdx.x;
+    const int s = threadIdx.x / NP, i = threadIdx.x % NP;
+    const int ks = blockDim.x / NP;
+    const int k0 = (int)((long long)blockIdx.y * p.N / gridDim.y);
+    const int k1 = (int)((long long)(blockIdx.y + 1) * p.N / gridDim.y);
+    float* out = p.mpart + (size_t)b * (p.n_alpha + 1) * p.N;
+    for (int c0 = k0; c0 < k1; c0 += ks) {
+        const int k = c0 + s < k1 ? c0 + s : p.N;  // p.N: no knot (loads masked, nothing written)
+        const bool kv = k < p.N, hn = kv && k < p.N - 1, rowv = kv && i < NC;
+        const float dx = ld1(p.dz, ix.dx(b, k, i), rowv);
+        const float du = ld1(p.dz, ix.du(b, k, i), hn && i < MC);
+        const float dxn = ld1(p.dz, ix.dx(b, k + 1, i), hn && i < NC);
+        MeritIn<SH> mi;
+        merit_rows<SH>(p, b, k, i, mi);
+        merit_knot<SH>(p, k, i, mi, dx, du, dxn, out + (kv ? k : 0), p.N);
+    }
+}
+
+template <int LPL>
+__global__ __launch_bounds__(256) void k_merit_sum(Params p)
+{
+    constexpr int P = 16 * LPL;
+    __shared__ __align__(16) float mer[(GATO_MAX_ALPHA + 1) * P];
+    const int b = blockIdx.x;
+    const float* in = p.mpart + (size_t)b * (p.n_alpha + 1) * p.N;
+    // row j of the values, zero-padded to P leaves; eight loads in flight per thread
+    const int tot = (p.n_alpha + 1) * P;
+    for (int t0 = threadIdx.x; t0 < tot; t0 += 8 * blockDim.x) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int t = t0 + u * blockDim.x, j = t / P, k = t % P;
+            v[u] = (t < tot && k < p.N) ? in[(size_t)j * p.N + k] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (t0 + u * blockDim.x < tot) mer[t0 + u * blockDim.x] = v[u];
+    }
+    __syncthreads();
+    int32_t best;
+    int lsfail;
+    if (merit_select<LPL>(p, b, mer, P, best, lsfail) && threadIdx.x == 0) {
+        p.best[b] = best;
+        if (lsfail) p.flags[b] |= GATO_F_LS_FAILED;
+    }
+}
+
 // Candidate-parallel variant: one workgroup per (solve, step size), each
 // recomputing a knot's step-size-independent products for its own step size
 // (the pages' per-candidate launch, against the fused per-knot evaluation of
@@ -502,6 +558,33 @@ struct Ops {
         }
         return hipGetLastError();
     }
+    // gato_sqp_step's merit with a workspace: a solve's knots spread over
+    // several workgroups when one workgroup per solve would leave the device
+    // short of work (512 workgroups wanted: two resident per CU, no second
+    // round), each taking at least one pass of 1024 / NP knots; else the
+    // one-kernel form.
+    static int merit_split(const Params& p)
+    {
+        const int per_pass = 1024 / SH::NP;
+        const int by_knots = (p.N + per_pass - 1) / per_pass;
+        const int by_batch = 512 / p.B;
+        return std::max(1, std::min(by_knots, by_batch));
+    }
+    static hipError_t merit_ws(const Params& p, hipStream_t st)
+    {
+        const int y = merit_split(p);
+        if (y == 1 || merit_per_candidate() || p.mpart == nullptr) return merit(p, st);
+        hipLaunchKernelGGL((k_merit_knots<SH>), dim3(p.B, y), dim3(1024), 0, st, p);
+        switch (leaves_for(p.N) / 16) {
+            case 4: hipLaunchKernelGGL((k_merit_sum<4>), dim3(p.B), dim3(256), 0, st, p); break;
+            case 8: hipLaunchKernelGGL((k_merit_sum<8>), dim3(p.B), dim3(256), 0, st, p); break;
+            case 16: hipLaunchKernelGGL((k_merit_sum<16>), dim3(p.B), dim3(256), 0, st, p); break;
+            case 32: hipLaunchKernelGGL((k_merit_sum<32>), dim3(p.B), dim3(256), 0, st, p); break;
+            case 64: hipLaunchKernelGGL((k_merit_sum<64>), dim3(p.B), dim3(256), 0, st, p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     static hipError_t direct(const Params& p, hipStream_t st)
     {
         constexpr int SPW = 64 / SH::NP;
@@ -572,7 +655,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // gato_sqp_step's workspace beyond the fused horizons.  Only the direct solves
 // run there, so it holds no Phi^-1.
 struct WsLayout {
-    size_t S, gamma, Qinv, Rinv, direct, total;
+    size_t S, mpart, gamma, Qinv, Rinv, direct, total;
 };
 
 static size_t direct_ws_bytes(const gato_dims_t* d)
@@ -588,6 +671,8 @@ static WsLayout ws_layout(const gato_dims_t* d)
     size_t off = 0;
     w.S = off;
     off += align256(B * N * 3 * n * n * sizeof(float));
+    w.mpart = off;  // the merit's per-knot values
+    off += align256(B * (GATO_MAX_ALPHA + 1) * N * sizeof(float));
     w.gamma = off;
     off += align256(B * N * n * sizeof(float));
     w.Qinv = off;
@@ -823,6 +908,7 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
     if (!fused) {
         char* ws = static_cast<char*>(workspace);
         p.S = reinterpret_cast<float*>(ws + wl.S);
+        p.mpart = reinterpret_cast<float*>(ws + wl.mpart);
         p.gamma = reinterpret_cast<float*>(ws + wl.gamma);
         p.Qinv = reinterpret_cast<float*>(ws + wl.Qinv);
         p.Rinv = reinterpret_cast<float*>(ws + wl.Rinv);
@@ -850,7 +936,7 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
         if ((cr ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
-        if (O::merit(p, stream) != hipSuccess) return GATO_E_HIP;
+        if (O::merit_ws(p, stream) != hipSuccess) return GATO_E_HIP;
         return GATO_OK;
     });
     if (times) {

@@ -29,6 +29,7 @@ struct Params {
     int win_own;  // knots owned by one form workgroup (0: the whole horizon)
     int s_upper_only;  // stage 1 alone: write S's diagonal and upper blocks only (the solve reads no lower block)
     float* dws;   // direct solve: pivot inverses [B][N][n][n], then eliminated right-hand sides [B][N][n]
+    float* mpart;  // merit split over workgroups: per-knot values [B][n_alpha + 1][N]
 };
 
 // The same value in every lane (the reductions below produce identical bits in

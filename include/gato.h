@@ -253,9 +253,12 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *    GATO_LONG_SOLVE=thomas or =cr forces either).
  *    lambda's input is not read, iters and relres are written as 0, and eps
  *    and max_iters are checked but unused.  S (no Phi^-1: the
- *    direct solves do not use it), gamma, Qinv, Rinv and the solve's rows go through `workspace`
+ *    direct solves do not use it), gamma, Qinv, Rinv, the solve's rows and
+ *    the merit's per-knot values go through `workspace`
  *    (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device
- *    memory).
+ *    memory).  With a small batch the merit then spreads a solve's knots over
+ *    several workgroups and sums their values in a second kernel, in the
+ *    same canonical order (identical bits).
  * times (nullable): per-stage device times; when given, the call synchronises.
  */
 int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,

@@ -57,11 +57,12 @@ def test_shapes_and_workspace(lib):
         assert not ops.gato_shape_supported(n, m, N), (n, m, N)
     assert ops.gato_workspace_bytes((14, 7, 64, 128)) == 0          # fused: no workspace
     ws = ops.gato_workspace_bytes((14, 7, 128, 512))
-    # the stage-1 outputs the direct solves read (S, gamma, Qinv, Rinv; no Phi^-1), each
-    # 256-byte aligned, then the larger of the two solves' workspaces
+    # the stage-1 outputs the direct solves read (S, gamma, Qinv, Rinv; no Phi^-1) and the
+    # merit's per-knot values (17 per knot), each 256-byte aligned, then the larger of the
+    # two solves' workspaces
     a = lambda x: (x * 4 + 255) // 256 * 256  # noqa: E731
     B, N = 512, 128
-    stage1 = a(B * N * 3 * 14 * 14) + a(B * N * 14) + a(B * N * 14 * 14) + a(B * (N - 1) * 7 * 7)
+    stage1 = a(B * N * 3 * 14 * 14) + a(B * 17 * N) + a(B * N * 14) + a(B * N * 14 * 14) + a(B * (N - 1) * 7 * 7)
     solve = max(ops.gato_direct_workspace_bytes((14, 7, N, B)), ops.gato_cr_workspace_bytes((14, 7, N, B)))
     assert ws == stage1 + solve
     assert ops.gato_workspace_bytes((13, 7, 64, 128)) == 0          # unsupported -> 0

@@ -182,6 +182,20 @@ def test_merit_bit_identical_across_workgroup_sizes():
     assert runs[0]["flags"][1] & 64  # ORed into the bits already there
 
 
+@pytest.mark.parametrize("cid,B,N", [(3, 4, 300), (3, 64, 128), (5, 8, 100), (4, 2, 1024)])
+def test_step_merit_split_is_bit_identical(cid, B, N):
+    """On horizons beyond the fused path, gato_sqp_step spreads a solve's merit knots
+    over several workgroups when the batch is small; its sums must carry the same bits
+    as gato_merit_eval's one-workgroup-per-solve kernel on the same dz."""
+    _ident("merit split", cid, B, N)
+    bt = _batch(cid, B, N=N)
+    g = gpu_sqp(bt, 1e-6, CAPS[cid])
+    m = gpu_merit(bt, g["dz"], 1.0)
+    for k in ("merit", "merit0", "best"):
+        np.testing.assert_array_equal(g[k], m[k])
+    np.testing.assert_array_equal(g["flags"] & ops.F_LS_FAILED, m["flags"] & ops.F_LS_FAILED)
+
+
 def test_merit_ascent_direction_fails_line_search():
     bt = _batch(2, 2)
     bt["x0"][:] = 0
