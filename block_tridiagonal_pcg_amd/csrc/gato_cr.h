@@ -872,11 +872,13 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
     float ga = ld1(p.gamma, ix.vn(b, a, i), rowi);
     float gn = ld1(p.gamma, ix.vn(b, a + 1, i), rowi);
 
-    // One elimination step on front f; groups with act false (their chunk has
-    // one interior knot fewer) run it with zero multipliers and keep their state.
-    auto step = [&](int f, bool act) {
+    // One elimination step on front f, given U_f (its coupling to f + 1) and
+    // D_{f+1}, gamma_{f+1} as loaded; groups with act false (their chunk has one
+    // interior knot fewer) run it with zero multipliers and keep their state.
+    auto step = [&](int f, bool act, const float* Uf, const float* Dx, float gx) {
         float x[KA];  // [D_f | F' | U_f | gamma_f]
-        ld_row<NC>(p.S, ix.blk(b, f, 2, i), act && rowi, x + 2 * NC);  // coupling f <-> f+1
+#pragma unroll
+        for (int c = 0; c < NC; ++c) x[2 * NC + c] = Uf[c];
         transpose(F, x + NC);
 #pragma unroll
         for (int c = 0; c < NC; ++c) x[c] = Dn[c];
@@ -926,9 +928,6 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
 #pragma unroll
             for (int k = 0; k < NC; ++k) F[k] = act ? (rowi ? 0.0f - r[k] : 0.0f) : F[k];
             // the next front: D_{f+1} -= W2' W2, gamma_{f+1} -= W2' w3
-            float Dx[NC];
-            ld_row<NC>(p.S, ix.blk(b, f + 1, 1, i), act && rowi, Dx);
-            const float gx = ld1(p.gamma, ix.vn(b, f + 1, i), act && rowi);
             acc = mma16_t{};
             mma_abt<NC>(acc, w2, w2);
             mma_rows<NC + 1>(acc, r);
@@ -950,9 +949,6 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
         // the next front (groups that are done keep their last knot's rows)
         transpose(x + 2 * NC, c);
         {
-            float Dx[NC];
-            ld_row<NC>(p.S, ix.blk(b, f + 1, 1, i), act && rowi, Dx);
-            const float gx = ld1(p.gamma, ix.vn(b, f + 1, i), act && rowi);
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
                 c[k] = (act && rowi) ? -c[k] : 0.0f;
@@ -964,12 +960,34 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
         dotb<NP, NC>(gn, Bc<NP>(x[3 * NC]), c);
     };
 
-    // the steps every chunk has, then the one that the longer chunks have in addition
+    // The steps every chunk has, then the one that the longer chunks have in
+    // addition; each step's rows are requested one step ahead, so that their
+    // latency overlaps the previous step's arithmetic.
     const int minint = N / ND_CHUNKS - 2;
-    for (int st = 0; st < minint; ++st) step(a + 1 + st, true);
-    if (maxint > minint) {
-        const bool act = nint > minint;
-        step(act ? a + 1 + minint : a + 1, act);
+    auto fetch = [&](int st, float* U, float* D, float& gv) {  // U_f, D_{f+1}, gamma_{f+1} of step st
+        const bool ok = st < nint && rowi;
+        const int f = ok ? a + 1 + st : a;
+        ld_row<NC>(p.S, ix.blk(b, f, 2, i), ok, U);
+        ld_row<NC>(p.S, ix.blk(b, f + 1, 1, i), ok, D);
+        gv = ld1(p.gamma, ix.vn(b, f + 1, i), ok);
+    };
+    float Uc[NC], Dc[NC], gc;
+    fetch(0, Uc, Dc, gc);
+    for (int st = 0; st < maxint; ++st) {
+        float Un[NC], Dnx[NC], gnx;
+        fetch(st + 1, Un, Dnx, gnx);
+        if (st < minint) {
+            step(a + 1 + st, true, Uc, Dc, gc);
+        } else {
+            const bool act = nint > minint;
+            step(act ? a + 1 + st : a + 1, act, Uc, Dc, gc);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            Uc[c] = Un[c];
+            Dc[c] = Dnx[c];
+        }
+        gc = gnx;
     }
 
     // rows of the boundary system: knot 2g (= a): [- | F | gamma_a | D_a];
