@@ -10,6 +10,9 @@
 //   k_direct      stage 2 by block Thomas elimination, one lane group per solve.
 // Stage 2 by block cyclic reduction (k_cr, k_cr_res) is in gato_cr.hip.
 //   k_merit       stage 3 alone; any workgroup size gives identical bits.
+//   k_merit_knots, k_merit_sum
+//                 the same stage with a solve's knots over several workgroups
+//                 (gato_sqp_step on long horizons with a small batch).
 #include "gato_internal.h"
 #include "gato_stages.h"
 

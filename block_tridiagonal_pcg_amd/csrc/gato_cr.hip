@@ -1,12 +1,13 @@
 // gato_cr.hip -- stage 2 by block cyclic reduction (gato_cr_solve, and the
 // long-horizon solve of gato_sqp_step while its log-depth pays).
 //
-// Kernels (one workgroup per solve):
+// Kernels (one workgroup per solve unless noted):
 //   k_cr_res     every knot of the solve held in registers and LDS (n <= 16, N <= 128).
 //   k_nd_reduce, k_cr_res<VIRT>, k_nd_back
 //                nested dissection for n <= 16, N > 128: chunk interiors eliminated
 //                in order, the chunks' boundary system reduced cyclically, then
-//                the interiors back-substituted.
+//                the interiors back-substituted (the two chunk kernels spread a
+//                solve's chunks over ND_SPLIT workgroups).
 //   k_cr         any horizon and shape, the reduced rows kept in the workspace.
 #include "gato_internal.h"
 #include "gato_cr.h"
