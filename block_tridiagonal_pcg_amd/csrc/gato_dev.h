@@ -32,8 +32,9 @@ struct Shape {
     static constexpr int SLOTS = SLOTS_ ? SLOTS_ : (NP == 16 ? 64 : 16);
     static constexpr int THREADS = SLOTS * NP;
     // Whether the formation's n x n products go to the matrix cores: a
-    // 16x16x1 MFMA step costs as much as ~7 DPP multiply-adds per row.
-    static constexpr bool MMA = NP == 16 && NC_ >= 8;
+    // 16x16x1 MFMA step costs as much as ~7 DPP multiply-adds per row, a
+    // 32x32x1 step as much as ~15 (and 32-lane broadcasts also pay a permlane).
+    static constexpr bool MMA = (NP == 16 && NC_ >= 8) || (NP == 32 && NC_ >= 16);
     static_assert(MC_ <= NC_ || MC_ <= NP, "controls must fit in a knot's lane group");
 };
 
@@ -265,19 +266,36 @@ __device__ __forceinline__ void gemm_rows(float* acc, const BcRow<NP, K>& x, con
     }
 }
 
-// ------------------------------------------------------------------ matrix-core products (NP = 16)
+// ------------------------------------------------------------------ matrix-core products
 
-// A product A B' of the wave's four knots at once on the matrix cores, with A,
-// B and the result all in row layout (lane i of a group holds row i).  One
-// V_MFMA_F32_16X16X1_4B_F32 per k: its four 16x16 blocks are the wave's four
-// lane groups, lane i of a group supplies B[i][k] as the first operand and
-// A[i][k] as the second, and each block accumulates D = B A' with D[a][b] in
-// lane 16*(a/4) + b, register 4*group + a%4.  `mma_rows` then moves tile (lane
-// row q, register quartet g) to (lane row g, quartet q) with two rounds of
-// permlane swaps, which leaves lane b of group g holding column b of D_g, i.e.
-// row b of A B'.  Each output element is its own K-term dot product, so
-// garbage in a padding lane's row only reaches that lane's row and column.
+// A product A B' of a wave's knots at once on the matrix cores, with A, B and
+// the result all in row layout (lane i of a group holds row i).  One MFMA step
+// per k: V_MFMA_F32_16X16X1_4B_F32 for 16-lane groups (four 16x16 blocks, one
+// per group), V_MFMA_F32_32X32X1_2B_F32 for 32-lane groups (two 32x32 blocks).
+// Lane i of a group supplies B[i][k] as the first operand and A[i][k] as the
+// second, so each block accumulates D = B A'.
+//   16 lanes: D[a][b] sits in lane 16*(a/4) + b, register 4*group + a%4.
+//             `mma_rows` moves tile (lane row q, register quartet g) to (lane
+//             row g, quartet q) with two rounds of permlane swaps.
+//   32 lanes: D[a][b] sits in lane 32*((a/4)%2) + b, register
+//             16*group + 4*(a/8) + a%4.  One round of permlane32 swaps brings
+//             each block's other lane half to its own group; a fixed renaming
+//             of registers then gives the columns in order.
+// Either way lane b of group g ends with column b of D_g, i.e. row b of A B'.
+// Each output element is its own dot product, so garbage in a padding lane's
+// row only reaches that lane's row and column.
 typedef float mma16_t __attribute__((ext_vector_type(16)));
+typedef float mma32_t __attribute__((ext_vector_type(32)));
+template <int NP>
+struct MmaAcc {
+    using type = mma16_t;
+};
+template <>
+struct MmaAcc<32> {
+    using type = mma32_t;
+};
+template <int NP>
+using mma_t = typename MmaAcc<NP>::type;
 
 // acc += A B' over columns k < K of the lane's rows a (of A) and b (of B)
 template <int K>
@@ -285,6 +303,13 @@ __device__ __forceinline__ void mma_abt(mma16_t& acc, const float* a, const floa
 {
 #pragma unroll
     for (int k = 0; k < K; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x1f32(b[k], a[k], acc, 0, 0, 0);
+}
+
+template <int K>
+__device__ __forceinline__ void mma_abt(mma32_t& acc, const float* a, const float* b)
+{
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(b[k], a[k], acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ void swap_rows32(float& x, float& y)
@@ -320,6 +345,21 @@ __device__ __forceinline__ void mma_rows(const mma16_t& acc, float* r)
     }
 #pragma unroll
     for (int c = 0; c < NCOL; ++c) r[c] = t[c];
+}
+
+template <int NCOL>
+__device__ __forceinline__ void mma_rows(const mma32_t& acc, float* r)
+{
+    static_assert(NCOL <= 32, "");
+    float t[32];
+#pragma unroll
+    for (int v = 0; v < 32; ++v) t[v] = acc[v];
+    // upper lane half of block 0 <-> lower lane half of block 1
+#pragma unroll
+    for (int v = 0; v < 16; ++v) swap_rows32(t[v], t[v + 16]);
+    // column c: lane half (c/4)%2 of register quartet c/8
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) r[c] = t[(c % 8 < 4) ? 4 * (c / 8) + c % 4 : 16 + 4 * (c / 8) + c % 4];
 }
 
 // ------------------------------------------------------------------ in-place Gauss-Jordan

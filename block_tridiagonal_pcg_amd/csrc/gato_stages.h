@@ -222,7 +222,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
         for (int c = 0; c < MC; ++c) V[c] = 0.0f;
         if constexpr (SH::MMA) {
-            mma16_t acc = {};
+            mma_t<NP> acc = {};
             mma_abt<NC>(acc, ar, qi);  // A_k Q~_k^-1' (Q~_k^-1 is symmetric)
             mma_rows<NC>(acc, W);
         } else {
@@ -232,7 +232,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         }
         gemm_rows<NP, MC, MC>(V, BcRow<NP, MC>(ri), br);
         if constexpr (SH::MMA) {
-            mma16_t acc = {};
+            mma_t<NP> acc = {};
             mma_abt<NC>(acc, ar, W);  // A_k W_k' = A_k Q~_k^-1 A_k'
             mma_abt<MC>(acc, V, br);  // V_k B_k' = B_k R_k^-1 B_k'
             mma_rows<NC>(acc, U);
@@ -342,10 +342,10 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         __syncthreads();
         if constexpr (SH::MMA) {
             // Z = D_k^-1 (O_k D_{k+1}^-1): Y holds the rows of (O_k D_{k+1}^-1)'
-            mma16_t acc = {};
+            mma_t<NP> acc = {};
             mma_abt<NC>(acc, Dn, O);
             mma_rows<NC>(acc, Y);
-            acc = mma16_t{};
+            acc = mma_t<NP>{};
             mma_abt<NC>(acc, di, Y);
             mma_rows<NC>(acc, Z);
         } else {
