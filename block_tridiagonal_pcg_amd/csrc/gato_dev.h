@@ -410,4 +410,51 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
     }
 }
 
+// The same elimination for 32-lane groups with the pivot row passed through
+// LDS instead of DPP: lane J of the group stores its row to the group's buffer
+// `pr` (16-byte aligned, at least K rounded up to 4 floats), and every lane
+// reads it back as float4s.  A 32-lane broadcast by DPP costs a permlane swap
+// and a DPP multiply-add per column; here a step is K/4 stores and loads and K
+// plain multiply-adds.  LDS accesses of one wave complete in order, and a
+// group never spans two waves, so no barrier is needed.  Same arithmetic as
+// gj_steps (the multiply-add a[c] + g * pivot_row[c] for every column).
+template <int K>
+__device__ __forceinline__ void gj_steps_lds(float* a, int lane, bool& bad, float* pr)
+{
+    constexpr int K4 = (K + 3) / 4;
+#pragma unroll
+    for (int J = 0; J < K; ++J) {
+        if (lane == J)
+#pragma unroll
+            for (int q = 0; q < K4; ++q) {
+                float4 v;
+                v.x = a[4 * q];
+                v.y = 4 * q + 1 < K ? a[4 * q + 1] : 0.0f;
+                v.z = 4 * q + 2 < K ? a[4 * q + 2] : 0.0f;
+                v.w = 4 * q + 3 < K ? a[4 * q + 3] : 0.0f;
+                reinterpret_cast<float4*>(pr)[q] = v;
+            }
+        __builtin_amdgcn_wave_barrier();
+        float row[4 * K4];
+#pragma unroll
+        for (int q = 0; q < K4; ++q) {
+            const float4 v = reinterpret_cast<const float4*>(pr)[q];
+            row[4 * q] = v.x;
+            row[4 * q + 1] = v.y;
+            row[4 * q + 2] = v.z;
+            row[4 * q + 3] = v.w;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const float piv = row[J];
+        bad |= !(piv > 0.0f) || !__builtin_isfinite(piv);
+        const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
+        const bool me = lane == J;
+        const float keep = a[J];
+        const float g = me ? (inv - 1.0f) : -(keep * inv);
+#pragma unroll
+        for (int c = 0; c < K; ++c) a[c] = __builtin_fmaf(row[c], g, a[c]);
+        a[J] = me ? inv : -(keep * inv);
+    }
+}
+
 }  // namespace gato

@@ -123,7 +123,18 @@ template <class SH>
 struct FormLds {
     float xw[SH::SLOTS][SH::NP][SH::NC + 1];  // one matrix row per lane (+1: bank spread)
     float xg[SH::SLOTS][SH::NP];
+    alignas(16) float piv[SH::NP == 32 ? SH::SLOTS : 1][(SH::NC + 3) / 4 * 4];  // pivot rows (32-lane groups)
 };
+
+// In-place inverse of the K x K SPD matrix whose row i is held by lane i of
+// group s: DPP broadcasts for 16-lane groups, the group's LDS row buffer for
+// 32-lane ones.
+template <class SH, int K>
+__device__ __forceinline__ void inv_rows(float* a, int i, bool& bad, FormLds<SH>& L, int s)
+{
+    if constexpr (SH::NP == 32) gj_steps_lds<K>(a, i, bad, L.piv[s]);
+    else gj_steps<SH::NP, K>(a, i, bad);
+}
 
 // ... and what it parks, which the fused step keeps for the recovery.
 template <class SH>
@@ -188,7 +199,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
-        gj_steps<NP, NC>(qi, i, badq);
+        inv_rows<SH, NC>(qi, i, badq, L, s);
         badq = lane_bit(__builtin_amdgcn_ballot_w64(badq));
         if (i < NC)
 #pragma unroll
@@ -196,7 +207,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         float ri[MC];
 #pragma unroll
         for (int c = 0; c < MC; ++c) ri[c] = (c == i) ? (urow ? ri0[c] : 1.0f) : ri0[c];
-        gj_steps<NP, MC>(ri, i, badr);
+        inv_rows<SH, MC>(ri, i, badr, L, s);
         badr = lane_bit(__builtin_amdgcn_ballot_w64(badr));
         if (i < MC)
 #pragma unroll
@@ -322,7 +333,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         di[c] = sd[c];
         out.sd[c] = rowv ? sd[c] : 0.0f;
     }
-    gj_steps<NP, NC>(di, i, bads);
+    inv_rows<SH, NC>(di, i, bads, L, s);
     bads = lane_bit(__builtin_amdgcn_ballot_w64(bads));
 #pragma unroll
     for (int c = 0; c < NC; ++c) L.xw[s][i][c] = di[c];
