@@ -78,8 +78,10 @@ def test_form_parity(cid):
     assert np.all(g["Pinv"][:, 0, 0] == 0) and np.all(g["Pinv"][:, -1, 2] == 0)
 
 
-def test_form_flags_match_oracle():
-    bt = _batch(2, 4)
+@pytest.mark.parametrize("cid", [2, 4])  # 16-lane groups (n = 12) and 32-lane groups (n = 24)
+def test_form_flags_match_oracle(cid):
+    _ident("form flags", cid)
+    bt = _batch(cid, 4)
     n = bt["dims"][0]
     bt["Q"][1, 5] = -np.eye(n, dtype=np.float32)
     bt["R"][2, 7] = -np.eye(bt["dims"][1], dtype=np.float32)
