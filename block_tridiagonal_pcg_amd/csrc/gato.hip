@@ -312,8 +312,9 @@ template <class SH>
 __global__ __launch_bounds__(64) void k_direct(Params p)
 {
     constexpr int SPW = 64 / SH::NP;
+    __shared__ __align__(16) float piv[SPW][(SH::NC + 3) / 4 * 4];  // pivot rows (32-lane groups)
     const int b = blockIdx.x * SPW + (int)(threadIdx.x / SH::NP);
-    direct_solve<SH>(p, b, b < p.B);
+    direct_solve<SH>(p, b, b < p.B, piv[threadIdx.x / SH::NP]);
 }
 
 // ------------------------------------------------------------------ stage 3 alone

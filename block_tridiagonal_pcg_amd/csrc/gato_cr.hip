@@ -150,15 +150,17 @@ bool cr_reads_lower(const gato_dims_t* d)
 }
 
 // The long-horizon solve of gato_sqp_step, chosen by a cost model measured on
-// MI355X (knots n = 14): block Thomas walks the knots in order, about 3.0 us
-// per knot whatever the batch until its one lane group per solve fills the
-// chip (about 1.6 ns per knot and solve beyond); cyclic reduction is
-// log-depth but does more arithmetic: about 0.15 us + 1.05 ns per knot per
-// solve with the register-resident kernel (N <= 128, n <= 16), 2.6 ns per knot
-// and solve with the nested dissection (N > 128, n <= 16) and 4.3 ns with the streaming
-// kernel (n > 16), once its batch fills the chip.  Cyclic reduction is taken
-// while its batch time stays below block Thomas's.  GATO_LONG_SOLVE=thomas or
-// =cr forces either (for measurements).
+// MI355X.  Block Thomas walks the knots in order: about 2.7 us per knot
+// whatever the batch (n <= 16; 6.9 us with 32-lane groups, n > 16) until its
+// one lane group per solve fills the chip, about 1.5 ns per knot and solve
+// beyond (5.6 ns for n > 16).  Cyclic reduction is log-depth but does more
+// arithmetic: about 0.15 us + 1.05 ns per knot per solve with the
+// register-resident kernel (N <= 128, n <= 16), 0.17 us + 2.28 ns per knot per
+// solve with the nested dissection (N > 128, n <= 16) and 17 ns per knot and
+// solve with the streaming kernel (n > 16), once its batch fills the chip.
+// Cyclic reduction is taken while its batch time stays below block Thomas's
+// (the n <= 16 constants are from n = 14, the n > 16 ones from n = 24).
+// GATO_LONG_SOLVE=thomas or =cr forces either (for measurements).
 bool cr_preferred(const gato_dims_t* d)
 {
     if (const char* env = std::getenv("GATO_LONG_SOLVE")) {
@@ -167,8 +169,9 @@ bool cr_preferred(const gato_dims_t* d)
     }
     const bool narrow = d->n <= 16 && !cr_streaming_forced();
     const double per_solve_us =
-        narrow ? (d->N <= 2 * ND_CHUNKS ? 0.15 + 0.00105 * d->N : 0.0026 * d->N) : 0.0043 * d->N;
-    const double thomas_us = std::max(3.0 * d->N, 0.0016 * d->N * d->B);
+        narrow ? (d->N <= 2 * ND_CHUNKS ? 0.15 + 0.00105 * d->N : 0.17 + 0.00228 * d->N) : 0.017 * d->N;
+    const bool wide = d->n > 16;  // 32-lane groups
+    const double thomas_us = std::max((wide ? 6.9 : 2.7) * d->N, (wide ? 0.0056 : 0.0015) * d->N * d->B);
     return d->B * per_solve_us < thomas_us;
 }
 

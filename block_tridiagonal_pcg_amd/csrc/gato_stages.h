@@ -737,7 +737,7 @@ __device__ __forceinline__ void recover(int i, bool rowv, bool urow, float lam, 
 // knot's dz is recovered as soon as lambda_k is known.  The next knot's rows
 // are requested before the current knot's arithmetic.
 template <class SH>
-__device__ __forceinline__ void direct_solve(const Params& p, int b, bool bv)
+__device__ __forceinline__ void direct_solve(const Params& p, int b, bool bv, float* pr)
 {
     constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
     const Ix<SH> ix{p.N};
@@ -770,17 +770,28 @@ __device__ __forceinline__ void direct_solve(const Params& p, int b, bool bv)
         const float ngam = ld1(p.gamma, ix.vn(bb, kn, i), nv);
 
         float T[NC], U[NC], H[NC];
+        if constexpr (SH::MMA) {
+            // on the matrix cores, with S_{k-1,k} = S_{k,k-1}' (S is symmetric)
+            mma_t<NP> acc = {};
+            mma_abt<NC>(acc, lo, Hi);  // T = S_{k,k-1} H_{k-1}^-1' (H_{k-1}^-1 symmetric; zero at k = 0)
+            mma_rows<NC>(acc, T);
+            acc = mma_t<NP>{};
+            mma_abt<NC>(acc, T, lo);  // U = T S_{k,k-1}'
+            mma_rows<NC>(acc, U);
+        } else {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) T[c] = U[c] = 0.0f;
-        gemm_rows<NP, NC, NC>(T, BcRow<NP, NC>(Hi), lo);  // T = S_{k,k-1} H_{k-1}^-1 (zero at k = 0)
-        gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(Sp), T);   // U = T S_{k-1,k}
+            for (int c = 0; c < NC; ++c) T[c] = U[c] = 0.0f;
+            gemm_rows<NP, NC, NC>(T, BcRow<NP, NC>(Hi), lo);  // T = S_{k,k-1} H_{k-1}^-1 (zero at k = 0)
+            gemm_rows<NP, NC, NC>(U, BcRow<NP, NC>(Sp), T);   // U = T S_{k-1,k}
+        }
         float tg = 0.0f;
         dotb<NP, NC>(tg, Bc<NP>(gh), T);
         const float gk = gam - tg;
 #pragma unroll
         for (int c = 0; c < NC; ++c) H[c] = (c == i && !rowi) ? 1.0f : dd[c] - U[c];  // identity rows off the problem
         bool bk = false;
-        gj_steps<NP, NC>(H, i, bk);
+        if constexpr (NP == 32) gj_steps_lds<NC>(H, i, bk, pr);
+        else gj_steps<NP, NC>(H, i, bk);
         bad |= bk;
         if (rowi) {
 #pragma unroll
