@@ -120,6 +120,24 @@ def test_pcg_parity(cid):
         assert np.abs(g["iters"] - o["iters"]).max() <= 2
 
 
+@pytest.mark.parametrize("cid,N", [(3, 65), (3, 129), (3, 200), (3, 256), (4, 17), (4, 40), (4, 64)])
+def test_pcg_streamed_horizons(cid, N):
+    """gato_pcg_solve beyond one workgroup's horizon (several knots per lane group, rows
+    re-read per product): up to 256 knots for 16-lane groups and 64 for 32-lane ones,
+    including ragged last chunks."""
+    B = 2
+    _ident("pcg streamed", cid, N, B)
+    bt = _batch(cid, B, N=N)
+    o_form = oracle.form_schur(*synth.inputs(bt))
+    g = gpu_pcg(bt, o_form, 1e-6, 400)
+    o = oracle.pcg_solve(o_form["S"], o_form["Pinv"], o_form["gamma"], o_form["Qinv"], o_form["Rinv"], bt["A"],
+                         bt["Bu"], bt["q"], bt["r"], 1e-6, 400)
+    assert (g["flags"] == 0).all() and (o["flags"] == 0).all()
+    assert (g["relres"] <= 1e-6).all()
+    assert rel_rows(g["dz"], o["dz"]).max() <= 1e-3
+    assert np.abs(g["iters"] - o["iters"]).max() <= 2
+
+
 def test_pcg_warm_start_and_flags():
     bt = _batch(3, 4)
     o_form = oracle.form_schur(*synth.inputs(bt))
