@@ -127,7 +127,8 @@ def input_bytes(n, m, N):
 
 
 def output_bytes(n, m, N, n_alpha):
-    return 4 * (N * n + N * n + (N - 1) * m + n_alpha + 4)
+    """lambda, dz and the merits per solve, plus merit0, best, iters, relres and flags."""
+    return 4 * (N * n + N * n + (N - 1) * m + n_alpha + 5)
 
 
 # ---------------------------------------------------------------- measured traffic
