@@ -119,6 +119,20 @@ __device__ __forceinline__ void tri_upper_solve(const float* ct, float v, float 
     }
 }
 
+// Forward substitution C x = v with the same factor, lane i holding row i of C
+// (column i of C': cl[c] = C'[c][i], zero for c > i) and v_i; on return x
+// holds x_i.  Runs from the first row down, one broadcast per row.
+template <int NP, int NC, int P = 0>
+__device__ __forceinline__ void tri_lower_solve(const float* cl, float v, float dinv, int lane, float& x)
+{
+    if constexpr (P < NC) {
+        const float xp = bcast<NP, P>(v * dinv);
+        if (lane == P) x = xp;
+        v = lane > P ? fmaf(-cl[P], xp, v) : v;
+        tri_lower_solve<NP, NC, P + 1>(cl, v, dinv, lane, x);
+    }
+}
+
 // The recovery of knot k's dz (recover(), the back substitution of the Schur
 // solve) from lambda_k and lambda_{k+1} in lane i's row, with the knot's rows of
 // Q~^-1, S_{k,k+1}, R^-1 and r, q and column i of B_k read here; ok false masks
@@ -451,10 +465,13 @@ __host__ __device__ constexpr int cr_group_even(int g, int M)
 // (2 * ND_CHUNKS of them); that system is reduced cyclically by the
 // register-resident kernel in its "virtual" mode; the interior knots are then
 // back-substituted chunk by chunk (k_nd_back).  Workspace, in floats:
-//   [B][N][n][W]     factor rows [W1 | W2 | w3 | C'] of the interior knots
+//   [B][N][FW]       the factor of each interior knot: rows [W1 | w3] (n x R1),
+//                    then C' packed by rows from the diagonal on (TRI)
 //   [B][2C][n][W]    rows [L | U | gamma | D] of the boundary system
 //   [B][C][n][16]    C' rows of the boundary system's odd knots
-// (C = ND_CHUNKS, W = CrRow<SH>::W).
+// (C = ND_CHUNKS, W = CrRow<SH>::W).  W2 = C^-1 U_f is not kept: the back
+// substitution applies C^-1 to U_f lambda_{f+1}, with U_f read from S again,
+// which costs one more triangular solve and saves a third of the factor's bytes.
 constexpr int ND_CHUNKS = 64;
 // The chunk kernels spread one solve's chunks over ND_SPLIT workgroups of
 // ND_GPW lane groups each: a batch that holds one solve per CU in the other
@@ -475,20 +492,28 @@ __host__ __device__ constexpr int nd_real(int v, int N)
     return (v & 1) ? nd_start(v / 2 + 1, N) - 1 : nd_start(v / 2, N);
 }
 
+// Floats of one interior knot's factor: n rows [W1 | w3] of R1 = round4(n + 1),
+// then the n (n + 1) / 2 entries of C' on and right of its diagonal, row after
+// row (row i from offset nd_tri_off(i, n)), padded to a float4.
+__host__ __device__ constexpr int nd_r1(int n) { return (n + 1 + 3) / 4 * 4; }
+__host__ __device__ constexpr int nd_tri_off(int i, int n) { return i * n - i * (i - 1) / 2; }
+__host__ __device__ constexpr int nd_fac_floats(int n) { return n * nd_r1(n) + (n * (n + 1) / 2 + 3) / 4 * 4; }
+
 template <class SH>
 struct NdWs {
-    static constexpr int NC = SH::NC, W = CrRow<SH>::W;
+    static constexpr int NC = SH::NC, W = CrRow<SH>::W, R1 = nd_r1(NC), FW = nd_fac_floats(NC);
     size_t B, N;
-    __host__ __device__ size_t fac(size_t b, size_t k, size_t i) const { return ((b * N + k) * NC + i) * W; }
+    __host__ __device__ size_t fac(size_t b, size_t k, size_t i) const { return (b * N + k) * FW + i * R1; }
+    __host__ __device__ size_t tri(size_t b, size_t k) const { return (b * N + k) * FW + NC * R1; }
     __host__ __device__ size_t vrow(size_t b, size_t v, size_t i) const
     {
-        return B * N * NC * W + ((b * 2 * ND_CHUNKS + v) * NC + i) * W;
+        return B * N * FW + ((b * 2 * ND_CHUNKS + v) * NC + i) * W;
     }
     __host__ __device__ size_t oc(size_t b, size_t g, size_t i) const
     {
-        return B * (N + 2 * ND_CHUNKS) * NC * W + ((b * ND_CHUNKS + g) * NC + i) * 16;
+        return B * (N * FW + 2 * ND_CHUNKS * NC * W) + ((b * ND_CHUNKS + g) * NC + i) * 16;
     }
-    __host__ __device__ size_t floats() const { return B * (N + 2 * ND_CHUNKS) * NC * W + B * ND_CHUNKS * NC * 16; }
+    __host__ __device__ size_t floats() const { return B * (N * FW + 2 * ND_CHUNKS * NC * W) + B * ND_CHUNKS * NC * 16; }
 };
 
 template <class SH>
@@ -884,18 +909,17 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
         for (int c = 0; c < NC; ++c) x[c] = Dn[c];
         x[3 * NC] = gn;
         chol_solve<NP, NC, KA>(x, i, bad, act);
-        if (act && rowi) {
-            float r[W];
+        if (act && rowi) {  // the factor: row i of [W1 | w3], then row i of C' from its diagonal on
+            constexpr int R1 = NdWs<SH>::R1;
+            float r[R1];
 #pragma unroll
-            for (int c = 0; c < W; ++c) r[c] = 0.0f;
+            for (int c = 0; c < R1; ++c) r[c] = c < NC ? x[NC + c] : 0.0f;
+            r[NC] = x[3 * NC];
+            st4<R1>(p.dws, nw.fac(b, f, i), r);
+            float* ct = p.dws + nw.tri(b, f) + (nd_tri_off(i, NC) - i);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                r[RW::L + c] = x[NC + c];
-                r[RW::U + c] = x[2 * NC + c];
-                r[RW::D + c] = x[c];
-            }
-            r[RW::G] = x[3 * NC];
-            st4<W>(p.dws, nw.fac(b, f, i), r);
+            for (int c = 0; c < NC; ++c)
+                if (c >= i) ct[c] = x[c];
         }
         if constexpr (SH::MMA && NC < 16) {
             // (columns)' (columns) on the matrix cores: lane c holds column c
@@ -1022,14 +1046,13 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
 
 // Back substitution of every chunk's interior knots (the chunk's first and last
 // knots have lambda from the boundary system), last interior knot first:
-//   lambda_f = C_f'^-1 (w3_f - W1_f lambda_a - W2_f lambda_{f+1}),
+//   lambda_f = C_f'^-1 (w3_f - W1_f lambda_a - C_f^-1 U_f lambda_{f+1}),
 // then the recovery of dz for every knot, spread over the lane groups.
 template <class SH>
 __device__ __forceinline__ void nd_back(const Params& p, int b)
 {
     constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
-    using RW = CrRow<SH>;
-    constexpr int W = RW::W;
+    constexpr int R1 = NdWs<SH>::R1;
     __shared__ int wg_flags;
     const Ix<SH> ix{p.N};
     const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
@@ -1038,38 +1061,61 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
     const int gl = threadIdx.x / NP;
     const int g = blockIdx.y * ND_GPW + gl;  // chunk
     const bool rowi = i < NC;
+    const int ii = rowi ? i : 0;
     const int a = nd_start(g, N), bk = nd_start(g + 1, N) - 1;
     const int maxsz = (N + ND_CHUNKS - 1) / ND_CHUNKS;
     if (threadIdx.x == 0) wg_flags = 0;
     bool nonfinite = false;
 
-    // interior lambdas, last interior knot first, the next factor row requested
-    // before this one's arithmetic
+    // What lane i needs of interior knot k: row i of [W1 | w3], row i of C' and
+    // column i of C' (both from the packed triangle, zero off it), and row i of
+    // U_k = S_{k,k+1}.  ok false reads zeros; k must still be a knot of the
+    // solve, and every index stays inside that knot's factor.
+    struct Fac {
+        float w[R1], row[NC], col[NC], u[NC];
+    };
+    auto fetch = [&](int k, bool ok, Fac& f) {
+        ld4<R1>(p.dws, nw.fac(b, k, ii), ok, f.w);
+        const float* t = p.dws + nw.tri(b, k);
+        const float* tr = t + (nd_tri_off(ii, NC) - ii);  // C'[i][c] at tr[c] for c >= i
+        const float* tc = t + ii;                         // C'[c][i] at tc[off(c) - c] for c <= i
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            f.row[c] = (ok && c >= i) ? tr[c] : 0.0f;
+            f.col[c] = (ok && c <= i) ? tc[nd_tri_off(c, NC) - c] : 0.0f;
+        }
+        ld_row<NC>(p.S, ix.blk(b, k, 2, ii), ok, f.u);
+    };
+
+    // interior lambdas, last interior knot first, the next knot's factor
+    // requested before this one's arithmetic
     const float la = ld1(p.lambda, ix.vn(b, a, i), rowi);
     float lamn = ld1(p.lambda, ix.vn(b, bk, i), rowi);  // lambda of the knot after the front
     const int maxint = maxsz - 2;
-    float cur[W];
-    ld4<W>(p.dws, nw.fac(b, bk - 1 > a ? bk - 1 : a, i), rowi && bk - 1 > a, cur);
+    Fac cur;
+    fetch(bk - 1 > a ? bk - 1 : a, rowi && bk - 1 > a, cur);
     for (int st = 0; st < maxint; ++st) {
         const int k = bk - 1 - st;
         const bool act = k > a;
         if (__builtin_amdgcn_ballot_w64(act) == 0) continue;
-        float nxt[W];
-        ld4<W>(p.dws, nw.fac(b, k - 1 > a ? k - 1 : a, i), rowi && k - 1 > a, nxt);
-        float acc = 0.0f;
-        dotb<NP, NC>(acc, Bc<NP>(la), cur + RW::L);
-        dotb<NP, NC>(acc, Bc<NP>(lamn), cur + RW::U);
+        Fac nxt;
+        fetch(k - 1 > a ? k - 1 : a, rowi && k - 1 > a, nxt);
+        float v = 0.0f;  // W1 lambda_a
+        dotb<NP, NC>(v, Bc<NP>(la), cur.w);
+        float u = 0.0f;  // U_k lambda_{k+1}
+        dotb<NP, NC>(u, Bc<NP>(lamn), cur.u);
         float dg = 1.0f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) dg = c == i ? cur[RW::D + c] : dg;
+        for (int c = 0; c < NC; ++c) dg = c == i ? cur.row[c] : dg;
+        const float dinv = __builtin_amdgcn_rcpf((act && rowi) ? dg : 1.0f);
+        float y = 0.0f;  // C^-1 U_k lambda_{k+1}, the W2 term
+        tri_lower_solve<NP, NC>(cur.col, u, dinv, i, y);
         float lin = 0.0f;
-        tri_upper_solve<NP, NC>(cur + RW::D, cur[RW::G] - acc, __builtin_amdgcn_rcpf((act && rowi) ? dg : 1.0f), i,
-                                lin);
+        tri_upper_solve<NP, NC>(cur.row, cur.w[NC] - v - y, dinv, i, lin);
         nonfinite |= act && rowi && !__builtin_isfinite(lin);
         if (act && rowi) p.lambda[ix.vn(b, k, i)] = lin;
         lamn = act ? lin : lamn;
-#pragma unroll
-        for (int c = 0; c < W; ++c) cur[c] = nxt[c];
+        cur = nxt;
     }
     __syncthreads();  // every lambda of this workgroup's chunks is written
 

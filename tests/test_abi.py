@@ -115,9 +115,14 @@ def test_validation_happens_before_any_launch(lib):
     # cyclic reduction: the same host checks
     cr = lib.gato_cr_solve
     need = lib.gato_cr_workspace_bytes(ctypes.byref(d))
-    # B=2 N=64 n=14: rows of 44 floats for the N knots and the 128 boundary knots of the
-    # nested dissection, plus that system's parked rows of 16 floats (64 per solve)
-    assert need == ((2 * ((64 + 128) * 14 * 44 + 64 * 14 * 16) * 4 + 255) // 256) * 256
+    # B=2 N=64 n=14: the nested dissection's interior factors (14 rows [W1 | w3] of 16
+    # floats and C''s 105-entry upper triangle, padded to 108, per knot), rows of 44
+    # floats for the 128 boundary knots and that system's parked rows of 16 floats (64
+    # per solve); more than the streaming kernel's 44-float rows for the N knots
+    assert need == ((2 * (64 * (14 * 16 + 108) + 128 * 14 * 44 + 64 * 14 * 16) * 4 + 255) // 256) * 256
+    # N=1024 B=1: the streaming kernel's rows, 44 floats per knot row, are the larger layout
+    long = lib.gato_cr_workspace_bytes(ctypes.byref(ops.Dims(14, 7, 1024, 1)))
+    assert long == ((1024 * 14 * 44 * 4 + 255) // 256) * 256
     assert cr(ctypes.byref(d), *P[:10], None, ctypes.c_size_t(need), None) == ops.E_WORKSPACE
     assert cr(ctypes.byref(d), *P[:10], ws, ctypes.c_size_t(need - 1), None) == ops.E_WORKSPACE
     assert cr(ctypes.byref(d), *P[:10], ctypes.c_void_p((1 << 20) + 4), ctypes.c_size_t(need), None) == ops.E_ALIGN
@@ -173,7 +178,7 @@ def test_cyclic_reduction_depth_matches_the_plan(lib):
 
 def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
     """Fused PCG where a workgroup holds the horizon; beyond, cyclic reduction while
-    its batch time (0.15 us + 1.05 ns per knot per solve resident, 0.17 us + 2.28 ns per
+    its batch time (0.15 us + 1.05 ns per knot per solve resident, 0.25 us + 1.9 ns per
     knot per solve with the nested dissection, 17 ns per knot and solve streaming for
     n > 16) stays below block Thomas's (2.7 us per knot, or 1.5 ns per knot and solve once
     the batch fills the chip; 6.9 us and 5.6 ns for n > 16)."""
