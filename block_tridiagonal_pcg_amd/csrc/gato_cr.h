@@ -133,30 +133,59 @@ __device__ __forceinline__ void tri_lower_solve(const float* cl, float v, float 
     }
 }
 
-// The recovery of knot k's dz (recover(), the back substitution of the Schur
-// solve) from lambda_k and lambda_{k+1} in lane i's row, with the knot's rows of
-// Q~^-1, S_{k,k+1}, R^-1 and r, q and column i of B_k read here; ok false masks
-// the loads and the stores (k must still be a knot of the horizon).
+// What lane i reads for the recovery of knot k's dz besides its row of
+// S_{k,k+1}: its rows of Q~^-1 and R^-1, column i of B_k, q_i and r_i.  ok
+// false reads zeros (k must still be a knot of the horizon).
 template <class SH>
-__device__ __forceinline__ void recover_knot(const Params& p, int b, int k, int i, bool ok, float lam, float lamn)
+struct RecRows {
+    float qi[SH::NC], ri[SH::MC], bc[SH::NC], qv, rv;
+};
+
+template <class SH>
+__device__ __forceinline__ void rec_load(const Params& p, int b, int k, int i, bool ok, RecRows<SH>& r)
+{
+    constexpr int NC = SH::NC, MC = SH::MC;
+    const Ix<SH> ix{p.N};
+    const bool rowv = ok && i < NC;
+    const bool urow = ok && k < p.N - 1 && i < MC;
+    ld_row<NC>(p.Qinv, ix.Q(b, k, i), rowv, r.qi);
+    ld_row<MC>(p.Rinv, ix.R(b, k, i), urow, r.ri);
+    ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, r.bc);  // column i of B_k
+    r.qv = ld1(p.q, ix.vn(b, k, i), rowv);
+    r.rv = ld1(p.r, ix.vm(b, k, i), urow);
+}
+
+// The recovery of knot k's dz (recover(), the back substitution of the Schur
+// solve) from lambda_k and lambda_{k+1} in lane i's row, given the rows
+// rec_load read and lane i's row of S_{k,k+1} (sup); ok false masks the stores.
+template <class SH>
+__device__ __forceinline__ void rec_store(const Params& p, int b, int k, int i, bool ok, const RecRows<SH>& r,
+                                          const float* sup, float lam, float lamn)
 {
     constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
     const Ix<SH> ix{p.N};
     const bool rowv = ok && i < NC;
     const bool urow = ok && k < p.N - 1 && i < MC;
-    float qi[NC], sup[NC], ri[MC], bc[NC];
-    ld_row<NC>(p.Qinv, ix.Q(b, k, i), rowv, qi);
-    ld_row<NC>(p.S, ix.blk(b, k, 2, i), rowv, sup);
-    ld_row<MC>(p.Rinv, ix.R(b, k, i), urow, ri);
-    ld_row<NC, MC>(p.Bu, ix.Bu(b, k, 0) + i, urow, bc);  // column i of B_k
-    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
-    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
     float h = 0.0f;  // (Q~_k^-1 q_k)_i, as the formation forms it
-    dotb<NP, NC>(h, Bc<NP>(qv), qi);
+    dotb<NP, NC>(h, Bc<NP>(r.qv), r.qi);
     float dx, du;
-    recover<SH>(i, rowv, urow, rowv ? lam : 0.0f, lamn, qi, sup, h, bc, rv, ri, dx, du);
+    recover<SH>(i, rowv, urow, rowv ? lam : 0.0f, lamn, r.qi, sup, h, r.bc, r.rv, r.ri, dx, du);
     if (rowv) p.dz[ix.dx(b, k, i)] = dx;
     if (urow) p.dz[ix.du(b, k, i)] = du;
+}
+
+// Both together, with the row of S_{k,k+1} read here too; ok false masks the
+// loads and the stores.
+template <class SH>
+__device__ __forceinline__ void recover_knot(const Params& p, int b, int k, int i, bool ok, float lam, float lamn)
+{
+    constexpr int NC = SH::NC;
+    const Ix<SH> ix{p.N};
+    RecRows<SH> r;
+    rec_load<SH>(p, b, k, i, ok, r);
+    float sup[NC];
+    ld_row<NC>(p.S, ix.blk(b, k, 2, i), ok && i < NC, sup);
+    rec_store<SH>(p, b, k, i, ok, r, sup, lam, lamn);
 }
 
 // One knot's row of the reduced system in the workspace, padded to whole
@@ -1047,32 +1076,35 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
 // Back substitution of every chunk's interior knots (the chunk's first and last
 // knots have lambda from the boundary system), last interior knot first:
 //   lambda_f = C_f'^-1 (w3_f - W1_f lambda_a - C_f^-1 U_f lambda_{f+1}),
-// then the recovery of dz for every knot, spread over the lane groups.
+// with the recovery of dz for every knot of the chunk by the same lane group:
+// the last knot first, then each interior knot as soon as its lambda is known
+// (U_f = S_{f,f+1} is then still in registers), the first knot last.
 template <class SH>
 __device__ __forceinline__ void nd_back(const Params& p, int b)
 {
-    constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
+    constexpr int NP = SH::NP, NC = SH::NC;
     constexpr int R1 = NdWs<SH>::R1;
     __shared__ int wg_flags;
     const Ix<SH> ix{p.N};
     const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
     const int N = p.N;
     const int i = threadIdx.x % NP;
-    const int gl = threadIdx.x / NP;
-    const int g = blockIdx.y * ND_GPW + gl;  // chunk
+    const int g = blockIdx.y * ND_GPW + threadIdx.x / NP;  // chunk
     const bool rowi = i < NC;
     const int ii = rowi ? i : 0;
     const int a = nd_start(g, N), bk = nd_start(g + 1, N) - 1;
-    const int maxsz = (N + ND_CHUNKS - 1) / ND_CHUNKS;
+    const int maxint = (N + ND_CHUNKS - 1) / ND_CHUNKS - 2;
     if (threadIdx.x == 0) wg_flags = 0;
     bool nonfinite = false;
 
     // What lane i needs of interior knot k: row i of [W1 | w3], row i of C' and
-    // column i of C' (both from the packed triangle, zero off it), and row i of
-    // U_k = S_{k,k+1}.  ok false reads zeros; k must still be a knot of the
-    // solve, and every index stays inside that knot's factor.
+    // column i of C' (both from the packed triangle, zero off it), row i of
+    // U_k = S_{k,k+1}, and the rest of the knot's recovery rows.  ok false
+    // reads zeros; k must still be a knot of the solve, and every index stays
+    // inside that knot's factor.
     struct Fac {
         float w[R1], row[NC], col[NC], u[NC];
+        RecRows<SH> rec;
     };
     auto fetch = [&](int k, bool ok, Fac& f) {
         ld4<R1>(p.dws, nw.fac(b, k, ii), ok, f.w);
@@ -1085,15 +1117,18 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
             f.col[c] = (ok && c <= i) ? tc[nd_tri_off(c, NC) - c] : 0.0f;
         }
         ld_row<NC>(p.S, ix.blk(b, k, 2, ii), ok, f.u);
+        rec_load<SH>(p, b, k, i, ok, f.rec);
     };
 
-    // interior lambdas, last interior knot first, the next knot's factor
-    // requested before this one's arithmetic
     const float la = ld1(p.lambda, ix.vn(b, a, i), rowi);
     float lamn = ld1(p.lambda, ix.vn(b, bk, i), rowi);  // lambda of the knot after the front
-    const int maxint = maxsz - 2;
     Fac cur;
     fetch(bk - 1 > a ? bk - 1 : a, rowi && bk - 1 > a, cur);
+    {
+        // the chunk's last knot: lambda_{bk+1} is the next chunk's first knot's
+        const float lnx = ld1(p.lambda, ix.vn(b, bk + 1 < N ? bk + 1 : bk, i), rowi && bk + 1 < N);
+        recover_knot<SH>(p, b, bk, i, true, lamn, lnx);
+    }
     for (int st = 0; st < maxint; ++st) {
         const int k = bk - 1 - st;
         const bool act = k > a;
@@ -1114,25 +1149,11 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
         tri_upper_solve<NP, NC>(cur.row, cur.w[NC] - v - y, dinv, i, lin);
         nonfinite |= act && rowi && !__builtin_isfinite(lin);
         if (act && rowi) p.lambda[ix.vn(b, k, i)] = lin;
+        rec_store<SH>(p, b, k, i, act, cur.rec, cur.u, lin, lamn);
         lamn = act ? lin : lamn;
         cur = nxt;
     }
-    __syncthreads();  // every lambda of this workgroup's chunks is written
-
-    // recovery of dz for the knots of this workgroup's chunks, spread over its
-    // lane groups (the knot after the last one starts the next chunk, whose
-    // lambda came from the boundary system)
-    const int k0 = nd_start(blockIdx.y * ND_GPW, N), k1 = nd_start((blockIdx.y + 1) * ND_GPW, N);
-    for (int t0 = k0; t0 < k1; t0 += ND_GPW) {
-        const int k = t0 + gl;
-        const bool ok = k < k1;
-        if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
-        const int kk = ok ? k : 0;
-        const bool rowv = ok && rowi;
-        const float lam = ld1(p.lambda, ix.vn(b, kk, i), rowv);
-        const float lamk = ld1(p.lambda, ix.vn(b, kk + 1 < N ? kk + 1 : kk, i), rowv && kk + 1 < N);
-        recover_knot<SH>(p, b, kk, i, ok, lam, lamk);
-    }
+    recover_knot<SH>(p, b, a, i, true, la, lamn);  // the chunk's first knot
     if (nonfinite) atomicOr(&wg_flags, GATO_F_NONFINITE);
     __syncthreads();
     if (threadIdx.x == 0 && wg_flags) atomicOr(p.flags + b, wg_flags);

@@ -178,7 +178,7 @@ def test_cyclic_reduction_depth_matches_the_plan(lib):
 
 def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
     """Fused PCG where a workgroup holds the horizon; beyond, cyclic reduction while
-    its batch time (0.15 us + 1.05 ns per knot per solve resident, 0.25 us + 1.9 ns per
+    its batch time (0.15 us + 1.05 ns per knot per solve resident, 0.28 us + 1.8 ns per
     knot per solve with the nested dissection, 17 ns per knot and solve streaming for
     n > 16) stays below block Thomas's (2.7 us per knot, or 1.5 ns per knot and solve once
     the batch fills the chip; 6.9 us and 5.6 ns for n > 16)."""
