@@ -881,7 +881,7 @@ struct NdLds {
 // C^-1 U_f, w3 = C^-1 gamma_f) updates
 //   D_a -= W1'W1, gamma_a -= W1'w3, F <- -W1'W2 (now the coupling a <-> f+1),
 //   D_{f+1} -= W2'W2, gamma_{f+1} -= W2'w3.
-// Each front's factor row goes to the workspace for the back substitution.
+// Each front's factor (W1, w3 and C') goes to the workspace for the back substitution.
 // Afterwards the chunk's first and last knots, with F between them and S's own
 // coupling to the next chunk, are rows of the boundary system.  Transposes go
 // through the group's own LDS tile (no barrier: the tile belongs to one wave).
