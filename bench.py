@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=128)
     ap.add_argument("--horizon", type=int, default=None, help="override the configuration's N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--refine", choices=("auto", "on", "off"), default="auto",
+                    help="one pass of KKT iterative refinement after a direct solve (GATO_REFINE); "
+                         "auto: on for the ill-conditioned workload 5")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-copy", action="store_true")
     ap.add_argument("--merit-variants", action="store_true",
@@ -184,7 +187,7 @@ def cpu_baseline(batch, n_alpha, seconds):
     cap = CAPS[batch["cid"]]
     args = [batch[f] for f in ("Q", "q", "R", "r", "A", "Bu", "e", "x0")]
     t0 = time.perf_counter()
-    oracle.sqp_step(*args, None, EPS, cap, al, MU)
+    first = oracle.sqp_step(*args, None, EPS, cap, al, MU)
     one = time.perf_counter() - t0
     reps = max(1, min(5000, int(math.ceil(seconds / max(one, 1e-6)))))
     t0 = time.perf_counter()
@@ -194,7 +197,38 @@ def cpu_baseline(batch, n_alpha, seconds):
     B = batch["dims"][3]
     return {"value": B * reps / wall, "unit": "solves/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "the full %d-solve batch of the timed workload, %d repeats (%.1f s wall), fp64, "
-                      "OpenMP over solves" % (B, reps, wall)}
+                      "OpenMP over solves" % (B, reps, wall)}, first
+
+
+def iters_summary(x):
+    import numpy as np
+
+    return {"min": int(x.min()), "median": float(np.median(x)), "max": int(x.max())}
+
+
+def exact_step(batch, n_alpha):
+    """The oracle's exact step on the batch: lambda by block Cholesky of S, then dz and
+    the merits (the reference for the direct solves)."""
+    import numpy as np
+
+    import oracle
+
+    ins = [batch[f] for f in ("Q", "q", "R", "r", "A", "Bu", "e", "x0")]
+    al = np.array([2.0 ** -i for i in range(n_alpha)])
+    form = oracle.form_schur(*ins)
+    lam = oracle.direct_solve(form["S"], form["gamma"])["lam"]
+    dz = oracle.recover(form["Qinv"], form["Rinv"], batch["A"], batch["Bu"], batch["q"], batch["r"], lam)
+    mer = oracle.merit_eval(*ins, dz, al, MU)
+    return {"dz": dz, "merit": mer["merit"], "best": mer["best"]}
+
+
+def rel_err_rows(g, o):
+    """Per-solve relative 2-norm error of g against o (rows = solves)."""
+    import numpy as np
+
+    g = np.asarray(g, dtype=np.float64).reshape(len(o), -1)
+    o = np.asarray(o, dtype=np.float64).reshape(len(o), -1)
+    return np.linalg.norm(g - o, axis=1) / np.maximum(np.linalg.norm(o, axis=1), 1e-300)
 
 
 # ---------------------------------------------------------------- merit launch variants
@@ -427,6 +461,11 @@ def main():
         solver_sweep(a)
         return
     torch.cuda.set_device(0)
+    refine = a.refine == "on" or (a.refine == "auto" and a.config == 5)
+    if refine:
+        os.environ["GATO_REFINE"] = "1"
+    else:
+        os.environ.pop("GATO_REFINE", None)
     cfg = synth.CONFIGS[a.config]
     batch = synth.make_batch(a.config, a.batch, N=a.horizon)
     batch["cid"] = a.config
@@ -515,7 +554,38 @@ def main():
         torch.cuda.synchronize()
         kernel_us = e0.elapsed_time(e1) * 1e3 / a.steps
         achieved_tflops = solve_flops / (kernel_us * 1e-6) / 1e12
-        del st1, sw
+        # the same formed system by PCG (gato_pcg_solve), for its iteration counts: the
+        # step itself takes the direct solve at this horizon
+        pst = ops.alloc_outputs(dims, n_alpha)
+        pcg_us, pcg_iters, pcg_dz = [], None, None
+        try:
+            for _ in range(3):
+                pst["lam"].zero_()
+                e0.record(stream)
+                ops.gato_pcg_solve(dims, st1["S"], st1["Pinv"], st1["gamma"], st1["Qinv"], st1["Rinv"], dev["Bu"],
+                                   dev["q"], dev["r"], EPS, cap, pst["lam"], pst["dz"], pst["iters"], pst["relres"],
+                                   pst["flags"], stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                pcg_us.append(e0.elapsed_time(e1) * 1e3)
+        except ops.GatoError as err:
+            pcg_alongside = {"note": "gato_pcg_solve does not hold this horizon (%s)" % err}
+        else:
+            pcg_iters = pst["iters"].cpu().numpy()
+            pcg_dz = pst["dz"].cpu().numpy()
+            at_cap = (pst["flags"].cpu().numpy() & ops.F_PCG_MAXITER) != 0
+            relres = pst["relres"].cpu().numpy()
+            pcg_alongside = {
+                "note": "stage 2 of the same formed system by gato_pcg_solve (cold start, eps and cap as the "
+                        "step's); the step itself takes the direct solve",
+                "iters": iters_summary(pcg_iters),
+                "at_cap": int(at_cap.sum()),
+                "relres_at_cap_max": float(relres[at_cap].max()) if at_cap.any() else None,
+                "us_per_call": float(np.median(pcg_us)),
+            }
+        del st1, sw, pst
+    if fused:
+        pcg_iters, pcg_alongside, pcg_dz = iters, None, None
     pcg_bytes = float(iters.sum()) * pcg_iter_bytes(n, N)
     pcg_equiv_gbps = pcg_bytes / (stage_us["linsys_us"] * 1e-6) / 1e9 if fused and stage_us["linsys_us"] > 0 else None
 
@@ -535,8 +605,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "n": n, "m": m, "N": N, "B": B, "eps": EPS, "max_iters": cap,
                    "n_alpha": n_alpha, "mu": MU, "lambda0": "zero (cold start: a zeroed buffer per step)",
-                   "path": "fused single kernel" if fused else "form + %s + merit" % (
-                       "block cyclic reduction" if solver == ops.SOLVER_CR else "block Thomas solve")},
+                   "path": "fused single kernel" if fused else "form + %s%s + merit" % (
+                       "block cyclic reduction" if solver == ops.SOLVER_CR else "block Thomas solve",
+                       " + one KKT refinement pass" if refine else "")},
         "roofline": {
             "bound": "alu",
             "kernel": kernel,
@@ -549,7 +620,8 @@ def main():
             "launch_avg_us": kernel_us,
             "step_launch_avg_us": kern_avg_s * 1e6,
         },
-        "pcg_iters": {"min": int(iters.min()), "median": float(np.median(iters)), "max": int(iters.max())},
+        "pcg_iters": iters_summary(iters),
+        "pcg_alongside": pcg_alongside,
         "stage_us_unfused": stage_us,
         "pcg_hbm_equivalent": {
             "algorithmic_bytes": pcg_bytes,
@@ -561,8 +633,35 @@ def main():
         "source_sha": source_digest(),
     }
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(batch, n_alpha, a.cpu_seconds)
+        rec["cpu_baseline"], o_step = cpu_baseline(batch, n_alpha, a.cpu_seconds)
         rec["cpu_baseline"]["gpu_over_cpu"] = value / rec["cpu_baseline"]["value"]
+        o_iters = o_step["iters"]
+        # the timed step's outputs (every step runs the same cold-started batch) against the
+        # oracle's on the whole batch: its PCG step where the step runs PCG, else its exact
+        # step (block Cholesky of S, then the recovery and the merits)
+        if fused:
+            ref, ref_name = o_step, "oracle step (fp64 PCG, same eps and cap)"
+        else:
+            ref, ref_name = exact_step(batch, n_alpha), "oracle exact step (fp64 block Cholesky of S)"
+        dz_err = rel_err_rows(out["dz"].cpu().numpy(), ref["dz"])
+        m_err = rel_err_rows(out["merit"].cpu().numpy().reshape(B * n_alpha, 1), ref["merit"].reshape(-1, 1))
+        rec["parity_vs_oracle"] = {
+            "reference": ref_name, "solves": B, "bar": {"dz_rel": 1e-3, "merit_rel": 1e-4},
+            "dz_rel_err": {"median": float(np.median(dz_err)), "max": float(dz_err.max())},
+            "merit_rel_err_max": float(m_err.max()),
+            "best_equal": int((out["best"].cpu().numpy() == ref["best"]).sum()),
+        }
+        if pcg_iters is not None:
+            # PCG iterations per solve, GPU (fp32) against the oracle (fp64), same solves
+            ratio = pcg_iters / np.maximum(o_iters, 1)
+            rec["pcg_iters_vs_oracle"] = {
+                "gpu": iters_summary(pcg_iters), "oracle": iters_summary(o_iters),
+                "gpu_over_oracle": {"min": float(ratio.min()), "median": float(np.median(ratio)),
+                                    "max": float(ratio.max())},
+                "max_abs_diff": int(np.abs(pcg_iters.astype(np.int64) - o_iters).max())}
+            if pcg_dz is not None:
+                e = rel_err_rows(pcg_dz, o_step["dz"])
+                rec["pcg_iters_vs_oracle"]["pcg_dz_rel_err"] = {"median": float(np.median(e)), "max": float(e.max())}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec))

@@ -109,6 +109,136 @@ __global__ void k_zero_i32(int32_t* x, int count)
     if (t < count) x[t] = 0;
 }
 
+// ------------------------------------------------------------------ iterative refinement
+
+// One pass of iterative refinement of the KKT system the Schur method solves
+// (G dz - C' lambda = -g, C dz = c; GATO paper Sec. II, eq. 2): the residual of
+// the first pass's (lambda, dz), accumulated in double from the problem data,
+// is the right-hand side (g', c') of a correction system with the same G and
+// C, whose q, r, e and x0 are
+//   q'_k = q_k + Q~_k dx_k - lambda_k + A_k' lambda_{k+1}
+//   r'_k = r_k + R_k du_k + B_k' lambda_{k+1}
+//   x0'  = x0 - dx_0
+//   e'_k = e_k + A_k dx_k + B_k du_k - dx_{k+1}
+// (rows of C: [I] for knot 0, [-A_k, -B_k, I] for knot k + 1).  The products of
+// fp32 data are exact in double and the sums nearly so, so the correction
+// carries the first pass's error however ill-conditioned S is, while the fp32
+// solve finds it with its usual relative accuracy.  S, Q~^-1 and R^-1 are those
+// of the first pass; the correction's gamma (gamma'_0 = x0' + h_0,
+// gamma'_{k+1} = e'_k - t_k + h_{k+1}, as the formation forms gamma) takes
+// h_k = Q~_k^-1 q'_k and t_k = A_k h_k + B_k R_k^-1 r'_k from here.
+// Lane group of NP lanes per knot, lane i: row i of each knot block; the
+// vectors a row needs whole go through the group's LDS rows.
+template <class SH>
+__global__ __launch_bounds__(256) void k_kkt_residual(const Params p, float* qc, float* rc, float* ec, float* x0c,
+                                                      float* hq, float* tq)
+{
+    constexpr int NP = SH::NP, n = SH::NC, m = SH::MC, G = 256 / NP;
+    __shared__ float vx[G][NP], vu[G][NP], vl[G][NP], vq[G][NP], vr[G][NP];
+    const Ix<SH> ix{p.N};
+    const int gl = threadIdx.x / NP, i = threadIdx.x % NP, b = blockIdx.y;
+    const int k = blockIdx.x * G + gl;
+    const bool kv = k < p.N, dyn = k < p.N - 1;
+    const int kk = kv ? k : 0;
+    // dx_k, du_k and lambda_{k+1}, whole, for every lane of the group
+    vx[gl][i] = (kv && i < n) ? p.dz[ix.dx(b, kk, i)] : 0.0f;
+    vu[gl][i] = (dyn && i < m) ? p.dz[ix.du(b, kk, i)] : 0.0f;
+    vl[gl][i] = (dyn && i < n) ? p.lambda[ix.vn(b, kk + 1, i)] : 0.0f;
+    __syncthreads();
+    float qv = 0.0f, rv = 0.0f;
+    if (kv && i < n) {
+        const double rh = p.rho != nullptr ? (double)p.rho[b] : 0.0;
+        double s = (double)p.q[ix.vn(b, kk, i)] + rh * vx[gl][i] - p.lambda[ix.vn(b, kk, i)];
+        const float* Qr = p.Q + ix.Q(b, kk, i);
+#pragma unroll
+        for (int c = 0; c < n; ++c) s += (double)Qr[c] * vx[gl][c];
+        if (dyn) {
+            const float* Ac = p.A + ix.A(b, kk, 0) + i;  // column i of A_k
+#pragma unroll
+            for (int c = 0; c < n; ++c) s += (double)Ac[c * n] * vl[gl][c];
+            const float* Ar = p.A + ix.A(b, kk, i);
+            const float* Br = p.Bu + ix.Bu(b, kk, i);
+            double t = (double)p.e[ix.e(b, kk, i)] - p.dz[ix.dx(b, kk + 1, i)];
+#pragma unroll
+            for (int c = 0; c < n; ++c) t += (double)Ar[c] * vx[gl][c];
+#pragma unroll
+            for (int c = 0; c < m; ++c) t += (double)Br[c] * vu[gl][c];
+            ec[ix.e(b, kk, i)] = (float)t;
+        }
+        qv = (float)s;
+        qc[ix.vn(b, kk, i)] = qv;
+        if (k == 0) x0c[(size_t)b * n + i] = (float)((double)p.x0[(size_t)b * n + i] - vx[gl][i]);
+    }
+    if (dyn && i < m) {
+        double s = (double)p.r[ix.vm(b, kk, i)];
+        const float* Rr = p.R + ix.R(b, kk, i);
+#pragma unroll
+        for (int c = 0; c < m; ++c) s += (double)Rr[c] * vu[gl][c];
+        const float* Bc_ = p.Bu + ix.Bu(b, kk, 0) + i;  // column i of B_k
+#pragma unroll
+        for (int c = 0; c < n; ++c) s += (double)Bc_[c * m] * vl[gl][c];
+        rv = (float)s;
+        rc[ix.vm(b, kk, i)] = rv;
+    }
+    vq[gl][i] = qv;
+    vr[gl][i] = rv;
+    __syncthreads();
+    // h_k = Q~_k^-1 q'_k and R_k^-1 r'_k, row i
+    float h = 0.0f, g = 0.0f;
+    if (kv && i < n) {
+        const float* Qi = p.Qinv + ix.Q(b, kk, i);
+#pragma unroll
+        for (int c = 0; c < n; ++c) h = fmaf(Qi[c], vq[gl][c], h);
+        hq[ix.vn(b, kk, i)] = h;
+    }
+    if (dyn && i < m) {
+        const float* Ri = p.Rinv + ix.R(b, kk, i);
+#pragma unroll
+        for (int c = 0; c < m; ++c) g = fmaf(Ri[c], vr[gl][c], g);
+    }
+    __syncthreads();  // the vectors above are read; their rows take h and R^-1 r'
+    vq[gl][i] = h;
+    vr[gl][i] = g;
+    __syncthreads();
+    if (dyn && i < n) {  // t_k = A_k h_k + B_k R_k^-1 r'_k, row i
+        const float* Ar = p.A + ix.A(b, kk, i);
+        const float* Br = p.Bu + ix.Bu(b, kk, i);
+        float t = 0.0f;
+#pragma unroll
+        for (int c = 0; c < n; ++c) t = fmaf(Ar[c], vq[gl][c], t);
+#pragma unroll
+        for (int c = 0; c < m; ++c) t = fmaf(Br[c], vr[gl][c], t);
+        tq[ix.vn(b, kk, i)] = t;
+    }
+}
+
+// The correction's gamma from k_kkt_residual's h_k and t_k; one thread per entry.
+__global__ void k_refine_gamma(float* gamma, const float* hq, const float* tq, const float* ec, const float* x0c,
+                               int n, int N, size_t total)
+{
+    const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const size_t b = t / ((size_t)N * n), r = t % ((size_t)N * n);
+    const int k = (int)(r / n), i = (int)(r % n);
+    gamma[t] = k == 0 ? x0c[b * n + i] + hq[t]
+                      : ec[(b * (N - 1) + (k - 1)) * n + i] - tq[t - n] + hq[t];
+}
+
+// lambda += the correction's lambda, dz += its dz, flags |= its flags.
+__global__ void k_refine_add(float* lam, const float* lamc, size_t nlam, float* dz, const float* dzc, size_t ndz,
+                             int32_t* flags, const int32_t* flc, int B)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < nlam + ndz + B; t += stride) {
+        if (t < nlam)
+            lam[t] += lamc[t];
+        else if (t < nlam + ndz)
+            dz[t - nlam] += dzc[t - nlam];
+        else
+            flags[t - nlam - ndz] |= flc[t - nlam - ndz];
+    }
+}
+
 template <class SH>
 struct FormOnlyLds {
     FormLds<SH> f;
@@ -487,6 +617,14 @@ static bool merit_per_candidate()
     return env && std::strcmp(env, "candidate") == 0;
 }
 
+// GATO_REFINE=1: gato_sqp_step follows its direct solve with one pass of
+// iterative refinement (k_kkt_residual).
+static bool refine_enabled()
+{
+    const char* env = std::getenv("GATO_REFINE");
+    return env && std::strcmp(env, "1") == 0;
+}
+
 template <class SH>
 struct Ops {
     static constexpr int SL = SH::SLOTS, KPW = SH::KPW;
@@ -589,6 +727,14 @@ struct Ops {
         }
         return hipGetLastError();
     }
+    static hipError_t residual(const Params& p, float* qc, float* rc, float* ec, float* x0c, float* hq, float* tq,
+                               hipStream_t st)
+    {
+        constexpr int G = 256 / SH::NP;
+        hipLaunchKernelGGL((k_kkt_residual<SH>), dim3((p.N + G - 1) / G, p.B), dim3(256), 0, st, p, qc, rc, ec, x0c,
+                           hq, tq);
+        return hipGetLastError();
+    }
     static hipError_t direct(const Params& p, hipStream_t st)
     {
         constexpr int SPW = 64 / SH::NP;
@@ -659,7 +805,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // gato_sqp_step's workspace beyond the fused horizons.  Only the direct solves
 // run there, so it holds no Phi^-1.
 struct WsLayout {
-    size_t S, mpart, gamma, Qinv, Rinv, direct, total;
+    size_t S, mpart, gamma, Qinv, Rinv, direct, qc, rc, ec, x0c, hq, tq, lamc, dzc, flc, total;
 };
 
 static size_t direct_ws_bytes(const gato_dims_t* d)
@@ -685,6 +831,27 @@ static WsLayout ws_layout(const gato_dims_t* d)
     off += align256(B * (N > 1 ? N - 1 : 1) * m * m * sizeof(float));
     w.direct = off;  // the block Thomas or the cyclic-reduction solve's workspace
     off += std::max(direct_ws_bytes(d), cr_ws_bytes(d));
+    // the refinement pass: the correction system's q, r, e, x0, the terms of its gamma
+    // (h_k, t_k) and its lambda, dz, flags
+    const size_t Nd = N > 1 ? N - 1 : 0;
+    w.qc = off;
+    off += align256(B * N * n * sizeof(float));
+    w.rc = off;
+    off += align256(B * Nd * m * sizeof(float));
+    w.ec = off;
+    off += align256(B * Nd * n * sizeof(float));
+    w.x0c = off;
+    off += align256(B * n * sizeof(float));
+    w.hq = off;
+    off += align256(B * N * n * sizeof(float));
+    w.tq = off;
+    off += align256(B * N * n * sizeof(float));
+    w.lamc = off;
+    off += align256(B * N * n * sizeof(float));
+    w.dzc = off;
+    off += align256(B * (N * n + Nd * m) * sizeof(float));
+    w.flc = off;
+    off += align256(B * sizeof(int32_t));
     w.total = off;
     return w;
 }
@@ -939,6 +1106,33 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
         if ((cr ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
+        if (refine_enabled()) {
+            // the correction system: its right-hand side and gamma (S, Q~^-1 and R^-1
+            // are the first pass's), its solve, then the sum with the first pass
+            char* ws = static_cast<char*>(workspace);
+            float* qc = reinterpret_cast<float*>(ws + wl.qc);
+            float* rc2 = reinterpret_cast<float*>(ws + wl.rc);
+            float* ec = reinterpret_cast<float*>(ws + wl.ec);
+            float* x0c = reinterpret_cast<float*>(ws + wl.x0c);
+            float* hq = reinterpret_cast<float*>(ws + wl.hq);
+            float* tq = reinterpret_cast<float*>(ws + wl.tq);
+            Params c = p;
+            c.q = qc; c.r = rc2; c.e = ec; c.x0 = x0c;
+            c.lambda = reinterpret_cast<float*>(ws + wl.lamc);
+            c.dz = reinterpret_cast<float*>(ws + wl.dzc);
+            c.flags = reinterpret_cast<int32_t*>(ws + wl.flc);
+            const size_t B = dims->B, nlam = B * dims->N * dims->n;
+            if (O::residual(p, qc, rc2, ec, x0c, hq, tq, stream) != hipSuccess) return GATO_E_HIP;
+            hipLaunchKernelGGL(k_refine_gamma, dim3((unsigned)((nlam + 255) / 256)), dim3(256), 0, stream, c.gamma, hq,
+                               tq, ec, x0c, dims->n, dims->N, nlam);
+            hipLaunchKernelGGL(k_zero_i32, dim3((dims->B + 255) / 256), dim3(256), 0, stream, c.flags, dims->B);
+            if (hipGetLastError() != hipSuccess) return GATO_E_HIP;
+            if ((cr ? cr_launch(c, stream) : O::direct(c, stream)) != hipSuccess) return GATO_E_HIP;
+            const size_t ndz = B * ((size_t)dims->N * dims->n + (size_t)(dims->N - 1) * dims->m);
+            hipLaunchKernelGGL(k_refine_add, dim3(1024), dim3(256), 0, stream, p.lambda, c.lambda, nlam, p.dz, c.dz,
+                               ndz, p.flags, c.flags, dims->B);
+            if (hipGetLastError() != hipSuccess) return GATO_E_HIP;
+        }
         if (times && hipEventRecord(ev[2], stream) != hipSuccess) return GATO_E_HIP;
         if (O::merit_ws(p, stream) != hipSuccess) return GATO_E_HIP;
         return GATO_OK;

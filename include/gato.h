@@ -251,11 +251,20 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *    and N <= 128, B * (0.28 + 0.0018 N) us < 2.7 N us for n <= 16 beyond
  *    (B < ~930-1300), B < ~400 for n > 16), else
  *    gato_direct_solve's block Thomas elimination (the environment variable
- *    GATO_LONG_SOLVE=thomas or =cr forces either).
+ *    GATO_LONG_SOLVE=thomas or =cr forces either).  With the environment
+ *    variable GATO_REFINE=1 the direct solve is followed by one pass of
+ *    iterative refinement of the KKT system (G dz - C' lambda = -g, C dz = c):
+ *    its residual, accumulated in double from the problem data, is the
+ *    right-hand side of a second pass through the same stages, whose lambda
+ *    and dz are added to the first's.  That roughly doubles the step's cost
+ *    and takes dz from the fp32 stages' accuracy on S (relative error up to
+ *    about cond(S) * 1e-7, so ~1e-3 at cond(S) ~ 1e6) to ~1e-6.  The merit is
+ *    evaluated on the refined dz; linsys_us includes the pass.
  *    lambda's input is not read, iters and relres are written as 0, and eps
  *    and max_iters are checked but unused.  S (no Phi^-1: the
- *    direct solves do not use it), gamma, Qinv, Rinv, the solve's rows and
- *    the merit's per-knot values go through `workspace`
+ *    direct solves do not use it), gamma, Qinv, Rinv, the solve's rows, the
+ *    refinement pass's buffers and the merit's per-knot values go through
+ *    `workspace`
  *    (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device
  *    memory).  With a small batch the merit then spreads a solve's knots over
  *    several workgroups and sums their values in a second kernel, in the

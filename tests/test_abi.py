@@ -64,7 +64,11 @@ def test_shapes_and_workspace(lib):
     B, N = 512, 128
     stage1 = a(B * N * 3 * 14 * 14) + a(B * 17 * N) + a(B * N * 14) + a(B * N * 14 * 14) + a(B * (N - 1) * 7 * 7)
     solve = max(ops.gato_direct_workspace_bytes((14, 7, N, B)), ops.gato_cr_workspace_bytes((14, 7, N, B)))
-    assert ws == stage1 + solve
+    # the refinement pass: the correction system's q, r, e, x0, the terms h_k and t_k of its
+    # gamma, then its lambda, dz and flags
+    refine = a(B * N * 14) + a(B * (N - 1) * 7) + a(B * (N - 1) * 14) + a(B * 14) + 2 * a(B * N * 14) + \
+        a(B * N * 14) + a(B * (N * 14 + (N - 1) * 7)) + a(B)
+    assert ws == stage1 + solve + refine
     assert ops.gato_workspace_bytes((13, 7, 64, 128)) == 0          # unsupported -> 0
 
 

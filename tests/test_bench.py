@@ -61,3 +61,24 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_rel_err_rows():
+    o = np.array([[3.0, 4.0], [1.0, 0.0]])
+    g = np.array([[3.0, 4.5], [1.0, 0.0]])
+    np.testing.assert_allclose(bench.rel_err_rows(g, o), [0.1, 0.0])
+
+
+def test_exact_step_matches_the_oracle_step():
+    """The direct-solve reference bench.py reports against: on a well-conditioned batch
+    it equals the oracle's PCG step to within PCG's tolerance."""
+    import oracle
+
+    bt = synth.make_batch(1, 3)
+    ex = bench.exact_step(bt, 8)
+    al = np.array([2.0 ** -i for i in range(8)])
+    st = oracle.sqp_step(*[bt[f] for f in ("Q", "q", "R", "r", "A", "Bu", "e", "x0")], None, 1e-10, 500, al,
+                         bench.MU)
+    assert bench.rel_err_rows(ex["dz"], st["dz"]).max() < 1e-7
+    assert bench.rel_err_rows(ex["merit"].reshape(-1, 1), st["merit"].reshape(-1, 1)).max() < 1e-7
+    assert (ex["best"] == st["best"]).all()

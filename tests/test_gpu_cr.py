@@ -176,6 +176,52 @@ def test_sqp_step_long_horizon_wide_knots():
     assert rel_rows(g["dz"], dz).max() <= 5e-5
 
 
+@pytest.mark.parametrize("solver", ["cr", "thomas"])
+def test_sqp_step_refinement_meets_the_bars_when_ill_conditioned(solver, monkeypatch):
+    """GATO_REFINE=1: one pass of iterative refinement of the KKT system after the
+    direct solve.  On the ill-conditioned long-horizon workload (cond(S) ~ 1e6, where
+    rounding S alone to fp32 moves dz by 1e-4 to 6e-4) the refined step is the
+    oracle's exact step within 2e-5 in dz and 1e-4 in every merit (the stated merit
+    bar, which the unrefined fp32 step misses on some of these solves)."""
+    from gpu_util import gpu_sqp
+
+    monkeypatch.setenv("GATO_LONG_SOLVE", solver)
+    B = 32
+    _ident("sqp refinement, workload 5", solver, B)
+    bt = synth.make_batch(5, B)
+    ins = synth.inputs(bt)
+    form = oracle.form_schur(*ins)
+    _, dz = _exact(bt, form)
+    merit = oracle.merit_eval(*ins, dz, synth.ALPHAS, 1.0)["merit"]
+    monkeypatch.delenv("GATO_REFINE", raising=False)
+    plain = gpu_sqp(bt, 1e-6, 2000)
+    monkeypatch.setenv("GATO_REFINE", "1")
+    g = gpu_sqp(bt, 1e-6, 2000)
+    e0, e = rel_rows(plain["dz"], dz), rel_rows(g["dz"], dz)
+    m0 = np.abs(plain["merit"] - merit) / np.abs(merit)
+    m = np.abs(g["merit"] - merit) / np.abs(merit)
+    print("dz rel err max %.3e -> %.3e; merit rel err max %.3e -> %.3e" % (e0.max(), e.max(), m0.max(), m.max()))
+    assert ((g["flags"] & ~ops.F_LS_FAILED) == 0).all()
+    assert e.max() <= 2e-5 and e.max() < 0.1 * e0.max()
+    assert m.max() <= 1e-4
+
+
+def test_sqp_step_refinement_keeps_a_well_conditioned_step(monkeypatch):
+    """With GATO_REFINE=1 a well-conditioned long-horizon step stays the oracle's exact
+    step (the correction is at the level of fp32 rounding)."""
+    from gpu_util import gpu_sqp
+
+    monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
+    monkeypatch.setenv("GATO_REFINE", "1")
+    _ident("sqp refinement, workload 3 at N=150")
+    bt = synth.make_batch(3, 6, N=150)
+    g = gpu_sqp(bt, 1e-6, 200)
+    form = oracle.form_schur(*synth.inputs(bt))
+    _, dz = _exact(bt, form)
+    assert (g["flags"] == 0).all()
+    assert rel_rows(g["dz"], dz).max() <= 5e-6
+
+
 @pytest.mark.parametrize("N", [9, 128, 300])
 def test_cr_reads_no_lower_block(N):
     """For n <= 16 the solve reads S's diagonal and upper blocks only (the lower ones

@@ -473,3 +473,22 @@ def test_cyclic_plan_is_fill_in_free_and_solves_exactly(cid, T):
         other[:, blk(f)] = 0.0
         lam[blk(f)] = np.linalg.solve(rows[:, blk(f)], gf - other @ lam)
     np.testing.assert_allclose(lam, want, rtol=0, atol=1e-9 * np.abs(want).max())
+
+
+def test_fp32_storage_of_S_sets_a_floor_on_the_ill_conditioned_workload():
+    """Rounding the exact S alone to fp32, then solving exactly in fp64, moves dz by
+    about 1e-4 on the ill-conditioned long-horizon workload (cond(S) ~ 1e6) but by
+    well under 1e-5 on the 7-DoF-arm workload: the floor that any fp32 S puts under
+    the GPU path's dz there, and the reason its direct solve can be refined from the
+    exact problem data."""
+    def err(cid):
+        bt = synth.make_batch(cid, 4)
+        f = oracle.form_schur(*synth.inputs(bt))
+        solve = lambda S: oracle.recover(f["Qinv"], f["Rinv"], bt["A"], bt["Bu"], bt["q"], bt["r"],  # noqa: E731
+                                         oracle.direct_solve(S, f["gamma"])["lam"])
+        exact, rounded = solve(f["S"]), solve(f["S"].astype(np.float32).astype(np.float64))
+        return np.linalg.norm(rounded - exact, axis=1) / np.linalg.norm(exact, axis=1)
+
+    e5, e3 = err(5), err(3)
+    assert 5e-5 < e5.max() < 1e-3
+    assert e3.max() < 1e-5
