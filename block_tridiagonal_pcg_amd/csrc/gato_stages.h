@@ -439,7 +439,28 @@ struct GlobalMat {
         return acc;
     }
     __device__ __forceinline__ float S(int k, float xp, float x, float xn) const { return mv(Sm, k, xp, x, xn); }
-    __device__ __forceinline__ float P(int k, float xp, float x, float xn) const { return mv(Pm, k, xp, x, xn); }
+    // Phi^-1 r in the stair preconditioner's factored form D^-1 (J S J) D^-1 r, D^-1 = blkdiag(Phi^-1_{k,k})
+    // and J = blkdiag((-1)^k I), which equals the assembled blocks: y_j = D_j^-1 r_j for j = k-1, k, k+1
+    // (row i of each inverse, with r's neighbours as the loop keeps them), w_k = (J S J y)_k, then
+    // z_k = (D_k^-1)' w_k (column i).  r'z = y' J S J y then stays positive while S is SPD in fp32, even
+    // where the assembled fp32 Phi^-1 is not (its condition can exceed 1e8 on ill-conditioned
+    // long horizons, and the D_k^-1 carry the rounding of their Gauss-Jordan inversion).
+    __device__ __forceinline__ float P(int k, float rp, float r, float rn) const
+    {
+        constexpr int NP = SH::NP, NC = SH::NC;
+        const bool v = k < ix.N && i < NC;
+        float t[NC], yp = 0.0f, y = 0.0f, yn = 0.0f, z = 0.0f;
+        ld_row<NC>(Pm, ix.blk(b, k > 0 ? k - 1 : 0, 1, i), v && k > 0, t);
+        dotb<NP, NC>(yp, Bc<NP>(rp), t);
+        ld_row<NC>(Pm, ix.blk(b, k, 1, i), v, t);
+        dotb<NP, NC>(y, Bc<NP>(r), t);
+        ld_row<NC>(Pm, ix.blk(b, k + 1 < ix.N ? k + 1 : k, 1, i), v && k + 1 < ix.N, t);
+        dotb<NP, NC>(yn, Bc<NP>(rn), t);
+        const float w = mv(Sm, k, -yp, y, -yn);
+        ld_row<NC, NC>(Pm, ix.blk(b, k, 1, 0) + i, v, t);  // column i of D_k^-1
+        dotb<NP, NC>(z, Bc<NP>(w), t);
+        return z;
+    }
     __device__ __forceinline__ void sup(int k, float (&out)[SH::NC]) const
     {
         ld_row<SH::NC>(Sm, ix.blk(b, k, 2, i), k < ix.N && i < SH::NC, out);

@@ -139,7 +139,13 @@ int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, con
  *   r = gamma - S lambda; z = Phi^-1 r; p = z; eta = r'z; then per iteration
  *   v = S p; a = eta / p'v; lambda += a p; r -= a v;
  *   stop when ||r||_2 <= eps ||gamma||_2;  z = Phi^-1 r; p = z + (r'z / eta) p.
- * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  Then the step
+ * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  Beyond the horizon one
+ * workgroup holds (N > 64 for n <= 16, N > 16 for n <= 32) z = Phi^-1 r is
+ * applied in the preconditioner's factored form D^-1 (J S J) (D^-1 r), with
+ * D^-1 = the diagonal blocks of Phi^-1 and J = blkdiag((-1)^k I): the same
+ * operator, which stays positive definite in fp32 while S does even where the
+ * assembled fp32 Phi^-1 does not (its condition can pass 1e8 on ill-conditioned
+ * long horizons); it reads S and the diagonal blocks of Phi^-1.  Then the step
  *   dx_k = Qinv_k (lambda_k - A_k' lambda_{k+1} - q_k),  dx_{N-1} = Qinv_{N-1}(lambda_{N-1} - q_{N-1}),
  *   du_k = Rinv_k (-B_k' lambda_{k+1} - r_k),
  * evaluated as dx_k = Qinv_k lambda_k + S_{k,k+1} lambda_{k+1} - Qinv_k q_k, since
