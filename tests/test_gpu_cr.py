@@ -206,15 +206,18 @@ def test_sqp_step_refinement_meets_the_bars_when_ill_conditioned(solver, monkeyp
     assert m.max() <= 1e-4
 
 
-def test_sqp_step_refinement_keeps_a_well_conditioned_step(monkeypatch):
+@pytest.mark.parametrize("cid,B,N", [(3, 6, 150), (3, 1, 65), (4, 3, 40), (4, 2, 17)])
+def test_sqp_step_refinement_keeps_a_well_conditioned_step(cid, B, N, monkeypatch):
     """With GATO_REFINE=1 a well-conditioned long-horizon step stays the oracle's exact
-    step (the correction is at the level of fp32 rounding)."""
+    step (the correction is at the level of fp32 rounding): 16-lane groups (n = 14) and
+    32-lane ones (n = 24), with a last residual workgroup holding one knot (N = 65 and
+    N = 17 beyond a multiple of the 16 and 8 knots a workgroup covers)."""
     from gpu_util import gpu_sqp
 
     monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
     monkeypatch.setenv("GATO_REFINE", "1")
-    _ident("sqp refinement, workload 3 at N=150")
-    bt = synth.make_batch(3, 6, N=150)
+    _ident("sqp refinement, well-conditioned", cid, B, N)
+    bt = synth.make_batch(cid, B, N=N)
     g = gpu_sqp(bt, 1e-6, 200)
     form = oracle.form_schur(*synth.inputs(bt))
     _, dz = _exact(bt, form)
