@@ -56,7 +56,7 @@ __global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
     int it = 0, pfl = 0;
     float rel = 0.0f;
     const RegMat<SH> M{&rw};
-    pcg<SH, 1>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
+    pcg_robust<SH, 1>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
 
     // recovery of dz (exchange rows of the PCG buffers: knot k at row k + 1)
     L.u.pcg.xv[s + 1][i] = lam;
@@ -358,7 +358,7 @@ __device__ __forceinline__ void pcg_and_recover(const Params& p, const MAT& M, P
     const int s = threadIdx.x / NP, i = threadIdx.x % NP;
     int it = 0, pfl = 0;
     float rel = 0.0f;
-    pcg<SH, C>(p, M, gam, lam, L, it, rel, pfl);
+    pcg_robust<SH, C>(p, M, gam, lam, L, it, rel, pfl);
 #pragma unroll
     for (int c = 0; c < C; ++c) L.xv[c * SL + s + 1][i] = lam[c];
     __syncthreads();

@@ -391,6 +391,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 // Block-tridiagonal rows in registers (one knot per lane group).
 template <class SH>
 struct RegMat {
+    static constexpr bool kAssembled = true;  // applies the assembled Phi^-1 blocks
     const Rows<SH>* rw;
     __device__ __forceinline__ float S(int, float xp, float x, float xn) const
     {
@@ -421,6 +422,7 @@ struct RegMat {
 // horizons longer than one workgroup holds); layout [B][N][3][n][n].
 template <class SH>
 struct GlobalMat {
+    static constexpr bool kAssembled = false;  // applies Phi^-1 in factored form
     const float* Sm;
     const float* Pm;
     Ix<SH> ix;
@@ -467,6 +469,59 @@ struct GlobalMat {
     }
 };
 
+// The register-resident rows with Phi^-1 applied in its factored form
+// D^-1 (J S J) D^-1, as GlobalMat applies it: y_k = D_k^-1 r_k (dsym: row i of
+// D_k^-1 symmetrised) goes to the neighbouring groups through the exchange
+// rows xy (one barrier), w_k = (J S J y)_k from the knot's S rows, z_k =
+// D_k^-1 w_k.  With D_k^-1 symmetric, r'z = y' (J S J) y, positive while S is
+// SPD in fp32.  One knot per lane group (C = 1).
+template <class SH>
+struct RegMatF : RegMat<SH> {
+    static constexpr bool kAssembled = false;
+    const float* dsym;
+    float (*xy)[SH::NP];
+    __device__ __forceinline__ float P(int k, float, float x, float) const
+    {
+        constexpr int NP = SH::NP, NC = SH::NC;
+        const int i = threadIdx.x % NP;
+        float y = 0.0f, w = 0.0f, z = 0.0f;
+        dotb<NP, NC>(y, Bc<NP>(x), dsym);
+        xy[k + 1][i] = y;
+        __syncthreads();
+        const float yp = xy[k][i], yn = xy[k + 2][i];
+        dotb<NP, NC>(w, Bc<NP>(-yp), this->rw->slo);
+        dotb<NP, NC>(w, Bc<NP>(y), this->rw->sd);
+        dotb<NP, NC>(w, Bc<NP>(-yn), this->rw->sup);
+        dotb<NP, NC>(z, Bc<NP>(w), dsym);
+        return z;
+    }
+};
+
+// Row i of (X + X')/2 for the row-per-lane block X of a lane group (lane i: row
+// i in x), through the group's exchange row ex (NP floats, within one wave):
+// column c of X is written there at step c and lane c reads it whole.
+template <class SH>
+__device__ __forceinline__ void sym_rows(const float* x, float* ex, float* out)
+{
+    constexpr int NC = SH::NC;
+    const int i = threadIdx.x % SH::NP;
+    float col[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) col[c] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        ex[i] = x[c];
+        __builtin_amdgcn_wave_barrier();
+        if (i == c) {
+#pragma unroll
+            for (int c2 = 0; c2 < NC; ++c2) col[c2] = ex[c2];
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) out[c] = 0.5f * (x[c] + col[c]);
+}
+
 // Leaves of the canonical knot sums: at least 64 and a power of two.
 __host__ __device__ constexpr int leaves_for(int knots)
 {
@@ -482,6 +537,7 @@ struct PcgLds {
     // exchange rows for knots -1 .. K (index + 1); rows 0 and K + 1 stay zero
     float xv[K + 2][SH::NP];
     float xz[K + 2][SH::NP];
+    float xy[K + 2][SH::NP];    // y = D^-1 r of the factored Phi^-1 (RegMatF)
     alignas(16) float red0[P];  // per-knot partial sums: p'v
     alignas(16) float red1[P];  //                        r'r
     alignas(16) float red2[P];  //                        r'z
@@ -524,6 +580,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         if (r == 0 || r == KK + 1 || (r - 1) % SL >= G) {
             L.xv[r][t % NP] = 0.0f;
             L.xz[r][t % NP] = 0.0f;
+            L.xy[r][t % NP] = 0.0f;
         }
     }
 
@@ -712,6 +769,30 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
     // The loop's barriers order every LDS access above; one more before the
     // caller reuses the buffers.
     __syncthreads();
+}
+
+// PCG as above; a solve that the assembled Phi^-1 leaves at the iteration cap
+// (its fp32 blocks can be indefinite where cond(Phi^-1) passes ~1e8) runs
+// again from its lambda with Phi^-1 in factored form, for up to max_iters more
+// iterations; iters counts both runs.  The decision is uniform over the
+// workgroup (one solve), and a solve that converges never takes it.
+template <class SH, int C, class MAT>
+__device__ __forceinline__ void pcg_robust(const Params& p, const MAT& M, const float* gam, float* lam,
+                                           PcgLds<SH, C>& L, int& iters_out, float& relres, int& flags_out)
+{
+    pcg<SH, C>(p, M, gam, lam, L, iters_out, relres, flags_out);
+    if constexpr (MAT::kAssembled) {
+        static_assert(C == 1, "one knot per lane group");
+        if (flags_out == GATO_F_PCG_MAXITER) {
+            float dsym[SH::NC];
+            sym_rows<SH>(M.rw->pd, L.xy[threadIdx.x / SH::NP + 1], dsym);
+            const RegMatF<SH> F{{M.rw}, dsym, L.xy};
+            int it2 = 0, fl2 = 0;
+            pcg<SH, C>(p, F, gam, lam, L, it2, relres, fl2);
+            iters_out += it2;
+            flags_out = fl2;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ stage 2b: recovery

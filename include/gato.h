@@ -139,7 +139,11 @@ int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, con
  *   r = gamma - S lambda; z = Phi^-1 r; p = z; eta = r'z; then per iteration
  *   v = S p; a = eta / p'v; lambda += a p; r -= a v;
  *   stop when ||r||_2 <= eps ||gamma||_2;  z = Phi^-1 r; p = z + (r'z / eta) p.
- * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  Beyond the horizon one
+ * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  Within the horizon one
+ * workgroup holds, the assembled Phi^-1 blocks are applied; a solve they leave
+ * at max_iters (their fp32 values can be indefinite where cond(Phi^-1) passes
+ * ~1e8) runs again from its lambda with Phi^-1 in the factored form below, for
+ * up to max_iters more iterations, and iters counts both runs.  Beyond the horizon one
  * workgroup holds (N > 64 for n <= 16, N > 16 for n <= 32) z = Phi^-1 r is
  * applied in the preconditioner's factored form D^-1 (J S J) (D^-1 r), with
  * D^-1 = the diagonal blocks of Phi^-1 and J = blkdiag((-1)^k I): the same
