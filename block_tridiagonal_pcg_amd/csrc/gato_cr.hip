@@ -158,7 +158,7 @@ bool cr_reads_lower(const gato_dims_t* d)
 // one lane group per solve fills the chip, about 1.5 ns per knot and solve
 // beyond (5.6 ns for n > 16).  Cyclic reduction is log-depth but does more
 // arithmetic: about 0.15 us + 1.05 ns per knot per solve with the
-// register-resident kernel (N <= 128, n <= 16), 0.28 us + 1.8 ns per knot per
+// register-resident kernel (N <= 128, n <= 16), 0.18 us + 1.9 ns per knot per
 // solve with the nested dissection (N > 128, n <= 16) and 17 ns per knot and
 // solve with the streaming kernel (n > 16), once its batch fills the chip.
 // Cyclic reduction is taken while its batch time stays below block Thomas's
@@ -172,7 +172,7 @@ bool cr_preferred(const gato_dims_t* d)
     }
     const bool narrow = d->n <= 16 && !cr_streaming_forced();
     const double per_solve_us =
-        narrow ? (d->N <= 2 * ND_CHUNKS ? 0.15 + 0.00105 * d->N : 0.28 + 0.0018 * d->N) : 0.017 * d->N;
+        narrow ? (d->N <= 2 * ND_CHUNKS ? 0.15 + 0.00105 * d->N : 0.18 + 0.0019 * d->N) : 0.017 * d->N;
     const bool wide = d->n > 16;  // 32-lane groups
     const double thomas_us = std::max((wide ? 6.9 : 2.7) * d->N, (wide ? 0.0056 : 0.0015) * d->N * d->B);
     return d->B * per_solve_us < thomas_us;

@@ -258,8 +258,8 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *  - otherwise stage 2 is a direct solve: gato_cr_solve's block cyclic
  *    reduction while the batch is small enough for its log-depth to pay
  *    (measured switch points: B * (0.15 + 0.00105 N) us < 2.7 N us for n <= 16
- *    and N <= 128, B * (0.28 + 0.0018 N) us < 2.7 N us for n <= 16 beyond
- *    (B < ~930-1300), B < ~400 for n > 16), else
+ *    and N <= 128, B * (0.18 + 0.0019 N) us < 2.7 N us for n <= 16 beyond
+ *    (B < ~1040-1300), B < ~400 for n > 16), else
  *    gato_direct_solve's block Thomas elimination (the environment variable
  *    GATO_LONG_SOLVE=thomas or =cr forces either).  With the environment
  *    variable GATO_REFINE=1 the direct solve is followed by one pass of
