@@ -492,3 +492,40 @@ def test_fp32_storage_of_S_sets_a_floor_on_the_ill_conditioned_workload():
     e5, e3 = err(5), err(3)
     assert 5e-5 < e5.max() < 1e-3
     assert e3.max() < 1e-5
+
+
+def test_kkt_correction_right_hand_side_recovers_the_exact_step():
+    """The right-hand side of the refinement pass (the KKT residual of (lambda, dz)
+    written as the q, r, e and x0 of a correction system with the same G and C):
+      q'_k = q_k + Q~_k dx_k - lambda_k + A_k' lambda_{k+1},   r'_k = r_k + R_k du_k + B_k' lambda_{k+1},
+      x0' = x0 - dx_0,   e'_k = e_k + A_k dx_k + B_k du_k - dx_{k+1}.
+    Solving that system exactly and adding its (lambda, dz) to a perturbed first pass
+    gives the exact step, so every sign and index of those formulas is pinned."""
+    bt = synth.make_batch(2, 2)
+    Q, q, R, r, A, Bu, e, x0 = [np.asarray(bt[f], np.float64) for f in ("Q", "q", "R", "r", "A", "Bu", "e", "x0")]
+    n, m, N, B = bt["dims"]
+    rho = np.array([0.3, 0.7])
+    f = oracle.form_schur(Q, q, R, r, A, Bu, e, x0, rho)
+    lam = oracle.direct_solve(f["S"], f["gamma"])["lam"]
+    dz = oracle.recover(f["Qinv"], f["Rinv"], A, Bu, q, r, lam)
+    rng = np.random.default_rng(5)
+    lam0 = lam + 1e-3 * rng.standard_normal(lam.shape)
+    dz0 = dz + 1e-3 * rng.standard_normal(dz.shape)
+
+    def parts(z):
+        dx = np.stack([z[:, k * (n + m):k * (n + m) + n] for k in range(N)], axis=1)
+        du = np.stack([z[:, k * (n + m) + n:(k + 1) * (n + m)] for k in range(N - 1)], axis=1)
+        return dx, du
+
+    dx, du = parts(dz0)
+    Qt = Q + rho[:, None, None, None] * np.eye(n)
+    qc = q + np.einsum("bkij,bkj->bki", Qt, dx) - lam0
+    qc[:, :-1] += np.einsum("bkji,bkj->bki", A, lam0[:, 1:])
+    rc = r + np.einsum("bkij,bkj->bki", R, du) + np.einsum("bkji,bkj->bki", Bu, lam0[:, 1:])
+    x0c = x0 - dx[:, 0]
+    ec = e + np.einsum("bkij,bkj->bki", A, dx[:, :-1]) + np.einsum("bkij,bkj->bki", Bu, du) - dx[:, 1:]
+    fc = oracle.form_schur(Q, qc, R, rc, A, Bu, ec, x0c, rho)
+    lamc = oracle.direct_solve(fc["S"], fc["gamma"])["lam"]
+    dzc = oracle.recover(fc["Qinv"], fc["Rinv"], A, Bu, qc, rc, lamc)
+    np.testing.assert_allclose(dz0 + dzc, dz, rtol=0, atol=1e-9 * np.abs(dz).max())
+    np.testing.assert_allclose(lam0 + lamc, lam, rtol=0, atol=1e-9 * np.abs(lam).max())
