@@ -45,9 +45,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=128)
     ap.add_argument("--horizon", type=int, default=None, help="override the configuration's N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--refine", choices=("auto", "on", "off"), default="auto",
-                    help="one pass of KKT iterative refinement after a direct solve (GATO_REFINE); "
-                         "auto: on for the ill-conditioned workload 5")
+    ap.add_argument("--refine", choices=("on", "off"), default="on",
+                    help="the KKT refinement pass after a direct solve (on: the library's default; "
+                         "off: gato_sqp_step_opts with refine = 0, for comparison)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-copy", action="store_true")
     ap.add_argument("--merit-variants", action="store_true",
@@ -289,13 +289,11 @@ def merit_variants(a):
             e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
             hip.hipEventCreate(ctypes.byref(e0))
             hip.hipEventCreate(ctypes.byref(e1))
-            for variant in ("fused", "candidate"):
+            for variant in (ops.MERIT_PER_KNOT, ops.MERIT_PER_CANDIDATE):
                 for waves in (1, 2, 4, 8, 16):
-                    os.environ["GATO_MERIT_VARIANT"] = variant
-                    os.environ["GATO_MERIT_WAVES"] = str(waves)
                     call = lambda: ops.gato_merit_eval(dims, *[dev[f] for f in synth.FIELDS], out["dz"],  # noqa
                                                        synth.ALPHAS, MU, out["merit"], out["merit0"], out["best"],
-                                                       out["flags"], stream=st.value)
+                                                       out["flags"], stream=st.value, variant=variant, waves=waves)
                     for _ in range(3):
                         call()
                     reps = 20
@@ -306,13 +304,11 @@ def merit_variants(a):
                     hip.hipEventSynchronize(e1)
                     ms = ctypes.c_float()
                     hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1)
-                    rows.append({"B": B, "cus": cus, "variant": variant, "threads": 64 * waves,
+                    rows.append({"B": B, "cus": cus, "variant": ["fused", "candidate"][variant], "threads": 64 * waves,
                                  "us": ms.value * 1e3 / reps})
             hip.hipEventDestroy(e0)
             hip.hipEventDestroy(e1)
             hip.hipStreamDestroy(st)
-    os.environ.pop("GATO_MERIT_VARIANT", None)
-    os.environ.pop("GATO_MERIT_WAVES", None)
     print(json.dumps({"study": "merit launch variants", "workload": synth.CONFIGS[a.config].name,
                       "unit": "us per launch", "rows": rows}))
 
@@ -461,11 +457,7 @@ def main():
         solver_sweep(a)
         return
     torch.cuda.set_device(0)
-    refine = a.refine == "on" or (a.refine == "auto" and a.config == 5)
-    if refine:
-        os.environ["GATO_REFINE"] = "1"
-    else:
-        os.environ.pop("GATO_REFINE", None)
+    refine = a.refine == "on"
     cfg = synth.CONFIGS[a.config]
     batch = synth.make_batch(a.config, a.batch, N=a.horizon)
     batch["cid"] = a.config
@@ -491,7 +483,8 @@ def main():
     def prepare(lam):
         return ops.prepared_sqp_step(dims, *[dev[f] for f in synth.FIELDS], None, EPS, cap, alphas, MU, lam,
                                      out["dz"], out["merit"], out["merit0"], out["best"], out["iters"],
-                                     out["relres"], out["flags"], workspace=ws, stream=stream)
+                                     out["relres"], out["flags"], workspace=ws, stream=stream,
+                                     refine=None if refine else 0)
 
     warm = prepare(out["lam"])
     for _ in range(a.warmup):
@@ -562,7 +555,8 @@ def main():
             for _ in range(3):
                 pst["lam"].zero_()
                 e0.record(stream)
-                ops.gato_pcg_solve(dims, st1["S"], st1["Pinv"], st1["gamma"], st1["Qinv"], st1["Rinv"], dev["Bu"],
+                ops.gato_pcg_solve(dims, st1["S"], st1["Pinv"], st1["gamma"], st1["Qinv"], st1["Rinv"], dev["A"],
+                                   dev["Bu"],
                                    dev["q"], dev["r"], EPS, cap, pst["lam"], pst["dz"], pst["iters"], pst["relres"],
                                    pst["flags"], stream=stream)
                 e1.record(stream)

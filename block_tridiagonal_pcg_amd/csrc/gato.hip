@@ -17,7 +17,6 @@
 #include "gato_stages.h"
 
 #include <algorithm>
-#include <cstdlib>
 #include <cstring>
 
 namespace gato {
@@ -597,32 +596,13 @@ __global__ void k_merit_pick(Params p)
 
 // ------------------------------------------------------------------ host side
 
-static int merit_waves_default(int N, int kpw)
+// Workgroup size of the standalone merit: enough waves for every knot at once,
+// at most 16 (waves = 0), or the caller's choice.
+static int merit_waves(int N, int kpw, int waves)
 {
-    const char* env = std::getenv("GATO_MERIT_WAVES");
-    if (env) {
-        const int w = std::atoi(env);
-        if (w >= 1 && w <= 16) return w;
-    }
+    if (waves >= 1 && waves <= 16) return waves;
     int w = (N + kpw - 1) / kpw;
     return w < 1 ? 1 : (w > 16 ? 16 : w);
-}
-
-// Launch variant of the standalone merit call: GATO_MERIT_VARIANT=candidate
-// selects the candidate-parallel kernels (for measurement; the default, one
-// workgroup per solve evaluating every step size per knot, is faster).
-static bool merit_per_candidate()
-{
-    const char* env = std::getenv("GATO_MERIT_VARIANT");
-    return env && std::strcmp(env, "candidate") == 0;
-}
-
-// GATO_REFINE=1: gato_sqp_step follows its direct solve with one pass of
-// iterative refinement (k_kkt_residual).
-static bool refine_enabled()
-{
-    const char* env = std::getenv("GATO_REFINE");
-    return env && std::strcmp(env, "1") == 0;
 }
 
 template <class SH>
@@ -671,12 +651,11 @@ struct Ops {
         }
         return hipGetLastError();
     }
-    static hipError_t merit(const Params& p, hipStream_t st)
+    static hipError_t merit(const Params& p, hipStream_t st, int variant = GATO_MERIT_PER_KNOT, int waves = 0)
     {
         const int P = leaves_for(p.N);
-        const int waves = merit_waves_default(p.N, KPW);
-        const dim3 blk(waves * 64);
-        if (merit_per_candidate()) {
+        const dim3 blk(merit_waves(p.N, KPW, waves) * 64);
+        if (variant == GATO_MERIT_PER_CANDIDATE) {
             const dim3 g(p.B, p.n_alpha + 1);
             switch (P / 16) {
                 case 4: hipLaunchKernelGGL((k_merit_cand<SH, 4>), g, blk, 0, st, p); break;
@@ -715,7 +694,7 @@ struct Ops {
     static hipError_t merit_ws(const Params& p, hipStream_t st)
     {
         const int y = merit_split(p);
-        if (y == 1 || merit_per_candidate() || p.mpart == nullptr) return merit(p, st);
+        if (y == 1 || p.mpart == nullptr) return merit(p, st);
         hipLaunchKernelGGL((k_merit_knots<SH>), dim3(p.B, y), dim3(1024), 0, st, p);
         switch (leaves_for(p.N) / 16) {
             case 4: hipLaunchKernelGGL((k_merit_sum<4>), dim3(p.B), dim3(256), 0, st, p); break;
@@ -926,7 +905,7 @@ int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, con
 }
 
 int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
-                   const float* gamma, const float* Qinv, const float* Rinv,
+                   const float* gamma, const float* Qinv, const float* Rinv, const float* A,
                    const float* Bu, const float* q, const float* r, float eps, int32_t max_iters,
                    float* lambda, float* dz, int32_t* iters, float* relres, int32_t* flags,
                    hipStream_t stream)
@@ -937,6 +916,7 @@ int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
     rc = check_ptrs({S, Pinv, gamma, Qinv, dyn(Rinv, dims), dyn(Bu, dims), q, dyn(r, dims),
                      lambda, dz, iters, relres, flags});
     if (rc) return rc;
+    if (A && !aligned4(A)) return GATO_E_ALIGN;  // not read: the recovery takes A_k' from S_{k,k+1}
     if (!(eps > 0.0f) || max_iters < 1) return GATO_E_PARAM;
     if (with_shape(dims->n, dims->m, [&](auto ops) { return decltype(ops)::pcg_supported(dims->N) ? 1 : 0; }) != 1)
         return GATO_E_UNSUPPORTED;
@@ -1021,14 +1001,15 @@ static int check_alpha(const float* alphas_host, int32_t n_alpha, float mu)
     return GATO_OK;
 }
 
-int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
-                    const float* r, const float* A, const float* Bu, const float* e,
-                    const float* x0, const float* dz, const float* alphas_host, int32_t n_alpha,
-                    float mu, float* merit, float* merit0, int32_t* best, int32_t* flags,
-                    hipStream_t stream)
+static int merit_call(const gato_dims_t* dims, const float* Q, const float* q, const float* R, const float* r,
+                      const float* A, const float* Bu, const float* e, const float* x0, const float* dz,
+                      const float* alphas_host, int32_t n_alpha, float mu, float* merit, float* merit0,
+                      int32_t* best, int32_t* flags, int32_t variant, int32_t waves, hipStream_t stream)
 {
     int rc = check_dims(dims);
     if (rc) return rc;
+    if (variant != GATO_MERIT_PER_KNOT && variant != GATO_MERIT_PER_CANDIDATE) return GATO_E_PARAM;
+    if (waves < 0 || waves > 16) return GATO_E_PARAM;
     if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
     rc = check_ptrs({Q, q, dyn(R, dims), dyn(r, dims), dyn(A, dims), dyn(Bu, dims), dyn(e, dims), x0, dz,
                      merit, merit0, best, flags});
@@ -1042,20 +1023,46 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
     for (int j = 0; j < n_alpha; ++j) p.alphas[j] = alphas_host[j];
     p.merit = merit; p.merit0 = merit0; p.best = best; p.flags = flags;
     return with_shape(dims->n, dims->m, [&](auto ops) {
-        return decltype(ops)::merit(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
+        return decltype(ops)::merit(p, stream, variant, waves) == hipSuccess ? GATO_OK : GATO_E_HIP;
     });
 }
 
-int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
-                  const float* r, const float* A, const float* Bu, const float* e,
-                  const float* x0, const float* rho, float eps, int32_t max_iters,
-                  const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
-                  float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
-                  int32_t* flags, void* workspace, size_t workspace_bytes,
-                  gato_stage_times_t* times, hipStream_t stream)
+int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                    const float* r, const float* A, const float* Bu, const float* e,
+                    const float* x0, const float* dz, const float* alphas_host, int32_t n_alpha,
+                    float mu, float* merit, float* merit0, int32_t* best, int32_t* flags,
+                    hipStream_t stream)
+{
+    return merit_call(dims, Q, q, R, r, A, Bu, e, x0, dz, alphas_host, n_alpha, mu, merit, merit0, best, flags,
+                      GATO_MERIT_PER_KNOT, 0, stream);
+}
+
+int gato_merit_eval_shape(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                          const float* r, const float* A, const float* Bu, const float* e,
+                          const float* x0, const float* dz, const float* alphas_host, int32_t n_alpha,
+                          float mu, float* merit, float* merit0, int32_t* best, int32_t* flags,
+                          int32_t variant, int32_t waves, hipStream_t stream)
+{
+    return merit_call(dims, Q, q, R, r, A, Bu, e, x0, dz, alphas_host, n_alpha, mu, merit, merit0, best, flags,
+                      variant, waves, stream);
+}
+
+int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                       const float* r, const float* A, const float* Bu, const float* e,
+                       const float* x0, const float* rho, float eps, int32_t max_iters,
+                       const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
+                       float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
+                       int32_t* flags, void* workspace, size_t workspace_bytes,
+                       gato_stage_times_t* times, const gato_step_opts_t* opts, hipStream_t stream)
 {
     int rc = check_dims(dims);
     if (rc) return rc;
+    const int solver = opts ? opts->solver : GATO_SOLVER_AUTO;
+    const int refine = opts ? opts->refine : 1;
+    if (solver != GATO_SOLVER_AUTO && solver != GATO_SOLVER_THOMAS && solver != GATO_SOLVER_CR &&
+        solver != GATO_SOLVER_CR_STREAM)
+        return GATO_E_PARAM;
+    if (refine != 0 && refine != 1) return GATO_E_PARAM;
     if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
     rc = check_ptrs({Q, q, dyn(R, dims), dyn(r, dims), dyn(A, dims), dyn(Bu, dims), dyn(e, dims), x0, lambda,
                      dz, merit, merit0, best, iters, relres, flags});
@@ -1101,12 +1108,13 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (fused) return O::fused(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
         // horizons a workgroup cannot hold: no Phi^-1, since a direct solve follows, and
         // no lower blocks of S when that solve reads only the upper ones
-        const bool cr = cr_preferred(dims);
-        p.s_upper_only = cr && !cr_reads_lower(dims);
+        const bool cr = solver == GATO_SOLVER_AUTO ? cr_preferred(dims) : solver != GATO_SOLVER_THOMAS;
+        p.cr_stream = solver == GATO_SOLVER_CR_STREAM;
+        p.s_upper_only = cr && !cr_reads_lower(dims, p.cr_stream != 0);
         if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
         if ((cr ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
-        if (refine_enabled()) {
+        if (refine) {
             // the correction system: its right-hand side and gamma (S, Q~^-1 and R^-1
             // are the first pass's), its solve, then the sum with the first pass
             char* ws = static_cast<char*>(workspace);
@@ -1153,6 +1161,19 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
         if (rc == GATO_OK && !ok) rc = GATO_E_HIP;
     }
     return rc;
+}
+
+int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                  const float* r, const float* A, const float* Bu, const float* e,
+                  const float* x0, const float* rho, float eps, int32_t max_iters,
+                  const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
+                  float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
+                  int32_t* flags, void* workspace, size_t workspace_bytes,
+                  gato_stage_times_t* times, hipStream_t stream)
+{
+    return gato_sqp_step_opts(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas_host, n_alpha, mu, lambda,
+                              dz, merit, merit0, best, iters, relres, flags, workspace, workspace_bytes, times,
+                              nullptr, stream);
 }
 
 }  // extern "C"

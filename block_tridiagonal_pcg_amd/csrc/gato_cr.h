@@ -249,6 +249,7 @@ __device__ __forceinline__ void cr_solve(const Params& p, int b)
 
     __shared__ int wg_flags;
     if (threadIdx.x == 0) wg_flags = 0;
+    __syncthreads();  // the flag word is zero before any wave can set a bit in it
     bool bad = false, nonfinite = false;
 
     int levels = 0;
@@ -590,6 +591,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     const int lev = me == 0 ? levels : 1 + __builtin_ctz(me);  // its elimination level (levels: the last solve)
 
     if (threadIdx.x == 0) sm.flags = 0;
+    __syncthreads();  // the flag word is zero before any wave can set a bit in it
     bool bad = false, nonfinite = false;
 
     // level 0, eliminations: the odd knots; their W rows go to LDS, and their C'
@@ -907,6 +909,7 @@ __device__ __forceinline__ void nd_reduce(const Params& p, int b)
     const int maxint = (N + ND_CHUNKS - 1) / ND_CHUNKS - 2;
     float(*t)[NC + 1] = sm.t[threadIdx.x / NP];
     if (threadIdx.x == 0) sm.flags = 0;
+    __syncthreads();  // the flag word is zero before any wave can set a bit in it
     bool bad = false;
 
     auto transpose = [&](const float* x, float* out) {  // out[c] = X[c][i], X's row i in lane i
@@ -1096,6 +1099,7 @@ __device__ __forceinline__ void nd_back(const Params& p, int b)
     const int a = nd_start(g, N), bk = nd_start(g + 1, N) - 1;
     const int maxint = (N + ND_CHUNKS - 1) / ND_CHUNKS - 2;
     if (threadIdx.x == 0) wg_flags = 0;
+    __syncthreads();  // the flag word is zero before any wave can set a bit in it
     bool nonfinite = false;
 
     // What lane i needs of interior knot k: row i of [W1 | w3], row i of C' and

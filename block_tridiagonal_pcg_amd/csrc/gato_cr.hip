@@ -13,8 +13,6 @@
 #include "gato_cr.h"
 
 #include <algorithm>
-#include <cstdlib>
-#include <cstring>
 
 namespace gato {
 
@@ -29,11 +27,7 @@ struct CrLaunch {
     static constexpr int MAXT = SH::NP == 16 ? 1024 : 512;
     static int threads(int N)
     {
-        int cap = MAXT / SH::NP;
-        if (const char* env = std::getenv("GATO_CR_GROUPS")) {  // lane groups per workgroup (measurements)
-            const int gr = std::atoi(env);
-            if (gr >= 1 && gr < cap) cap = gr;
-        }
+        const int cap = MAXT / SH::NP;
         const int want = (N + 1) / 2;
         const int groups = want < 1 ? 1 : (want < cap ? want : cap);
         return ((groups + SH::KPW - 1) / SH::KPW) * 64;
@@ -75,16 +69,10 @@ __global__ __launch_bounds__(ND_GPW * 16) void k_nd_back(Params p)
     nd_back<SH>(p, blockIdx.x);
 }
 
-static bool cr_streaming_forced()  // GATO_CR_VARIANT=stream: the streaming kernel for every N (measurements)
-{
-    const char* env = std::getenv("GATO_CR_VARIANT");
-    return env && std::strcmp(env, "stream") == 0;
-}
-
 template <class SH>
-static bool cr_resident(int N)
+static bool cr_resident(int N, bool stream)
 {
-    if constexpr (SH::NP == 16) return N <= 2 * CrResLds<SH>::MAXG && !cr_streaming_forced();
+    if constexpr (SH::NP == 16) return N <= 2 * CrResLds<SH>::MAXG && !stream;
     return false;
 }
 
@@ -92,12 +80,12 @@ template <class SH>
 static hipError_t cr_launch_shape(const Params& p, hipStream_t st)
 {
     if constexpr (SH::NP == 16) {
-        if (cr_resident<SH>(p.N)) {
+        if (cr_resident<SH>(p.N, p.cr_stream != 0)) {
             const int groups = (p.N + 1) / 2;
             hipLaunchKernelGGL((k_cr_res<SH>), dim3(p.B), dim3(((groups + SH::KPW - 1) / SH::KPW) * 64), 0, st, p);
             return hipGetLastError();
         }
-        if (!cr_streaming_forced()) {  // N > 128: nested dissection
+        if (!p.cr_stream) {  // N > 128: nested dissection
             static_assert(2 * ND_CHUNKS == 2 * CrResLds<SH>::MAXG, "boundary system = one resident workgroup");
             const dim3 chunks(p.B, ND_SPLIT), blk(ND_GPW * SH::NP);
             hipLaunchKernelGGL((k_nd_reduce<SH>), chunks, blk, 0, st, p);
@@ -147,9 +135,9 @@ size_t cr_ws_bytes(const gato_dims_t* d)
     return align256((stream > nd ? stream : nd) * sizeof(float));
 }
 
-bool cr_reads_lower(const gato_dims_t* d)
+bool cr_reads_lower(const gato_dims_t* d, bool stream)
 {
-    return !(d->n <= 16 && !cr_streaming_forced());
+    return !(d->n <= 16 && !stream);
 }
 
 // The long-horizon solve of gato_sqp_step, chosen by a cost model measured on
@@ -163,14 +151,9 @@ bool cr_reads_lower(const gato_dims_t* d)
 // solve with the streaming kernel (n > 16), once its batch fills the chip.
 // Cyclic reduction is taken while its batch time stays below block Thomas's
 // (the n <= 16 constants are from n = 14, the n > 16 ones from n = 24).
-// GATO_LONG_SOLVE=thomas or =cr forces either (for measurements).
 bool cr_preferred(const gato_dims_t* d)
 {
-    if (const char* env = std::getenv("GATO_LONG_SOLVE")) {
-        if (std::strcmp(env, "thomas") == 0) return false;
-        if (std::strcmp(env, "cr") == 0) return true;
-    }
-    const bool narrow = d->n <= 16 && !cr_streaming_forced();
+    const bool narrow = d->n <= 16;
     const double per_solve_us =
         narrow ? (d->N <= 2 * ND_CHUNKS ? 0.15 + 0.00105 * d->N : 0.18 + 0.0019 * d->N) : 0.017 * d->N;
     const bool wide = d->n > 16;  // 32-lane groups

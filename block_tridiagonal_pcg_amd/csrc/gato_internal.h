@@ -21,14 +21,15 @@ struct Params;
 size_t cr_ws_bytes(const gato_dims_t* d);
 
 // Launches the cyclic reduction for p (shape p.n x p.m, which must be one this
-// build has kernels for): the register-resident kernel where it applies, else
-// the streaming one.
+// build has kernels for): the register-resident kernel or the nested
+// dissection where they apply and p.cr_stream is 0, else the streaming one.
 hipError_t cr_launch(const Params& p, hipStream_t st);
 
 // Whether the cyclic reduction cr_launch runs for these dimensions reads the
-// lower blocks S_{k,k-1} (the streaming kernel does; the register-resident
-// kernel and the nested dissection read the upper blocks only).
-bool cr_reads_lower(const gato_dims_t* d);
+// lower blocks S_{k,k-1} (the streaming kernel does, and runs for n > 16 or
+// when `stream` asks for it; the register-resident kernel and the nested
+// dissection read the upper blocks only).
+bool cr_reads_lower(const gato_dims_t* d, bool stream);
 
 // Whether gato_sqp_step takes cyclic reduction rather than block Thomas
 // beyond the fused horizons, by the measured cost model.

@@ -28,6 +28,7 @@ struct Params {
     float alphas[GATO_MAX_ALPHA];
     int win_own;  // knots owned by one form workgroup (0: the whole horizon)
     int s_upper_only;  // stage 1 alone: write S's diagonal and upper blocks only (the solve reads no lower block)
+    int cr_stream;     // cyclic reduction: the streaming kernel (every level's rows in the workspace) for any n
     float* dws;   // direct solve: pivot inverses [B][N][n][n], then eliminated right-hand sides [B][N][n]
     float* mpart;  // merit split over workgroups: per-knot values [B][n_alpha + 1][N]
 };
@@ -553,9 +554,14 @@ struct PcgLds {
 // the same arithmetic as their owners, so the products need no more exchange.
 // lambda is accumulated in fp64: on ill-conditioned solves it sums hundreds of
 // small steps, and in fp32 that sum alone would cost ~1e-3 in dz.
+// Internal stop code of pcg() (not a GATO_F_* bit): with the assembled Phi^-1,
+// r'z <= 0 while the residual is above the tolerance, i.e. the fp32
+// preconditioner is not positive definite on this solve.
+constexpr int PCG_INDEFINITE = 1 << 16;
+
 template <class SH, int C, class MAT>
 __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* gam, float* lam, PcgLds<SH, C>& L,
-                                    int& iters_out, float& relres, int& flags_out)
+                                    int max_iters, int& iters_out, float& relres, int& flags_out)
 {
     constexpr int NP = SH::NP, SL = SH::SLOTS, KK = PcgLds<SH, C>::K, P = PcgLds<SH, C>::P;
     constexpr int LPL = P / 16;  // leaves per lane of the canonical sum
@@ -670,7 +676,10 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         __syncthreads();
     }
     if (!__builtin_isfinite(rr)) flags |= GATO_F_NONFINITE;
-    if (!(rr <= tol2) && !flags && iters >= p.max_iters) flags |= GATO_F_PCG_MAXITER;
+    if constexpr (MAT::kAssembled) {
+        if (!(rr <= tol2) && !flags && !(eta > 0.0f)) flags |= PCG_INDEFINITE;
+    }
+    if (!(rr <= tol2) && !flags && iters >= max_iters) flags |= GATO_F_PCG_MAXITER;
     if (!(rr <= tol2) && !flags) {
         // One exit, after the second barrier: a breakdown at the first one leaves
         // lambda, r and the count as they are and only sets the stop code, so every
@@ -745,7 +754,8 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 if (!__builtin_isfinite(rr)) stop = GATO_F_NONFINITE;
                 else if (rr <= tol2) stop = -1;  // converged
                 else if (!__builtin_isfinite(rz)) stop = GATO_F_NONFINITE;
-                else if (iters >= p.max_iters) stop = GATO_F_PCG_MAXITER;
+                else if (MAT::kAssembled && !(rz > 0.0f)) stop = PCG_INDEFINITE;
+                else if (iters >= max_iters) stop = GATO_F_PCG_MAXITER;
             }
             if (stop) {
                 if (stop > 0) flags |= stop;
@@ -771,26 +781,32 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
     __syncthreads();
 }
 
-// PCG as above; a solve that the assembled Phi^-1 leaves at the iteration cap
-// (its fp32 blocks can be indefinite where cond(Phi^-1) passes ~1e8) runs
-// again from its lambda with Phi^-1 in factored form, for up to max_iters more
-// iterations; iters counts both runs.  The decision is uniform over the
-// workgroup (one solve), and a solve that converges never takes it.
+// PCG as above within p.max_iters iterations in all.  With the assembled Phi^-1
+// a solve whose r'z stops being positive (its fp32 blocks can be indefinite
+// where cond(Phi^-1) passes ~1e8) switches at that iteration to Phi^-1 in
+// factored form and restarts from its current lambda with the iterations left;
+// iters counts both runs.  The decision is uniform over the workgroup (one
+// solve), and a solve whose r'z stays positive never takes it.
 template <class SH, int C, class MAT>
 __device__ __forceinline__ void pcg_robust(const Params& p, const MAT& M, const float* gam, float* lam,
                                            PcgLds<SH, C>& L, int& iters_out, float& relres, int& flags_out)
 {
-    pcg<SH, C>(p, M, gam, lam, L, iters_out, relres, flags_out);
+    pcg<SH, C>(p, M, gam, lam, L, p.max_iters, iters_out, relres, flags_out);
     if constexpr (MAT::kAssembled) {
         static_assert(C == 1, "one knot per lane group");
-        if (flags_out == GATO_F_PCG_MAXITER) {
-            float dsym[SH::NC];
-            sym_rows<SH>(M.rw->pd, L.xy[threadIdx.x / SH::NP + 1], dsym);
-            const RegMatF<SH> F{{M.rw}, dsym, L.xy};
-            int it2 = 0, fl2 = 0;
-            pcg<SH, C>(p, F, gam, lam, L, it2, relres, fl2);
-            iters_out += it2;
-            flags_out = fl2;
+        if (flags_out == PCG_INDEFINITE) {
+            const int left = p.max_iters - iters_out;
+            if (left <= 0) {
+                flags_out = GATO_F_PCG_MAXITER;
+            } else {
+                float dsym[SH::NC];
+                sym_rows<SH>(M.rw->pd, L.xy[threadIdx.x / SH::NP + 1], dsym);
+                const RegMatF<SH> F{{M.rw}, dsym, L.xy};
+                int it2 = 0, fl2 = 0;
+                pcg<SH, C>(p, F, gam, lam, L, left, it2, relres, fl2);
+                iters_out += it2;
+                flags_out = fl2;
+            }
         }
     }
 }

@@ -38,7 +38,9 @@ EXPORTS = (
     "gato_cr_workspace_bytes",
     "gato_cr_levels",
     "gato_merit_eval",
+    "gato_merit_eval_shape",
     "gato_sqp_step",
+    "gato_sqp_step_opts",
     "gato_workspace_bytes",
     "gato_step_solver",
     "gato_status_string",
@@ -54,6 +56,10 @@ class GatoError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32), ("N", ctypes.c_int32), ("B", ctypes.c_int32)]
+
+
+class StepOpts(ctypes.Structure):
+    _fields_ = [("solver", ctypes.c_int32), ("refine", ctypes.c_int32)]
 
 
 class StageTimes(ctypes.Structure):
@@ -79,7 +85,7 @@ def load():
             lib = ctypes.CDLL(_LIB_PATH)
             P, I, F, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
             lib.gato_form_schur.argtypes = [P] * 17
-            lib.gato_pcg_solve.argtypes = [P] * 9 + [F, I] + [P] * 6
+            lib.gato_pcg_solve.argtypes = [P] * 10 + [F, I] + [P] * 6
             lib.gato_direct_solve.argtypes = [P] * 12 + [Z, P]
             lib.gato_direct_workspace_bytes.argtypes = [P]
             lib.gato_direct_workspace_bytes.restype = Z
@@ -89,7 +95,9 @@ def load():
             lib.gato_cr_levels.argtypes = [I]
             lib.gato_cr_levels.restype = I
             lib.gato_merit_eval.argtypes = [P] * 11 + [I, F] + [P] * 5
+            lib.gato_merit_eval_shape.argtypes = [P] * 11 + [I, F] + [P] * 4 + [I, I, P]
             lib.gato_sqp_step.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P]
+            lib.gato_sqp_step_opts.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P, P]
             lib.gato_step_solver.argtypes = [P]
             lib.gato_step_solver.restype = ctypes.c_int
             lib.gato_workspace_bytes.argtypes = [P, I]
@@ -98,7 +106,7 @@ def load():
             lib.gato_status_string.restype = ctypes.c_char_p
             lib.gato_shape_supported.argtypes = [I, I, I]
             for f in ("gato_form_schur", "gato_pcg_solve", "gato_direct_solve", "gato_cr_solve", "gato_merit_eval",
-                      "gato_sqp_step", "gato_shape_supported"):
+                      "gato_merit_eval_shape", "gato_sqp_step", "gato_sqp_step_opts", "gato_shape_supported"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -170,17 +178,18 @@ def gato_form_schur(dims, Q, q, R, r, A, Bu, e, x0, rho, S, Pinv, gamma, Qinv, R
     return _raise("gato_form_schur", rc)
 
 
-def gato_pcg_solve(dims, S, Pinv, gamma, Qinv, Rinv, Bu, q, r, eps, max_iters, lam, dz, iters, relres,
+def gato_pcg_solve(dims, S, Pinv, gamma, Qinv, Rinv, A, Bu, q, r, eps, max_iters, lam, dz, iters, relres,
                    flags, stream=None):
+    """A may be None: the library takes A_k' from S's upper blocks and does not read it."""
     n, m, N, B = dims
     sh = _shapes(n, m, N, B)
-    for t, k in ((S, "S"), (Pinv, "Pinv"), (gamma, "gamma"), (Qinv, "Qinv"), (Rinv, "Rinv"),
+    for t, k in ((S, "S"), (Pinv, "Pinv"), (gamma, "gamma"), (Qinv, "Qinv"), (Rinv, "Rinv"), (A, "A"),
                  (Bu, "Bu"), (q, "q"), (r, "r"), (lam, "lam"), (dz, "dz"), (relres, "B_")):
         _chk(t, k, shape=sh[k])
     _chk(iters, "iters", torch.int32, sh["B_"])
     _chk(flags, "flags", torch.int32, sh["B_"])
     d = _dims(n, m, N, B)
-    rc = load().gato_pcg_solve(ctypes.byref(d), _p(S), _p(Pinv), _p(gamma), _p(Qinv), _p(Rinv), _p(Bu),
+    rc = load().gato_pcg_solve(ctypes.byref(d), _p(S), _p(Pinv), _p(gamma), _p(Qinv), _p(Rinv), _p(A), _p(Bu),
                                _p(q), _p(r), float(eps), int(max_iters), _p(lam), _p(dz), _p(iters),
                                _p(relres), _p(flags), _stream(stream))
     return _raise("gato_pcg_solve", rc)
@@ -242,7 +251,8 @@ def gato_cr_solve(dims, S, gamma, Qinv, Rinv, Bu, q, r, lam, dz, flags, workspac
     return _raise("gato_cr_solve", rc)
 
 
-SOLVER_FUSED_PCG, SOLVER_THOMAS, SOLVER_CR = 0, 1, 2
+SOLVER_AUTO, SOLVER_FUSED_PCG, SOLVER_THOMAS, SOLVER_CR, SOLVER_CR_STREAM = -1, 0, 1, 2, 3
+MERIT_PER_KNOT, MERIT_PER_CANDIDATE = 0, 1
 
 
 def gato_step_solver(dims):
@@ -259,7 +269,10 @@ def _alphas(alphas):
     return arr, len(a)
 
 
-def gato_merit_eval(dims, Q, q, R, r, A, Bu, e, x0, dz, alphas, mu, merit, merit0, best, flags, stream=None):
+def gato_merit_eval(dims, Q, q, R, r, A, Bu, e, x0, dz, alphas, mu, merit, merit0, best, flags, stream=None,
+                    variant=None, waves=0):
+    """With variant None, gato_merit_eval; else gato_merit_eval_shape with that launch
+    variant (MERIT_PER_KNOT / MERIT_PER_CANDIDATE) and `waves` wavefronts per workgroup."""
     n, m, N, B = dims
     sh = _shapes(n, m, N, B)
     for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
@@ -270,10 +283,12 @@ def gato_merit_eval(dims, Q, q, R, r, A, Bu, e, x0, dz, alphas, mu, merit, merit
     _chk(best, "best", torch.int32, sh["B_"])
     _chk(flags, "flags", torch.int32, sh["B_"])
     d = _dims(n, m, N, B)
-    rc = load().gato_merit_eval(ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0),
-                                _p(dz), arr, na, float(mu), _p(merit), _p(merit0), _p(best), _p(flags),
-                                _stream(stream))
-    return _raise("gato_merit_eval", rc)
+    args = (ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0), _p(dz), arr, na, float(mu),
+            _p(merit), _p(merit0), _p(best), _p(flags))
+    if variant is None:
+        return _raise("gato_merit_eval", load().gato_merit_eval(*args, _stream(stream)))
+    rc = load().gato_merit_eval_shape(*args, int(variant), int(waves), _stream(stream))
+    return _raise("gato_merit_eval_shape", rc)
 
 
 def gato_workspace_bytes(dims, n_alpha=8):
@@ -285,10 +300,17 @@ def gato_shape_supported(n, m, N):
     return bool(load().gato_shape_supported(int(n), int(m), int(N)))
 
 
+def _opts(solver, refine):
+    if solver is None and refine is None:
+        return None
+    return StepOpts(SOLVER_AUTO if solver is None else int(solver), 1 if refine is None else int(refine))
+
+
 def gato_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas, mu, lam, dz, merit, merit0,
-                  best, iters, relres, flags, workspace=None, times=False, stream=None):
+                  best, iters, relres, flags, workspace=None, times=False, stream=None, solver=None, refine=None):
     """One SQP iteration's core.  `workspace` is a uint8 CUDA tensor (or None when the
-    fused path needs none); with times=True returns a StageTimes (the call synchronises)."""
+    fused path needs none); with times=True returns a StageTimes (the call synchronises).
+    With solver or refine given the call is gato_sqp_step_opts with those choices."""
     n, m, N, B = dims
     sh = _shapes(n, m, N, B)
     for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
@@ -304,12 +326,14 @@ def gato_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas, m
         ws_ptr, ws_bytes = _p(workspace), workspace.numel()
     st = StageTimes() if times else None
     d = _dims(n, m, N, B)
-    rc = load().gato_sqp_step(ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0),
-                              _p(rho), float(eps), int(max_iters), arr, na, float(mu), _p(lam), _p(dz),
-                              _p(merit), _p(merit0), _p(best), _p(iters), _p(relres), _p(flags), ws_ptr,
-                              ctypes.c_size_t(ws_bytes), ctypes.byref(st) if st is not None else None,
-                              _stream(stream))
-    _raise("gato_sqp_step", rc)
+    args = (ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0), _p(rho), float(eps),
+            int(max_iters), arr, na, float(mu), _p(lam), _p(dz), _p(merit), _p(merit0), _p(best), _p(iters),
+            _p(relres), _p(flags), ws_ptr, ctypes.c_size_t(ws_bytes), ctypes.byref(st) if st is not None else None)
+    o = _opts(solver, refine)
+    if o is None:
+        _raise("gato_sqp_step", load().gato_sqp_step(*args, _stream(stream)))
+    else:
+        _raise("gato_sqp_step_opts", load().gato_sqp_step_opts(*args, ctypes.byref(o), _stream(stream)))
     return st
 
 
@@ -340,9 +364,10 @@ def alloc_outputs(dims, n_alpha=8, device="cuda"):
 
 
 def prepared_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas, mu, lam, dz, merit, merit0,
-                      best, iters, relres, flags, workspace=None, stream=None):
+                      best, iters, relres, flags, workspace=None, stream=None, solver=None, refine=None):
     """Check and marshal gato_sqp_step's arguments once; return a callable that only
-    makes the C call (for timing loops).  The tensors must stay alive and in place."""
+    makes the C call (for timing loops).  The tensors must stay alive and in place.
+    With solver or refine given it calls gato_sqp_step_opts with those choices."""
     n, m, N, B = dims
     sh = _shapes(n, m, N, B)
     for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
@@ -357,11 +382,17 @@ def prepared_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alpha
         _chk(workspace, "workspace", torch.uint8)
         ws_ptr, ws_bytes = _p(workspace), workspace.numel()
     d = _dims(n, m, N, B)
-    fn = load().gato_sqp_step
+    o = _opts(solver, refine)
     args = (ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0), _p(rho), float(eps),
             int(max_iters), arr, na, float(mu), _p(lam), _p(dz), _p(merit), _p(merit0), _p(best), _p(iters),
-            _p(relres), _p(flags), ws_ptr, ctypes.c_size_t(ws_bytes), None, _stream(stream))
-    keep = (d, arr)  # noqa: F841  (kept alive by the closure)
+            _p(relres), _p(flags), ws_ptr, ctypes.c_size_t(ws_bytes), None)
+    if o is None:
+        fn = load().gato_sqp_step
+        args = args + (_stream(stream),)
+    else:
+        fn = load().gato_sqp_step_opts
+        args = args + (ctypes.byref(o), _stream(stream))
+    keep = (d, arr, o)  # noqa: F841  (kept alive by the closure)
 
     def call():
         rc = fn(*args)
@@ -401,7 +432,7 @@ def stage_times(dims, dev, eps, max_iters, alphas, mu, reps=10, stream=None):
             gato_direct_solve(dims, out["S"], out["gamma"], out["Qinv"], out["Rinv"], dev["Bu"], dev["q"], dev["r"],
                               out["lam"], out["dz"], out["flags"], dws, stream=st)
         else:
-            gato_pcg_solve(dims, out["S"], out["Pinv"], out["gamma"], out["Qinv"], out["Rinv"], dev["Bu"],
+            gato_pcg_solve(dims, out["S"], out["Pinv"], out["gamma"], out["Qinv"], out["Rinv"], dev["A"], dev["Bu"],
                            dev["q"], dev["r"], eps, max_iters, out["lam"], out["dz"], out["iters"], out["relres"],
                            out["flags"], stream=st)
         ev[3].record(st)

@@ -139,27 +139,30 @@ int gato_form_schur(const gato_dims_t* dims, const float* Q, const float* q, con
  *   r = gamma - S lambda; z = Phi^-1 r; p = z; eta = r'z; then per iteration
  *   v = S p; a = eta / p'v; lambda += a p; r -= a v;
  *   stop when ||r||_2 <= eps ||gamma||_2;  z = Phi^-1 r; p = z + (r'z / eta) p.
- * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  Within the horizon one
- * workgroup holds, the assembled Phi^-1 blocks are applied; a solve they leave
- * at max_iters (their fp32 values can be indefinite where cond(Phi^-1) passes
- * ~1e8) runs again from its lambda with Phi^-1 in the factored form below,
- * for up to max_iters more iterations, and iters counts both runs.  Beyond the
- * horizon one workgroup holds (N > 64 for n <= 16, N > 16 for n <= 32) z = Phi^-1 r is
- * applied in the preconditioner's factored form D^-1 (J S J) (D^-1 r), with
- * D^-1 = the diagonal blocks of Phi^-1 and J = blkdiag((-1)^k I): the same
- * operator, which stays positive definite in fp32 while S does even where the
- * assembled fp32 Phi^-1 does not (its condition can pass 1e8 on ill-conditioned
- * long horizons); it reads S and the diagonal blocks of Phi^-1.  Then the step
+ * ||gamma|| = 0 gives lambda = 0 after 0 iterations.  iters never exceeds
+ * max_iters.  Within the horizon one workgroup holds, the assembled Phi^-1
+ * blocks are applied; their fp32 values can be indefinite where cond(Phi^-1)
+ * passes ~1e8, which shows as r'z <= 0 while the residual is above the
+ * tolerance.  Such a solve switches at that iteration to Phi^-1 in the factored
+ * form below and restarts from its current lambda with the iterations left of
+ * max_iters (iters counts both runs).  Beyond the horizon one workgroup holds
+ * (N > 64 for n <= 16, N > 16 for n <= 32) z = Phi^-1 r is always applied in the
+ * preconditioner's factored form D^-1 (J S J) (D^-1 r), with D^-1 = the diagonal
+ * blocks of Phi^-1 and J = blkdiag((-1)^k I): the same operator, which stays
+ * positive definite in fp32 while S does even where the assembled fp32 Phi^-1
+ * does not; it reads S and the diagonal blocks of Phi^-1.  Then the step
  *   dx_k = Qinv_k (lambda_k - A_k' lambda_{k+1} - q_k),  dx_{N-1} = Qinv_{N-1}(lambda_{N-1} - q_{N-1}),
  *   du_k = Rinv_k (-B_k' lambda_{k+1} - r_k),
  * evaluated as dx_k = Qinv_k lambda_k + S_{k,k+1} lambda_{k+1} - Qinv_k q_k, since
- * S_{k,k+1} = -Q~_k^-1 A_k' (so A is not an argument: S, Qinv, q, Bu, Rinv, r
- * must be those of one problem, as gato_form_schur writes them).
+ * S_{k,k+1} = -Q~_k^-1 A_k'.  A is therefore not read and may be NULL (it is
+ * kept in the argument list so that the call takes the QP data as the problem
+ * states it); S, Qinv, q, Bu, Rinv and r must be those of one problem, as
+ * gato_form_schur writes them.
  * Writes lambda, dz, iters (S-products in the loop), relres (recurred
  * ||r|| / ||gamma||) and ORs PCG_MAXITER / PCG_BREAKDOWN / NONFINITE into flags.
  */
 int gato_pcg_solve(const gato_dims_t* dims, const float* S, const float* Pinv,
-                   const float* gamma, const float* Qinv, const float* Rinv,
+                   const float* gamma, const float* Qinv, const float* Rinv, const float* A,
                    const float* Bu, const float* q, const float* r, float eps, int32_t max_iters,
                    float* lambda, float* dz, int32_t* iters, float* relres, int32_t* flags,
                    hipStream_t stream);
@@ -246,6 +249,28 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
                     float mu, float* merit, float* merit0, int32_t* best, int32_t* flags,
                     hipStream_t stream);
 
+/* Launch shapes of the merit (the GATO docs' "Merit launch timing": one block
+ * per solve evaluating every candidate per knot, against one block per
+ * candidate, at several block sizes).  gato_merit_eval with an explicit shape:
+ *   variant GATO_MERIT_PER_KNOT: one workgroup per solve; each knot's
+ *           step-size-independent products are formed once and every step size
+ *           rescales them (gato_merit_eval's choice);
+ *   variant GATO_MERIT_PER_CANDIDATE: one workgroup per (solve, step size, and
+ *           the step size 0 of merit0), each recomputing the knot's products,
+ *           then a selection kernel;
+ *   waves:  wavefronts of 64 lanes per workgroup, 1..16, or 0 for
+ *           gato_merit_eval's choice (enough for every knot at once, at most 16).
+ * Every shape gives bit-identical merit, merit0, best and flags (the sums
+ * over knots are the same canonical pairwise tree).  GATO_E_PARAM for an
+ * unknown variant or waves outside [0, 16]. */
+#define GATO_MERIT_PER_KNOT 0
+#define GATO_MERIT_PER_CANDIDATE 1
+int gato_merit_eval_shape(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                          const float* r, const float* A, const float* Bu, const float* e,
+                          const float* x0, const float* dz, const float* alphas_host, int32_t n_alpha,
+                          float mu, float* merit, float* merit0, int32_t* best, int32_t* flags,
+                          int32_t variant, int32_t waves, hipStream_t stream);
+
 /*
  * The three stages in one call (one SQP iteration's linear-algebra core,
  * GATO paper Sec. III, Fig. 2 steps a-c).  Outputs are those of the three
@@ -259,29 +284,26 @@ int gato_merit_eval(const gato_dims_t* dims, const float* Q, const float* q, con
  *    reduction while the batch is small enough for its log-depth to pay
  *    (measured switch points: B * (0.15 + 0.00105 N) us < 2.7 N us for n <= 16
  *    and N <= 128, B * (0.18 + 0.0019 N) us < 2.7 N us for n <= 16 beyond
- *    (B < ~1040-1300), B < ~400 for n > 16), else
- *    gato_direct_solve's block Thomas elimination (the environment variable
- *    GATO_LONG_SOLVE=thomas or =cr forces either).  With the environment
- *    variable GATO_REFINE=1 the direct solve is followed by one pass of
- *    iterative refinement of the KKT system (G dz - C' lambda = -g, C dz = c):
- *    its residual, accumulated in double from the problem data, is the
- *    right-hand side of a correction system with the same S, Q~^-1 and R^-1,
- *    whose gamma is formed from it and which the same direct solve solves;
- *    its lambda and dz are added to the first pass's.  That adds one solve
- *    and two light kernels (0.258 -> 0.467 ms per step on an ill-conditioned
- *    N = 128, B = 512 batch) and takes dz from the fp32 stages' accuracy on S
- *    (relative error up to about cond(S) * 1e-7, so ~1e-3 at cond(S) ~ 1e6)
- *    to ~1e-5.  The merit is evaluated on the refined dz; linsys_us includes
- *    the pass.
+ *    (B < ~1040-1300), B < ~400 for n > 16), else gato_direct_solve's block
+ *    Thomas elimination.  The direct solve is followed by one pass of
+ *    iterative refinement of the KKT system (G dz - C' lambda = -g, C dz = c;
+ *    the paper's eq. 2): its residual, accumulated in double from the problem
+ *    data, is the right-hand side of a correction system with the same S,
+ *    Q~^-1 and R^-1, whose gamma is formed from it and which the same direct
+ *    solve solves; its lambda and dz are added to the first pass's.  The fp32
+ *    stages alone leave dz with a relative error of up to about
+ *    cond(S) * 1e-7 (~1e-3 at cond(S) ~ 1e6, where rounding S to fp32 already
+ *    moves dz by up to 6e-4); the pass brings it to ~1e-5 for one more solve
+ *    and two light kernels.  The merit is evaluated on the refined dz;
+ *    linsys_us includes the pass.
  *    lambda's input is not read, iters and relres are written as 0, and eps
  *    and max_iters are checked but unused.  S (no Phi^-1: the
  *    direct solves do not use it), gamma, Qinv, Rinv, the solve's rows, the
  *    refinement pass's buffers and the merit's per-knot values go through
- *    `workspace`
- *    (gato_workspace_bytes() bytes, 256-byte aligned, caller-owned device
- *    memory).  With a small batch the merit then spreads a solve's knots over
- *    several workgroups and sums their values in a second kernel, in the
- *    same canonical order (identical bits).
+ *    `workspace` (gato_workspace_bytes() bytes, 256-byte aligned,
+ *    caller-owned device memory).  With a small batch the merit then spreads
+ *    a solve's knots over several workgroups and sums their values in a
+ *    second kernel, in the same canonical order (identical bits).
  * times (nullable): per-stage device times; when given, the call synchronises.
  */
 int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
@@ -292,12 +314,42 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
                   int32_t* flags, void* workspace, size_t workspace_bytes,
                   gato_stage_times_t* times, hipStream_t stream);
 
-/* The stage-2 solver gato_sqp_step runs for these dims (horizon policy above),
- * in the calling process's environment: GATO_SOLVER_FUSED_PCG, GATO_SOLVER_THOMAS
- * or GATO_SOLVER_CR; a negative status for invalid or unsupported dims. */
-#define GATO_SOLVER_FUSED_PCG 0
-#define GATO_SOLVER_THOMAS 1
-#define GATO_SOLVER_CR 2
+/* Stage-2 solvers of gato_sqp_step (gato_step_solver's result, and a choice
+ * in gato_step_opts_t). */
+#define GATO_SOLVER_AUTO (-1)     /* the horizon policy above */
+#define GATO_SOLVER_FUSED_PCG 0   /* one fused kernel with PCG */
+#define GATO_SOLVER_THOMAS 1      /* block Thomas (gato_direct_solve) */
+#define GATO_SOLVER_CR 2          /* block cyclic reduction (gato_cr_solve) */
+#define GATO_SOLVER_CR_STREAM 3   /* block cyclic reduction with every level's rows in the
+                                     workspace (the kernel n > 16 always uses) */
+
+/* Per-call choices of gato_sqp_step_opts.  They select among kernels and
+ * passes; none of them changes the problem solved.
+ *   solver: for horizons beyond the fused ones, GATO_SOLVER_AUTO (the
+ *           horizon policy), GATO_SOLVER_THOMAS, GATO_SOLVER_CR or
+ *           GATO_SOLVER_CR_STREAM; ignored where the fused path applies.
+ *   refine: 1 (the default of gato_sqp_step) runs the KKT refinement pass
+ *           after a direct solve, 0 leaves the fp32 direct solve's step as
+ *           it is; ignored where the fused path applies. */
+typedef struct {
+    int32_t solver;
+    int32_t refine;
+} gato_step_opts_t;
+
+/* gato_sqp_step with explicit choices: arguments and outputs as there, plus
+ * opts (nullable: {GATO_SOLVER_AUTO, 1}, i.e. exactly gato_sqp_step).  An
+ * unknown solver or a refine outside {0, 1} returns GATO_E_PARAM. */
+int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                       const float* r, const float* A, const float* Bu, const float* e,
+                       const float* x0, const float* rho, float eps, int32_t max_iters,
+                       const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
+                       float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
+                       int32_t* flags, void* workspace, size_t workspace_bytes,
+                       gato_stage_times_t* times, const gato_step_opts_t* opts, hipStream_t stream);
+
+/* The stage-2 solver gato_sqp_step runs for these dims (the horizon policy
+ * above, a pure function of dims): GATO_SOLVER_FUSED_PCG, GATO_SOLVER_THOMAS or
+ * GATO_SOLVER_CR; a negative status for invalid or unsupported dims. */
 int gato_step_solver(const gato_dims_t* dims);
 
 /* Workspace gato_sqp_step needs for these dims (0 when the fused path applies). */

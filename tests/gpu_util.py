@@ -38,7 +38,7 @@ def gpu_pcg(batch, form, eps, max_iters, lambda0=None, flags=None):
     relres = torch.zeros(B, dtype=torch.float32, device="cuda")
     fl = torch.as_tensor(np.zeros(B, np.int32) if flags is None else np.asarray(flags, np.int32)).cuda()
     ops.gato_pcg_solve(dims, t(form["S"]), t(form["Pinv"]), t(form["gamma"]), t(form["Qinv"]), t(form["Rinv"]),
-                       t(batch["Bu"]), t(batch["q"]), t(batch["r"]), eps, max_iters, lam, dz,
+                       t(batch["A"]), t(batch["Bu"]), t(batch["q"]), t(batch["r"]), eps, max_iters, lam, dz,
                        iters, relres, fl)
     torch.cuda.synchronize()
     return dict(lam=cpu(lam), dz=cpu(dz), iters=cpu(iters), relres=cpu(relres), flags=cpu(fl))
@@ -68,7 +68,7 @@ def gpu_direct(batch, form, flags=None, solver="thomas"):
     return dict(lam=cpu(lam), dz=cpu(dz), flags=cpu(fl))
 
 
-def gpu_merit(batch, dz, mu, alphas=ALPHAS, flags=None):
+def gpu_merit(batch, dz, mu, alphas=ALPHAS, flags=None, variant=None, waves=0):
     dims = batch["dims"]
     B = dims[3]
     dev = ops.to_device(batch)
@@ -77,12 +77,15 @@ def gpu_merit(batch, dz, mu, alphas=ALPHAS, flags=None):
     merit0 = torch.zeros(B, dtype=torch.float32, device="cuda")
     best = torch.zeros(B, dtype=torch.int32, device="cuda")
     fl = torch.as_tensor(np.zeros(B, np.int32) if flags is None else np.asarray(flags, np.int32)).cuda()
-    ops.gato_merit_eval(dims, *[dev[f] for f in synth.FIELDS], dzt, alphas, mu, merit, merit0, best, fl)
+    ops.gato_merit_eval(dims, *[dev[f] for f in synth.FIELDS], dzt, alphas, mu, merit, merit0, best, fl,
+                        variant=variant, waves=waves)
     torch.cuda.synchronize()
     return dict(merit=cpu(merit), merit0=cpu(merit0), best=cpu(best), flags=cpu(fl))
 
 
-def gpu_sqp(batch, eps, max_iters, mu=1.0, alphas=ALPHAS, rho=None, lambda0=None, times=False):
+def gpu_sqp(batch, eps, max_iters, mu=1.0, alphas=ALPHAS, rho=None, lambda0=None, times=False, solver=None,
+            refine=None):
+    """gato_sqp_step (gato_sqp_step_opts when solver or refine is given) on a synth batch."""
     dims = batch["dims"]
     n, m, N, B = dims
     dev = ops.to_device(batch)
@@ -95,7 +98,7 @@ def gpu_sqp(batch, eps, max_iters, mu=1.0, alphas=ALPHAS, rho=None, lambda0=None
         ws.fill_(255)  # every float NaN: a read of a row the step did not write shows in the result
     st = ops.gato_sqp_step(dims, *[dev[f] for f in synth.FIELDS], rh, eps, max_iters, alphas, mu, out["lam"],
                            out["dz"], out["merit"], out["merit0"], out["best"], out["iters"], out["relres"],
-                           out["flags"], workspace=ws, times=times)
+                           out["flags"], workspace=ws, times=times, solver=solver, refine=refine)
     torch.cuda.synchronize()
     res = {k: cpu(out[k]) for k in ("lam", "dz", "merit", "merit0", "best", "iters", "relres", "flags")}
     res["times"] = st
@@ -109,6 +112,18 @@ def rel_rows(a, b):
     den = np.linalg.norm(b, axis=1)
     den[den == 0] = 1.0
     return np.linalg.norm(a - b, axis=1) / den
+
+
+def btd_relres(S, gamma, lam):
+    """Per-solve ||S lam - gamma|| / ||gamma|| in fp64 for block-tridiagonal S in the
+    [B][N][3][n][n] block-row layout (block row k = [S_{k,k-1}, S_{k,k}, S_{k,k+1}])."""
+    S = np.asarray(S, np.float64)
+    lam = np.asarray(lam, np.float64)
+    v = np.einsum("bkij,bkj->bki", S[:, :, 1], lam)
+    v[:, 1:] += np.einsum("bkij,bkj->bki", S[:, 1:, 0], lam[:, :-1])
+    v[:, :-1] += np.einsum("bkij,bkj->bki", S[:, :-1, 2], lam[:, 1:])
+    g = np.asarray(gamma, np.float64)
+    return np.linalg.norm((v - g).reshape(len(g), -1), axis=1) / np.linalg.norm(g.reshape(len(g), -1), axis=1)
 
 
 def merit_rel(gpu_merit_vals, ref):

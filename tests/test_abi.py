@@ -23,12 +23,91 @@ def lib():
     return ops.load()
 
 
+def _prototypes():
+    """{function: [(type, name), ...]} of every declaration in the header."""
+    text = re.sub(r"/\*.*?\*/", " ", open(os.path.join(ROOT, "include", "gato.h")).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"(?:int32_t|int|size_t|const char\*)\s+(gato_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = []
+        for arg in m.group(2).split(","):
+            arg = " ".join(arg.split())
+            if arg in ("", "void"):
+                continue
+            name = re.search(r"(\w+)$", arg).group(1)
+            params.append((arg[: -len(name)].replace(" *", "*").strip(), name))
+        out[m.group(1)] = params
+    return out
+
+
+# The four calls of the boundary, argument by argument (type, name), as the QP data
+# enters them: the problem arrays in the order the paper states the problem, then the
+# stage's outputs, then the stream.
+BOUNDARY = {
+    "gato_form_schur": [
+        ("const gato_dims_t*", "dims"), ("const float*", "Q"), ("const float*", "q"), ("const float*", "R"),
+        ("const float*", "r"), ("const float*", "A"), ("const float*", "Bu"), ("const float*", "e"),
+        ("const float*", "x0"), ("const float*", "rho"), ("float*", "S"), ("float*", "Pinv"), ("float*", "gamma"),
+        ("float*", "Qinv"), ("float*", "Rinv"), ("int32_t*", "flags"), ("hipStream_t", "stream")],
+    "gato_pcg_solve": [
+        ("const gato_dims_t*", "dims"), ("const float*", "S"), ("const float*", "Pinv"), ("const float*", "gamma"),
+        ("const float*", "Qinv"), ("const float*", "Rinv"), ("const float*", "A"), ("const float*", "Bu"),
+        ("const float*", "q"), ("const float*", "r"), ("float", "eps"), ("int32_t", "max_iters"),
+        ("float*", "lambda"), ("float*", "dz"), ("int32_t*", "iters"), ("float*", "relres"), ("int32_t*", "flags"),
+        ("hipStream_t", "stream")],
+    "gato_merit_eval": [
+        ("const gato_dims_t*", "dims"), ("const float*", "Q"), ("const float*", "q"), ("const float*", "R"),
+        ("const float*", "r"), ("const float*", "A"), ("const float*", "Bu"), ("const float*", "e"),
+        ("const float*", "x0"), ("const float*", "dz"), ("const float*", "alphas_host"), ("int32_t", "n_alpha"),
+        ("float", "mu"), ("float*", "merit"), ("float*", "merit0"), ("int32_t*", "best"), ("int32_t*", "flags"),
+        ("hipStream_t", "stream")],
+    "gato_sqp_step": [
+        ("const gato_dims_t*", "dims"), ("const float*", "Q"), ("const float*", "q"), ("const float*", "R"),
+        ("const float*", "r"), ("const float*", "A"), ("const float*", "Bu"), ("const float*", "e"),
+        ("const float*", "x0"), ("const float*", "rho"), ("float", "eps"), ("int32_t", "max_iters"),
+        ("const float*", "alphas_host"), ("int32_t", "n_alpha"), ("float", "mu"), ("float*", "lambda"),
+        ("float*", "dz"), ("float*", "merit"), ("float*", "merit0"), ("int32_t*", "best"), ("int32_t*", "iters"),
+        ("float*", "relres"), ("int32_t*", "flags"), ("void*", "workspace"), ("size_t", "workspace_bytes"),
+        ("gato_stage_times_t*", "times"), ("hipStream_t", "stream")],
+    "gato_workspace_bytes": [("const gato_dims_t*", "dims"), ("int32_t", "n_alpha")],
+    "gato_status_string": [("int", "code")],
+}
+
+
 def test_header_declares_the_abi():
     assert _declared() == sorted([
         "gato_cr_levels", "gato_cr_solve", "gato_cr_workspace_bytes",
         "gato_direct_solve", "gato_direct_workspace_bytes", "gato_form_schur", "gato_merit_eval",
-        "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step", "gato_status_string", "gato_step_solver",
-        "gato_workspace_bytes"])
+        "gato_merit_eval_shape", "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step", "gato_sqp_step_opts",
+        "gato_status_string", "gato_step_solver", "gato_workspace_bytes"])
+
+
+def test_boundary_signatures():
+    """The header's argument lists of the boundary calls, type and name, in order."""
+    protos = _prototypes()
+    for fn, args in BOUNDARY.items():
+        assert protos[fn] == args, fn
+    # the variants add their choices just before the stream and change nothing else
+    assert protos["gato_sqp_step_opts"] == BOUNDARY["gato_sqp_step"][:-1] + [
+        ("const gato_step_opts_t*", "opts"), ("hipStream_t", "stream")]
+    assert protos["gato_merit_eval_shape"] == BOUNDARY["gato_merit_eval"][:-1] + [
+        ("int32_t", "variant"), ("int32_t", "waves"), ("hipStream_t", "stream")]
+
+
+def test_binding_argument_counts_match_the_header(lib):
+    """ops.py declares as many ctypes arguments as the header has parameters."""
+    protos = _prototypes()
+    for fn in _declared():
+        assert len(getattr(lib, fn).argtypes) == len(protos[fn]), fn
+
+
+def test_library_reads_no_environment():
+    """Every choice that changes which kernel or pass runs is a call argument: the
+    library's sources read no environment variable."""
+    csrc = os.path.join(ROOT, "block_tridiagonal_pcg_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".inc", ".cpp")):
+            text = open(os.path.join(csrc, f)).read()
+            assert "getenv" not in text and "environ" not in text, f
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -98,11 +177,15 @@ def test_validation_happens_before_any_launch(lib):
     P = [ctypes.c_void_p(4096 * (j + 1)) for j in range(17)]
     f = lib.gato_pcg_solve
     # eps <= 0 and max_iters < 1
-    assert f(ctypes.byref(d), *P[:8], 0.0, 10, *P[8:13], None) == ops.E_PARAM
-    assert f(ctypes.byref(d), *P[:8], 1e-6, 0, *P[8:13], None) == ops.E_PARAM
-    assert f(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:8], 1e-6, 10, *P[8:13], None) == ops.OK
+    assert f(ctypes.byref(d), *P[:9], 0.0, 10, *P[9:14], None) == ops.E_PARAM
+    assert f(ctypes.byref(d), *P[:9], 1e-6, 0, *P[9:14], None) == ops.E_PARAM
+    assert f(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:9], 1e-6, 10, *P[9:14], None) == ops.OK
+    # A is not read, but a pointer given must still be aligned
+    misA = list(P)
+    misA[5] = ctypes.c_void_p(4096 * 6 + 2)
+    assert f(ctypes.byref(d), *misA[:9], 1e-6, 10, *misA[9:14], None) == ops.E_ALIGN
     # PCG holds at most four knots per lane group
-    assert f(ctypes.byref(ops.Dims(14, 7, 257, 2)), *P[:8], 1e-6, 10, *P[8:13], None) == ops.E_UNSUPPORTED
+    assert f(ctypes.byref(ops.Dims(14, 7, 257, 2)), *P[:9], 1e-6, 10, *P[9:14], None) == ops.E_UNSUPPORTED
 
     # direct solve: workspace size, alignment and presence are checked on the host
     dd = lib.gato_direct_solve
@@ -141,6 +224,11 @@ def test_validation_happens_before_any_launch(lib):
     assert g(ctypes.byref(d), *P[:9], al, 17, 1.0, *P[9:13], None) == ops.E_PARAM
     assert g(ctypes.byref(d), *P[:9], al, 8, -1.0, *P[9:13], None) == ops.E_PARAM
     assert g(ctypes.byref(d), *P[:9], None, 8, 1.0, *P[9:13], None) == ops.E_NULL
+    gs = lib.gato_merit_eval_shape
+    assert gs(ctypes.byref(d), *P[:9], al, 8, 1.0, *P[9:13], 2, 0, None) == ops.E_PARAM   # unknown variant
+    assert gs(ctypes.byref(d), *P[:9], al, 8, 1.0, *P[9:13], 0, 17, None) == ops.E_PARAM  # waves > 16
+    assert gs(ctypes.byref(d), *P[:9], al, 8, 1.0, *P[9:13], 1, -1, None) == ops.E_PARAM  # waves < 0
+    assert gs(ctypes.byref(ops.Dims(14, 7, 64, 0)), *P[:9], al, 8, 1.0, *P[9:13], 1, 4, None) == ops.OK
 
     h = lib.gato_sqp_step
     long_d = ops.Dims(14, 7, 128, 4)
@@ -152,6 +240,17 @@ def test_validation_happens_before_any_launch(lib):
     ok_size = ctypes.c_size_t(ops.gato_workspace_bytes((14, 7, 128, 4)))
     assert h(ctypes.byref(long_d), *args, ctypes.c_void_p((1 << 20) + 4), ok_size, None, None) == ops.E_ALIGN
     assert h(ctypes.byref(ops.Dims(14, 7, 128, 0)), *args, None, ctypes.c_size_t(0), None, None) == ops.OK
+    # gato_sqp_step_opts: the same checks, and its choices are validated first
+    ho = lib.gato_sqp_step_opts
+    for solver, refine in ((0, 1), (4, 1), (-2, 0), (-1, 2), (2, -1)):
+        o = ops.StepOpts(solver, refine)
+        assert ho(ctypes.byref(long_d), *args, ctypes.c_void_p(1 << 20), ok_size, None, ctypes.byref(o),
+                  None) == ops.E_PARAM, (solver, refine)
+    o = ops.StepOpts(ops.SOLVER_THOMAS, 0)
+    assert ho(ctypes.byref(long_d), *args, None, ctypes.c_size_t(0), None, ctypes.byref(o), None) == ops.E_WORKSPACE
+    assert ho(ctypes.byref(ops.Dims(14, 7, 128, 0)), *args, None, ctypes.c_size_t(0), None, ctypes.byref(o),
+              None) == ops.OK
+    assert ho(ctypes.byref(ops.Dims(14, 7, 128, 0)), *args, None, ctypes.c_size_t(0), None, None, None) == ops.OK
 
 
 def test_single_knot_allows_empty_dynamics(lib):
@@ -180,7 +279,7 @@ def test_cyclic_reduction_depth_matches_the_plan(lib):
         assert ops.gato_cr_levels(N) == len(oracle.cyclic_plan(N)), N
 
 
-def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
+def test_horizon_policy_picks_the_measured_solver(lib):
     """Fused PCG where a workgroup holds the horizon; beyond, cyclic reduction while
     its batch time (0.15 us + 1.05 ns per knot per solve resident, 0.18 us + 1.9 ns per
     knot per solve with the nested dissection, 17 ns per knot and solve streaming for
@@ -188,8 +287,6 @@ def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
     the batch fills the chip; 6.9 us and 5.6 ns for n > 16)."""
     from block_tridiagonal_pcg_amd import ops
 
-    monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
-    monkeypatch.delenv("GATO_CR_VARIANT", raising=False)
     F, T, C = ops.SOLVER_FUSED_PCG, ops.SOLVER_THOMAS, ops.SOLVER_CR
     cases = {(14, 7, 64, 128): F, (24, 12, 16, 4): F, (14, 7, 65, 512): C, (14, 7, 65, 1024): T,
              (14, 7, 128, 512): C, (14, 7, 128, 1024): C, (14, 7, 128, 2048): T,
@@ -197,10 +294,5 @@ def test_horizon_policy_picks_the_measured_solver(lib, monkeypatch):
              (14, 7, 1024, 1024): C, (14, 7, 1024, 2048): T, (24, 12, 100, 8): C, (24, 12, 100, 256): C, (24, 12, 100, 512): T, (24, 12, 100, 1024): T}
     for dims, want in cases.items():
         assert ops.gato_step_solver(dims) == want, dims
-    monkeypatch.setenv("GATO_LONG_SOLVE", "thomas")
-    assert ops.gato_step_solver((14, 7, 128, 16)) == T
-    assert ops.gato_step_solver((14, 7, 64, 16)) == F  # the fused path is not affected
-    monkeypatch.setenv("GATO_LONG_SOLVE", "cr")
-    assert ops.gato_step_solver((14, 7, 1024, 4096)) == C
     with pytest.raises(ops.GatoError):
         ops.gato_step_solver((13, 7, 128, 16))

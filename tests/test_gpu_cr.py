@@ -124,38 +124,43 @@ def test_cr_agrees_with_block_thomas():
 
 
 @pytest.mark.parametrize("N", [2, 3, 17, 64, 100, 127, 128, 129, 191, 300, 1024])
-def test_cr_resident_and_streaming_kernels_agree(N, monkeypatch):
+def test_cr_resident_and_streaming_kernels_agree(N):
     """Up to 128 knots (n <= 16) the solve runs with every knot held in registers
     and LDS, beyond that as a nested dissection (chunk interiors, then the
-    boundary system in registers); GATO_CR_VARIANT=stream selects the kernel that
-    keeps the reduced rows in the workspace.  Both are held to the oracle, and to
-    each other."""
+    boundary system in registers); GATO_SOLVER_CR_STREAM selects the kernel that
+    keeps the reduced rows in the workspace (the one n > 16 always uses).  Every
+    kernel is held to the oracle; beyond the fused horizon (where the step takes a
+    direct solve) the resident and streaming kernels also run on the same formed
+    system through gato_sqp_step_opts, refinement off, and are held to each other."""
+    from gpu_util import gpu_sqp
+
     _ident("cr variants", N)
     bt = synth.make_batch(2, 3, N=N)
     form = oracle.form_schur(*synth.inputs(bt))
     _, dz = _exact(bt, form)
     res = _cr(bt, form)
-    monkeypatch.setenv("GATO_CR_VARIANT", "stream")
-    st = _cr(bt, form)
-    for g in (res, st):
-        assert (g["flags"] == 0).all()
-        assert rel_rows(g["dz"], dz).max() <= 5e-5
-    assert rel_rows(res["dz"], st["dz"]).max() <= 2e-5
+    assert (res["flags"] == 0).all()
+    assert rel_rows(res["dz"], dz).max() <= 5e-5
+    if N > 64:
+        a = gpu_sqp(bt, 1e-6, 200, solver=ops.SOLVER_CR, refine=0)
+        st = gpu_sqp(bt, 1e-6, 200, solver=ops.SOLVER_CR_STREAM, refine=0)
+        for g in (a, st):
+            assert (g["flags"] & ~ops.F_LS_FAILED == 0).all()
+            assert rel_rows(g["dz"], dz).max() <= 5e-5
+        assert rel_rows(a["dz"], st["dz"]).max() <= 2e-5
 
 
-@pytest.mark.parametrize("solver", ["cr", "thomas", None])
-def test_sqp_step_long_horizon_with_either_solver(solver, monkeypatch):
+@pytest.mark.parametrize("solver", ["cr", "thomas", "stream", None])
+def test_sqp_step_long_horizon_with_either_solver(solver):
     """gato_sqp_step beyond the fused horizons, with the policy's choice and with
-    each solver forced: the step is the oracle's exact step within the bar."""
+    each solver chosen through gato_sqp_step_opts: the step is the oracle's exact step
+    within the bar."""
     from gpu_util import gpu_sqp
 
-    if solver:
-        monkeypatch.setenv("GATO_LONG_SOLVE", solver)
-    else:
-        monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
     _ident("sqp long horizon", solver)
     bt = synth.make_batch(3, 6, N=150)
-    g = gpu_sqp(bt, 1e-6, 200)
+    which = {"cr": ops.SOLVER_CR, "thomas": ops.SOLVER_THOMAS, "stream": ops.SOLVER_CR_STREAM, None: None}[solver]
+    g = gpu_sqp(bt, 1e-6, 200, solver=which)
     form = oracle.form_schur(*synth.inputs(bt))
     _, dz = _exact(bt, form)
     assert (g["iters"] == 0).all()
@@ -177,15 +182,15 @@ def test_sqp_step_long_horizon_wide_knots():
 
 
 @pytest.mark.parametrize("solver", ["cr", "thomas"])
-def test_sqp_step_refinement_meets_the_bars_when_ill_conditioned(solver, monkeypatch):
-    """GATO_REFINE=1: one pass of iterative refinement of the KKT system after the
-    direct solve.  On the ill-conditioned long-horizon workload (cond(S) ~ 1e6, where
+def test_sqp_step_refinement_meets_the_bars_when_ill_conditioned(solver):
+    """gato_sqp_step follows its direct solve with one pass of iterative refinement of
+    the KKT system.  On the ill-conditioned long-horizon workload (cond(S) ~ 1e6, where
     rounding S alone to fp32 moves dz by 1e-4 to 6e-4) the refined step is the
     oracle's exact step within 2e-5 in dz and 1e-4 in every merit (the stated merit
-    bar, which the unrefined fp32 step misses on some of these solves)."""
+    bar), ten times closer than the same step with the pass switched off."""
     from gpu_util import gpu_sqp
 
-    monkeypatch.setenv("GATO_LONG_SOLVE", solver)
+    which = {"cr": ops.SOLVER_CR, "thomas": ops.SOLVER_THOMAS}[solver]
     B = 32
     _ident("sqp refinement, workload 5", solver, B)
     bt = synth.make_batch(5, B)
@@ -193,10 +198,8 @@ def test_sqp_step_refinement_meets_the_bars_when_ill_conditioned(solver, monkeyp
     form = oracle.form_schur(*ins)
     _, dz = _exact(bt, form)
     merit = oracle.merit_eval(*ins, dz, synth.ALPHAS, 1.0)["merit"]
-    monkeypatch.delenv("GATO_REFINE", raising=False)
-    plain = gpu_sqp(bt, 1e-6, 2000)
-    monkeypatch.setenv("GATO_REFINE", "1")
-    g = gpu_sqp(bt, 1e-6, 2000)
+    plain = gpu_sqp(bt, 1e-6, 2000, solver=which, refine=0)
+    g = gpu_sqp(bt, 1e-6, 2000, solver=which)
     e0, e = rel_rows(plain["dz"], dz), rel_rows(g["dz"], dz)
     m0 = np.abs(plain["merit"] - merit) / np.abs(merit)
     m = np.abs(g["merit"] - merit) / np.abs(merit)
@@ -207,15 +210,13 @@ def test_sqp_step_refinement_meets_the_bars_when_ill_conditioned(solver, monkeyp
 
 
 @pytest.mark.parametrize("cid,B,N", [(3, 6, 150), (3, 1, 65), (4, 3, 40), (4, 2, 17)])
-def test_sqp_step_refinement_keeps_a_well_conditioned_step(cid, B, N, monkeypatch):
-    """With GATO_REFINE=1 a well-conditioned long-horizon step stays the oracle's exact
-    step (the correction is at the level of fp32 rounding): 16-lane groups (n = 14) and
-    32-lane ones (n = 24), with a last residual workgroup holding one knot (N = 65 and
-    N = 17 beyond a multiple of the 16 and 8 knots a workgroup covers)."""
+def test_sqp_step_refinement_keeps_a_well_conditioned_step(cid, B, N):
+    """The refinement pass leaves a well-conditioned long-horizon step the oracle's
+    exact step (the correction is at the level of fp32 rounding): 16-lane groups
+    (n = 14) and 32-lane ones (n = 24), with a last residual workgroup holding one
+    knot (N = 65 and N = 17 beyond a multiple of the 16 and 8 knots a workgroup covers)."""
     from gpu_util import gpu_sqp
 
-    monkeypatch.delenv("GATO_LONG_SOLVE", raising=False)
-    monkeypatch.setenv("GATO_REFINE", "1")
     _ident("sqp refinement, well-conditioned", cid, B, N)
     bt = synth.make_batch(cid, B, N=N)
     g = gpu_sqp(bt, 1e-6, 200)

@@ -18,7 +18,8 @@ import torch
 
 import oracle
 from block_tridiagonal_pcg_amd import ops, synth
-from gpu_util import (ALPHAS, CAPS, gpu_form, gpu_merit, gpu_pcg, gpu_sqp, merit_rel, rel_rows, select)
+from gpu_util import (ALPHAS, CAPS, btd_relres, gpu_form, gpu_merit, gpu_pcg, gpu_sqp, merit_rel, rel_rows,
+                      select)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,13 +47,6 @@ def _direct_path(bt):
     """gato_sqp_step solves S lambda = gamma directly when a workgroup cannot hold the horizon."""
     n, _, N, _ = bt["dims"]
     return N > (64 if n <= 16 else 16)
-
-
-def _exact_dz(bt):
-    """The exact step of the oracle: fp64 formation, block Cholesky of S, recovery."""
-    f = oracle.form_schur(*[bt[k] for k in synth.FIELDS])
-    lam = oracle.direct_solve(f["S"], f["gamma"])["lam"]
-    return oracle.recover(f["Qinv"], f["Rinv"], bt["A"], bt["Bu"], bt["q"], bt["r"], lam)
 
 
 # ---------------------------------------------------------------- stage 1
@@ -156,8 +150,8 @@ def test_pcg_streamed_converges_where_the_assembled_preconditioner_is_indefinite
     ops.gato_form_schur(dims, *[dev[f] for f in synth.FIELDS], None, st["S"], st["Pinv"], st["gamma"],
                         st["Qinv"], st["Rinv"], st["flags"])
     st["lam"].zero_()
-    ops.gato_pcg_solve(dims, st["S"], st["Pinv"], st["gamma"], st["Qinv"], st["Rinv"], dev["Bu"], dev["q"],
-                       dev["r"], 1e-6, 2000, st["lam"], st["dz"], st["iters"], st["relres"], st["flags"])
+    ops.gato_pcg_solve(dims, st["S"], st["Pinv"], st["gamma"], st["Qinv"], st["Rinv"], dev["A"], dev["Bu"],
+                       dev["q"], dev["r"], 1e-6, 2000, st["lam"], st["dz"], st["iters"], st["relres"], st["flags"])
     torch.cuda.synchronize()
     o_form = oracle.form_schur(*synth.inputs(bt))
     o = oracle.pcg_solve(o_form["S"], o_form["Pinv"], o_form["gamma"], o_form["Qinv"], o_form["Rinv"], bt["A"],
@@ -169,16 +163,94 @@ def test_pcg_streamed_converges_where_the_assembled_preconditioner_is_indefinite
     assert rel_rows(st["dz"].cpu().numpy(), o["dz"]).max() <= 1e-3
 
 
+def test_pcg_iterations_match_the_oracle_on_the_ill_conditioned_workload():
+    """Every solve of the ill-conditioned long-horizon workload (B = 512, N = 128, cap
+    2000): gato_form_schur, then gato_pcg_solve (two knots per lane group, Phi^-1 in
+    factored form) against the oracle's PCG on its own fp64 formation.  The two count
+    S-products under the same exit test; the fp32 iteration differs from the fp64 one
+    by rounding, so the counts are compared as a ratio: no solve at the cap, each
+    within [0.75, 1.5] of the oracle's, the median within [0.9, 1.15]; dz within the
+    1e-3 bar of the oracle's PCG step."""
+    bt = _batch(5, 512)
+    dims = bt["dims"]
+    _ident("pcg iterations vs oracle, workload 5", dims)
+    dev = ops.to_device(bt)
+    st = ops.alloc_outputs(dims, 8)
+    ops.gato_form_schur(dims, *[dev[f] for f in synth.FIELDS], None, st["S"], st["Pinv"], st["gamma"],
+                        st["Qinv"], st["Rinv"], st["flags"])
+    st["lam"].zero_()
+    ops.gato_pcg_solve(dims, st["S"], st["Pinv"], st["gamma"], st["Qinv"], st["Rinv"], dev["A"], dev["Bu"],
+                       dev["q"], dev["r"], 1e-6, 2000, st["lam"], st["dz"], st["iters"], st["relres"], st["flags"])
+    torch.cuda.synchronize()
+    o_form = oracle.form_schur(*synth.inputs(bt))
+    o = oracle.pcg_solve(o_form["S"], o_form["Pinv"], o_form["gamma"], o_form["Qinv"], o_form["Rinv"], bt["A"],
+                         bt["Bu"], bt["q"], bt["r"], 1e-6, 2000)
+    it, fl = st["iters"].cpu().numpy(), st["flags"].cpu().numpy()
+    ratio = it / np.maximum(o["iters"], 1)
+    err = rel_rows(st["dz"].cpu().numpy(), o["dz"])
+    print("iters gpu %d..%d (median %.0f), oracle %d..%d (median %.0f); ratio %.3f..%.3f median %.3f; "
+          "dz rel err max %.3e" % (it.min(), it.max(), np.median(it), o["iters"].min(), o["iters"].max(),
+                                   np.median(o["iters"]), ratio.min(), ratio.max(), np.median(ratio), err.max()))
+    assert (fl == 0).all() and (o["flags"] == 0).all()
+    assert (it < 2000).all()
+    assert ratio.min() >= 0.75 and ratio.max() <= 1.5
+    assert 0.9 <= np.median(ratio) <= 1.15
+    assert err.max() <= 1e-3
+
+
+def test_pcg_respects_the_iteration_cap_where_the_preconditioner_turns_indefinite():
+    """Within one workgroup's horizon (N = 64, register-resident rows) on the
+    ill-conditioned workload's generators, the assembled fp32 Phi^-1 is not positive
+    definite on some solves.  A solve whose r'z stops being positive switches to the
+    factored form with the iterations left: iters never exceeds max_iters, a solve at the
+    cap is flagged, and every solve not flagged meets the exit test, with a true residual
+    (fp64, on the oracle's S) within 5e-5.  (With cond(S) ~ 1e6 a residual of 1e-6
+    bounds dz only loosely: on this batch one converged solve sits 3.3e-3 from the
+    oracle's PCG step, the others within 6e-4.  These horizons are off the workload
+    list; the ill-conditioned workload itself runs at N = 128.)"""
+    bt = _batch(5, 512, N=64)
+    dims = bt["dims"]
+    _ident("pcg cap, workload 5 generators at N = 64", dims)
+    o_form = oracle.form_schur(*synth.inputs(bt))
+    o = oracle.pcg_solve(o_form["S"], o_form["Pinv"], o_form["gamma"], o_form["Qinv"], o_form["Rinv"], bt["A"],
+                         bt["Bu"], bt["q"], bt["r"], 1e-6, 2000)
+    for cap in (2000, 300):
+        dev = ops.to_device(bt)
+        st = ops.alloc_outputs(dims, 8)
+        ops.gato_form_schur(dims, *[dev[f] for f in synth.FIELDS], None, st["S"], st["Pinv"], st["gamma"],
+                            st["Qinv"], st["Rinv"], st["flags"])
+        st["lam"].zero_()
+        st["flags"].zero_()
+        ops.gato_pcg_solve(dims, st["S"], st["Pinv"], st["gamma"], st["Qinv"], st["Rinv"], dev["A"], dev["Bu"],
+                           dev["q"], dev["r"], 1e-6, cap, st["lam"], st["dz"], st["iters"], st["relres"], st["flags"])
+        torch.cuda.synchronize()
+        it, fl, rr = st["iters"].cpu().numpy(), st["flags"].cpu().numpy(), st["relres"].cpu().numpy()
+        capped = (fl & ops.F_PCG_MAXITER) != 0
+        done = ~capped
+        err = rel_rows(st["dz"].cpu().numpy(), o["dz"])
+        true_res = btd_relres(o_form["S"], o_form["gamma"], st["lam"].cpu().numpy())
+        print("cap %d: iters max %d, capped %d, oracle iters max %d; not capped: true residual max %.2e, "
+              "dz err vs the oracle's PCG step max %.3e, over 1e-3 %d" % (
+                  cap, it.max(), capped.sum(), o["iters"].max(), true_res[done].max(initial=0.0),
+                  err[done].max(initial=0.0), (err[done] > 1e-3).sum()))
+        assert (it <= cap).all()
+        assert (it[capped] == cap).all()
+        assert (fl & ~ops.F_PCG_MAXITER == 0).all()
+        assert (rr[done] <= 1e-6).all()
+        assert (true_res[done] <= 5e-5).all()
+        if cap < o["iters"].min():
+            assert capped.all()
+
+
 def test_pcg_warm_start_and_flags():
     bt = _batch(3, 4)
     o_form = oracle.form_schur(*synth.inputs(bt))
     exact = oracle.direct_solve(o_form["S"], o_form["gamma"])["lam"]
     warm = gpu_pcg(bt, o_form, 1e-6, 200, lambda0=exact)
     assert (warm["iters"] <= 1).all()
-    # a solve that reaches the cap runs once more from its lambda with Phi^-1 in
-    # factored form, for up to max_iters more: one iteration each here, still capped
+    # the cap is honoured: one iteration, then the flag
     capped = gpu_pcg(bt, o_form, 1e-6, 1)
-    assert (capped["flags"] & ops.F_PCG_MAXITER).all() and (capped["iters"] == 2).all()
+    assert (capped["flags"] & ops.F_PCG_MAXITER).all() and (capped["iters"] == 1).all()
     bad = dict(o_form)
     bad["gamma"] = o_form["gamma"].copy()
     bad["gamma"][2, 3, 1] = np.nan
@@ -215,20 +287,10 @@ def test_merit_bit_identical_across_workgroup_sizes():
     fused per-knot or candidate-parallel decomposition) gives the same bits."""
     bt = _batch(5, 3)
     dz = np.random.default_rng(0).standard_normal((3, 128 * 14 + 127 * 7)).astype(np.float32) * 0.1
-    runs = []
-    saved = {k: os.environ.get(k) for k in ("GATO_MERIT_WAVES", "GATO_MERIT_VARIANT")}
-    try:
-        for variant in ("fused", "candidate"):
-            os.environ["GATO_MERIT_VARIANT"] = variant
-            for w in ("1", "2", "3", "8", "16"):
-                os.environ["GATO_MERIT_WAVES"] = w
-                runs.append(gpu_merit(bt, dz, 1.3, flags=np.array([0, 64, 0], np.int32)))
-    finally:
-        for k, v in saved.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+    runs = [gpu_merit(bt, dz, 1.3, flags=np.array([0, 64, 0], np.int32))]  # gato_merit_eval's own choice
+    for variant in (ops.MERIT_PER_KNOT, ops.MERIT_PER_CANDIDATE):
+        for w in (0, 1, 2, 3, 8, 16):
+            runs.append(gpu_merit(bt, dz, 1.3, flags=np.array([0, 64, 0], np.int32), variant=variant, waves=w))
     for r in runs[1:]:
         for k in ("merit", "merit0", "best", "flags"):
             np.testing.assert_array_equal(r[k], runs[0][k])
@@ -267,30 +329,39 @@ SQP_CASES = [(1, 1), (2, 1), (2, 8), (2, 16), (3, 1), (3, 8), (3, 16), (3, 64), 
 
 @pytest.mark.parametrize("cid,B", SQP_CASES, ids=["cfg%d-B%d" % c for c in SQP_CASES])
 def test_sqp_step_parity(cid, B):
+    """gato_sqp_step as shipped, every solve of every batch against the oracle."""
     _ident("sqp_step", cid, B)
     bt = _batch(cid, B)
     g = gpu_sqp(bt, 1e-6, CAPS[cid])
-    # the oracle checks every solve, or an evenly spaced sample of 64 at the largest batch
-    idx = np.arange(B) if B <= 256 else np.linspace(0, B - 1, 64).astype(int)
-    sub = {f: bt[f][idx] for f in synth.FIELDS}
-    o = oracle.sqp_step(*[sub[f] for f in synth.FIELDS], None, 1e-6, CAPS[cid], A64, 1.0)
+    ins = synth.inputs(bt)
     if _direct_path(bt):
-        # the step comes from the direct solve: compare with the exact step and the
-        # stage-1 flag bits (the oracle's PCG may stop at its cap on these solves)
-        o["dz"] = _exact_dz(sub)
+        # the step comes from the direct solve and its refinement pass: compare with the
+        # oracle's exact step (block Cholesky of S) and the stage-1 flag bits
+        f = oracle.form_schur(*ins)
+        lam = oracle.direct_solve(f["S"], f["gamma"])["lam"]
+        o = {"dz": oracle.recover(f["Qinv"], f["Rinv"], bt["A"], bt["Bu"], bt["q"], bt["r"], lam),
+             "flags": f["flags"]}
         assert (g["iters"] == 0).all()
-        o["flags"] = o["flags"] & ~(ops.F_PCG_MAXITER | ops.F_PCG_BREAKDOWN)
-    err = rel_rows(g["dz"][idx], o["dz"])
-    print("cfg%d B%d: dz rel err max %.3e median %.3e; iters gpu %d..%d oracle %d..%d" % (
-        cid, B, err.max(), np.median(err), g["iters"].min(), g["iters"].max(), o["iters"].min(), o["iters"].max()))
+    else:
+        o = oracle.sqp_step(*ins, None, 1e-6, CAPS[cid], A64, 1.0)
+    err = rel_rows(g["dz"], o["dz"])
+    print("cfg%d B%d: dz rel err max %.3e median %.3e; iters gpu %d..%d" % (
+        cid, B, err.max(), np.median(err), g["iters"].min(), g["iters"].max()))
     assert err.max() <= 1e-3
-    assert ((g["flags"][idx] & ~ops.F_LS_FAILED) == (o["flags"] & ~ops.F_LS_FAILED)).all()
+    assert ((g["flags"] & ~ops.F_LS_FAILED) == (o["flags"] & ~ops.F_LS_FAILED)).all()
     # merit of the GPU's own step, against the oracle's merit of that same step
-    om = oracle.merit_eval(*[sub[f] for f in synth.FIELDS], g["dz"][idx].astype(np.float64), A64, 1.0)
-    assert merit_rel(g["merit"][idx], om).max() <= 1e-4
+    om = oracle.merit_eval(*ins, g["dz"].astype(np.float64), A64, 1.0)
+    assert merit_rel(g["merit"], om).max() <= 1e-4
     np.testing.assert_array_equal(g["best"], select(g["merit"], g["merit0"]))
-    if not _direct_path(bt):
-        assert np.abs(g["iters"][idx] - o["iters"]).max() <= 2
+    if _direct_path(bt):
+        # and the merits of the oracle's exact step: the step is exact within the bars
+        oe = oracle.merit_eval(*ins, o["dz"], A64, 1.0)
+        me = merit_rel(g["merit"], oe)
+        print("merit vs the exact step's: max %.3e" % me.max())
+        assert me.max() <= 1e-4
+        np.testing.assert_array_equal(g["best"], oe["best"])
+    else:
+        assert np.abs(g["iters"] - o["iters"]).max() <= 2
 
 
 def test_fused_step_equals_staged_calls():
