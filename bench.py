@@ -12,9 +12,11 @@ and HIP events on the launch stream around it give the kernel's average time.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (N must be 1)
 --config C --batch B --horizon N (the configuration's generators at another
-horizon) --no-cpu-baseline --profile-copy (adds a 256 MiB device copy, the
-reference kernel for scaling rocprofv3 byte counters).  Study modes, each one
-JSON line instead of the step: --merit-variants, --sqp-driver, --solver-sweep.
+horizon) --refine on|off --no-cpu-baseline.  Every run also times a 256 MiB
+device copy (its rate is reported beside the published HBM peak; under the
+profiler it is the reference kernel for scaling byte counters) and the K steps
+once more one by one (median and 90th percentile).  Study modes, each one JSON
+line instead of the step: --merit-variants, --sqp-driver, --solver-sweep.
 """
 import argparse
 import hashlib
@@ -49,7 +51,7 @@ def parse():
                     help="the KKT refinement pass after a direct solve (on: the library's default; "
                          "off: gato_sqp_step_opts with refine = 0, for comparison)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--profile-copy", action="store_true")
+    ap.add_argument("--profile-copy", action="store_true", help="accepted for old command lines; the copy always runs")
     ap.add_argument("--merit-variants", action="store_true",
                     help="instead of the step: time the merit call's launch variants (one JSON line)")
     ap.add_argument("--sqp-driver", action="store_true",
@@ -178,26 +180,76 @@ def measured_traffic(workload):
 # ---------------------------------------------------------------- CPU baseline
 
 
+def cpu_model():
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def _median_time(fn, reps):
+    import statistics
+
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts), ts
+
+
 def cpu_baseline(batch, n_alpha, seconds):
+    """The oracle as it stands, on this host's cores: the whole step (form, PCG,
+    recovery, merit, selection; same eps and cap) over the timed batch on all the
+    threads OpenMP gives it, then on one thread over a sample of the batch, then its
+    three stages alone; medians of repeated runs.  About `seconds` of wall time."""
     import numpy as np
 
     import oracle
 
     al = np.array([2.0 ** -i for i in range(n_alpha)])
     cap = CAPS[batch["cid"]]
+    B = batch["dims"][3]
     args = [batch[f] for f in ("Q", "q", "R", "r", "A", "Bu", "e", "x0")]
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     first = oracle.sqp_step(*args, None, EPS, cap, al, MU)
     one = time.perf_counter() - t0
-    reps = max(1, min(5000, int(math.ceil(seconds / max(one, 1e-6)))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        oracle.sqp_step(*args, None, EPS, cap, al, MU)
-    wall = time.perf_counter() - t0
-    B = batch["dims"][3]
-    return {"value": B * reps / wall, "unit": "solves/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "the full %d-solve batch of the timed workload, %d repeats (%.1f s wall), fp64, "
-                      "OpenMP over solves" % (B, reps, wall)}, first
+    # all threads: the whole batch, at least 5 repeats, about half the budget
+    reps = max(5, min(2000, int(0.5 * seconds / max(one, 1e-6))))
+    med, ts = _median_time(lambda: oracle.sqp_step(*args, None, EPS, cap, al, MU), reps)
+    # one thread: a leading sample of the batch sized for ~30 % of the budget over 5 repeats
+    per_solve_1 = one * threads / B  # assumes the threads scale; only sizes the sample
+    b1 = int(max(1, min(B, 0.3 * seconds / 5 / max(per_solve_1, 1e-9))))
+    sub = [x[:b1] for x in args]
+    oracle.set_num_threads(1)
+    try:
+        med1, _ = _median_time(lambda: oracle.sqp_step(*sub, None, EPS, cap, al, MU), 5)
+    finally:
+        oracle.set_num_threads(threads)
+    # the stages alone (all threads, whole batch, median of 3)
+    f = oracle.form_schur(*args)
+    t_form, _ = _median_time(lambda: oracle.form_schur(*args), 3)
+    t_pcg, _ = _median_time(lambda: oracle.pcg_solve(f["S"], f["Pinv"], f["gamma"], f["Qinv"], f["Rinv"],
+                                                     batch["A"], batch["Bu"], batch["q"], batch["r"], EPS, cap), 3)
+    t_mer, _ = _median_time(lambda: oracle.merit_eval(*args, first["dz"], al, MU), 3)
+    rec = {"value": B / med, "unit": "solves/s", "cores": threads, "kind": "oracle",
+           "sample": "the full %d-solve batch of the timed workload, median of %d repeats (%.1f s), fp64, "
+                     "OpenMP over solves" % (B, reps, sum(ts)),
+           "one_core": {"value": b1 / med1, "unit": "solves/s", "cores": 1,
+                        "sample": "solves 0..%d of the batch, median of 5 repeats" % (b1 - 1)},
+           "stage_us": {"schur_us": t_form * 1e6, "linsys_us": t_pcg * 1e6, "merit_us": t_mer * 1e6,
+                        "note": "whole batch, all threads, median of 3; linsys is PCG plus the recovery"},
+           "cpu_model": cpu_model(),
+           "compiler": "gcc " + " ".join(oracle.CFLAGS),
+           "statistic": "median"}
+    return rec, first
 
 
 def iters_summary(x):
@@ -471,12 +523,20 @@ def main():
     ws = ops.workspace_for(dims, n_alpha)
     stream = torch.cuda.current_stream()
 
-    if a.profile_copy:
-        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    # a plain device copy of 256 MiB: the measured memory rate beside the published peak
+    # (and, under the profiler, the reference kernel for scaling its byte counters)
+    src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
 
     # pre-marshalled calls (argument checks once, then only the C call per step), each
     # step with its own zeroed starting point
@@ -502,6 +562,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_avg_s = ev0.elapsed_time(ev1) / 1e3 / a.steps
+
+    # the same K steps again, each between two HIP events on the launch stream (the
+    # pages' per-solve statistics: median and 90th percentile of single steps)
+    lam0.zero_()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for k, step in enumerate(steps):
+        step()
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step_us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(a.steps)])
+    del evs
 
     iters = out["iters"].cpu().numpy()
     flags = out["flags"].cpu().numpy()
@@ -592,6 +665,9 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": wall / a.steps * 1e3,
+        "step_us": {"median": float(np.median(per_step_us)), "p90": float(np.percentile(per_step_us, 90)),
+                    "mean": float(per_step_us.mean()), "min": float(per_step_us.min()),
+                    "note": "each of K steps between two HIP events on the launch stream, in a second pass"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -613,6 +689,9 @@ def main():
             "flops_per_launch": flops if fused else solve_flops,
             "launch_avg_us": kernel_us,
             "step_launch_avg_us": kern_avg_s * 1e6,
+            "copy_GBps": copy_gbps,
+            "copy_note": "a 256 MiB device-to-device copy (read + write bytes / time), beside the published "
+                         "8 TB/s",
         },
         "pcg_iters": iters_summary(iters),
         "pcg_alongside": pcg_alongside,

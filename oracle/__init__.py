@@ -12,6 +12,8 @@ from .ref import (  # noqa: F401
     build,
     load,
     num_threads,
+    set_num_threads,
+    CFLAGS,
     form_schur,
     pcg_solve,
     merit_eval,

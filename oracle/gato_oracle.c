@@ -694,3 +694,16 @@ int gato_ref_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set that number (for timing the oracle on fewer cores); returns the new value.
+ * Scheduling only: every solve is computed by one thread, whichever. */
+int gato_ref_set_num_threads(int t)
+{
+#ifdef _OPENMP
+    if (t >= 1) omp_set_num_threads(t);
+    return omp_get_max_threads();
+#else
+    (void)t;
+    return 1;
+#endif
+}

@@ -33,14 +33,15 @@ class _Dims(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int), ("m", ctypes.c_int), ("N", ctypes.c_int), ("B", ctypes.c_int)]
 
 
+# gcc flags of the oracle build: OpenMP over solves, no fast-math (no reassociation)
+CFLAGS = ("-O2", "-fopenmp", "-fno-fast-math")
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP over solves, no fast-math)."""
+    """Compile the oracle with gcc (CFLAGS)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(
-            ["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"],
-            check=True,
-        )
+        subprocess.run(["gcc", *CFLAGS, "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -57,9 +58,10 @@ def configure(lib):
     lib.gato_ref_direct_solve.argtypes = [P, P, P, P, P]
     lib.gato_ref_recover.argtypes = [P] * 9
     lib.gato_ref_num_threads.argtypes = []
+    lib.gato_ref_set_num_threads.argtypes = [I]
     for f in ("gato_ref_form_schur", "gato_ref_pcg_solve", "gato_ref_merit_eval",
               "gato_ref_sqp_step", "gato_ref_direct_solve", "gato_ref_recover",
-              "gato_ref_num_threads"):
+              "gato_ref_num_threads", "gato_ref_set_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -76,6 +78,11 @@ def load():
 
 def num_threads() -> int:
     return int(load().gato_ref_num_threads())
+
+
+def set_num_threads(t: int) -> int:
+    """Threads of the OpenMP loops over solves from now on; returns the new count."""
+    return int(load().gato_ref_set_num_threads(int(t)))
 
 
 def _f64(a):

@@ -82,3 +82,21 @@ def test_exact_step_matches_the_oracle_step():
     assert bench.rel_err_rows(ex["dz"], st["dz"]).max() < 1e-7
     assert bench.rel_err_rows(ex["merit"].reshape(-1, 1), st["merit"].reshape(-1, 1)).max() < 1e-7
     assert (ex["best"] == st["best"]).all()
+
+
+def test_cpu_baseline_reports_all_cores_one_core_and_stages():
+    """The CPU-baseline leg's record: all-thread and one-thread rates, the oracle's
+    stages, CPU model and compiler, and the oracle's step as its second value."""
+    import oracle
+
+    bt = synth.make_batch(2, 4)
+    bt["cid"] = 2
+    rec, first = bench.cpu_baseline(bt, 8, 0.5)
+    assert rec["kind"] == "oracle" and rec["unit"] == "solves/s" and rec["value"] > 0
+    assert rec["cores"] == oracle.num_threads()
+    assert rec["one_core"]["cores"] == 1 and rec["one_core"]["value"] > 0
+    assert all(rec["stage_us"][k] > 0 for k in ("schur_us", "linsys_us", "merit_us"))
+    assert rec["compiler"].startswith("gcc ") and "-fno-fast-math" in rec["compiler"]
+    assert rec["cpu_model"]
+    assert oracle.num_threads() == rec["cores"]  # the thread count is restored
+    assert first["dz"].shape == (4, 32 * 12 + 31 * 6)
