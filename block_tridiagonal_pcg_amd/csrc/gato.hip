@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 namespace gato {
 
@@ -840,6 +841,34 @@ static bool fused_path(const gato_dims_t* d)
     return with_shape(d->n, d->m, [&](auto ops) { return decltype(ops)::fused_ok(d->N) ? 1 : 0; }) == 1;
 }
 
+// ------------------------------------------------------------------ allocation-free scratch
+
+// gato_sqp_step_noalloc's workspace: one array per device, held from the load of
+// this code object on that device until the process ends.  Host code never
+// uses its name as an address (on the host it is a stand-in, not device
+// memory); the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[GATO_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the calling thread's current device, looked
+// up on the first call there (with that device current); nullptr if the lookup
+// fails.
+static void* scratch_ptr()
+{
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
 }  // namespace gato
 
 using namespace gato;
@@ -1161,6 +1190,29 @@ int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, 
         if (rc == GATO_OK && !ok) rc = GATO_E_HIP;
     }
     return rc;
+}
+
+int gato_sqp_step_noalloc(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                          const float* r, const float* A, const float* Bu, const float* e,
+                          const float* x0, const float* rho, float eps, int32_t max_iters,
+                          const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
+                          float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
+                          int32_t* flags, hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
+    const bool fused = fused_path(dims);
+    if (!fused && ws_layout(dims).total > (size_t)GATO_NOALLOC_SCRATCH_BYTES) return GATO_E_WORKSPACE;
+    void* ws = nullptr;
+    size_t wsb = 0;
+    if (!fused) {
+        ws = scratch_ptr();
+        if (ws == nullptr) return GATO_E_HIP;
+        wsb = (size_t)GATO_NOALLOC_SCRATCH_BYTES;
+    }
+    return gato_sqp_step_opts(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas_host, n_alpha, mu, lambda,
+                              dz, merit, merit0, best, iters, relres, flags, ws, wsb, nullptr, nullptr, stream);
 }
 
 int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const float* R,

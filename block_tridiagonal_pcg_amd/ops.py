@@ -41,6 +41,7 @@ EXPORTS = (
     "gato_merit_eval_shape",
     "gato_sqp_step",
     "gato_sqp_step_opts",
+    "gato_sqp_step_noalloc",
     "gato_workspace_bytes",
     "gato_step_solver",
     "gato_status_string",
@@ -98,6 +99,7 @@ def load():
             lib.gato_merit_eval_shape.argtypes = [P] * 11 + [I, F] + [P] * 4 + [I, I, P]
             lib.gato_sqp_step.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P]
             lib.gato_sqp_step_opts.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9 + [Z, P, P, P]
+            lib.gato_sqp_step_noalloc.argtypes = [P] * 10 + [F, I, P, I, F] + [P] * 9
             lib.gato_step_solver.argtypes = [P]
             lib.gato_step_solver.restype = ctypes.c_int
             lib.gato_workspace_bytes.argtypes = [P, I]
@@ -106,7 +108,8 @@ def load():
             lib.gato_status_string.restype = ctypes.c_char_p
             lib.gato_shape_supported.argtypes = [I, I, I]
             for f in ("gato_form_schur", "gato_pcg_solve", "gato_direct_solve", "gato_cr_solve", "gato_merit_eval",
-                      "gato_merit_eval_shape", "gato_sqp_step", "gato_sqp_step_opts", "gato_shape_supported"):
+                      "gato_merit_eval_shape", "gato_sqp_step", "gato_sqp_step_opts", "gato_sqp_step_noalloc",
+                      "gato_shape_supported"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -335,6 +338,31 @@ def gato_sqp_step(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas, m
     else:
         _raise("gato_sqp_step_opts", load().gato_sqp_step_opts(*args, ctypes.byref(o), _stream(stream)))
     return st
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gato_sqp_step_noalloc(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, alphas, mu, lam, dz, merit, merit0,
+                          best, iters, relres, flags, stream=None):
+    """gato_sqp_step with the library's fixed per-device scratch array in place of a
+    workspace (for callers that cannot allocate); raises GatoError(E_WORKSPACE) when
+    the dims need more than NOALLOC_SCRATCH_BYTES."""
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0"),
+                 (rho, "rho"), (lam, "lam"), (dz, "dz"), (merit0, "B_"), (relres, "B_")):
+        _chk(t, k, shape=sh[k])
+    arr, na = _alphas(alphas)
+    _chk(merit, "merit", shape=(B, na))
+    for t, k in ((best, "best"), (iters, "iters"), (flags, "flags")):
+        _chk(t, k, torch.int32, sh["B_"])
+    d = _dims(n, m, N, B)
+    rc = load().gato_sqp_step_noalloc(ctypes.byref(d), _p(Q), _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0),
+                                      _p(rho), float(eps), int(max_iters), arr, na, float(mu), _p(lam), _p(dz),
+                                      _p(merit), _p(merit0), _p(best), _p(iters), _p(relres), _p(flags),
+                                      _stream(stream))
+    return _raise("gato_sqp_step_noalloc", rc)
 
 
 # ---------------------------------------------------------------- allocation helpers

@@ -347,6 +347,32 @@ int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, 
                        int32_t* flags, void* workspace, size_t workspace_bytes,
                        gato_stage_times_t* times, const gato_step_opts_t* opts, hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gato_sqp_step without a workspace argument or stage times.  Where
+ * gato_sqp_step needs a workspace (horizons beyond the fused ones), this call
+ * uses a fixed array of GATO_NOALLOC_SCRATCH_BYTES in device memory that the
+ * library holds on each GPU it runs on, from the first use there until the
+ * process ends; it allocates nothing and calls no allocating routine.  Dims
+ * whose gato_workspace_bytes() exceed that size return GATO_E_WORKSPACE
+ * (before anything is enqueued).  The array of the calling thread's current
+ * device is used, so `stream` must belong to that device.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  Nothing in the
+ * array needs to start at zero (every row is written before it is read), and
+ * each call leaves its own values there.  Results are those of gato_sqp_step
+ * (the same kernels in the same order).  A failed lookup of the array returns
+ * GATO_E_HIP.
+ */
+#define GATO_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gato_sqp_step_noalloc(const gato_dims_t* dims, const float* Q, const float* q, const float* R,
+                          const float* r, const float* A, const float* Bu, const float* e,
+                          const float* x0, const float* rho, float eps, int32_t max_iters,
+                          const float* alphas_host, int32_t n_alpha, float mu, float* lambda, float* dz,
+                          float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
+                          int32_t* flags, hipStream_t stream);
+
 /* The stage-2 solver gato_sqp_step runs for these dims (the horizon policy
  * above, a pure function of dims): GATO_SOLVER_FUSED_PCG, GATO_SOLVER_THOMAS or
  * GATO_SOLVER_CR; a negative status for invalid or unsupported dims. */

@@ -77,8 +77,9 @@ def test_header_declares_the_abi():
     assert _declared() == sorted([
         "gato_cr_levels", "gato_cr_solve", "gato_cr_workspace_bytes",
         "gato_direct_solve", "gato_direct_workspace_bytes", "gato_form_schur", "gato_merit_eval",
-        "gato_merit_eval_shape", "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step", "gato_sqp_step_opts",
-        "gato_status_string", "gato_step_solver", "gato_workspace_bytes"])
+        "gato_merit_eval_shape", "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step",
+        "gato_sqp_step_noalloc", "gato_sqp_step_opts", "gato_status_string", "gato_step_solver",
+        "gato_workspace_bytes"])
 
 
 def test_boundary_signatures():
@@ -91,6 +92,28 @@ def test_boundary_signatures():
         ("const gato_step_opts_t*", "opts"), ("hipStream_t", "stream")]
     assert protos["gato_merit_eval_shape"] == BOUNDARY["gato_merit_eval"][:-1] + [
         ("int32_t", "variant"), ("int32_t", "waves"), ("hipStream_t", "stream")]
+    # the allocation-free step: no workspace and no stage times (nothing that allocates)
+    assert protos["gato_sqp_step_noalloc"] == BOUNDARY["gato_sqp_step"][:-4] + [("hipStream_t", "stream")]
+
+
+def test_noalloc_rejects_dims_beyond_its_scratch(lib):
+    """The allocation-free step serves the fused horizons without scratch and longer
+    ones within its fixed array; beyond it the host returns E_WORKSPACE before looking
+    at any pointer or touching a device (none is present here)."""
+    from block_tridiagonal_pcg_amd import ops
+
+    text = open(os.path.join(ROOT, "include", "gato.h")).read()
+    assert re.search(r"#define GATO_NOALLOC_SCRATCH_BYTES \(64u << 20\)", text)
+    assert ops.NOALLOC_SCRATCH_BYTES == 64 << 20
+    al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
+    f = lib.gato_sqp_step_noalloc
+    for dims in ((14, 7, 128, 512), (14, 7, 1024, 64), (24, 12, 200, 256)):
+        assert ops.gato_workspace_bytes(dims) > ops.NOALLOC_SCRATCH_BYTES
+        assert f(ctypes.byref(ops.Dims(*dims)), *[None] * 9, 1e-6, 200, al, 8, 1.0, *[None] * 8, None) == \
+            ops.E_WORKSPACE, dims
+    assert f(ctypes.byref(ops.Dims(14, 7, 128, 0)), *[None] * 9, 1e-6, 200, al, 8, 1.0, *[None] * 8, None) == ops.OK
+    assert f(ctypes.byref(ops.Dims(13, 7, 128, 4)), *[None] * 9, 1e-6, 200, al, 8, 1.0, *[None] * 8,
+             None) == ops.E_UNSUPPORTED
 
 
 def test_binding_argument_counts_match_the_header(lib):
