@@ -371,12 +371,18 @@ __device__ __forceinline__ void mma_rows(const mma32_t& acc, float* r)
 // positive or not finite; the elimination then continues with the bad pivot
 // and the result is flagged, not repaired.
 //
-// Step j: every lane i != j subtracts A[i][j]/A[j][j] times row j, the pivot
-// row is scaled by 1/A[j][j], and column j becomes the matching column of the
-// inverse (the classical in-place form).  The pivot lane uses the same fused
-// update with multiplier (1/piv - 1), so all lanes run one instruction stream.
+// Step j: every lane i != j subtracts A[i][j]/A[j][j] times row j and column j
+// becomes the matching column of the inverse (the classical in-place form),
+// but the pivot row is left unscaled: every row stays a multiple of its row of
+// the classical form (row j by the factor A[j][j], its pivot), which every
+// later step carries consistently, since it only adds multiples of the current
+// pivot row to other rows with multipliers taken from those rows.  Each lane
+// keeps the reciprocal of its own pivot and scales its row once, at the end
+// (gj_finish).  Scaling the pivot row inside the step by a fused multiply-add
+// with the multiplier (1/piv - 1) would round that multiplier in absolute
+// terms, a relative error of up to 2^-24 * piv in the inverse's row.
 template <int NP, int K, int J = 0>
-__device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
+__device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad, float& rinv)
 {
     if constexpr (J < K) {
         float piv;
@@ -396,7 +402,7 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
         const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
         const bool me = lane == J;
         const float f = a[J];
-        const float g = me ? (inv - 1.0f) : -(f * inv);
+        const float g = me ? 0.0f : -(f * inv);
         float keep = a[J];
         if constexpr (NP == 16) {
             BcBs<(K < 16 ? K : 16)>::template run<J & 15>(a, g);
@@ -404,10 +410,27 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
             BcRow<32, K> src(a);
             axpyb<32, K, J>(a, src, g);
         }
-        // column J of the inverse: -A[i][j]/piv off the pivot row, 1/piv on it
-        a[J] = me ? inv : -(keep * inv);
-        gj_steps<NP, K, J + 1>(a, lane, bad);
+        // column J of the inverse: -A[i][j]/piv off the pivot row; on it the unscaled 1
+        a[J] = me ? 1.0f : -(keep * inv);
+        rinv = me ? inv : rinv;
+        gj_steps<NP, K, J + 1>(a, lane, bad, rinv);
     }
+}
+
+// The deferred scaling of gj_steps: row i times the reciprocal of its pivot.
+template <int K>
+__device__ __forceinline__ void gj_finish(float* a, float rinv)
+{
+#pragma unroll
+    for (int c = 0; c < K; ++c) a[c] *= rinv;
+}
+
+template <int NP, int K>
+__device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
+{
+    float rinv = 1.0f;
+    gj_steps<NP, K, 0>(a, lane, bad, rinv);
+    gj_finish<K>(a, rinv);
 }
 
 // The same elimination for 32-lane groups with the pivot row passed through
@@ -417,11 +440,13 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
 // and a DPP multiply-add per column; here a step is K/4 stores and loads and K
 // plain multiply-adds.  LDS accesses of one wave complete in order, and a
 // group never spans two waves, so no barrier is needed.  Same arithmetic as
-// gj_steps (the multiply-add a[c] + g * pivot_row[c] for every column).
+// gj_steps (the multiply-add a[c] + g * pivot_row[c] for every column, the
+// pivot row left unscaled, each row scaled by its pivot's reciprocal at the end).
 template <int K>
 __device__ __forceinline__ void gj_steps_lds(float* a, int lane, bool& bad, float* pr)
 {
     constexpr int K4 = (K + 3) / 4;
+    float rinv = 1.0f;
 #pragma unroll
     for (int J = 0; J < K; ++J) {
         if (lane == J)
@@ -450,11 +475,13 @@ __device__ __forceinline__ void gj_steps_lds(float* a, int lane, bool& bad, floa
         const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
         const bool me = lane == J;
         const float keep = a[J];
-        const float g = me ? (inv - 1.0f) : -(keep * inv);
+        const float g = me ? 0.0f : -(keep * inv);
 #pragma unroll
         for (int c = 0; c < K; ++c) a[c] = __builtin_fmaf(row[c], g, a[c]);
-        a[J] = me ? inv : -(keep * inv);
+        a[J] = me ? 1.0f : -(keep * inv);
+        rinv = me ? inv : rinv;
     }
+    gj_finish<K>(a, rinv);
 }
 
 }  // namespace gato

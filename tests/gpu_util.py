@@ -126,6 +126,23 @@ def btd_relres(S, gamma, lam):
     return np.linalg.norm((v - g).reshape(len(g), -1), axis=1) / np.linalg.norm(g.reshape(len(g), -1), axis=1)
 
 
+def btd_min_pivot_eig(X):
+    """Per solve, the smallest eigenvalue over the pivots of the block LDL'
+    factorisation of the symmetric part of a block-tridiagonal matrix X in the
+    [B][N][3][n][n] block-row layout, in fp64: positive exactly when the symmetric
+    part is positive definite (Sylvester's law of inertia)."""
+    X = np.asarray(X, np.float64)
+    Bn, N = X.shape[:2]
+    sym = lambda M: 0.5 * (M + np.swapaxes(M, -1, -2))  # noqa: E731
+    H = sym(X[:, 0, 1])
+    lo = np.linalg.eigvalsh(H).min(axis=1)
+    for k in range(N - 1):
+        U = 0.5 * (X[:, k, 2] + np.swapaxes(X[:, k + 1, 0], -1, -2))  # coupling k -> k+1
+        H = sym(X[:, k + 1, 1]) - np.swapaxes(U, -1, -2) @ np.linalg.solve(H, U)
+        lo = np.minimum(lo, np.linalg.eigvalsh(H).min(axis=1))
+    return lo
+
+
 def merit_rel(gpu_merit_vals, ref):
     """Relative merit error with the denominator max(|M_ref(a)|, M0_ref) (avoids near-zero division)."""
     den = np.maximum(np.abs(ref["merit"]), ref["merit0"][:, None])

@@ -18,8 +18,8 @@ import torch
 
 import oracle
 from block_tridiagonal_pcg_amd import ops, synth
-from gpu_util import (ALPHAS, CAPS, btd_relres, gpu_form, gpu_merit, gpu_pcg, gpu_sqp, merit_rel, rel_rows,
-                      select)
+from gpu_util import (ALPHAS, CAPS, btd_min_pivot_eig, btd_relres, gpu_form, gpu_merit, gpu_pcg, gpu_sqp,
+                      merit_rel, rel_rows, select)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,49 @@ def test_form_parity(cid):
     # out-of-range blocks are written as zeros
     assert np.all(g["S"][:, 0, 0] == 0) and np.all(g["S"][:, -1, 2] == 0)
     assert np.all(g["Pinv"][:, 0, 0] == 0) and np.all(g["Pinv"][:, -1, 2] == 0)
+
+
+@pytest.mark.parametrize("cid", [2, 4])  # 16-lane groups (n = 12) and 32-lane groups (n = 24)
+def test_inverses_keep_their_accuracy_at_large_pivots(cid):
+    """Q and R scaled by 1e3: the Gauss-Jordan inverses scale each row by its pivot's
+    reciprocal once, at the end, so the inverses, S and Phi^-1 keep fp32 accuracy
+    (~1e-7) however large the pivots.  Scaling the pivot row inside each step with the
+    multiplier 1/piv - 1 rounds that multiplier in absolute terms; with dense Q at this
+    scale that cost ~1.3e-5 (16-lane groups)."""
+    _ident("inverses at large pivots", cid)
+    bt = _batch(cid, 16)
+    bt["Q"] = (bt["Q"] * np.float32(1e3)).astype(np.float32)
+    bt["R"] = (bt["R"] * np.float32(1e3)).astype(np.float32)
+    g = gpu_form(bt)
+    o = oracle.form_schur(*synth.inputs(bt))
+    errs = {k: rel_rows(g[k], o[k]).max() for k in ("Qinv", "Rinv", "S", "gamma", "Pinv")}
+    print(errs)
+    assert max(errs.values()) <= 1e-6
+    assert (g["flags"] == 0).all()
+
+
+def test_stair_preconditioner_on_the_ill_conditioned_workload():
+    """Phi^-1 from gato_form_schur on all 512 solves of workload 5 against the oracle's,
+    and its definiteness (the sign of the smallest eigenvalue over the block LDL' pivots
+    of its symmetric part, in fp64).  The exact Phi^-1 rounded to fp32 is definite on
+    every solve, but the fp32 inversions of the D_k (condition up to ~5e5) leave Phi^-1
+    within ~5e-5 of the oracle's, enough to make it indefinite on a few solves; PCG
+    therefore switches to the factored form there (tested above)."""
+    bt = _batch(5, 512)
+    _ident("Phi^-1 on workload 5", bt["dims"])
+    g = gpu_form(bt)
+    o = oracle.form_schur(*synth.inputs(bt))
+    err = rel_rows(g["Pinv"], o["Pinv"])
+    derr = rel_rows(g["Pinv"][:, :, 1], o["Pinv"][:, :, 1])
+    ev = btd_min_pivot_eig(g["Pinv"])
+    ev32 = btd_min_pivot_eig(o["Pinv"].astype(np.float32))
+    print("Phi^-1 rel err max %.3e median %.3e; D^-1 max %.3e; indefinite on the GPU: %d (%s); "
+          "exact rounded to fp32: %d" % (err.max(), np.median(err), derr.max(), (ev <= 0).sum(),
+                                         np.nonzero(ev <= 0)[0].tolist(), (ev32 <= 0).sum()))
+    assert err.max() <= 1e-4 and derr.max() <= 1e-4
+    assert (ev32 > 0).all()
+    assert (ev <= 0).sum() <= 16
+    assert rel_rows(g["S"], o["S"]).max() <= 1e-6
 
 
 @pytest.mark.parametrize("cid", [2, 4])  # 16-lane groups (n = 12) and 32-lane groups (n = 24)
