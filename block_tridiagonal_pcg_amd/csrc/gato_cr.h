@@ -577,18 +577,19 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     const NdWs<SH> nw{(size_t)p.B, (size_t)p.N};
     const int N = VIRT ? 2 * ND_CHUNKS : p.N;
     const int M = (N + 1) / 2;  // even knots, one per lane group
-    const int i = threadIdx.x % NP;
-    const int g = threadIdx.x / NP;
-    const bool rowi = i < NC;
-    const int ii = rowi ? i : 0;  // LDS row index that stays inside a slot
-    const bool hasG = g < M;
+    // lane indices (formed again from the thread index after the forward sweep)
+    int i = threadIdx.x % NP;
+    int g = threadIdx.x / NP;
+    bool rowi = i < NC;
+    int ii = rowi ? i : 0;  // LDS row index that stays inside a slot
+    bool hasG = g < M;
     int levels = 0;  // reduction levels, ceil(log2 N)
     for (int s = 1; s < N; s *= 2) ++levels;
-    const int jo = 2 * g + 1;  // this group's odd knot
-    const bool hasO = hasG && jo < N;
-    const int me = hasG ? cr_group_even(g, M) : 0;
-    const int ke = 2 * me;  // this group's even knot
-    const int lev = me == 0 ? levels : 1 + __builtin_ctz(me);  // its elimination level (levels: the last solve)
+    int jo = 2 * g + 1;  // this group's odd knot
+    bool hasO = hasG && jo < N;
+    int me = hasG ? cr_group_even(g, M) : 0;
+    int ke = 2 * me;  // this group's even knot
+    int lev = me == 0 ? levels : 1 + __builtin_ctz(me);  // its elimination level (levels: the last solve)
 
     if (threadIdx.x == 0) sm.flags = 0;
     __syncthreads();  // the flag word is zero before any wave can set a bit in it
@@ -798,8 +799,23 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         __syncthreads();
     }
 
-    // From here on, addresses come from a fresh copy of the solve index.
+    // From here on, addresses and lane indices come from fresh copies of the
+    // solve index and the thread index: what is formed from them above need not
+    // stay live (or be spilled) until the back substitution and the recovery.
     const int bl = late(b);
+    {
+        const int tx = late_lane((int)threadIdx.x);
+        i = tx % NP;
+        g = tx / NP;
+    }
+    rowi = i < NC;
+    ii = rowi ? i : 0;
+    hasG = g < M;
+    jo = 2 * g + 1;
+    hasO = hasG && jo < N;
+    me = hasG ? cr_group_even(g, M) : 0;
+    ke = 2 * me;
+    lev = me == 0 ? levels : 1 + __builtin_ctz(me);
 
     // back substitution, levels in reverse: lambda_j = C_j'^-1 (w3 - W1 lambda_{j-s} - W2 lambda_{j+s})
     auto back = [&](bool act, int k, int s, const float* ct, const float* w1, const float* w2, float w3) {

@@ -48,6 +48,14 @@ __device__ __forceinline__ int late(int x)
     return x;
 }
 
+// The same for a per-lane value (a thread index): indices and addresses formed
+// from the copy are recomputed where they are used.
+__device__ __forceinline__ int late_lane(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ float uniform(float x)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
