@@ -754,11 +754,22 @@ static int check_ptrs(std::initializer_list<const void*> req)
     return GATO_OK;
 }
 
+// Dims of a shape this build has kernels for (every entry point).
 static int check_dims(const gato_dims_t* d)
 {
     if (d == nullptr) return GATO_E_NULL;
     if (d->n < 1 || d->m < 1 || d->N < 1 || d->B < 0) return GATO_E_DIMS;
-    if (!gato_shape_supported(d->n, d->m, d->N)) return GATO_E_UNSUPPORTED;
+    if (gato_shape_supported(d->n, d->m, d->N) != 1) return GATO_E_UNSUPPORTED;
+    return GATO_OK;
+}
+
+// Dims gato_sqp_step serves: a shape with kernels, or one it embeds in a larger
+// shape that has them (padded_dims).
+static int check_dims_step(const gato_dims_t* d)
+{
+    if (d == nullptr) return GATO_E_NULL;
+    if (d->n < 1 || d->m < 1 || d->N < 1 || d->B < 0) return GATO_E_DIMS;
+    if (gato_shape_supported(d->n, d->m, d->N) == 0) return GATO_E_UNSUPPORTED;
     return GATO_OK;
 }
 
@@ -841,6 +852,122 @@ static bool fused_path(const gato_dims_t* d)
     return with_shape(d->n, d->m, [&](auto ops) { return decltype(ops)::fused_ok(d->N) ? 1 : 0; }) == 1;
 }
 
+// ------------------------------------------------------------------ shapes served by padding
+
+// A problem of a shape without kernels of its own is solved inside the smallest
+// shape with kernels that holds it (fewest states, then fewest controls): its
+// Q_k and R_k get identity rows and columns beyond n and m, A_k, B_k, q, r, e
+// and x0 zeros.  The added states then have x0 = 0, e = 0 and no coupling to the
+// others, and the added controls no effect on any state, so the padded QP is the
+// original one plus a separate part whose solution is zero: its dz and lambda
+// entries are exactly zero (PCG keeps them at zero from a zero start, since the
+// padded blocks of S and Phi^-1 do not couple them to the rest), and its merit
+// terms are zero.  The original problem's dz, lambda, merits and flags are the
+// padded problem's, read at the original rows.
+static bool native_shape(int n, int m)
+{
+    return with_shape(n, m, [](auto) { return 1; }) == 1;
+}
+
+static bool padded_dims(const gato_dims_t* d, gato_dims_t* pd)
+{
+    int bn = 0, bm = 0;
+#define GATO_PAD_SHAPE(n_, m_) \
+    if (n_ >= d->n && m_ >= d->m && (bn == 0 || n_ < bn || (n_ == bn && m_ < bm))) { bn = n_; bm = m_; }
+    GATO_FOR_SHAPES(GATO_PAD_SHAPE)
+#undef GATO_PAD_SHAPE
+    if (bn == 0) return false;
+    *pd = *d;
+    pd->n = bn;
+    pd->m = bm;
+    return true;
+}
+
+// The padded copies in gato_sqp_step's workspace, then the padded step's own workspace.
+struct PadLayout {
+    size_t Q, q, R, r, A, Bu, e, x0, lam, dz, inner, total;
+};
+
+static PadLayout pad_layout(const gato_dims_t* pd)
+{
+    const size_t B = pd->B, N = pd->N, n = pd->n, m = pd->m, Nd = N > 1 ? N - 1 : 0;
+    PadLayout w;
+    size_t off = 0;
+    auto take = [&](size_t floats) {
+        const size_t at = off;
+        off += align256(floats * sizeof(float));
+        return at;
+    };
+    w.Q = take(B * N * n * n);
+    w.q = take(B * N * n);
+    w.R = take(B * Nd * m * m);
+    w.r = take(B * Nd * m);
+    w.A = take(B * Nd * n * n);
+    w.Bu = take(B * Nd * n * m);
+    w.e = take(B * Nd * n);
+    w.x0 = take(B * n);
+    w.lam = take(B * N * n);
+    w.dz = take(B * (N * n + Nd * m));
+    w.inner = off;
+    w.total = off + (fused_path(pd) ? 0 : ws_layout(pd).total);
+    return w;
+}
+
+// dst: nblk blocks of Rp x Cp from src's nblk blocks of R x C (R <= Rp, C <= Cp):
+// the source entry where there is one, else `diag` on the diagonal and 0 off it.
+__global__ void k_pad_blocks(float* dst, const float* src, size_t nblk, int R, int C, int Rp, int Cp, float diag)
+{
+    const size_t per = (size_t)Rp * Cp, total = nblk * per;
+    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+        const size_t blk = t / per;
+        const int r = (int)((t % per) / Cp), c = (int)(t % Cp);
+        dst[t] = (r < R && c < C) ? src[(blk * R + r) * C + c] : (r == c ? diag : 0.0f);
+    }
+}
+
+// The inverse: dst's nblk blocks of R x C from the leading rows and columns of src's Rp x Cp blocks.
+__global__ void k_unpad_blocks(float* dst, const float* src, size_t nblk, int R, int C, int Rp, int Cp)
+{
+    const size_t per = (size_t)R * C, total = nblk * per;
+    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+        const size_t blk = t / per;
+        const int r = (int)((t % per) / C), c = (int)(t % C);
+        dst[t] = src[(blk * Rp + r) * Cp + c];
+    }
+}
+
+// dz [B][N n + (N-1) m] (dx_0, du_0, ..., dx_{N-1}) from the padded step's [B][N np + (N-1) mp].
+__global__ void k_unpad_dz(float* dz, const float* dzp, int B, int N, int n, int m, int np, int mp)
+{
+    const size_t per = (size_t)N * n + (size_t)(N - 1) * m, perp = (size_t)N * np + (size_t)(N - 1) * mp;
+    const size_t total = (size_t)B * per;
+    for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+        const size_t b = t / per, o = t % per;
+        const size_t k = o / (size_t)(n + m);
+        const int w = (int)(o % (size_t)(n + m));  // the last knot has w < n only
+        dz[t] = dzp[b * perp + k * (size_t)(np + mp) + (w < n ? w : np + (w - n))];
+    }
+}
+
+static hipError_t pad_launch(hipStream_t st, float* dst, const float* src, size_t nblk, int R, int C, int Rp, int Cp,
+                             float diag)
+{
+    const size_t total = nblk * (size_t)Rp * Cp;
+    if (total == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_pad_blocks, dim3(grid), dim3(256), 0, st, dst, src, nblk, R, C, Rp, Cp, diag);
+    return hipGetLastError();
+}
+
+static hipError_t unpad_launch(hipStream_t st, float* dst, const float* src, size_t nblk, int R, int C, int Rp, int Cp)
+{
+    const size_t total = nblk * (size_t)R * C;
+    if (total == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_unpad_blocks, dim3(grid), dim3(256), 0, st, dst, src, nblk, R, C, Rp, Cp);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ allocation-free scratch
 
 // gato_sqp_step_noalloc's workspace: one array per device, held from the load of
@@ -878,8 +1005,10 @@ extern "C" {
 int gato_shape_supported(int32_t n, int32_t m, int32_t N)
 {
     if (n < 1 || m < 1 || N < 1) return 0;
-    const int r = with_shape(n, m, [&](auto ops) { return decltype(ops)::supported(N) ? 1 : 0; });
-    return r == 1;
+    if (native_shape(n, m)) return with_shape(n, m, [&](auto ops) { return decltype(ops)::supported(N) ? 1 : 0; });
+    gato_dims_t d{n, m, N, 1}, pd;
+    if (!padded_dims(&d, &pd)) return 0;
+    return with_shape(pd.n, pd.m, [&](auto ops) { return decltype(ops)::supported(N) ? 2 : 0; });
 }
 
 const char* gato_status_string(int code)
@@ -899,16 +1028,23 @@ const char* gato_status_string(int code)
 
 int gato_step_solver(const gato_dims_t* dims)
 {
-    const int rc = check_dims(dims);
+    const int rc = check_dims_step(dims);
     if (rc) return rc;
-    if (fused_path(dims)) return GATO_SOLVER_FUSED_PCG;
-    return cr_preferred(dims) ? GATO_SOLVER_CR : GATO_SOLVER_THOMAS;
+    gato_dims_t d = *dims;
+    if (!native_shape(d.n, d.m)) padded_dims(dims, &d);
+    if (fused_path(&d)) return GATO_SOLVER_FUSED_PCG;
+    return cr_preferred(&d) ? GATO_SOLVER_CR : GATO_SOLVER_THOMAS;
 }
 
 size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha)
 {
     (void)n_alpha;
-    if (check_dims(dims) != GATO_OK || dims->B == 0) return 0;
+    if (check_dims_step(dims) != GATO_OK || dims->B == 0) return 0;
+    if (!native_shape(dims->n, dims->m)) {
+        gato_dims_t pd;
+        padded_dims(dims, &pd);
+        return pad_layout(&pd).total;
+    }
     if (fused_path(dims)) return 0;
     return ws_layout(dims).total;
 }
@@ -1084,8 +1220,53 @@ int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, 
                        int32_t* flags, void* workspace, size_t workspace_bytes,
                        gato_stage_times_t* times, const gato_step_opts_t* opts, hipStream_t stream)
 {
-    int rc = check_dims(dims);
+    int rc = check_dims_step(dims);
     if (rc) return rc;
+    if (!native_shape(dims->n, dims->m)) {
+        // a shape without kernels of its own: solve the padded problem (padded_dims)
+        if (opts && ((opts->solver != GATO_SOLVER_AUTO && opts->solver != GATO_SOLVER_THOMAS &&
+                      opts->solver != GATO_SOLVER_CR && opts->solver != GATO_SOLVER_CR_STREAM) ||
+                     (opts->refine != 0 && opts->refine != 1)))
+            return GATO_E_PARAM;
+        if (dims->B == 0) return GATO_OK;
+        rc = check_ptrs({Q, q, dyn(R, dims), dyn(r, dims), dyn(A, dims), dyn(Bu, dims), dyn(e, dims), x0, lambda,
+                         dz, merit, merit0, best, iters, relres, flags});
+        if (rc) return rc;
+        if (rho && !aligned4(rho)) return GATO_E_ALIGN;
+        if (!(eps > 0.0f) || max_iters < 1) return GATO_E_PARAM;
+        rc = check_alpha(alphas_host, n_alpha, mu);
+        if (rc) return rc;
+        gato_dims_t pd;
+        padded_dims(dims, &pd);
+        const PadLayout pl = pad_layout(&pd);
+        if (workspace == nullptr || workspace_bytes < pl.total) return GATO_E_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return GATO_E_ALIGN;
+        char* ws = static_cast<char*>(workspace);
+        auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+        const int n = dims->n, m = dims->m, np = pd.n, mp = pd.m, N = dims->N;
+        const size_t B = dims->B, Nd = N > 1 ? N - 1 : 0;
+        hipError_t e2 = pad_launch(stream, at(pl.Q), Q, B * N, n, n, np, np, 1.0f);
+        if (e2 == hipSuccess) e2 = pad_launch(stream, at(pl.q), q, B * N, n, 1, np, 1, 0.0f);
+        if (e2 == hipSuccess && Nd) e2 = pad_launch(stream, at(pl.R), R, B * Nd, m, m, mp, mp, 1.0f);
+        if (e2 == hipSuccess && Nd) e2 = pad_launch(stream, at(pl.r), r, B * Nd, m, 1, mp, 1, 0.0f);
+        if (e2 == hipSuccess && Nd) e2 = pad_launch(stream, at(pl.A), A, B * Nd, n, n, np, np, 0.0f);
+        if (e2 == hipSuccess && Nd) e2 = pad_launch(stream, at(pl.Bu), Bu, B * Nd, n, m, np, mp, 0.0f);
+        if (e2 == hipSuccess && Nd) e2 = pad_launch(stream, at(pl.e), e, B * Nd, n, 1, np, 1, 0.0f);
+        if (e2 == hipSuccess) e2 = pad_launch(stream, at(pl.x0), x0, B, n, 1, np, 1, 0.0f);
+        if (e2 == hipSuccess) e2 = pad_launch(stream, at(pl.lam), lambda, B * N, n, 1, np, 1, 0.0f);
+        if (e2 != hipSuccess) return GATO_E_HIP;
+        rc = gato_sqp_step_opts(&pd, at(pl.Q), at(pl.q), Nd ? at(pl.R) : nullptr, Nd ? at(pl.r) : nullptr,
+                                Nd ? at(pl.A) : nullptr, Nd ? at(pl.Bu) : nullptr, Nd ? at(pl.e) : nullptr,
+                                at(pl.x0), rho, eps, max_iters, alphas_host, n_alpha, mu, at(pl.lam), at(pl.dz), merit,
+                                merit0, best, iters, relres, flags, ws + pl.inner, workspace_bytes - pl.inner, times,
+                                opts, stream);
+        if (rc != GATO_OK) return rc;
+        if (unpad_launch(stream, lambda, at(pl.lam), B * N, n, 1, np, 1) != hipSuccess) return GATO_E_HIP;
+        const size_t total = B * ((size_t)N * n + Nd * m);
+        const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 4096);
+        hipLaunchKernelGGL(k_unpad_dz, dim3(grid), dim3(256), 0, stream, dz, at(pl.dz), (int)B, N, n, m, np, mp);
+        return hipGetLastError() == hipSuccess ? GATO_OK : GATO_E_HIP;
+    }
     const int solver = opts ? opts->solver : GATO_SOLVER_AUTO;
     const int refine = opts ? opts->refine : 1;
     if (solver != GATO_SOLVER_AUTO && solver != GATO_SOLVER_THOMAS && solver != GATO_SOLVER_CR &&
@@ -1199,14 +1380,14 @@ int gato_sqp_step_noalloc(const gato_dims_t* dims, const float* Q, const float* 
                           float* merit, float* merit0, int32_t* best, int32_t* iters, float* relres,
                           int32_t* flags, hipStream_t stream)
 {
-    int rc = check_dims(dims);
+    int rc = check_dims_step(dims);
     if (rc) return rc;
     if (dims->B == 0) return GATO_OK;  // nothing to do; pointers may be empty
-    const bool fused = fused_path(dims);
-    if (!fused && ws_layout(dims).total > (size_t)GATO_NOALLOC_SCRATCH_BYTES) return GATO_E_WORKSPACE;
+    const size_t need = gato_workspace_bytes(dims, n_alpha);
+    if (need > (size_t)GATO_NOALLOC_SCRATCH_BYTES) return GATO_E_WORKSPACE;
     void* ws = nullptr;
     size_t wsb = 0;
-    if (!fused) {
+    if (need > 0) {
         ws = scratch_ptr();
         if (ws == nullptr) return GATO_E_HIP;
         wsb = (size_t)GATO_NOALLOC_SCRATCH_BYTES;

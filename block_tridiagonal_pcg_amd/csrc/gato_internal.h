@@ -9,8 +9,10 @@
 #include "gato.h"
 
 // (n, m) of the shapes this build has kernels for: those of the configurations
-// the benchmark and tests use, plus n = m = 1 for hand-checkable examples.
-#define GATO_FOR_SHAPES(X) X(14, 7) X(12, 6) X(24, 12) X(4, 2) X(1, 1)
+// the benchmark and tests use, n = m = 1 for hand-checkable examples, and
+// (28, 14), the widest whose fused step fits a workgroup's LDS, so that
+// gato_sqp_step can serve any n <= 28, m <= 14 by padding.
+#define GATO_FOR_SHAPES(X) X(14, 7) X(12, 6) X(24, 12) X(4, 2) X(1, 1) X(28, 14)
 
 namespace gato {
 

@@ -94,17 +94,17 @@ struct Ix {
 };
 
 // Masked loads read this page instead of the problem arrays, which may be
-// absent in a call (NULL) or empty (N = 1).  2048 floats cover the widest
-// strided read (a column of the cyclic reduction's 24 x 76 workspace rows);
+// absent in a call (NULL) or empty (N = 1).  4096 floats cover the widest
+// strided read (a column of the cyclic reduction's 28 x 88 workspace rows);
 // module globals are zero-initialised.
-static __device__ __align__(16) float g_zero_page[2048];
+static __device__ __align__(16) float g_zero_page[4096];
 
 // Load K floats at base[off + j * STRIDE] when ok, else zeros; the address is
 // selected before the loads, which are then unconditional.
 template <int K, int STRIDE = 1>
 __device__ __forceinline__ void ld_row(const float* base, size_t off, bool ok, float* out)
 {
-    static_assert((K - 1) * STRIDE < 2048, "masked row read exceeds the zero page");
+    static_assert((K - 1) * STRIDE < 4096, "masked row read exceeds the zero page");
     const float* a = ok ? base + off : g_zero_page;
 #pragma unroll
     for (int j = 0; j < K; ++j) {

@@ -300,7 +300,9 @@ def gato_workspace_bytes(dims, n_alpha=8):
 
 
 def gato_shape_supported(n, m, N):
-    return bool(load().gato_shape_supported(int(n), int(m), int(N)))
+    """1: the build has kernels for (n, m); 2: gato_sqp_step serves it by padding to a
+    compiled shape (the stage calls do not); 0: unsupported."""
+    return int(load().gato_shape_supported(int(n), int(m), int(N)))
 
 
 def _opts(solver, refine):

@@ -52,8 +52,8 @@
  * ---------------------------------------------------------------- errors
  * Host-side validation runs before anything is enqueued and returns a
  * negative GATO_E_* code (nothing enqueued) for: a NULL required pointer,
- * dims < 1, a shape (n, m, N) this build
- * has no kernel for (GATO_E_UNSUPPORTED), a pointer not 4-byte aligned,
+ * dims < 1, a shape (n, m, N) the call does not serve (GATO_E_UNSUPPORTED;
+ * see gato_shape_supported), a pointer not 4-byte aligned,
  * eps <= 0, max_iters < 1, n_alpha outside [1, GATO_MAX_ALPHA], mu < 0 or a
  * workspace smaller than gato_workspace_bytes().  B = 0 returns GATO_OK
  * once the dims are valid, before any pointer is looked at (empty tensors may
@@ -378,16 +378,30 @@ int gato_sqp_step_noalloc(const gato_dims_t* dims, const float* Q, const float* 
  * GATO_SOLVER_CR; a negative status for invalid or unsupported dims. */
 int gato_step_solver(const gato_dims_t* dims);
 
-/* Workspace gato_sqp_step needs for these dims (0 when the fused path applies). */
+/* Workspace gato_sqp_step needs for these dims (0 when the fused path applies to
+ * a shape with kernels of its own; the padded copies otherwise, see
+ * gato_shape_supported). */
 size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha);
 
 /* Static description of a status code. */
 const char* gato_status_string(int code);
 
-/* Non-zero if this build has kernels for (n, m, N): (n, m) in {(14,7), (12,6),
- * (24,12), (4,2), (1,1)} and 1 <= N <= 1024.  gato_pcg_solve alone is further
- * limited to N <= 256 for n <= 16 and N <= 64 for n <= 32 (four knots per lane
- * group) and returns GATO_E_UNSUPPORTED beyond. */
+/* Whether this build serves (n, m, N): 1 if it has kernels for (n, m), which are
+ * (14,7), (12,6), (24,12), (4,2), (1,1) and (28,14), and 1 <= N <= 1024;
+ * 2 if only the step calls (gato_sqp_step, gato_sqp_step_opts,
+ * gato_sqp_step_noalloc) serve it, by padding; 0 otherwise.  Padding: a shape
+ * without kernels, n <= 28 and m <= 14, is solved inside the smallest compiled
+ * shape (n', m') with n' >= n and m' >= m (fewest states, then fewest controls):
+ * Q_k and R_k get identity rows and columns beyond n and m, and A_k, B_k, q,
+ * r, e, x0 and lambda's input zeros.  The added states and controls then form a
+ * separate part of the QP whose solution is exactly zero, so the original
+ * problem's dz, lambda, merits, selection, iterations and flags are the padded
+ * problem's at the original rows.  The padded copies go through the step's
+ * workspace (gato_workspace_bytes counts them, on the fused path too) and cost
+ * two light copy kernels; stage times, when asked for, cover the padded step.
+ * gato_pcg_solve alone is further limited to N <= 256 for n <= 16 and N <= 64
+ * for n <= 32 (four knots per lane group) and returns GATO_E_UNSUPPORTED beyond;
+ * the stage calls return GATO_E_UNSUPPORTED for shapes served by padding. */
 int gato_shape_supported(int32_t n, int32_t m, int32_t N);
 
 #ifdef __cplusplus

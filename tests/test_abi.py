@@ -112,7 +112,7 @@ def test_noalloc_rejects_dims_beyond_its_scratch(lib):
         assert f(ctypes.byref(ops.Dims(*dims)), *[None] * 9, 1e-6, 200, al, 8, 1.0, *[None] * 8, None) == \
             ops.E_WORKSPACE, dims
     assert f(ctypes.byref(ops.Dims(14, 7, 128, 0)), *[None] * 9, 1e-6, 200, al, 8, 1.0, *[None] * 8, None) == ops.OK
-    assert f(ctypes.byref(ops.Dims(13, 7, 128, 4)), *[None] * 9, 1e-6, 200, al, 8, 1.0, *[None] * 8,
+    assert f(ctypes.byref(ops.Dims(29, 7, 128, 4)), *[None] * 9, 1e-6, 200, al, 8, 1.0, *[None] * 8,
              None) == ops.E_UNSUPPORTED
 
 
@@ -155,7 +155,7 @@ def test_shapes_and_workspace(lib):
     for n, m, N in ((14, 7, 64), (12, 6, 32), (24, 12, 16), (4, 2, 8), (14, 7, 128), (1, 1, 2), (14, 7, 1),
                     (14, 7, 1024), (24, 12, 200)):
         assert ops.gato_shape_supported(n, m, N), (n, m, N)
-    for n, m, N in ((13, 7, 64), (14, 7, 0), (14, 7, 1025), (24, 12, 1025)):
+    for n, m, N in ((14, 7, 0), (14, 7, 1025), (24, 12, 1025), (29, 5, 10), (10, 15, 10), (0, 1, 4)):
         assert not ops.gato_shape_supported(n, m, N), (n, m, N)
     assert ops.gato_workspace_bytes((14, 7, 64, 128)) == 0          # fused: no workspace
     ws = ops.gato_workspace_bytes((14, 7, 128, 512))
@@ -171,7 +171,41 @@ def test_shapes_and_workspace(lib):
     refine = a(B * N * 14) + a(B * (N - 1) * 7) + a(B * (N - 1) * 14) + a(B * 14) + 2 * a(B * N * 14) + \
         a(B * N * 14) + a(B * (N * 14 + (N - 1) * 7)) + a(B)
     assert ws == stage1 + solve + refine
-    assert ops.gato_workspace_bytes((13, 7, 64, 128)) == 0          # unsupported -> 0
+    assert ops.gato_workspace_bytes((29, 7, 64, 128)) == 0          # unsupported -> 0
+
+
+def test_shapes_served_by_padding(lib):
+    """A shape without kernels: gato_sqp_step runs it inside the smallest compiled shape
+    that holds it (2 from gato_shape_supported), with the padded copies in its workspace
+    even on the fused path; the stage calls take only compiled shapes."""
+    from block_tridiagonal_pcg_amd import ops
+
+    assert ops.gato_shape_supported(14, 7, 64) == 1 and ops.gato_shape_supported(28, 14, 16) == 1
+    for n, m in ((10, 5), (13, 7), (3, 1), (16, 8), (20, 10), (26, 13), (28, 1), (12, 12)):
+        assert ops.gato_shape_supported(n, m, 30) == 2, (n, m)
+    # the padded copies: Q, q, R, r, A, Bu, e, x0, lambda, dz in the (12, 6) shape, each 256-byte aligned
+    a = lambda x: (x * 4 + 255) // 256 * 256  # noqa: E731
+    B, N, n, m = 8, 32, 12, 6
+    pads = a(B * N * n * n) + a(B * N * n) + a(B * (N - 1) * m * m) + a(B * (N - 1) * m) + \
+        a(B * (N - 1) * n * n) + a(B * (N - 1) * n * m) + a(B * (N - 1) * n) + a(B * n) + a(B * N * n) + \
+        a(B * (N * n + (N - 1) * m))
+    assert ops.gato_workspace_bytes((10, 5, 32, 8)) == pads  # fused at (12, 6): nothing more
+    assert ops.gato_workspace_bytes((10, 5, 100, 4)) > ops.gato_workspace_bytes((12, 6, 100, 4))
+    assert ops.gato_step_solver((10, 5, 32, 8)) == ops.SOLVER_FUSED_PCG
+    assert ops.gato_step_solver((18, 9, 16, 8)) == ops.SOLVER_FUSED_PCG
+    assert ops.gato_step_solver((18, 9, 17, 8)) != ops.SOLVER_FUSED_PCG
+    good = [ctypes.c_void_p(4096 * (j + 1)) for j in range(15)]
+    assert _call_form(lib, ops.Dims(10, 5, 32, 2), good) == ops.E_UNSUPPORTED
+    # the step checks its workspace for the padded layout before anything runs
+    al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
+    P = [ctypes.c_void_p(4096 * (j + 1)) for j in range(17)]
+    args = [*P[:9], 1e-6, 200, al, 8, 1.0, *P[9:17]]
+    h = lib.gato_sqp_step
+    d = ops.Dims(10, 5, 32, 8)
+    assert h(ctypes.byref(d), *args, None, ctypes.c_size_t(0), None, None) == ops.E_WORKSPACE
+    assert h(ctypes.byref(d), *args, ctypes.c_void_p(1 << 20), ctypes.c_size_t(pads - 1), None, None) == \
+        ops.E_WORKSPACE
+    assert h(ctypes.byref(d), *args, ctypes.c_void_p((1 << 20) + 4), ctypes.c_size_t(pads), None, None) == ops.E_ALIGN
 
 
 def _call_form(lib, dims, ptrs):
@@ -187,7 +221,7 @@ def test_validation_happens_before_any_launch(lib):
     d = ops.Dims(14, 7, 64, 2)
     assert _call_form(lib, None, good) == ops.E_NULL
     assert _call_form(lib, ops.Dims(14, 7, 0, 2), good) == ops.E_DIMS
-    assert _call_form(lib, ops.Dims(13, 7, 64, 2), good) == ops.E_UNSUPPORTED
+    assert _call_form(lib, ops.Dims(29, 7, 64, 2), good) == ops.E_UNSUPPORTED
     bad = list(good)
     bad[0] = None
     assert _call_form(lib, d, bad) == ops.E_NULL
@@ -318,4 +352,4 @@ def test_horizon_policy_picks_the_measured_solver(lib):
     for dims, want in cases.items():
         assert ops.gato_step_solver(dims) == want, dims
     with pytest.raises(ops.GatoError):
-        ops.gato_step_solver((13, 7, 128, 16))
+        ops.gato_step_solver((29, 7, 128, 16))
