@@ -375,12 +375,12 @@ def sqp_driver(a, iters=10, N=64, dof=7):
     import numpy as np
     import torch
 
-    from block_tridiagonal_pcg_amd import driver, plant
+    from block_tridiagonal_pcg_amd import driver, synth
 
     torch.cuda.set_device(0)
-    P = plant.Chain(dof)
+    P = synth.Chain(dof)
     B = a.batch
-    xi, xr, rho = plant.seed(P, B)
+    xi, xr, rho = synth.chain_seed(P, B)
     driver.solve(P, xi, xr, rho, N, 2, record=False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -413,8 +413,6 @@ def sqp_driver(a, iters=10, N=64, dof=7):
     if not a.no_cpu_baseline:
         import oracle
         from oracle import driver_ref
-
-        from block_tridiagonal_pcg_amd import synth
 
         oracle.load()
         Bs = min(B, 16)

@@ -9,8 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgato.so")
-SOURCES = ["gato.hip", "gato_cr.hip"]
-HEADERS = ["gato_dev.h", "gato_stages.h", "gato_cr.h", "gato_internal.h", "dpp_asm.inc", os.path.join("..", "..", "include", "gato.h")]
+SOURCES = ["gato.hip", "gato_cr.hip", "gato_driver.hip"]
+HEADERS = ["gato_dev.h", "gato_stages.h", "gato_cr.h", "gato_internal.h", "dpp_asm.inc", os.path.join("..", "..", "include", "gato.h"), os.path.join("..", "..", "include", "gato_driver.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

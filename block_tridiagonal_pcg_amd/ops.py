@@ -46,6 +46,8 @@ EXPORTS = (
     "gato_step_solver",
     "gato_status_string",
     "gato_shape_supported",
+    "gato_chain_qp",
+    "gato_take_step",
 )
 
 
@@ -61,6 +63,12 @@ class Dims(ctypes.Structure):
 
 class StepOpts(ctypes.Structure):
     _fields_ = [("solver", ctypes.c_int32), ("refine", ctypes.c_int32)]
+
+
+class ChainParams(ctypes.Structure):
+    _fields_ = [("dof", ctypes.c_int32), ("h", ctypes.c_float), ("a", ctypes.c_float), ("c", ctypes.c_float),
+                ("kappa", ctypes.c_float), ("w_theta", ctypes.c_float), ("w_omega", ctypes.c_float),
+                ("w_u", ctypes.c_float)]
 
 
 class StageTimes(ctypes.Structure):
@@ -107,9 +115,11 @@ def load():
             lib.gato_status_string.argtypes = [ctypes.c_int]
             lib.gato_status_string.restype = ctypes.c_char_p
             lib.gato_shape_supported.argtypes = [I, I, I]
+            lib.gato_chain_qp.argtypes = [P] * 15
+            lib.gato_take_step.argtypes = [P, P, I, P, P, P, P, P, F, F, P]
             for f in ("gato_form_schur", "gato_pcg_solve", "gato_direct_solve", "gato_cr_solve", "gato_merit_eval",
                       "gato_merit_eval_shape", "gato_sqp_step", "gato_sqp_step_opts", "gato_sqp_step_noalloc",
-                      "gato_shape_supported"):
+                      "gato_shape_supported", "gato_chain_qp", "gato_take_step"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -365,6 +375,48 @@ def gato_sqp_step_noalloc(dims, Q, q, R, r, A, Bu, e, x0, rho, eps, max_iters, a
                                       _p(merit), _p(merit0), _p(best), _p(iters), _p(relres), _p(flags),
                                       _stream(stream))
     return _raise("gato_sqp_step_noalloc", rc)
+
+
+# ---------------------------------------------------------------- the SQP driver's kernels
+
+
+def chain_params(P):
+    """The C struct of a synth.Chain's parameters."""
+    return ChainParams(int(P.dof), float(P.h), float(P.a), float(P.c), float(P.kappa), float(P.w_theta),
+                       float(P.w_omega), float(P.w_u))
+
+
+def gato_chain_qp(dims, plant, X, U, x_init, x_ref, Q, q, R, r, A, Bu, e, x0, stream=None):
+    """The chain plant's QP data at (X, U) (include/gato_driver.h); `plant` is a ChainParams."""
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    _chk(X, "X", shape=(B, N, n))
+    _chk(U, "U", shape=(B, N - 1, m))
+    _chk(x_init, "x_init", shape=(B, n))
+    _chk(x_ref, "x_ref", shape=(B, n))
+    for t, k in ((Q, "Q"), (q, "q"), (R, "R"), (r, "r"), (A, "A"), (Bu, "Bu"), (e, "e"), (x0, "x0")):
+        _chk(t, k, shape=sh[k])
+    d = _dims(n, m, N, B)
+    rc = load().gato_chain_qp(ctypes.byref(d), ctypes.byref(plant), _p(X), _p(U), _p(x_init), _p(x_ref), _p(Q),
+                              _p(q), _p(R), _p(r), _p(A), _p(Bu), _p(e), _p(x0), _stream(stream))
+    return _raise("gato_chain_qp", rc)
+
+
+def gato_take_step(dims, alphas, dz, best, X, U, rho, rho_min, rho_max, stream=None):
+    """X += a dX, U += a dU with a = alphas[best] (0 on a failed line search), and the
+    damping update (include/gato_driver.h)."""
+    n, m, N, B = dims
+    sh = _shapes(n, m, N, B)
+    _chk(dz, "dz", shape=sh["dz"])
+    _chk(best, "best", torch.int32, sh["B_"])
+    _chk(X, "X", shape=(B, N, n))
+    _chk(U, "U", shape=(B, N - 1, m))
+    _chk(rho, "rho", shape=(B,))
+    arr, na = _alphas(alphas)
+    d = _dims(n, m, N, B)
+    rc = load().gato_take_step(ctypes.byref(d), arr, na, _p(dz), _p(best), _p(X), _p(U), _p(rho), float(rho_min),
+                               float(rho_max), _stream(stream))
+    return _raise("gato_take_step", rc)
 
 
 # ---------------------------------------------------------------- allocation helpers

@@ -105,3 +105,51 @@ def make_batch(cid: int, B: int, *, n: int | None = None, m: int | None = None,
 def inputs(batch: dict):
     """The eight problem arrays in the C-ABI argument order."""
     return [batch[f] for f in FIELDS]
+
+
+# ---------------------------------------------------------------- the SQP driver's plant
+
+
+@dataclass(frozen=True)
+class Chain:
+    """Parameters of the analytic plant the multi-iteration SQP driver runs on (a
+    synthetic stand-in for the robot models the pages linearise with GRiD): a chain of
+    `dof` coupled, damped pendulums, state x = [theta, omega], control u (torques), so
+    n = 2 dof and m = dof; explicit Euler with step h,
+        theta' = theta + h omega,
+        omega' = omega + h (-a sin(theta) - c omega + kappa L theta + u),
+    L the path-graph Laplacian over the joints (free ends); the cost tracks a target,
+        1/2 (x - x_ref)' diag(w_theta, w_omega) (x - x_ref) + 1/2 w_u u'u.
+    The arithmetic lives on each side of its own: the device driver's kernels
+    (gato_chain_qp) and the reference driver's fp64 plant (oracle)."""
+    dof: int
+    h: float = 0.02
+    a: float = 9.81
+    c: float = 0.5
+    kappa: float = 2.0
+    w_theta: float = 10.0
+    w_omega: float = 0.1
+    w_u: float = 0.01
+
+    @property
+    def n(self):
+        return 2 * self.dof
+
+    @property
+    def m(self):
+        return self.dof
+
+
+def chain_seed(P: Chain, B: int, first: int = 0):
+    """Per-solve initial states and targets (fp64 numpy; solve b is the same for every
+    B): angles and rates drawn small, target angles in [-0.6, 0.6] rad; and the
+    starting damping rho, log-spaced over 1e-8 .. 1e1 across the batch."""
+    x_init = np.zeros((B, P.n))
+    x_ref = np.zeros((B, P.n))
+    for j in range(B):
+        rng = np.random.default_rng(np.random.SeedSequence([71, first + j]))
+        x_init[j, :P.dof] = rng.uniform(-0.3, 0.3, P.dof)
+        x_init[j, P.dof:] = rng.uniform(-0.2, 0.2, P.dof)
+        x_ref[j, :P.dof] = rng.uniform(-0.6, 0.6, P.dof)
+    rho = np.logspace(-8, 1, B) if B > 1 else np.array([1e-4])
+    return x_init, x_ref, rho

@@ -1,17 +1,16 @@
 """Reference for the multi-iteration SQP driver: the same outer loop as the device
 driver, in fp64 numpy around the oracle's sqp_step.  Test infrastructure only.
 
-Per iteration: linearise the plant about (X, U) (block_tridiagonal_pcg_amd.plant, the
-input module both sides share; it holds none of the method's arithmetic), one
-oracle sqp_step warm-started from the previous lambda, the step X += a dX,
+Per iteration: linearise the plant about (X, U) (plant_ref, this package's fp64 plant;
+its parameters come from the shared input module), one oracle sqp_step warm-started
+from the previous lambda, the step X += a dX,
 U += a dU with the selected step size a (none when the line search failed), and
 the damping update: a full step divides rho by 10, a shortened one keeps it, a
 failed line search multiplies it by 10, within [1e-8, 10].
 """
 import numpy as np
 
-from block_tridiagonal_pcg_amd import plant
-
+from . import plant_ref as plant
 from .ref import sqp_step
 
 

@@ -9,8 +9,13 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _headers():
+    inc = os.path.join(ROOT, "include")
+    return "\n".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
+
+
 def _declared():
-    text = open(os.path.join(ROOT, "include", "gato.h")).read()
+    text = _headers()
     return sorted(set(re.findall(r"^\s*(?:int32_t|int|size_t|const char\*)\s+(gato_\w+)\s*\(", text, re.M)))
 
 
@@ -25,7 +30,7 @@ def lib():
 
 def _prototypes():
     """{function: [(type, name), ...]} of every declaration in the header."""
-    text = re.sub(r"/\*.*?\*/", " ", open(os.path.join(ROOT, "include", "gato.h")).read(), flags=re.S)
+    text = re.sub(r"/\*.*?\*/", " ", _headers(), flags=re.S)
     out = {}
     for m in re.finditer(r"(?:int32_t|int|size_t|const char\*)\s+(gato_\w+)\s*\(([^)]*)\)\s*;", text):
         params = []
@@ -79,7 +84,34 @@ def test_header_declares_the_abi():
         "gato_direct_solve", "gato_direct_workspace_bytes", "gato_form_schur", "gato_merit_eval",
         "gato_merit_eval_shape", "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step",
         "gato_sqp_step_noalloc", "gato_sqp_step_opts", "gato_status_string", "gato_step_solver",
-        "gato_workspace_bytes"])
+        "gato_workspace_bytes", "gato_chain_qp", "gato_take_step"])
+
+
+def test_driver_calls_validate_on_the_host(lib):
+    """The SQP driver's kernels: bad dims and parameters return before any launch."""
+    from block_tridiagonal_pcg_amd import ops, synth
+
+    prm = ops.chain_params(synth.Chain(7))
+    P = [ctypes.c_void_p(4096 * (j + 1)) for j in range(12)]
+    f = lib.gato_chain_qp
+    assert f(ctypes.byref(ops.Dims(14, 7, 16, 2)), None, *P, None) == ops.E_NULL
+    assert f(ctypes.byref(ops.Dims(12, 7, 16, 2)), ctypes.byref(prm), *P, None) == ops.E_DIMS  # n != 2 dof
+    assert f(ctypes.byref(ops.Dims(14, 6, 16, 2)), ctypes.byref(prm), *P, None) == ops.E_DIMS  # m != dof
+    assert f(ctypes.byref(ops.Dims(14, 7, 1, 2)), ctypes.byref(prm), *P, None) == ops.E_DIMS   # no dynamics
+    assert f(ctypes.byref(ops.Dims(14, 7, 16, 2)), ctypes.byref(prm), *P[:11], None, None) == ops.E_NULL
+    assert f(ctypes.byref(ops.Dims(14, 7, 16, 0)), ctypes.byref(prm), *[None] * 12, None) == ops.OK
+    bad = ops.chain_params(synth.Chain(7, h=0.0))
+    assert f(ctypes.byref(ops.Dims(14, 7, 16, 2)), ctypes.byref(bad), *P, None) == ops.E_PARAM
+    g = lib.gato_take_step
+    al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
+    d = ctypes.byref(ops.Dims(14, 7, 16, 2))
+    assert g(d, al, 0, *P[:5], 1e-8, 10.0, None) == ops.E_PARAM
+    assert g(d, al, 17, *P[:5], 1e-8, 10.0, None) == ops.E_PARAM
+    assert g(d, al, 8, *P[:5], 0.0, 10.0, None) == ops.E_PARAM
+    assert g(d, al, 8, *P[:5], 1.0, 0.5, None) == ops.E_PARAM
+    assert g(d, None, 8, *P[:5], 1e-8, 10.0, None) == ops.E_NULL
+    assert g(d, al, 8, None, *P[1:5], 1e-8, 10.0, None) == ops.E_NULL
+    assert g(ctypes.byref(ops.Dims(14, 7, 16, 0)), al, 8, *[None] * 5, 1e-8, 10.0, None) == ops.OK
 
 
 def test_boundary_signatures():

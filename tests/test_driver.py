@@ -13,11 +13,12 @@ the fixed point.
 import numpy as np
 import pytest
 
-from block_tridiagonal_pcg_amd import plant, synth
+from block_tridiagonal_pcg_amd import synth
+from oracle import plant_ref as plant
 
 
 def test_plant_jacobians_match_central_differences():
-    P = plant.Chain(3)
+    P = synth.Chain(3)
     rng = np.random.default_rng(5)
     X = rng.uniform(-0.5, 0.5, (2, 4, P.n))
     U = rng.uniform(-0.5, 0.5, (2, 3, P.m))
@@ -39,7 +40,7 @@ def test_plant_jacobians_match_central_differences():
 
 
 def test_plant_cost_terms_are_the_gradient_of_the_cost():
-    P = plant.Chain(2)
+    P = synth.Chain(2)
     rng = np.random.default_rng(6)
     X = rng.uniform(-1, 1, (1, 5, P.n))
     U = rng.uniform(-1, 1, (1, 4, P.m))
@@ -59,8 +60,8 @@ def test_plant_cost_terms_are_the_gradient_of_the_cost():
 def test_reference_driver_converges_and_follows_the_damping_rule():
     from oracle import driver_ref
 
-    P = plant.Chain(2)
-    xi, xr, rho0 = plant.seed(P, 4)
+    P = synth.Chain(2)
+    xi, xr, rho0 = synth.chain_seed(P, 4)
     res = driver_ref.solve(P, xi, xr, rho0, 16, 6, synth.ALPHAS)
     h = res["history"]
     d0 = plant.defect(P, np.repeat(xi[:, None, :], 16, axis=1), np.zeros((4, 15, 2)), xi)
@@ -89,8 +90,8 @@ def test_device_driver_matches_reference(dof, N, B):
     ops.load()
     oracle.load()
     print("case: driver", dof, N, B, flush=True)
-    P = plant.Chain(dof)
-    xi, xr, rho0 = plant.seed(P, B)
+    P = synth.Chain(dof)
+    xi, xr, rho0 = synth.chain_seed(P, B)
     iters = 10
     g = driver.solve(P, xi, xr, rho0, N, iters)
     o = driver_ref.solve(P, xi, xr, rho0, N, iters, synth.ALPHAS)
@@ -121,8 +122,8 @@ def test_driver_graph_replays_match_eager_iterations():
         pytest.fail("GPU tests need a GPU")
     ops.load()
     print("case: driver graph replay", flush=True)
-    P = plant.Chain(7)
-    xi, xr, rho0 = plant.seed(P, 16)
+    P = synth.Chain(7)
+    xi, xr, rho0 = synth.chain_seed(P, 16)
 
     def grab(store):
         return lambda k, st: store.append({f: st[f].cpu().numpy().copy() for f in ("X", "U", "rho", "best")})
@@ -136,3 +137,53 @@ def test_driver_graph_replays_match_eager_iterations():
         np.testing.assert_allclose(b["rho"], a["rho"], rtol=1e-6, err_msg="iteration %d" % k)
         for f in ("X", "U"):
             np.testing.assert_allclose(b[f], a[f], rtol=1e-5, atol=1e-6, err_msg="%s, iteration %d" % (f, k))
+
+
+@pytest.mark.gpu
+def test_device_plant_matches_the_reference_plant():
+    """gato_chain_qp (fp32, on the device) against the fp64 reference plant at random
+    trajectories: the Jacobians, defects and cost terms it forms, and the initial-state
+    defect; and gato_take_step against the step and damping rule applied on the host."""
+    import torch
+
+    from block_tridiagonal_pcg_amd import ops
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    ops.load()
+    print("case: device plant", flush=True)
+    for dof, N, B in ((7, 16, 3), (2, 5, 2), (12, 9, 2)):
+        P = synth.Chain(dof)
+        n, m = P.n, P.m
+        rng = np.random.default_rng(dof)
+        X = rng.uniform(-1, 1, (B, N, n)).astype(np.float32)
+        U = rng.uniform(-1, 1, (B, N - 1, m)).astype(np.float32)
+        xi = rng.uniform(-1, 1, (B, n)).astype(np.float32)
+        xr = rng.uniform(-1, 1, (B, n)).astype(np.float32)
+        dims = (n, m, N, B)
+        t = lambda a: torch.as_tensor(a).cuda().contiguous()  # noqa: E731
+        sh = ops._shapes(n, m, N, B)
+        out = {k: torch.full(sh[k], float("nan"), device="cuda") for k in synth.FIELDS}
+        ops.gato_chain_qp(dims, ops.chain_params(P), t(X), t(U), t(xi), t(xr), *[out[k] for k in synth.FIELDS])
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy() for k, v in out.items()}
+        X64, U64 = X.astype(np.float64), U.astype(np.float64)
+        A, Bu, e = plant.linearize(P, X64, U64)
+        Q, q, R, r = plant.cost_terms(P, X64, U64, xr.astype(np.float64))
+        for k, ref in (("A", A), ("Bu", Bu), ("e", e), ("Q", Q), ("q", q), ("R", R), ("r", r),
+                       ("x0", xi.astype(np.float64) - X64[:, 0])):
+            np.testing.assert_allclose(g[k], ref, rtol=2e-6, atol=2e-6, err_msg=k)
+        # the step and the damping rule
+        dz = rng.standard_normal(sh["dz"]).astype(np.float32)
+        best = np.array([0, -1] + [3] * (B - 2), np.int32)[:B]
+        rho = np.array([1e-7, 5.0] + [0.1] * (B - 2), np.float32)[:B]
+        Xt, Ut, rt = t(X.copy()), t(U.copy()), t(rho.copy())
+        ops.gato_take_step(dims, synth.ALPHAS, t(dz), t(best), Xt, Ut, rt, 1e-8, 10.0)
+        torch.cuda.synchronize()
+        a = np.where(best >= 0, synth.ALPHAS[np.maximum(best, 0)], 0.0).astype(np.float32)
+        full = np.concatenate([dz, np.zeros((B, m), np.float32)], -1).reshape(B, N, n + m)
+        np.testing.assert_allclose(Xt.cpu().numpy(), X + a[:, None, None] * full[..., :n], rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(Ut.cpu().numpy(), U + a[:, None, None] * full[:, :N - 1, n:], rtol=1e-6,
+                                   atol=1e-7)
+        want = np.where(best == 0, np.maximum(rho / 10, 1e-8), np.where(best < 0, np.minimum(rho * 10, 10.0), rho))
+        np.testing.assert_allclose(rt.cpu().numpy(), want, rtol=1e-6)
