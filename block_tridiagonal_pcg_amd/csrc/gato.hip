@@ -115,18 +115,16 @@ __global__ void k_zero_i32(int32_t* x, int count)
 // (G dz - C' lambda = -g, C dz = c; GATO paper Sec. II, eq. 2): the residual of
 // the first pass's (lambda, dz), accumulated in double from the problem data,
 // is the right-hand side (g', c') of a correction system with the same G and
-// C, whose q, r, e and x0 are
-//   q'_k = q_k + Q~_k dx_k - lambda_k + A_k' lambda_{k+1}
-//   r'_k = r_k + R_k du_k + B_k' lambda_{k+1}
-//   x0'  = x0 - dx_0
-//   e'_k = e_k + A_k dx_k + B_k du_k - dx_{k+1}
-// (rows of C: [I] for knot 0, [-A_k, -B_k, I] for knot k + 1).  The products of
+// C, whose q, r, e and x0 (kkt_rows) are q'_k, r'_k, e'_k and x0' (rows of C:
+// [I] for knot 0, [-A_k, -B_k, I] for knot k + 1).  The products of
 // fp32 data are exact in double and the sums nearly so, so the correction
 // carries the first pass's error however ill-conditioned S is, while the fp32
 // solve finds it with its usual relative accuracy.  S, Q~^-1 and R^-1 are those
 // of the first pass; the correction's gamma (gamma'_0 = x0' + h_0,
 // gamma'_{k+1} = e'_k - t_k + h_{k+1}, as the formation forms gamma) takes
-// h_k = Q~_k^-1 q'_k and t_k = A_k h_k + B_k R_k^-1 r'_k from here.
+// h_k = Q~_k^-1 q'_k and t_k = A_k h_k + B_k R_k^-1 r'_k from here.  (The
+// register-resident cyclic reduction runs the whole pass inside its kernel;
+// this one serves the other direct solves.)
 // Lane group of NP lanes per knot, lane i: row i of each knot block; the
 // vectors a row needs whole go through the group's LDS rows.
 template <class SH>
@@ -145,41 +143,19 @@ __global__ __launch_bounds__(256) void k_kkt_residual(const Params p, float* qc,
     vu[gl][i] = (dyn && i < m) ? p.dz[ix.du(b, kk, i)] : 0.0f;
     vl[gl][i] = (dyn && i < n) ? p.lambda[ix.vn(b, kk + 1, i)] : 0.0f;
     __syncthreads();
-    float qv = 0.0f, rv = 0.0f;
+    float qv, rv, ev, x0v;
+    {
+        const bool rowv = kv && i < n;
+        const float lam = rowv ? p.lambda[ix.vn(b, kk, i)] : 0.0f;
+        const float dxn = (dyn && i < n) ? p.dz[ix.dx(b, kk + 1, i)] : 0.0f;
+        kkt_rows<SH>(p, b, kk, i, kv, vx[gl], vu[gl], vl[gl], lam, dxn, qv, rv, ev, x0v);
+    }
     if (kv && i < n) {
-        const double rh = p.rho != nullptr ? (double)p.rho[b] : 0.0;
-        double s = (double)p.q[ix.vn(b, kk, i)] + rh * vx[gl][i] - p.lambda[ix.vn(b, kk, i)];
-        const float* Qr = p.Q + ix.Q(b, kk, i);
-#pragma unroll
-        for (int c = 0; c < n; ++c) s += (double)Qr[c] * vx[gl][c];
-        if (dyn) {
-            const float* Ac = p.A + ix.A(b, kk, 0) + i;  // column i of A_k
-#pragma unroll
-            for (int c = 0; c < n; ++c) s += (double)Ac[c * n] * vl[gl][c];
-            const float* Ar = p.A + ix.A(b, kk, i);
-            const float* Br = p.Bu + ix.Bu(b, kk, i);
-            double t = (double)p.e[ix.e(b, kk, i)] - p.dz[ix.dx(b, kk + 1, i)];
-#pragma unroll
-            for (int c = 0; c < n; ++c) t += (double)Ar[c] * vx[gl][c];
-#pragma unroll
-            for (int c = 0; c < m; ++c) t += (double)Br[c] * vu[gl][c];
-            ec[ix.e(b, kk, i)] = (float)t;
-        }
-        qv = (float)s;
+        if (dyn) ec[ix.e(b, kk, i)] = ev;
         qc[ix.vn(b, kk, i)] = qv;
-        if (k == 0) x0c[(size_t)b * n + i] = (float)((double)p.x0[(size_t)b * n + i] - vx[gl][i]);
+        if (k == 0) x0c[(size_t)b * n + i] = x0v;
     }
-    if (dyn && i < m) {
-        double s = (double)p.r[ix.vm(b, kk, i)];
-        const float* Rr = p.R + ix.R(b, kk, i);
-#pragma unroll
-        for (int c = 0; c < m; ++c) s += (double)Rr[c] * vu[gl][c];
-        const float* Bc_ = p.Bu + ix.Bu(b, kk, 0) + i;  // column i of B_k
-#pragma unroll
-        for (int c = 0; c < n; ++c) s += (double)Bc_[c * m] * vl[gl][c];
-        rv = (float)s;
-        rc[ix.vm(b, kk, i)] = rv;
-    }
+    if (dyn && i < m) rc[ix.vm(b, kk, i)] = rv;
     vq[gl][i] = qv;
     vr[gl][i] = rv;
     __syncthreads();
@@ -1323,8 +1299,12 @@ int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, 
         p.s_upper_only = cr && !cr_reads_lower(dims, p.cr_stream != 0);
         if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;
         if (times && hipEventRecord(ev[1], stream) != hipSuccess) return GATO_E_HIP;
-        if ((cr ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) return GATO_E_HIP;
-        if (refine) {
+        if (refine && cr && cr_refines_inside(dims, p.cr_stream != 0)) {
+            // the solve and its refinement pass in one kernel, on the solve's factors
+            if (cr_launch_refined(p, stream) != hipSuccess) return GATO_E_HIP;
+        } else if ((cr ? cr_launch(p, stream) : O::direct(p, stream)) != hipSuccess) {
+            return GATO_E_HIP;
+        } else if (refine) {
             // the correction system: its right-hand side and gamma (S, Q~^-1 and R^-1
             // are the first pass's), its solve, then the sum with the first pass
             char* ws = static_cast<char*>(workspace);

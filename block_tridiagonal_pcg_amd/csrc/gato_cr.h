@@ -554,7 +554,15 @@ struct CrResLds {
     float os[MAXG][NC][YW];  // [W1 | W2 | w3] rows of the odd knots (level 0), kept to the end
     union {
         float es[MAXG / 2][NC][YW];  // [W1 | W2 | w3] rows of the even knots eliminated at one level
-        float lam[2 * MAXG][NC];     // lambda, once the forward sweep is over
+        struct {
+            float lam[2 * MAXG][NC];  // lambda, once the forward sweep is over
+            // the in-kernel refinement pass: the first pass's dx_k and du_k, and
+            // t_k and e'_k less its dx_{k+1} term, which knot k + 1's gamma' takes
+            float dx[2 * MAXG][NC];
+            float du[2 * MAXG][SH::MC];
+            float ex[2 * MAXG][NC];
+            double epd[2 * MAXG][NC];
+        };
     };
     int flags;
 };
@@ -562,9 +570,19 @@ struct CrResLds {
 // VIRT: solve the boundary system of the nested dissection (2 * ND_CHUNKS knots,
 // rows from the workspace) and write its lambda at the real knots, instead of
 // solving S itself and recovering dz.
-template <class SH, bool VIRT = false>
+// REF: follow the solve with one pass of iterative refinement of the KKT
+// system (kkt_rows) inside the kernel: the first pass's lambda and dz stay in
+// registers, the residual in double gives the correction's gamma' (formed as
+// the formation forms gamma), and the correction is solved with the factors the
+// first pass left (C' and the W rows of every eliminated knot: the odd knots'
+// in LDS and the workspace, the even knots' in registers), by a second sweep
+// over the same levels on the right-hand side alone (w3' = C^-1 gamma' by
+// forward substitution, the kept knots' gamma' less W2' w3' and W1' w3') and a
+// second back substitution.  lambda and dz are the sums of the two passes.
+template <class SH, bool VIRT = false, bool REF = false>
 __device__ __forceinline__ void cr_resident(const Params& p, int b)
 {
+    static_assert(!(VIRT && REF), "the refinement pass is for the whole solve");
     constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
     static_assert(NP == 16, "one knot row per lane of a 16-lane group");
     using LDS = CrResLds<SH>;
@@ -599,6 +617,10 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     // rows, needed only by the last back-substitution step, to the workspace
     // (16 floats per row, M knots per solve)
     const size_t ocrow = VIRT ? nw.oc(b, hasO ? g : 0, ii) : (((size_t)b * M + (hasO ? g : 0)) * NC + ii) * 16;
+    // REF: the even knots' C' rows go to the workspace too, after the odd knots'
+    // (row i of group g's even knot at ec_at(b, g) + 16 i), and q' and r' after them
+    const size_t ec0 = (size_t)p.B * M * NC * 16;
+    auto ec_at = [&](int bb, int gg) { return ec0 + ((size_t)bb * M + gg) * NC * 16; };
     {
         const bool ld = hasO && rowi;
         const int jj = hasO ? jo : 0;
@@ -767,6 +789,14 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
 #pragma unroll
                 for (int c = 0; c < YW; ++c) sm.es[g - first][i][c] = e[NC + c];
             }
+            if constexpr (REF) {
+                if (elim && rowi) {
+                    float r[16];
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) r[c] = c < NC ? e[c] : 0.0f;
+                    st4<16>(p.dws, ec_at(b, g) + 16 * ii, r);
+                }
+            }
         }
         __syncthreads();
         const bool kept = hasG && lev > l;
@@ -788,6 +818,14 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
             for (int c = 0; c < NC; ++c) a[c] = e[c];
             a[NC] = e[3 * NC];
             chol_solve<NP, NC, NC + 1>(a, i, bad, last);
+            if constexpr (REF) {
+                if (last && rowi) {
+                    float r[16];
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) r[c] = c < NC ? a[c] : 0.0f;
+                    st4<16>(p.dws, ec_at(b, 0) + 16 * ii, r);
+                }
+            }
             float dg = 1.0f;
 #pragma unroll
             for (int c = 0; c < NC; ++c) dg = c == i ? a[c] : dg;
@@ -802,20 +840,22 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     // From here on, addresses and lane indices come from fresh copies of the
     // solve index and the thread index: what is formed from them above need not
     // stay live (or be spilled) until the back substitution and the recovery.
-    const int bl = late(b);
-    {
+    int bl = late(b);
+    auto refresh = [&]() {
+        bl = late(b);
         const int tx = late_lane((int)threadIdx.x);
         i = tx % NP;
         g = tx / NP;
-    }
-    rowi = i < NC;
-    ii = rowi ? i : 0;
-    hasG = g < M;
-    jo = 2 * g + 1;
-    hasO = hasG && jo < N;
-    me = hasG ? cr_group_even(g, M) : 0;
-    ke = 2 * me;
-    lev = me == 0 ? levels : 1 + __builtin_ctz(me);
+        rowi = i < NC;
+        ii = rowi ? i : 0;
+        hasG = g < M;
+        jo = 2 * g + 1;
+        hasO = hasG && jo < N;
+        me = hasG ? cr_group_even(g, M) : 0;
+        ke = 2 * me;
+        lev = me == 0 ? levels : 1 + __builtin_ctz(me);
+    };
+    refresh();
 
     // back substitution, levels in reverse: lambda_j = C_j'^-1 (w3 - W1 lambda_{j-s} - W2 lambda_{j+s})
     auto back = [&](bool act, int k, int s, const float* ct, const float* w1, const float* w2, float w3) {
@@ -833,25 +873,30 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         nonfinite |= act && rowi && !__builtin_isfinite(lam);
         if (act && rowi) sm.lam[k][i] = lam;
     };
-    for (int l = levels - 1; l >= 1; --l) {
-        const bool act = hasG && lev == l;
-        if (__builtin_amdgcn_ballot_w64(act) != 0) back(act, ke, 1 << l, e, e + NC, e + 2 * NC, e[3 * NC]);
-        __syncthreads();
-    }
-    if (levels >= 1) {
-        if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
-            float w1[NC], w2[NC], oc[16];
-            const size_t ocl = VIRT ? nw.oc(bl, hasO ? g : 0, ii) : (((size_t)bl * M + (hasO ? g : 0)) * NC + ii) * 16;
-            ld4<16>(p.dws, ocl, hasO && rowi, oc);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                w1[c] = sm.os[hasO ? g : 0][ii][c];
-                w2[c] = sm.os[hasO ? g : 0][ii][NC + c];
-            }
-            back(hasO, jo, 1, oc, w1, w2, sm.os[hasO ? g : 0][ii][2 * NC]);
+    // every level's back substitution (the w3 of the even knots in e, of the odd knots in their LDS rows)
+    auto back_sweep = [&]() {
+        for (int l = levels - 1; l >= 1; --l) {
+            const bool act = hasG && lev == l;
+            if (__builtin_amdgcn_ballot_w64(act) != 0) back(act, ke, 1 << l, e, e + NC, e + 2 * NC, e[3 * NC]);
+            __syncthreads();
         }
-        __syncthreads();
-    }
+        if (levels >= 1) {
+            if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
+                float w1[NC], w2[NC], oc[16];
+                const size_t ocl =
+                    VIRT ? nw.oc(bl, hasO ? g : 0, ii) : (((size_t)bl * M + (hasO ? g : 0)) * NC + ii) * 16;
+                ld4<16>(p.dws, ocl, hasO && rowi, oc);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    w1[c] = sm.os[hasO ? g : 0][ii][c];
+                    w2[c] = sm.os[hasO ? g : 0][ii][NC + c];
+                }
+                back(hasO, jo, 1, oc, w1, w2, sm.os[hasO ? g : 0][ii][2 * NC]);
+            }
+            __syncthreads();
+        }
+    };
+    back_sweep();
 
     if constexpr (VIRT) {
         // lambda of the boundary knots, at their real positions
@@ -861,18 +906,282 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
             const int v = w == 0 ? ke : jo;
             if (ok && rowi) p.lambda[ix.vn(bl, nd_real(v, p.N), i)] = sm.lam[v][i];
         }
-    }
-    // recovery of this group's knots, and lambda to memory (both knots' loads issued together)
+    } else if constexpr (!REF) {
+        // recovery of this group's knots, and lambda to memory (both knots' loads issued together)
 #pragma unroll
-    for (int w = 0; w < (VIRT ? 0 : 2); ++w) {
-        const bool ok = w == 0 ? hasG : hasO;
-        if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
-        const int kk = ok ? (w == 0 ? ke : jo) : 0;
-        const bool rowv = ok && rowi;
-        const float lam = rowv ? sm.lam[kk][ii] : 0.0f;
-        const float lamn = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
-        if (rowv) p.lambda[ix.vn(bl, kk, i)] = lam;
-        recover_knot<SH>(p, bl, kk, i, ok, lam, lamn);
+        for (int w = 0; w < 2; ++w) {
+            const bool ok = w == 0 ? hasG : hasO;
+            if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+            const int kk = ok ? (w == 0 ? ke : jo) : 0;
+            const bool rowv = ok && rowi;
+            const float lam = rowv ? sm.lam[kk][ii] : 0.0f;
+            const float lamn = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
+            if (rowv) p.lambda[ix.vn(bl, kk, i)] = lam;
+            recover_knot<SH>(p, bl, kk, i, ok, lam, lamn);
+        }
+    } else {
+        // ---- per knot: the first pass's dz (to memory, where the sums below add to
+        // it, and to LDS), then the KKT residual (kkt_rows' q', r', e', x0', here
+        // with the rows the recovery read kept for it) and the pieces of the
+        // correction's gamma' as the formation forms gamma: h = Q~^-1 q',
+        // t = A h + B R^-1 r'; e' less its dx_{k+1} term (in double) and t go to
+        // LDS for knot k + 1.  q' and r' wait in the workspace, after the C' rows,
+        // for the correction's recovery (this solve's rows from qpw and rpw on).
+        refresh();
+        float* const qpw = p.dws + 2 * ec0 + (size_t)bl * N * NC;
+        float* const rpw = p.dws + 2 * ec0 + (size_t)p.B * N * NC + (size_t)bl * N * MC;
+        float hh[2], gp[2];
+        float x0p = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            mem_order();  // one knot's rows at a time
+            const bool ok = w == 0 ? hasG : hasO;
+            hh[w] = 0.0f;
+            if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+            const int kk = ok ? (w == 0 ? ke : jo) : 0;
+            // this knot's addresses from a fresh copy of the lane index (not kept for both knots)
+            const int i = late_lane((int)threadIdx.x) % NP;
+            const bool rowi = i < NC;
+            const int ii = rowi ? i : 0;
+            const bool rowv = ok && rowi, dyn = ok && kk < N - 1, urow = dyn && i < MC;
+            const float lam = rowv ? sm.lam[kk][ii] : 0.0f;
+            const float lamn = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
+            RecRows<SH> r;
+            rec_load<SH>(p, bl, kk, i, ok, r);
+            float dx, du;
+            {
+                float sup[NC];
+                ld_row<NC>(p.S, ix.blk(bl, kk, 2, i), rowv, sup);
+                float h = 0.0f;
+                dotb<NP, NC>(h, Bc<NP>(r.qv), r.qi);
+                recover<SH>(i, rowv, urow, lam, lamn, r.qi, sup, h, r.bc, r.rv, r.ri, dx, du);
+            }
+            float* const lamb = p.lambda + (size_t)bl * N * NC;  // this solve's lambda and dz
+            float* const dzb = p.dz + ix.dx(bl, 0, 0);
+            if (rowv) {
+                sm.dx[kk][i] = dx;
+                lamb[(unsigned)(kk * NC + i)] = lam;
+                dzb[(unsigned)(kk * (NC + MC) + i)] = dx;
+            }
+            if (urow) {
+                sm.du[kk][i] = du;
+                dzb[(unsigned)(kk * (NC + MC) + NC + i)] = du;
+            }
+            __builtin_amdgcn_wave_barrier();  // the knot's dx and du, whole, for its own lanes
+            seq_after(dx);
+            const float* xv = sm.dx[kk];
+            const float* uv = sm.du[kk];
+            const float* lv = sm.lam[dyn ? kk + 1 : kk];
+            // q'_k and r'_k (the terms of kkt_rows, in its order)
+            double s = 0.0, sr = 0.0;
+            {
+                float qr[NC];
+                ld_row<NC>(p.Q, ix.Q(bl, kk, i), rowv, qr);
+                const double rh = p.rho != nullptr ? (double)p.rho[bl] : 0.0;
+                s = (double)r.qv + rh * (rowv ? xv[ii] : 0.0f) - lam;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) s += (double)qr[c] * xv[c];
+            }
+            seq_after(s);
+            if (dyn) {
+                float ac[NC];
+                ld_row<NC, NC>(p.A, ix.A(bl, kk, 0) + i, rowi, ac);  // column i of A_k
+#pragma unroll
+                for (int c = 0; c < NC; ++c) s += (double)ac[c] * lv[c];
+            }
+            seq_after(s);
+            {
+                float rr[MC];
+                ld_row<MC>(p.R, ix.R(bl, kk, i), urow, rr);
+                sr = (double)r.rv;
+#pragma unroll
+                for (int c = 0; c < MC; ++c) sr += (double)rr[c] * uv[c];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) sr += (double)r.bc[c] * lv[c];  // B_k' lambda_{k+1}
+            }
+            const float qv = rowv ? (float)s : 0.0f, rv = urow ? (float)sr : 0.0f;
+            float h = 0.0f, gr = 0.0f;
+            dotb<NP, NC>(h, Bc<NP>(qv), r.qi);
+            dotb<NP, MC>(gr, Bc<NP>(rv), r.ri);
+            h = rowv ? h : 0.0f;
+            gr = urow ? gr : 0.0f;
+            if (rowv) qpw[(unsigned)(kk * NC + i)] = qv;
+            if (urow) rpw[(unsigned)(kk * MC + i)] = rv;
+            seq_after(h);
+            seq_after(gr);
+            // e'_k without its -dx_{k+1} (double), t_k = A_k h + B_k R_k^-1 r'_k, and x0'
+            {
+                float ar[NC], br[MC];
+                ld_row<NC>(p.A, ix.A(bl, kk, i), dyn && rowi, ar);
+                ld_row<MC>(p.Bu, ix.Bu(bl, kk, i), dyn && rowi, br);
+                const float ev = ld1(p.e, ix.e(bl, kk, i), dyn && rowi);
+                double te = (double)ev;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) te += (double)ar[c] * xv[c];
+#pragma unroll
+                for (int c = 0; c < MC; ++c) te += (double)br[c] * uv[c];
+                float tt = 0.0f;
+                dotb<NP, NC>(tt, Bc<NP>(h), ar);
+                dotb<NP, MC>(tt, Bc<NP>(gr), br);
+                if (dyn && rowi) {
+                    sm.epd[kk][i] = te;
+                    sm.ex[kk][i] = tt;
+                }
+                const float x0v = ld1(p.x0, (size_t)bl * NC + i, rowv && kk == 0);
+                if (rowv && kk == 0) x0p = (float)((double)x0v - dx);
+            }
+            hh[w] = h;
+        }
+        __syncthreads();
+        refresh();
+        // gamma'_0 = x0' + h_0, gamma'_{k+1} = (e'_k - t_k) + h_{k+1}, e'_k = e_k + A dx_k + B du_k - dx_{k+1}
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const bool ok = w == 0 ? hasG : hasO;
+            const int kk = ok ? (w == 0 ? ke : jo) : 0;
+            const bool rowv = ok && rowi;
+            const int km = kk > 0 ? kk - 1 : 0;
+            const float ep = (float)(sm.epd[km][ii] - (double)sm.dx[kk][ii]);
+            const float gx = (rowv && kk > 0) ? ep - sm.ex[km][ii] : x0p;
+            gp[w] = rowv ? gx + hh[w] : 0.0f;
+        }
+        __syncthreads();  // the exchange rows are read before the second sweep reuses their LDS
+
+        // ---- the second sweep: gamma' through the first pass's eliminations.
+        // The kept knots' gamma' less W2m' w3m and W1p' w3p (rows of the
+        // eliminated neighbours k - s and k + s, read by columns).
+        auto gupdate = [&](bool kept, bool hasL, bool hasU, const float* Wm, const float* Wp) {
+            const bool okm = kept && hasL && rowi, okp = kept && hasU && rowi;
+            float s = 0.0f;
+#pragma unroll
+            for (int l = 0; l < NC; ++l) s = fmaf(okm ? Wm[l * YW + NC + ii] : 0.0f, okm ? Wm[l * YW + 2 * NC] : 0.0f, s);
+#pragma unroll
+            for (int l = 0; l < NC; ++l) s = fmaf(okp ? Wp[l * YW + ii] : 0.0f, okp ? Wp[l * YW + 2 * NC] : 0.0f, s);
+            if (kept && rowi) e[3 * NC] -= s;
+        };
+        refresh();
+        e[3 * NC] = hasG ? gp[0] : 0.0f;
+        // the factors back in registers: the even knot's C' rows (the last Schur
+        // complement's for knot 0), and the odd knot's C' by columns (row i of C)
+        float cl[NC];
+        {
+            float ct[16];
+            ld4<16>(p.dws, ec_at(bl, hasG ? g : 0) + 16 * ii, hasG && rowi, ct);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) e[c] = ct[c];
+            ld_row<NC, 16>(p.dws, ((size_t)bl * M + (hasO ? g : 0)) * NC * 16 + ii, hasO && rowi, cl);
+        }
+        // level 0: the odd knots
+        if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
+            float dg = 1.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) dg = c == i ? cl[c] : dg;
+            float w3 = 0.0f;
+            tri_lower_solve<NP, NC>(cl, (hasO && rowi) ? gp[1] : 0.0f,
+                                    __builtin_amdgcn_rcpf((hasO && rowi) ? dg : 1.0f), i, w3);
+            if (hasO && rowi) sm.os[g][i][2 * NC] = w3;
+        }
+        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(hasG) != 0) {
+            const bool hasL = ke > 0, hasU = ke + 1 < N;
+            gupdate(hasG, hasL, hasU, &sm.os[hasL ? me - 1 : 0][0][0], &sm.os[hasU ? me : 0][0][0]);
+        }
+        __syncthreads();
+        // levels 1 .. levels-1: w3' with C by columns, then the W rows to the level's slot
+        for (int l = 1; l < levels; ++l) {
+            const int s = 1 << l;
+            const int first = 1 + cr_mult(M, l);
+            const bool elim = hasG && lev == l;
+            if (__builtin_amdgcn_ballot_w64(elim) != 0) {
+                // C' through the knot's own slot of the level (one wave): row i of C back
+                float* slot = &sm.es[elim ? g - first : 0][0][0];
+                if (elim && rowi)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) slot[i * YW + c] = e[c];
+                __builtin_amdgcn_wave_barrier();
+                float cc[NC];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) cc[c] = (elim && rowi) ? slot[c * YW + ii] : 0.0f;
+                __builtin_amdgcn_wave_barrier();
+                float dg = 1.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) dg = c == i ? e[c] : dg;
+                float w3 = 0.0f;
+                tri_lower_solve<NP, NC>(cc, (elim && rowi) ? e[3 * NC] : 0.0f,
+                                        __builtin_amdgcn_rcpf((elim && rowi) ? dg : 1.0f), i, w3);
+                e[3 * NC] = elim ? w3 : e[3 * NC];
+                if (elim && rowi)
+#pragma unroll
+                    for (int c = 0; c < YW; ++c) slot[i * YW + c] = e[NC + c];
+            }
+            __syncthreads();
+            const bool kept = hasG && lev > l;
+            if (__builtin_amdgcn_ballot_w64(kept) != 0) {
+                const bool hasL = ke > 0, hasU = ke + s < N;
+                const int gm = hasL ? cr_even_group((ke - s) / 2, M) - first : 0;
+                const int gq = hasU ? cr_even_group((ke + s) / 2, M) - first : 0;
+                gupdate(kept, hasL, hasU, &sm.es[gm][0][0], &sm.es[gq][0][0]);
+            }
+            __syncthreads();
+        }
+        // last level: knot 0, with the factor of its last Schur complement
+        {
+            const bool last = g == 0;
+            if (__builtin_amdgcn_ballot_w64(last) != 0) {
+                float* slot = &sm.es[0][0][0];
+                if (last && rowi)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) slot[i * YW + c] = e[c];
+                __builtin_amdgcn_wave_barrier();
+                float cc[NC];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) cc[c] = (last && rowi) ? slot[c * YW + ii] : 0.0f;
+                __builtin_amdgcn_wave_barrier();
+                float dg = 1.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) dg = c == i ? e[c] : dg;
+                const float dinv = __builtin_amdgcn_rcpf((last && rowi) ? dg : 1.0f);
+                float w3 = 0.0f, lam = 0.0f;
+                tri_lower_solve<NP, NC>(cc, (last && rowi) ? e[3 * NC] : 0.0f, dinv, i, w3);
+                tri_upper_solve<NP, NC>(e, w3, dinv, i, lam);
+                nonfinite |= last && rowi && !__builtin_isfinite(lam);
+                if (last && rowi) sm.lam[0][i] = lam;
+            }
+            __syncthreads();
+        }
+        refresh();
+        back_sweep();
+
+        // ---- the correction's dz (its q' and r', h = Q~^-1 q' as above), and the sums
+        // (both knots' loads issued together)
+        refresh();
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const bool ok = w == 0 ? hasG : hasO;
+            if (__builtin_amdgcn_ballot_w64(ok) == 0) continue;
+            const int kk = ok ? (w == 0 ? ke : jo) : 0;
+            const bool rowv = ok && rowi, urow = ok && kk < N - 1 && i < MC;
+            const float mu = rowv ? sm.lam[kk][ii] : 0.0f;
+            const float mun = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
+            float qi[NC], ri[MC], bc[NC], sup[NC];
+            ld_row<NC>(p.Qinv, ix.Q(bl, kk, i), rowv, qi);
+            ld_row<MC>(p.Rinv, ix.R(bl, kk, i), urow, ri);
+            ld_row<NC, MC>(p.Bu, ix.Bu(bl, kk, 0) + i, urow, bc);  // column i of B_k
+            ld_row<NC>(p.S, ix.blk(bl, kk, 2, i), rowv, sup);
+            const float qv = ld1(qpw, (unsigned)(kk * NC + i), rowv);
+            const float rv = ld1(rpw, (unsigned)(kk * MC + i), urow);
+            float h = 0.0f;  // (Q~_k^-1 q'_k)_i, as above
+            dotb<NP, NC>(h, Bc<NP>(qv), qi);
+            float ddx, ddu;
+            recover<SH>(i, rowv, urow, mu, mun, qi, sup, h, bc, rv, ri, ddx, ddu);
+            float* const lamb = p.lambda + (size_t)bl * N * NC;  // this solve's lambda and dz
+            float* const dzb = p.dz + ix.dx(bl, 0, 0);
+            if (rowv) {
+                lamb[(unsigned)(kk * NC + i)] += mu;
+                dzb[(unsigned)(kk * (NC + MC) + i)] += ddx;
+            }
+            if (urow) dzb[(unsigned)(kk * (NC + MC) + NC + i)] += ddu;
+        }
     }
 
     const int fl = (bad ? GATO_F_S_NOT_SPD : 0) | (nonfinite ? GATO_F_NONFINITE : 0);

@@ -3,6 +3,7 @@
 //
 // Kernels (one workgroup per solve unless noted):
 //   k_cr_res     every knot of the solve held in registers and LDS (n <= 16, N <= 128).
+//   k_cr_res_ref the same followed by a pass of KKT iterative refinement on its factors.
 //   k_nd_reduce, k_cr_res<VIRT>, k_nd_back
 //                nested dissection for n <= 16, N > 128: chunk interiors eliminated
 //                in order, the chunks' boundary system reduced cyclically, then
@@ -46,6 +47,14 @@ template <class SH>
 __global__ __launch_bounds__(1024) void k_cr_res(Params p)
 {
     cr_resident<SH>(p, blockIdx.x);
+}
+
+// The same, followed inside the kernel by one pass of KKT iterative refinement
+// that reuses the solve's factors (gato_sqp_step's default on these horizons).
+template <class SH>
+__global__ __launch_bounds__(1024) void k_cr_res_ref(Params p)
+{
+    cr_resident<SH, false, true>(p, blockIdx.x);
 }
 
 // Nested dissection (n <= 16, N > 128): the chunk kernels take ND_SPLIT
@@ -98,6 +107,20 @@ static hipError_t cr_launch_shape(const Params& p, hipStream_t st)
     return hipGetLastError();
 }
 
+template <class SH>
+static hipError_t cr_launch_refined_shape(const Params& p, hipStream_t st)
+{
+    if constexpr (SH::NP == 16) {
+        if (cr_resident<SH>(p.N, p.cr_stream != 0)) {
+            const int groups = (p.N + 1) / 2;
+            hipLaunchKernelGGL((k_cr_res_ref<SH>), dim3(p.B), dim3(((groups + SH::KPW - 1) / SH::KPW) * 64), 0, st,
+                               p);
+            return hipGetLastError();
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
 template <class F>
 static int with_cr_shape(int n, int m, F&& f)
 {
@@ -118,6 +141,21 @@ hipError_t cr_launch(const Params& p, hipStream_t st)
     return e;
 }
 
+bool cr_refines_inside(const gato_dims_t* d, bool stream)
+{
+    return d->n <= 16 && d->N <= 128 && !stream;
+}
+
+hipError_t cr_launch_refined(const Params& p, hipStream_t st)
+{
+    hipError_t e = hipErrorInvalidValue;
+    with_cr_shape(p.n, p.m, [&](auto sh) {
+        e = cr_launch_refined_shape<decltype(sh)>(p, st);
+        return 0;
+    });
+    return e;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Cyclic reduction: one row [L | U | gamma | D] per knot row, padded to float4s.
@@ -125,14 +163,16 @@ static size_t cr_row_floats(int n) { return (size_t)(3 * n + 1 + 3) / 4 * 4; }
 
 size_t cr_ws_bytes(const gato_dims_t* d)
 {
-    // the largest of the three layouts: the streaming kernel's rows (B N n W), the
-    // resident kernel's parked rows (B ceil(N/2) n 16, never more than the first)
-    // and the nested dissection's (the interior knots' factors, the boundary
-    // system's rows and its parked rows)
+    // the largest of the layouts: the streaming kernel's rows (B N n W), the
+    // resident kernel's parked rows (B ceil(N/2) n 16) with, for its refinement
+    // pass, the even knots' as many and q' and r' (B N (n + m)), and the nested
+    // dissection's (the interior
+    // knots' factors, the boundary system's rows and its parked rows)
     const size_t B = d->B, N = d->N, n = d->n, W = cr_row_floats(d->n);
     const size_t stream = B * N * n * W;
     const size_t nd = B * (N * nd_fac_floats(d->n) + 2 * ND_CHUNKS * n * W) + B * ND_CHUNKS * n * 16;
-    return align256((stream > nd ? stream : nd) * sizeof(float));
+    const size_t ref = 2 * B * ((N + 1) / 2) * n * 16 + B * N * (n + d->m);
+    return align256(std::max({stream, nd, ref}) * sizeof(float));
 }
 
 bool cr_reads_lower(const gato_dims_t* d, bool stream)

@@ -33,6 +33,16 @@ hipError_t cr_launch(const Params& p, hipStream_t st);
 // dissection read the upper blocks only).
 bool cr_reads_lower(const gato_dims_t* d, bool stream);
 
+// Whether the cyclic reduction for these dimensions runs the refinement pass
+// inside its kernel (cr_launch_refined): the register-resident kernel, n <= 16
+// and N <= 128, unless `stream` asks for the streaming one.
+bool cr_refines_inside(const gato_dims_t* d, bool stream);
+
+// The register-resident cyclic reduction followed, in the same kernel, by one
+// pass of KKT iterative refinement (the problem data, S, gamma, Q~^-1 and R^-1
+// of p; lambda and dz are the refined ones); only where cr_refines_inside.
+hipError_t cr_launch_refined(const Params& p, hipStream_t st);
+
 // Whether gato_sqp_step takes cyclic reduction rather than block Thomas
 // beyond the fused horizons, by the measured cost model.
 bool cr_preferred(const gato_dims_t* d);

@@ -56,6 +56,16 @@ __device__ __forceinline__ int late_lane(int x)
     return x;
 }
 
+// No memory access moves across this point: the loads after it are issued
+// after what comes before has used its own, so the rows of two phases are not
+// live at once.
+__device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }
+
+// x is formed before this point and no memory access moves across it: the
+// loads x needs are consumed here, before any later load is issued.
+__device__ __forceinline__ void seq_after(float x) { asm volatile("" ::"v"(x) : "memory"); }
+__device__ __forceinline__ void seq_after(double x) { asm volatile("" ::"v"(x) : "memory"); }
+
 __device__ __forceinline__ float uniform(float x)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -843,6 +853,72 @@ __device__ __forceinline__ void recover(int i, bool rowv, bool urow, float lam, 
     dotb<NP, MC>(y, Bc<NP>(u), ri);
     dx = rowv ? x - h : 0.0f;
     du = urow ? y : 0.0f;
+}
+
+// ------------------------------------------------------------------ refinement residual
+
+// Lane i's rows of the residual of the KKT system the Schur method solves
+// (G dz - C' lambda = -g, C dz = c; GATO paper Sec. II, eq. 2) at knot k, the
+// right-hand side of one pass of iterative refinement:
+//   q'_k = q_k + Q~_k dx_k - lambda_k + A_k' lambda_{k+1}
+//   r'_k = r_k + R_k du_k + B_k' lambda_{k+1}
+//   e'_k = e_k + A_k dx_k + B_k du_k - dx_{k+1}
+//   x0'  = x0 - dx_0                                     (k = 0)
+// accumulated in double from the fp32 problem data and rounded once.  dx, du,
+// ln: dx_k, du_k and lambda_{k+1} whole (any memory every lane can read);
+// lam: (lambda_k)_i; dxn: (dx_{k+1})_i.  Rows and knots outside the problem
+// give zeros.  SEQ: one row of the problem data in registers at a time (each
+// product is summed before the next row is requested), for callers that keep
+// many registers live across this.
+template <class SH, bool SEQ = false>
+__device__ __forceinline__ void kkt_rows(const Params& p, int b, int k, int i, bool kv, const float* dx,
+                                         const float* du, const float* ln, float lam, float dxn, float& qv,
+                                         float& rv, float& ev, float& x0v)
+{
+    auto step = [](double x) {
+        if constexpr (SEQ) seq_after(x);
+    };
+    constexpr int n = SH::NC, m = SH::MC;
+    const Ix<SH> ix{p.N};
+    const bool dyn = kv && k < p.N - 1;
+    qv = rv = ev = x0v = 0.0f;
+    if (kv && i < n) {
+        const double rh = p.rho != nullptr ? (double)p.rho[b] : 0.0;
+        double s = (double)p.q[ix.vn(b, k, i)] + rh * dx[i] - lam;
+        const float* Qr = p.Q + ix.Q(b, k, i);
+#pragma unroll
+        for (int c = 0; c < n; ++c) s += (double)Qr[c] * dx[c];
+        step(s);
+        if (dyn) {
+            const float* Ac = p.A + ix.A(b, k, 0) + i;  // column i of A_k
+#pragma unroll
+            for (int c = 0; c < n; ++c) s += (double)Ac[c * n] * ln[c];
+            step(s);
+            const float* Ar = p.A + ix.A(b, k, i);
+            const float* Br = p.Bu + ix.Bu(b, k, i);
+            double t = (double)p.e[ix.e(b, k, i)] - dxn;
+#pragma unroll
+            for (int c = 0; c < n; ++c) t += (double)Ar[c] * dx[c];
+            step(t);
+#pragma unroll
+            for (int c = 0; c < m; ++c) t += (double)Br[c] * du[c];
+            step(t);
+            ev = (float)t;
+        }
+        qv = (float)s;
+        if (k == 0) x0v = (float)((double)p.x0[(size_t)b * n + i] - dx[i]);
+    }
+    if (dyn && i < m) {
+        double s = (double)p.r[ix.vm(b, k, i)];
+        const float* Rr = p.R + ix.R(b, k, i);
+#pragma unroll
+        for (int c = 0; c < m; ++c) s += (double)Rr[c] * du[c];
+        step(s);
+        const float* Bc_ = p.Bu + ix.Bu(b, k, 0) + i;  // column i of B_k
+#pragma unroll
+        for (int c = 0; c < n; ++c) s += (double)Bc_[c * m] * ln[c];
+        rv = (float)s;
+    }
 }
 
 // ------------------------------------------------------------------ stage 2, direct

@@ -226,6 +226,53 @@ def test_sqp_step_refinement_keeps_a_well_conditioned_step(cid, B, N):
     assert rel_rows(g["dz"], dz).max() <= 5e-6
 
 
+@pytest.mark.parametrize("nm,cid,N", [((14, 7), 3, 65), ((14, 7), 3, 100), ((14, 7), 3, 127), ((14, 7), 3, 128),
+                                      ((12, 6), 2, 97), ((4, 2), 1, 128), ((1, 1), 1, 77)])
+def test_sqp_step_refinement_inside_the_resident_reduction(nm, cid, N):
+    """With n <= 16 and 65 <= N <= 128 gato_sqp_step's cyclic reduction runs the refinement
+    pass inside its kernel, on the factors of its own first pass (the correction's
+    right-hand side through the same eliminations, then a second back substitution).
+    On every shape that kernel has, with odd and even horizons, the refined step is the
+    oracle's exact step within 5e-6 in dz and 1e-5 in every merit (the workspace is NaN
+    before the call: a row the pass reads without writing would show)."""
+    from gpu_util import gpu_sqp
+
+    B = 3
+    _ident("sqp refinement in the resident kernel", nm, cid, N, B)
+    bt = synth.make_batch(cid, B, n=nm[0], m=nm[1], N=N)
+    ins = synth.inputs(bt)
+    g = gpu_sqp(bt, 1e-6, 200)
+    form = oracle.form_schur(*ins)
+    _, dz = _exact(bt, form)
+    merit = oracle.merit_eval(*ins, dz, synth.ALPHAS, 1.0)["merit"]
+    assert ((g["flags"] & ~ops.F_LS_FAILED) == 0).all()
+    assert (g["iters"] == 0).all()
+    assert rel_rows(g["dz"], dz).max() <= 5e-6
+    assert (np.abs(g["merit"] - merit) / np.abs(merit)).max() <= 1e-5
+
+
+def test_refinement_inside_the_kernel_agrees_with_the_separate_pass():
+    """On the ill-conditioned long-horizon workload the register-resident reduction
+    with its in-kernel refinement (solver CR) and the streaming reduction followed by
+    the refinement pass's own kernels (solver CR_STREAM) give the same refined step:
+    each within 2e-5 of the oracle's exact step in dz, and within 2e-5 of each other,
+    where the two unrefined solves differ by up to ~1e-3."""
+    from gpu_util import gpu_sqp
+
+    B = 16
+    _ident("refinement in the kernel vs the separate pass, workload 5", B)
+    bt = synth.make_batch(5, B)
+    form = oracle.form_schur(*synth.inputs(bt))
+    _, dz = _exact(bt, form)
+    a = gpu_sqp(bt, 1e-6, 2000, solver=ops.SOLVER_CR)
+    s = gpu_sqp(bt, 1e-6, 2000, solver=ops.SOLVER_CR_STREAM)
+    for r in (a, s):
+        assert ((r["flags"] & ~ops.F_LS_FAILED) == 0).all()
+        assert rel_rows(r["dz"], dz).max() <= 2e-5
+    assert rel_rows(a["dz"], s["dz"]).max() <= 2e-5
+    assert np.array_equal(a["best"], s["best"])
+
+
 @pytest.mark.parametrize("N", [9, 128, 300])
 def test_cr_reads_no_lower_block(N):
     """For n <= 16 the solve reads S's diagonal and upper blocks only (the lower ones
