@@ -289,13 +289,15 @@ int gato_merit_eval_shape(const gato_dims_t* dims, const float* Q, const float* 
  *    iterative refinement of the KKT system (G dz - C' lambda = -g, C dz = c;
  *    the paper's eq. 2): its residual, accumulated in double from the problem
  *    data, is the right-hand side of a correction system with the same S,
- *    Q~^-1 and R^-1, whose gamma is formed from it and which the same direct
- *    solve solves; its lambda and dz are added to the first pass's.  The fp32
+ *    Q~^-1 and R^-1, whose gamma is formed from it and which the same
+ *    factorisation of S solves; its lambda and dz are added to the first
+ *    pass's.  The register-resident cyclic reduction (n <= 16, N <= 128) runs
+ *    the pass inside its kernel on the factors of its first pass; the other
+ *    direct solves run it as separate kernels and a second solve.  The fp32
  *    stages alone leave dz with a relative error of up to about
  *    cond(S) * 1e-7 (~1e-3 at cond(S) ~ 1e6, where rounding S to fp32 already
- *    moves dz by up to 6e-4); the pass brings it to ~1e-5 for one more solve
- *    and two light kernels.  The merit is evaluated on the refined dz;
- *    linsys_us includes the pass.
+ *    moves dz by up to 6e-4); the pass brings it to ~1e-5.  The merit is
+ *    evaluated on the refined dz; linsys_us includes the pass.
  *    lambda's input is not read, iters and relres are written as 0, and eps
  *    and max_iters are checked but unused.  S (no Phi^-1: the
  *    direct solves do not use it), gamma, Qinv, Rinv, the solve's rows, the
