@@ -406,8 +406,31 @@ __global__ __launch_bounds__(SH::THREADS) void k_pcg_stream(Params p)
         gam[c] = ld1(p.gamma, ix.vn(b, k, i), rowv);
         lam[c] = ld1(p.lambda, ix.vn(b, k, i), rowv);
     }
-    const GlobalMat<SH> M{p.S, p.Pinv, ix, b, i};
-    pcg_and_recover<SH, C>(p, M, L, gam, lam);
+    if constexpr (C == 2 && NP == 16) {
+        // two knots per lane group: S's diagonal rows in registers and the D_k^-1 in
+        // LDS (HybMat), so only S's off-diagonal blocks stream at every iteration
+        constexpr int DS = NC | 1;  // odd row stride: a lane group's rows fall in distinct banks
+        __shared__ float dinv[2 * SL][NC][DS];
+        float sd[C][NC];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int k = c * SL + s;
+            const bool rowv = k < p.N && i < NC;
+            float t[NC];
+            ld_row<NC>(p.S, ix.blk(b, k, 1, i), rowv, sd[c]);
+            ld_row<NC>(p.Pinv, ix.blk(b, k, 1, i), rowv, t);
+            if (i < NC)
+#pragma unroll
+                for (int col = 0; col < NC; ++col) dinv[k][i][col] = t[col];
+        }
+        __syncthreads();
+        const HybMat<SH, C, DS> M{p.S, ix, b, i, sd, dinv, L.xy};
+        pcg_and_recover<SH, C>(p, M, L, gam, lam);
+    } else {
+        // phased for 16-lane groups (less traffic); 32-lane ones measure faster without the extra barrier
+        const GlobalMat<SH, NP == 16> M{p.S, p.Pinv, ix, b, i, L.xy};
+        pcg_and_recover<SH, C>(p, M, L, gam, lam);
+    }
 }
 
 // ------------------------------------------------------------------ stage 2, direct

@@ -411,6 +411,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 template <class SH>
 struct RegMat {
     static constexpr bool kAssembled = true;  // applies the assembled Phi^-1 blocks
+    static constexpr bool kPhased = false;    // Phi^-1 r in one call (see HybMat)
     const Rows<SH>* rw;
     __device__ __forceinline__ float S(int, float xp, float x, float xn) const
     {
@@ -439,13 +440,27 @@ struct RegMat {
 
 // Block-tridiagonal rows read from global memory at every product (for
 // horizons longer than one workgroup holds); layout [B][N][3][n][n].
-template <class SH>
+// Phi^-1 r in the stair preconditioner's factored form D^-1 (J S J) D^-1 r,
+// D^-1 = blkdiag(Phi^-1_{k,k}) and J = blkdiag((-1)^k I), which equals the
+// assembled blocks: y_j = D_j^-1 r_j for j = k-1, k, k+1, w_k = (J S J y)_k,
+// then z_k = (D_k^-1)' w_k (column i).  r'z = y' J S J y then stays positive
+// while S is SPD in fp32, even where the assembled fp32 Phi^-1 is not (its
+// condition can exceed 1e8 on ill-conditioned long horizons, and the D_k^-1
+// carry the rounding of their Gauss-Jordan inversion).
+// PH (phased): y in two phases around one barrier, P1 forming y_k = D_k^-1 r_k
+// (row i) and leaving it in the exchange rows xy, P2 taking the neighbours'
+// y from there; D^-1 is then read twice per application instead of four
+// times.  Without it (P) each lane forms y_{k-1} and y_{k+1} too, from the
+// copies of r's neighbours the loop keeps; the bits are the same either way.
+template <class SH, bool PH = true>
 struct GlobalMat {
     static constexpr bool kAssembled = false;  // applies Phi^-1 in factored form
+    static constexpr bool kPhased = PH;
     const float* Sm;
     const float* Pm;
     Ix<SH> ix;
     int b, i;
+    float (*xy)[SH::NP];
     __device__ __forceinline__ float mv(const float* X, int k, float xp, float x, float xn) const
     {
         constexpr int NP = SH::NP, NC = SH::NC;
@@ -460,12 +475,7 @@ struct GlobalMat {
         return acc;
     }
     __device__ __forceinline__ float S(int k, float xp, float x, float xn) const { return mv(Sm, k, xp, x, xn); }
-    // Phi^-1 r in the stair preconditioner's factored form D^-1 (J S J) D^-1 r, D^-1 = blkdiag(Phi^-1_{k,k})
-    // and J = blkdiag((-1)^k I), which equals the assembled blocks: y_j = D_j^-1 r_j for j = k-1, k, k+1
-    // (row i of each inverse, with r's neighbours as the loop keeps them), w_k = (J S J y)_k, then
-    // z_k = (D_k^-1)' w_k (column i).  r'z = y' J S J y then stays positive while S is SPD in fp32, even
-    // where the assembled fp32 Phi^-1 is not (its condition can exceed 1e8 on ill-conditioned
-    // long horizons, and the D_k^-1 carry the rounding of their Gauss-Jordan inversion).
+    __device__ __forceinline__ float S(int k, float xp, float x, float xn, int) const { return mv(Sm, k, xp, x, xn); }
     __device__ __forceinline__ float P(int k, float rp, float r, float rn) const
     {
         constexpr int NP = SH::NP, NC = SH::NC;
@@ -478,6 +488,26 @@ struct GlobalMat {
         ld_row<NC>(Pm, ix.blk(b, k + 1 < ix.N ? k + 1 : k, 1, i), v && k + 1 < ix.N, t);
         dotb<NP, NC>(yn, Bc<NP>(rn), t);
         const float w = mv(Sm, k, -yp, y, -yn);
+        ld_row<NC, NC>(Pm, ix.blk(b, k, 1, 0) + i, v, t);  // column i of D_k^-1
+        dotb<NP, NC>(z, Bc<NP>(w), t);
+        return z;
+    }
+    __device__ __forceinline__ float P1(int k, float r) const
+    {
+        constexpr int NP = SH::NP, NC = SH::NC;
+        const bool v = k < ix.N && i < NC;
+        float t[NC], y = 0.0f;
+        ld_row<NC>(Pm, ix.blk(b, k, 1, i), v, t);
+        dotb<NP, NC>(y, Bc<NP>(r), t);
+        xy[k + 1][i] = y;
+        return y;
+    }
+    __device__ __forceinline__ float P2(int k, float y, int) const
+    {
+        constexpr int NP = SH::NP, NC = SH::NC;
+        const bool v = k < ix.N && i < NC;
+        const float w = mv(Sm, k, -xy[k][i], y, -xy[k + 2][i]);
+        float t[NC], z = 0.0f;
         ld_row<NC, NC>(Pm, ix.blk(b, k, 1, 0) + i, v, t);  // column i of D_k^-1
         dotb<NP, NC>(z, Bc<NP>(w), t);
         return z;
@@ -515,6 +545,74 @@ struct RegMatF : RegMat<SH> {
         return z;
     }
 };
+
+// Rows for horizons of two knots per lane group (n <= 16), between RegMat and
+// GlobalMat: S's diagonal blocks in registers (sd[c]: row i of S_{k,k} of the
+// group's knot in chunk c), its off-diagonal blocks read from memory at every
+// product, and the diagonal blocks D_k^-1 of the factored Phi^-1 in LDS
+// (dinv[k][row][col]), read by rows for y = D^-1 r and by columns for
+// z = D^-T w, in GlobalMat's two phases.  The products and their order are
+// GlobalMat's, so the results are its bits, with the diagonal blocks read once
+// instead of at every iteration.
+template <class SH, int C, int DS>
+struct HybMat {
+    static constexpr bool kAssembled = false;
+    static constexpr bool kPhased = true;
+    const float* Sm;
+    Ix<SH> ix;
+    int b, i;
+    const float (*sd)[SH::NC];
+    const float (*dinv)[SH::NC][DS];
+    float (*xy)[SH::NP];
+    __device__ __forceinline__ float S(int k, float xp, float x, float xn, int c) const
+    {
+        constexpr int NP = SH::NP, NC = SH::NC;
+        const bool v = k < ix.N && i < NC;
+        float acc = 0.0f, t[NC];
+        ld_row<NC>(Sm, ix.blk(b, k, 0, i), v, t);
+        dotb<NP, NC>(acc, Bc<NP>(xp), t);
+        dotb<NP, NC>(acc, Bc<NP>(x), sd[c]);
+        ld_row<NC>(Sm, ix.blk(b, k, 2, i), v, t);
+        dotb<NP, NC>(acc, Bc<NP>(xn), t);
+        return acc;
+    }
+    // y_k = D_k^-1 r_k (row i), left in the exchange rows for the neighbours
+    __device__ __forceinline__ float P1(int k, float r) const
+    {
+        constexpr int NP = SH::NP, NC = SH::NC;
+        const bool v = k < ix.N && i < NC;
+        float y = 0.0f;
+        dotb<NP, NC>(y, Bc<NP>(r), dinv[k][v ? i : 0]);
+        y = v ? y : 0.0f;
+        xy[k + 1][i] = y;
+        return y;
+    }
+    // after the barrier: w_k = (J S J y)_k, then z_k = (D_k^-1)' w_k (column i)
+    __device__ __forceinline__ float P2(int k, float y, int c) const
+    {
+        constexpr int NP = SH::NP, NC = SH::NC;
+        const bool v = k < ix.N && i < NC;
+        const float w = S(k, -xy[k][i], y, -xy[k + 2][i], c);
+        const int ii = i < NC ? i : 0;
+        float col[NC], z = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NC; ++r) col[r] = v ? dinv[k][r][ii] : 0.0f;
+        dotb<NP, NC>(z, Bc<NP>(w), col);
+        return z;
+    }
+    __device__ __forceinline__ void sup(int k, float (&out)[SH::NC]) const
+    {
+        ld_row<SH::NC>(Sm, ix.blk(b, k, 2, i), k < ix.N && i < SH::NC, out);
+    }
+};
+
+// S p for the knot k of chunk c, for matrices that keep rows per chunk.
+template <class MAT>
+__device__ __forceinline__ float mat_S(const MAT& M, int c, int k, float xp, float x, float xn)
+{
+    if constexpr (MAT::kPhased) return M.S(k, xp, x, xn, c);
+    else return M.S(k, xp, x, xn);
+}
 
 // Row i of (X + X')/2 for the row-per-lane block X of a lane group (lane i: row
 // i in x), through the group's exchange row ex (NP floats, within one wave):
@@ -649,7 +747,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
     float r[C], rp[C], rn[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        r[c] = gam[c] - M.S(row(c) - 1, lp[c], lam[c], ln[c]);
+        r[c] = gam[c] - mat_S(M, c, row(c) - 1, lp[c], lam[c], ln[c]);
         L.xz[row(c)][i] = r[c];
     }
     __syncthreads();
@@ -670,9 +768,17 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
     float rr, eta;
     {
         float z[C];
+        if constexpr (MAT::kPhased) {
+            float y[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) y[c] = M.P1(row(c) - 1, r[c]);
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < C; ++c) z[c] = M.P2(row(c) - 1, y[c], c);
+        }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
+            if constexpr (!MAT::kPhased) z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
             const float a = groupsum<NP>(r[c] * r[c]);
             const float bb = groupsum<NP>(r[c] * z[c]);
             if (lead) {
@@ -707,7 +813,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             float v[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                v[c] = M.S(row(c) - 1, pp[c], pv[c], pn[c]);
+                v[c] = mat_S(M, c, row(c) - 1, pp[c], pv[c], pn[c]);
                 const float t = groupsum<NP>(pv[c] * v[c]);
                 if (lead) L.red0[row(c) - 1] = t;
                 L.xv[row(c)][i] = v[c];
@@ -741,9 +847,17 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             iters += stop ? 0 : 1;
             // z = Phi^-1 r ; r'r, r'z ; z to neighbours
             float z[C];
+            if constexpr (MAT::kPhased) {
+                float y[C];
+#pragma unroll
+                for (int c = 0; c < C; ++c) y[c] = M.P1(row(c) - 1, r[c]);
+                __syncthreads();
+#pragma unroll
+                for (int c = 0; c < C; ++c) z[c] = M.P2(row(c) - 1, y[c], c);
+            }
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
+                if constexpr (!MAT::kPhased) z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
                 const float ta = groupsum<NP>(r[c] * r[c]);
                 const float tb = groupsum<NP>(r[c] * z[c]);
                 if (lead) {
