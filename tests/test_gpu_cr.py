@@ -251,6 +251,27 @@ def test_sqp_step_refinement_inside_the_resident_reduction(nm, cid, N):
     assert (np.abs(g["merit"] - merit) / np.abs(merit)).max() <= 1e-5
 
 
+def test_sqp_step_refinement_inside_the_resident_reduction_with_damping():
+    """The in-kernel refinement pass with a per-solve damping rho (Q~ = Q + rho I in the
+    residual as in the formation) and a lambda input that a direct solve does not read:
+    the refined step is the oracle's exact step of the damped system within 5e-6, its
+    merits (undamped Q) within 1e-5."""
+    from gpu_util import gpu_sqp
+
+    B, N = 4, 100
+    _ident("sqp refinement in the resident kernel, damped", B, N)
+    bt = synth.make_batch(3, B, N=N)
+    ins = synth.inputs(bt)
+    rho = np.array([1e-3, 1e-1, 1.0, 10.0], np.float32)
+    g = gpu_sqp(bt, 1e-6, 200, rho=rho, lambda0=np.full((B, N, bt["dims"][0]), 7.0))
+    form = oracle.form_schur(*ins, rho=rho)
+    _, dz = _exact(bt, form)
+    merit = oracle.merit_eval(*ins, dz, synth.ALPHAS, 1.0)["merit"]
+    assert ((g["flags"] & ~ops.F_LS_FAILED) == 0).all()
+    assert rel_rows(g["dz"], dz).max() <= 5e-6
+    assert (np.abs(g["merit"] - merit) / np.abs(merit)).max() <= 1e-5
+
+
 def test_refinement_inside_the_kernel_agrees_with_the_separate_pass():
     """On the ill-conditioned long-horizon workload the register-resident reduction
     with its in-kernel refinement (solver CR) and the streaming reduction followed by

@@ -157,11 +157,13 @@ def test_pcg_parity(cid):
         assert np.abs(g["iters"] - o["iters"]).max() <= 2
 
 
-@pytest.mark.parametrize("cid,N", [(3, 65), (3, 129), (3, 200), (3, 256), (4, 17), (4, 40), (4, 64)])
+@pytest.mark.parametrize("cid,N", [(3, 65), (3, 100), (2, 100), (1, 90), (3, 129), (3, 200), (3, 256), (4, 17),
+                                   (4, 40), (4, 64)])
 def test_pcg_streamed_horizons(cid, N):
     """gato_pcg_solve beyond one workgroup's horizon (several knots per lane group, rows
     re-read per product): up to 256 knots for 16-lane groups and 64 for 32-lane ones,
-    including ragged last chunks."""
+    including ragged last chunks; with two knots per 16-lane group (N <= 128) S's
+    diagonal blocks and D^-1 stay on chip, for every shape that kernel has."""
     B = 2
     _ident("pcg streamed", cid, N, B)
     bt = _batch(cid, B, N=N)
