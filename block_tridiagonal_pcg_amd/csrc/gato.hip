@@ -6,9 +6,15 @@
 //   k_form        stage 1 alone, one workgroup per window of knots (any N).
 //   k_pcg_res     stage 2 alone with S and Phi^-1 rows loaded once into registers.
 //   k_pcg_stream  stage 2 alone for horizons longer than a workgroup holds:
-//                 C knots per lane group, rows re-read from memory per product.
+//                 C knots per lane group; with two (n <= 16) S's diagonal blocks
+//                 and D^-1 stay on chip and only S's other blocks are re-read
+//                 per product, otherwise every row is.
 //   k_direct      stage 2 by block Thomas elimination, one lane group per solve.
-// Stage 2 by block cyclic reduction (k_cr, k_cr_res) is in gato_cr.hip.
+//   k_kkt_residual, k_refine_gamma, k_refine_add
+//                 the KKT refinement pass around a second direct solve (block
+//                 Thomas, the streaming and nested-dissection reductions).
+// Stage 2 by block cyclic reduction (k_cr, k_cr_res, k_cr_res_ref with the
+// refinement pass inside) is in gato_cr.hip.
 //   k_merit       stage 3 alone; any workgroup size gives identical bits.
 //   k_merit_knots, k_merit_sum
 //                 the same stage with a solve's knots over several workgroups
