@@ -16,7 +16,7 @@ horizon) --refine on|off --no-cpu-baseline.  Every run also times a 256 MiB
 device copy (its rate is reported beside the published HBM peak; under the
 profiler it is the reference kernel for scaling byte counters) and the K steps
 once more one by one (median and 90th percentile).  Study modes, each one JSON
-line instead of the step: --merit-variants, --sqp-driver, --solver-sweep.
+line instead of the step: --merit-variants, --sqp-driver, --solver-sweep, --step-sweep.
 """
 import argparse
 import hashlib
@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--solver-sweep", action="store_true",
                     help="instead of the step: time the block Thomas and cyclic-reduction solves over horizons "
                          "and batch sizes (the measurements behind gato_sqp_step's switch)")
+    ap.add_argument("--step-sweep", action="store_true",
+                    help="instead of the step: time the whole step (refinement on) with cyclic reduction and "
+                         "with block Thomas over horizons and batch sizes, beside gato_step_solver's choice")
     return ap.parse_args()
 
 
@@ -431,7 +434,10 @@ def solver_sweep(a):
     """gato_direct_solve (block Thomas) and gato_cr_solve (block cyclic reduction) on
     stage-1 outputs of the given configuration's generators, over horizons and batch
     sizes; the batch is 64 generated solves tiled on the device (the solves' times do
-    not depend on their values).  Also reports gato_step_solver's choice."""
+    not depend on their values).  Also reports gato_step_solver's choice, which is
+    that of the step with its refinement pass: for n <= 16 and N <= 128 it compares the
+    refined steps (see --step-sweep), so it can differ there from the faster of these
+    two solves alone."""
     import torch
 
     from block_tridiagonal_pcg_amd import ops, synth
@@ -480,6 +486,60 @@ def solver_sweep(a):
                       "unit": "us per call", "rows": rows}))
 
 
+def step_sweep(a):
+    """gato_sqp_step_opts with solver CR and with solver THOMAS (refinement on, the step's
+    default) on the given configuration's generators over horizons and batch sizes, the
+    batch being 64 generated solves tiled on the device; median of 15 calls each, beside
+    gato_step_solver's choice for those dims."""
+    import numpy as np
+    import torch
+
+    from block_tridiagonal_pcg_amd import ops, synth
+
+    torch.cuda.set_device(0)
+
+    def time_step(dims, dev, solver):
+        out = ops.alloc_outputs(dims, 8)
+        ws = ops.workspace_for(dims, 8)
+        call = ops.prepared_sqp_step(dims, *[dev[f] for f in synth.FIELDS], None, 1e-6, 200, synth.ALPHAS, 1.0,
+                                     out["lam"], out["dz"], out["merit"], out["merit0"], out["best"], out["iters"],
+                                     out["relres"], out["flags"], workspace=ws, solver=solver)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(15):
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    rows = []
+    for N in (65, 128, 256, 512):
+        base = synth.make_batch(a.config, 64, N=N)
+        dev0 = ops.to_device(base)
+        n, m = base["dims"][0], base["dims"][1]
+        for B in (512, 1024, 1536, 2048, 3072):
+            dev = {k: v.repeat((B + 63) // 64, *([1] * (v.dim() - 1)))[:B].contiguous()
+                   for k, v in dev0.items() if k != "dims"}
+            dims = (n, m, N, B)
+            tc = time_step(dims, dev, ops.SOLVER_CR)
+            td = time_step(dims, dev, ops.SOLVER_THOMAS)
+            choice = ops.gato_step_solver(dims)
+            rows.append({"N": N, "B": B, "cr_us": round(tc, 1), "thomas_us": round(td, 1),
+                         "faster": "cr" if tc < td else "thomas",
+                         "policy": {ops.SOLVER_CR: "cr", ops.SOLVER_THOMAS: "thomas"}.get(choice, "fused")})
+            print("N=%4d B=%5d cr %9.1f us  thomas %9.1f us  policy %s" % (N, B, tc, td, rows[-1]["policy"]),
+                  file=sys.stderr, flush=True)
+            del dev
+            torch.cuda.empty_cache()
+    print(json.dumps({"study": "long-horizon step, refinement on", "workload": synth.CONFIGS[a.config].name,
+                      "unit": "us per step", "rows": rows}))
+
+
 # ---------------------------------------------------------------- main
 
 
@@ -505,6 +565,9 @@ def main():
         return
     if a.solver_sweep:
         solver_sweep(a)
+        return
+    if a.step_sweep:
+        step_sweep(a)
         return
     torch.cuda.set_device(0)
     refine = a.refine == "on"

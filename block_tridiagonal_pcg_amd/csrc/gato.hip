@@ -1038,7 +1038,7 @@ int gato_step_solver(const gato_dims_t* dims)
     gato_dims_t d = *dims;
     if (!native_shape(d.n, d.m)) padded_dims(dims, &d);
     if (fused_path(&d)) return GATO_SOLVER_FUSED_PCG;
-    return cr_preferred(&d) ? GATO_SOLVER_CR : GATO_SOLVER_THOMAS;
+    return cr_preferred(&d, true) ? GATO_SOLVER_CR : GATO_SOLVER_THOMAS;
 }
 
 size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha)
@@ -1323,7 +1323,7 @@ int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, 
         if (fused) return O::fused(p, stream) == hipSuccess ? GATO_OK : GATO_E_HIP;
         // horizons a workgroup cannot hold: no Phi^-1, since a direct solve follows, and
         // no lower blocks of S when that solve reads only the upper ones
-        const bool cr = solver == GATO_SOLVER_AUTO ? cr_preferred(dims) : solver != GATO_SOLVER_THOMAS;
+        const bool cr = solver == GATO_SOLVER_AUTO ? cr_preferred(dims, refine != 0) : solver != GATO_SOLVER_THOMAS;
         p.cr_stream = solver == GATO_SOLVER_CR_STREAM;
         p.s_upper_only = cr && !cr_reads_lower(dims, p.cr_stream != 0);
         if (O::form(p, stream, false) != hipSuccess) return GATO_E_HIP;

@@ -191,9 +191,18 @@ bool cr_reads_lower(const gato_dims_t* d, bool stream)
 // solve with the streaming kernel (n > 16), once its batch fills the chip.
 // Cyclic reduction is taken while its batch time stays below block Thomas's
 // (the n <= 16 constants are from n = 14, the n > 16 ones from n = 24).
-bool cr_preferred(const gato_dims_t* d)
+// With the refinement pass (the step's default) the register-resident kernel
+// refines on its own factors while block Thomas solves twice, so there the
+// whole refined steps are compared instead, as measured (workload-3 data,
+// N = 65 and 128, B up to 3072): about B (0.220 + 0.00363 N) us with the
+// reduction against 3.6 N + 0.00465 N B us with block Thomas.  Elsewhere both
+// solvers repeat their solve for the pass and the comparison of the solves
+// stands.
+bool cr_preferred(const gato_dims_t* d, bool refine)
 {
     const bool narrow = d->n <= 16;
+    if (refine && narrow && d->N <= 2 * ND_CHUNKS)
+        return d->B * (0.220 + 0.00363 * d->N) < 3.6 * d->N + 0.00465 * d->N * d->B;
     const double per_solve_us =
         narrow ? (d->N <= 2 * ND_CHUNKS ? 0.15 + 0.00105 * d->N : 0.18 + 0.0019 * d->N) : 0.017 * d->N;
     const bool wide = d->n > 16;  // 32-lane groups

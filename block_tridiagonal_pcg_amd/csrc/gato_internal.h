@@ -44,7 +44,8 @@ bool cr_refines_inside(const gato_dims_t* d, bool stream);
 hipError_t cr_launch_refined(const Params& p, hipStream_t st);
 
 // Whether gato_sqp_step takes cyclic reduction rather than block Thomas
-// beyond the fused horizons, by the measured cost model.
-bool cr_preferred(const gato_dims_t* d);
+// beyond the fused horizons, by the measured cost model of the step with
+// (refine) or without its refinement pass.
+bool cr_preferred(const gato_dims_t* d, bool refine);
 
 }  // namespace gato

@@ -370,15 +370,20 @@ def test_cyclic_reduction_depth_matches_the_plan(lib):
 
 def test_horizon_policy_picks_the_measured_solver(lib):
     """Fused PCG where a workgroup holds the horizon; beyond, cyclic reduction while
-    its batch time (0.15 us + 1.05 ns per knot per solve resident, 0.18 us + 1.9 ns per
-    knot per solve with the nested dissection, 17 ns per knot and solve streaming for
-    n > 16) stays below block Thomas's (2.7 us per knot, or 1.5 ns per knot and solve once
-    the batch fills the chip; 6.9 us and 5.6 ns for n > 16)."""
+    its batch time (0.18 us + 1.9 ns per knot per solve with the nested dissection,
+    17 ns per knot and solve streaming for n > 16) stays below block Thomas's (2.7 us per
+    knot, or 1.5 ns per knot and solve once the batch fills the chip; 6.9 us and 5.6 ns
+    for n > 16).  Where the register-resident reduction runs (n <= 16, N <= 128) it
+    refines on its own factors, so the refined steps are compared, as measured:
+    B (0.220 + 0.00363 N) us against 3.6 N + 0.00465 N B us for block Thomas (at N = 65
+    the reduction's step took 478 us against 592 at B = 1024 and 941 against 862 at
+    B = 2048; at N = 128, 1409 against 1648 at B = 2048)."""
     from block_tridiagonal_pcg_amd import ops
 
     F, T, C = ops.SOLVER_FUSED_PCG, ops.SOLVER_THOMAS, ops.SOLVER_CR
-    cases = {(14, 7, 64, 128): F, (24, 12, 16, 4): F, (14, 7, 65, 512): C, (14, 7, 65, 1024): T,
-             (14, 7, 128, 512): C, (14, 7, 128, 1024): C, (14, 7, 128, 2048): T,
+    cases = {(14, 7, 64, 128): F, (24, 12, 16, 4): F, (14, 7, 65, 512): C, (14, 7, 65, 1024): C,
+             (14, 7, 65, 2048): T, (14, 7, 128, 512): C, (14, 7, 128, 1024): C, (14, 7, 128, 2048): C,
+             (14, 7, 128, 4096): C, (14, 7, 128, 8192): T,
              (14, 7, 256, 512): C, (14, 7, 256, 1024): C, (14, 7, 256, 2048): T, (14, 7, 1024, 64): C,
              (14, 7, 1024, 1024): C, (14, 7, 1024, 2048): T, (24, 12, 100, 8): C, (24, 12, 100, 256): C, (24, 12, 100, 512): T, (24, 12, 100, 1024): T}
     for dims, want in cases.items():
