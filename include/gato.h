@@ -281,11 +281,13 @@ int gato_merit_eval_shape(const gato_dims_t* dims, const float* Q, const float* 
  *    for n <= 32), the stages run fused in one kernel with PCG, and no
  *    workspace is used;
  *  - otherwise stage 2 is a direct solve: gato_cr_solve's block cyclic
- *    reduction while the batch is small enough for its log-depth to pay
- *    (measured switch points: B * (0.15 + 0.00105 N) us < 2.7 N us for n <= 16
- *    and N <= 128, B * (0.18 + 0.0019 N) us < 2.7 N us for n <= 16 beyond
- *    (B < ~1040-1300), B < ~400 for n > 16), else gato_direct_solve's block
- *    Thomas elimination.  The direct solve is followed by one pass of
+ *    reduction while the batch is small enough for its log-depth to pay, else
+ *    gato_direct_solve's block Thomas elimination (measured switch points: for
+ *    n <= 16 and N <= 128, where the reduction refines on its own factors, the
+ *    refined steps B * (0.220 + 0.00363 N) us < 3.6 N + 0.00465 N B us, or
+ *    without the refinement pass the solves B * (0.15 + 0.00105 N) us <
+ *    2.7 N us; B * (0.18 + 0.0019 N) us < 2.7 N us for n <= 16 beyond
+ *    (B < ~1040-1300); B < ~400 for n > 16).  The direct solve is followed by one pass of
  *    iterative refinement of the KKT system (G dz - C' lambda = -g, C dz = c;
  *    the paper's eq. 2): its residual, accumulated in double from the problem
  *    data, is the right-hand side of a correction system with the same S,
