@@ -447,7 +447,7 @@ template <class SH>
 __global__ __launch_bounds__(64) void k_direct(Params p)
 {
     constexpr int SPW = 64 / SH::NP;
-    __shared__ __align__(16) float piv[SPW][(SH::NC + 3) / 4 * 4];  // pivot rows (32-lane groups)
+    __shared__ __align__(16) float piv[SPW][GJ_LDS_BLOCK * ((SH::NC + 3) / 4 * 4)];  // pivot rows (32-lane groups)
     const int b = blockIdx.x * SPW + (int)(threadIdx.x / SH::NP);
     direct_solve<SH>(p, b, b < p.B, piv[threadIdx.x / SH::NP]);
 }

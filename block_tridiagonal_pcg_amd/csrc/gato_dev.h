@@ -433,23 +433,33 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
     gj_finish<K>(a, rinv);
 }
 
-// The same elimination for 32-lane groups with the pivot row passed through
-// LDS instead of DPP: lane J of the group stores its row to the group's buffer
-// `pr` (16-byte aligned, at least K rounded up to 4 floats), and every lane
-// reads it back as float4s.  A 32-lane broadcast by DPP costs a permlane swap
-// and a DPP multiply-add per column; here a step is K/4 stores and loads and K
-// plain multiply-adds.  LDS accesses of one wave complete in order, and a
-// group never spans two waves, so no barrier is needed.  Same arithmetic as
-// gj_steps (the multiply-add a[c] + g * pivot_row[c] for every column, the
-// pivot row left unscaled, each row scaled by its pivot's reciprocal at the end).
-template <int K>
-__device__ __forceinline__ void gj_steps_lds(float* a, int lane, bool& bad, float* pr)
+// The same elimination for 32-lane groups with the pivot rows passed through
+// LDS instead of DPP: a 32-lane broadcast by DPP costs a permlane swap and a
+// DPP multiply-add per column, here a step is a few float4 stores and loads and
+// K plain multiply-adds.  The LDS round trip, not the arithmetic, bounds a
+// step, so gj_lds_block(K) pivots share one: lanes J0 .. J0+BS-1 store their
+// rows to the group's buffer `pr` (16-byte aligned, GJ_LDS_BLOCK rows of K
+// rounded up to 4 floats), every lane reads them back, and before each of
+// those pivots takes its step every lane applies the block's earlier steps to
+// its copies of the later pivot rows, with the same multiply-adds their own
+// lanes apply to them, so every row ends with the bits of one pivot row per
+// round trip.  LDS accesses of one wave complete in order, and a group never
+// spans two waves, so no barrier is needed.  Same arithmetic as gj_steps (the
+// multiply-add a[c] + g * pivot_row[c] for every column, the pivot row left
+// unscaled, each row scaled by its pivot's reciprocal at the end).
+// Three rows per round trip measured fastest at n = 24 (the step 66.5 -> 59.3 us
+// at B = 256, against 61.3 us with two and 60.9 with four); wider rows (n = 28)
+// take two, where three would spill registers in the fused step.
+constexpr int GJ_LDS_BLOCK = 3;  // the most rows any K takes (the buffers' size)
+__host__ __device__ constexpr int gj_lds_block(int K) { return K > 24 ? 2 : GJ_LDS_BLOCK; }
+
+template <int K, int BS, int J0 = 0>
+__device__ __forceinline__ void gj_block_lds(float* a, int lane, bool& bad, float* pr, float& rinv)
 {
-    constexpr int K4 = (K + 3) / 4;
-    float rinv = 1.0f;
-#pragma unroll
-    for (int J = 0; J < K; ++J) {
-        if (lane == J)
+    if constexpr (J0 < K) {
+        constexpr int K4 = (K + 3) / 4, NB = (K - J0 < BS) ? K - J0 : BS;
+        const int bl = lane - J0;
+        if (bl >= 0 && bl < NB)
 #pragma unroll
             for (int q = 0; q < K4; ++q) {
                 float4 v;
@@ -457,30 +467,53 @@ __device__ __forceinline__ void gj_steps_lds(float* a, int lane, bool& bad, floa
                 v.y = 4 * q + 1 < K ? a[4 * q + 1] : 0.0f;
                 v.z = 4 * q + 2 < K ? a[4 * q + 2] : 0.0f;
                 v.w = 4 * q + 3 < K ? a[4 * q + 3] : 0.0f;
-                reinterpret_cast<float4*>(pr)[q] = v;
+                reinterpret_cast<float4*>(pr)[bl * K4 + q] = v;
             }
         __builtin_amdgcn_wave_barrier();
-        float row[4 * K4];
+        float rows[NB][4 * K4];
 #pragma unroll
-        for (int q = 0; q < K4; ++q) {
-            const float4 v = reinterpret_cast<const float4*>(pr)[q];
-            row[4 * q] = v.x;
-            row[4 * q + 1] = v.y;
-            row[4 * q + 2] = v.z;
-            row[4 * q + 3] = v.w;
-        }
+        for (int r = 0; r < NB; ++r)
+#pragma unroll
+            for (int q = 0; q < K4; ++q) {
+                const float4 v = reinterpret_cast<const float4*>(pr)[r * K4 + q];
+                rows[r][4 * q] = v.x;
+                rows[r][4 * q + 1] = v.y;
+                rows[r][4 * q + 2] = v.z;
+                rows[r][4 * q + 3] = v.w;
+            }
         __builtin_amdgcn_wave_barrier();
-        const float piv = row[J];
-        bad |= !(piv > 0.0f) || !__builtin_isfinite(piv);
-        const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
-        const bool me = lane == J;
-        const float keep = a[J];
-        const float g = me ? 0.0f : -(keep * inv);
 #pragma unroll
-        for (int c = 0; c < K; ++c) a[c] = __builtin_fmaf(row[c], g, a[c]);
-        a[J] = me ? 1.0f : -(keep * inv);
-        rinv = me ? inv : rinv;
+        for (int r = 0; r < NB; ++r) {
+            const int J = J0 + r;
+            const float piv = rows[r][J];
+            bad |= !(piv > 0.0f) || !__builtin_isfinite(piv);
+            const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
+            const bool me = lane == J;
+            const float keep = a[J];
+            const float g = me ? 0.0f : -(keep * inv);
+#pragma unroll
+            for (int c = 0; c < K; ++c) a[c] = __builtin_fmaf(rows[r][c], g, a[c]);
+            a[J] = me ? 1.0f : -(keep * inv);
+            rinv = me ? inv : rinv;
+            // the block's later pivot rows take this step as their lanes do
+#pragma unroll
+            for (int r2 = r + 1; r2 < NB; ++r2) {
+                const float k2 = rows[r2][J];
+                const float g2 = -(k2 * inv);
+#pragma unroll
+                for (int c = 0; c < K; ++c) rows[r2][c] = __builtin_fmaf(rows[r][c], g2, rows[r2][c]);
+                rows[r2][J] = -(k2 * inv);
+            }
+        }
+        gj_block_lds<K, BS, J0 + BS>(a, lane, bad, pr, rinv);
     }
+}
+
+template <int K>
+__device__ __forceinline__ void gj_steps_lds(float* a, int lane, bool& bad, float* pr)
+{
+    float rinv = 1.0f;
+    gj_block_lds<K, gj_lds_block(K)>(a, lane, bad, pr, rinv);
     gj_finish<K>(a, rinv);
 }
 

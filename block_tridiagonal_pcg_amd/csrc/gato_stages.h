@@ -142,7 +142,7 @@ template <class SH>
 struct FormLds {
     float xw[SH::SLOTS][SH::NP][SH::NC + 1];  // one matrix row per lane (+1: bank spread)
     float xg[SH::SLOTS][SH::NP];
-    alignas(16) float piv[SH::NP == 32 ? SH::SLOTS : 1][(SH::NC + 3) / 4 * 4];  // pivot rows (32-lane groups)
+    alignas(16) float piv[SH::NP == 32 ? SH::SLOTS : 1][GJ_LDS_BLOCK * ((SH::NC + 3) / 4 * 4)];  // pivot rows (32-lane groups)
 };
 
 // In-place inverse of the K x K SPD matrix whose row i is held by lane i of
