@@ -434,6 +434,40 @@ def test_solve_independent_of_batch_position():
         np.testing.assert_array_equal(h["merit"][0], g["merit"][b])
 
 
+@pytest.mark.parametrize("cid,B", [(3, 16384), (5, 4096)])
+def test_large_batches_give_every_copy_the_same_bits(cid, B):
+    """Batches far beyond one round of workgroups (16384 fused steps; 4096 long-horizon steps
+    through the direct solve and its refinement pass): 32 generated solves tiled B/32 times.
+    Every copy must give the bits of the first, and the first copies meet the oracle's bars."""
+    _ident("large batch", cid, B)
+    T = 32
+    base = _batch(cid, T)
+    big = {f: np.tile(base[f], (B // T,) + (1,) * (base[f].ndim - 1)) for f in synth.FIELDS}
+    n, m, N, _ = base["dims"]
+    big["dims"] = (n, m, N, B)
+    g = gpu_sqp(big, 1e-6, CAPS[cid])
+    del big
+    for key in ("lam", "dz", "merit", "merit0", "best", "iters", "relres", "flags"):
+        a = g[key].reshape((B // T, T) + g[key].shape[1:])
+        assert np.array_equal(a, np.broadcast_to(a[:1], a.shape)), key
+    first = {k: g[k][:T] for k in ("dz", "merit", "merit0", "best", "iters", "flags")}
+    ins = synth.inputs(base)
+    if _direct_path(base):
+        f = oracle.form_schur(*ins)
+        lam = oracle.direct_solve(f["S"], f["gamma"])["lam"]
+        o = {"dz": oracle.recover(f["Qinv"], f["Rinv"], base["A"], base["Bu"], base["q"], base["r"], lam),
+             "flags": f["flags"]}
+        assert (first["iters"] == 0).all()
+    else:
+        o = oracle.sqp_step(*ins, None, 1e-6, CAPS[cid], A64, 1.0)
+        assert np.abs(first["iters"] - o["iters"]).max() <= 2
+    assert rel_rows(first["dz"], o["dz"]).max() <= 1e-3
+    assert ((first["flags"] & ~ops.F_LS_FAILED) == (o["flags"] & ~ops.F_LS_FAILED)).all()
+    om = oracle.merit_eval(*ins, first["dz"].astype(np.float64), A64, 1.0)
+    assert merit_rel(first["merit"], om).max() <= 1e-4
+    np.testing.assert_array_equal(first["best"], select(first["merit"], first["merit0"]))
+
+
 def test_stage_times_reported():
     g = gpu_sqp(_batch(3, 8), 1e-6, 200, times=True)
     assert g["times"].total_us > 0
