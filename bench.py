@@ -546,7 +546,7 @@ def step_sweep(a):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np

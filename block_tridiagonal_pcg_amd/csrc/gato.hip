@@ -737,7 +737,7 @@ struct Ops {
     static bool pcg_supported(int N) { return N >= 1 && stream_chunks(N) != 0; }
 };
 
-// Shapes with kernels in this build (GATO_FOR_SHAPES).
+// Shapes the library has kernels for (GATO_FOR_SHAPES).
 template <class F>
 static int with_shape(int n, int m, F&& f)
 {
@@ -759,7 +759,7 @@ static int check_ptrs(std::initializer_list<const void*> req)
     return GATO_OK;
 }
 
-// Dims of a shape this build has kernels for (every entry point).
+// Dims of a shape the library has kernels for (every entry point).
 static int check_dims(const gato_dims_t* d)
 {
     if (d == nullptr) return GATO_E_NULL;

@@ -8,7 +8,7 @@
 
 #include "gato.h"
 
-// (n, m) of the shapes this build has kernels for: those of the configurations
+// (n, m) of the shapes the library has kernels for: those of the configurations
 // the benchmark and tests use, n = m = 1 for hand-checkable examples, and
 // (28, 14), the widest whose fused step fits a workgroup's LDS, so that
 // gato_sqp_step can serve any n <= 28, m <= 14 by padding.

@@ -390,7 +390,7 @@ size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha);
 /* Static description of a status code. */
 const char* gato_status_string(int code);
 
-/* Whether this build serves (n, m, N): 1 if it has kernels for (n, m), which are
+/* Whether the library serves (n, m, N): 1 if it has kernels for (n, m), which are
  * (14,7), (12,6), (24,12), (4,2), (1,1) and (28,14), and 1 <= N <= 1024;
  * 2 if only the step calls (gato_sqp_step, gato_sqp_step_opts,
  * gato_sqp_step_noalloc) serve it, by padding; 0 otherwise.  Padding: a shape
