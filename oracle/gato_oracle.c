@@ -18,6 +18,10 @@
  * formulas are the textbook range-space (Schur-complement) method for the
  * equality-constrained QP that the surrounding prose describes.  Every
  * reading taken where the text is silent is named at the function doing it.
+ * One of them is parity unpinned against the pages: the form of the stair
+ * preconditioner, which the paper cites but does not print (its closed form,
+ * symmetry and definiteness under the reading are pinned; only the PCG
+ * iteration counts depend on it, not lambda or dz beyond the exit tolerance).
  *
  * Problem data, per solve b (N knot points, n states, m controls):
  *   Q[k] n x n (k < N), q[k] n, R[k] m x m (k < N-1), r[k] m,
