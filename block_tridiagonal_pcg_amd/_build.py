@@ -2,8 +2,10 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,7 +19,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
@@ -39,12 +40,29 @@ def build(force: bool = True, out: str = LIB, verbose: bool = False) -> str:
     if not force and os.path.exists(out) and all(os.path.getmtime(out) >= os.path.getmtime(d) for d in deps):
         return out
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + srcs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objdir = tempfile.mkdtemp(prefix="gato_build_")
+    try:
+        # each source compiles on its own (they share no device code), side by side
+        objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+        cmds = [[hipcc()] + HIPCC_FLAGS + inc + ["-c", "-o", o, s] for s, o in zip(srcs, objs)]
+        cmds.append([hipcc()] + HIPCC_FLAGS + ["-shared", "-o", tmp] + objs)
+        procs = []
+        for c in cmds[:-1]:
+            if verbose:
+                print(" ".join(c), flush=True)
+            procs.append(subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+        logs = [pr.communicate()[0] for pr in procs]
+        for pr, log in zip(procs, logs):
+            if pr.returncode != 0:
+                raise RuntimeError("hipcc failed:\n" + log)
+        if verbose:
+            print(" ".join(cmds[-1]), flush=True)
+        res = subprocess.run(cmds[-1], capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + res.stdout + res.stderr)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     os.replace(tmp, out)
     return out
 
