@@ -41,8 +41,10 @@ struct FusedLds {
     int flags;
 };
 
-template <class SH>
-__global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
+// VS: the PCG's stop test on the vector unit (pcg()), for launches of at most
+// 512 threads, which also leaves the kernel up to 256 registers per lane.
+template <class SH, bool VS>
+__global__ __launch_bounds__(VS && SH::THREADS > 512 ? 512 : SH::THREADS) void k_sqp_fused(Params p)
 {
     constexpr int NP = SH::NP, NC = SH::NC, MC = SH::MC;
     __shared__ FusedLds<SH> L;
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(SH::THREADS) void k_sqp_fused(Params p)
     int it = 0, pfl = 0;
     float rel = 0.0f;
     const RegMat<SH> M{&rw};
-    pcg_robust<SH, 1>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
+    pcg_robust<SH, 1, RegMat<SH>, VS>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
 
     // recovery of dz (exchange rows of the PCG buffers: knot k at row k + 1)
     L.u.pcg.xv[s + 1][i] = lam;
@@ -726,9 +728,18 @@ struct Ops {
         hipLaunchKernelGGL((k_direct<SH>), dim3((p.B + SPW - 1) / SPW), dim3(64), 0, st, p);
         return hipGetLastError();
     }
+    // The PCG's stop test on the vector unit at up to two waves per SIMD (pcg())
     static hipError_t fused(const Params& p, hipStream_t st)
     {
-        hipLaunchKernelGGL((k_sqp_fused<SH>), dim3(p.B), dim3(threads_for(p.N)), 0, st, p);
+        const int threads = threads_for(p.N);
+        if constexpr (SH::THREADS <= 512) {
+            hipLaunchKernelGGL((k_sqp_fused<SH, true>), dim3(p.B), dim3(threads), 0, st, p);
+        } else {
+            if (threads <= 512)
+                hipLaunchKernelGGL((k_sqp_fused<SH, true>), dim3(p.B), dim3(threads), 0, st, p);
+            else
+                hipLaunchKernelGGL((k_sqp_fused<SH, false>), dim3(p.B), dim3(threads), 0, st, p);
+        }
         return hipGetLastError();
     }
     // formation (windowed), the direct solve and the merit take any N up to the

@@ -66,6 +66,8 @@ __device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ void seq_after(float x) { asm volatile("" ::"v"(x) : "memory"); }
 __device__ __forceinline__ void seq_after(double x) { asm volatile("" ::"v"(x) : "memory"); }
 
+__device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ float uniform(float x)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -670,12 +672,19 @@ struct PcgLds {
 // the same arithmetic as their owners, so the products need no more exchange.
 // lambda is accumulated in fp64: on ill-conditioned solves it sums hundreds of
 // small steps, and in fp32 that sum alone would cost ~1e-3 in dz.
+// The step lengths alpha and beta are formed in vector registers from the
+// totals every lane holds (the same bits in each), so the updates do not wait
+// for a copy to scalar registers.  VS (vector stop): the stop test too, and
+// one scalar copy of its outcome for the loop's branch.  That suits one or two
+// waves per SIMD, where the scalar round trips of the test sit on the
+// iteration's critical path; with four waves per SIMD the vector unit is the
+// busier one, and the test is cheaper on the scalar unit.
 // Internal stop code of pcg() (not a GATO_F_* bit): with the assembled Phi^-1,
 // r'z <= 0 while the residual is above the tolerance, i.e. the fp32
 // preconditioner is not positive definite on this solve.
 constexpr int PCG_INDEFINITE = 1 << 16;
 
-template <class SH, int C, class MAT>
+template <class SH, int C, class MAT, bool VS = false>
 __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* gam, float* lam, PcgLds<SH, C>& L,
                                     int max_iters, int& iters_out, float& relres, int& flags_out)
 {
@@ -805,6 +814,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
     }
     if (!(rr <= tol2) && !flags && iters >= max_iters) flags |= GATO_F_PCG_MAXITER;
     if (!(rr <= tol2) && !flags) {
+        int itv = iters;
         // One exit, after the second barrier: a breakdown at the first one leaves
         // lambda, r and the count as they are and only sets the stop code, so every
         // loop-carried value has a single definition per iteration.
@@ -825,14 +835,15 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 vp[c] = L.xv[row(c) - 1][i];
                 vn[c] = L.xv[row(c) + 1][i];
             }
-            const float pSp = uniform(canon_sum<LPL>(L.red0));
+            const float pSpv = canon_sum<LPL>(L.red0);
+            const float pSp = VS ? pSpv : uniform(pSpv);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 pin(vp[c]);
                 pin(vn[c]);
             }
             int stop = !__builtin_isfinite(pSp) ? GATO_F_NONFINITE : !(pSp > 0.0f) ? GATO_F_PCG_BREAKDOWN : 0;
-            const float a = uniform(eta * __builtin_amdgcn_rcpf(pSp));
+            const float a = eta * __builtin_amdgcn_rcpf(pSpv);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 const double l1 = fma((double)a, (double)pv[c], lamd[c]);
@@ -844,7 +855,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 rp[c] = stop ? rp[c] : rp1;
                 rn[c] = stop ? rn[c] : rn1;
             }
-            iters += stop ? 0 : 1;
+            itv += stop ? 0 : 1;
             // z = Phi^-1 r ; r'r, r'z ; z to neighbours
             float z[C];
             if constexpr (MAT::kPhased) {
@@ -873,27 +884,31 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 zp[c] = L.xz[row(c) - 1][i];
                 zn[c] = L.xz[row(c) + 1][i];
             }
-            float rz;
-            canon_sum2<LPL>(L.red1, L.red2, rr, rz);
-            rr = uniform(rr);
-            rz = uniform(rz);
+            float rrv, rzv;
+            canon_sum2<LPL>(L.red1, L.red2, rrv, rzv);
+            rr = VS ? rrv : uniform(rrv);
+            const float rz = VS ? rzv : uniform(rzv);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 pin(zp[c]);
                 pin(zn[c]);
             }
-            if (!stop) {
-                if (!__builtin_isfinite(rr)) stop = GATO_F_NONFINITE;
-                else if (rr <= tol2) stop = -1;  // converged
-                else if (!__builtin_isfinite(rz)) stop = GATO_F_NONFINITE;
-                else if (MAT::kAssembled && !(rz > 0.0f)) stop = PCG_INDEFINITE;
-                else if (iters >= max_iters) stop = GATO_F_PCG_MAXITER;
+            // the first stop of the iteration holds; then, in this order of
+            // precedence: r'r not finite, converged, r'z not finite, r'z <= 0
+            // with the assembled Phi^-1, the cap (selects, one branch)
+            {
+                int st = itv >= max_iters ? GATO_F_PCG_MAXITER : 0;
+                st = (MAT::kAssembled && !(rz > 0.0f)) ? PCG_INDEFINITE : st;
+                st = !__builtin_isfinite(rz) ? GATO_F_NONFINITE : st;
+                st = rr <= tol2 ? -1 : st;  // converged
+                st = !__builtin_isfinite(rr) ? GATO_F_NONFINITE : st;
+                stop = uniform_i(stop ? stop : st);
             }
-            if (stop) {
-                if (stop > 0) flags |= stop;
+            if (__builtin_expect(stop != 0, 0)) {
+                flags |= stop > 0 ? stop : 0;
                 break;
             }
-            const float be = uniform(rz * __builtin_amdgcn_rcpf(eta));
+            const float be = rzv * __builtin_amdgcn_rcpf(eta);
             eta = rz;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -902,6 +917,8 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 pn[c] = fmaf(be, pn[c], zn[c]);
             }
         }
+        iters = uniform_i(itv);
+        rr = uniform(rr);
     }
 #pragma unroll
     for (int c = 0; c < C; ++c) lam[c] = (float)lamd[c];
@@ -919,11 +936,11 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
 // factored form and restarts from its current lambda with the iterations left;
 // iters counts both runs.  The decision is uniform over the workgroup (one
 // solve), and a solve whose r'z stays positive never takes it.
-template <class SH, int C, class MAT>
+template <class SH, int C, class MAT, bool VS = false>
 __device__ __forceinline__ void pcg_robust(const Params& p, const MAT& M, const float* gam, float* lam,
                                            PcgLds<SH, C>& L, int& iters_out, float& relres, int& flags_out)
 {
-    pcg<SH, C>(p, M, gam, lam, L, p.max_iters, iters_out, relres, flags_out);
+    pcg<SH, C, MAT, VS>(p, M, gam, lam, L, p.max_iters, iters_out, relres, flags_out);
     if constexpr (MAT::kAssembled) {
         static_assert(C == 1, "one knot per lane group");
         if (flags_out == PCG_INDEFINITE) {
@@ -935,7 +952,7 @@ __device__ __forceinline__ void pcg_robust(const Params& p, const MAT& M, const 
                 sym_rows<SH>(M.rw->pd, L.xy[threadIdx.x / SH::NP + 1], dsym);
                 const RegMatF<SH> F{{M.rw}, dsym, L.xy};
                 int it2 = 0, fl2 = 0;
-                pcg<SH, C>(p, F, gam, lam, L, left, it2, relres, fl2);
+                pcg<SH, C, RegMatF<SH>, VS>(p, F, gam, lam, L, left, it2, relres, fl2);
                 iters_out += it2;
                 flags_out = fl2;
             }
