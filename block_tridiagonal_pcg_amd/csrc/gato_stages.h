@@ -68,6 +68,13 @@ __device__ __forceinline__ void seq_after(double x) { asm volatile("" ::"v"(x) :
 
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// This wave's issue priority (0 lowest .. 3), when ON.
+template <bool ON, int K>
+__device__ __forceinline__ void wave_prio()
+{
+    if constexpr (ON) __builtin_amdgcn_s_setprio(K);
+}
+
 __device__ __forceinline__ float uniform(float x)
 {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -672,6 +679,10 @@ struct PcgLds {
 // the same arithmetic as their owners, so the products need no more exchange.
 // lambda is accumulated in fp64: on ill-conditioned solves it sums hundreds of
 // small steps, and in fp32 that sum alone would cost ~1e-3 in dz.
+// With four waves per SIMD (VS false) each phase between barriers lowers the
+// wave's priority as it goes (3 for the chain after the barrier, 2 for the
+// product, 1 after it), so the waves of a SIMD that are behind issue first and
+// the four finish their products closer together.
 // The step lengths alpha and beta are formed in vector registers from the
 // totals every lane holds (the same bits in each), so the updates do not wait
 // for a copy to scalar registers.  VS (vector stop): the stop test too, and
@@ -820,15 +831,18 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
         // loop-carried value has a single definition per iteration.
         for (;;) {
             // v = S p ; p'v ; v to neighbours
+            wave_prio<!VS, 2>();
             float v[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 v[c] = mat_S(M, c, row(c) - 1, pp[c], pv[c], pn[c]);
+                wave_prio<!VS, 1>();
                 const float t = groupsum<NP>(pv[c] * v[c]);
                 if (lead) L.red0[row(c) - 1] = t;
                 L.xv[row(c)][i] = v[c];
             }
             __syncthreads();
+            wave_prio<!VS, 3>();
             float vp[C], vn[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -857,6 +871,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             }
             itv += stop ? 0 : 1;
             // z = Phi^-1 r ; r'r, r'z ; z to neighbours
+            wave_prio<!VS, 2>();
             float z[C];
             if constexpr (MAT::kPhased) {
                 float y[C];
@@ -869,6 +884,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 if constexpr (!MAT::kPhased) z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
+                wave_prio<!VS, 1>();
                 const float ta = groupsum<NP>(r[c] * r[c]);
                 const float tb = groupsum<NP>(r[c] * z[c]);
                 if (lead) {
@@ -878,6 +894,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 L.xz[row(c)][i] = z[c];
             }
             __syncthreads();
+            wave_prio<!VS, 3>();
             float zp[C], zn[C];
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -917,6 +934,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 pn[c] = fmaf(be, pn[c], zn[c]);
             }
         }
+        wave_prio<!VS, 0>();
         iters = uniform_i(itv);
         rr = uniform(rr);
     }
