@@ -368,8 +368,9 @@ __device__ __forceinline__ void mma_rows(const mma32_t& acc, float* r)
 // (rows beyond K are ignored), by Gauss-Jordan elimination without pivoting
 // (the matrices are symmetric positive definite, whose pivots are the positive
 // diagonal entries of their LDL' factor).  `bad` is set when a pivot is not
-// positive or not finite; the elimination then continues with the bad pivot
-// and the result is flagged, not repaired.
+// positive or not finite (by gj_steps in the lane whose row gave the pivot, by
+// gj_steps_lds in every lane; callers take it over the group); the elimination
+// then continues with the bad pivot and the result is flagged, not repaired.
 //
 // Step j: every lane i != j subtracts A[i][j]/A[j][j] times row j and column j
 // becomes the matching column of the inverse (the classical in-place form),
@@ -382,7 +383,7 @@ __device__ __forceinline__ void mma_rows(const mma32_t& acc, float* r)
 // with the multiplier (1/piv - 1) would round that multiplier in absolute
 // terms, a relative error of up to 2^-24 * piv in the inverse's row.
 template <int NP, int K, int J = 0>
-__device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad, float& rinv)
+__device__ __forceinline__ void gj_steps(float* a, int lane, float& mypiv, float& rinv)
 {
     if constexpr (J < K) {
         float piv;
@@ -398,9 +399,9 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad, float& r
             dup_rows(a[J], lo, hi);
             piv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(hi), 0x150 + (J & 15), 0xF, 0xF, false));
         }
-        bad |= !(piv > 0.0f) || !__builtin_isfinite(piv);
         const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
         const bool me = lane == J;
+        mypiv = me ? piv : mypiv;
         const float f = a[J];
         const float g = me ? 0.0f : -(f * inv);
         float keep = a[J];
@@ -413,7 +414,7 @@ __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad, float& r
         // column J of the inverse: -A[i][j]/piv off the pivot row; on it the unscaled 1
         a[J] = me ? 1.0f : -(keep * inv);
         rinv = me ? inv : rinv;
-        gj_steps<NP, K, J + 1>(a, lane, bad, rinv);
+        gj_steps<NP, K, J + 1>(a, lane, mypiv, rinv);
     }
 }
 
@@ -425,12 +426,14 @@ __device__ __forceinline__ void gj_finish(float* a, float rinv)
     for (int c = 0; c < K; ++c) a[c] *= rinv;
 }
 
+// Each lane keeps the pivot of its own row's step and tests it once at the end.
 template <int NP, int K>
 __device__ __forceinline__ void gj_steps(float* a, int lane, bool& bad)
 {
-    float rinv = 1.0f;
-    gj_steps<NP, K, 0>(a, lane, bad, rinv);
+    float rinv = 1.0f, mypiv = 1.0f;
+    gj_steps<NP, K, 0>(a, lane, mypiv, rinv);
     gj_finish<K>(a, rinv);
+    bad |= !(mypiv > 0.0f) || !__builtin_isfinite(mypiv);
 }
 
 // The same elimination for 32-lane groups with the pivot rows passed through

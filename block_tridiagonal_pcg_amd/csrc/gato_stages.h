@@ -88,6 +88,15 @@ __device__ __forceinline__ bool lane_bit(uint64_t mask)
     return (mask >> (threadIdx.x & 63)) & 1u;
 }
 
+// Whether any lane of this lane's group of NP has its bit set in mask.
+template <int NP>
+__device__ __forceinline__ bool group_any(uint64_t mask)
+{
+    const int sh = (threadIdx.x & 63) & ~(NP - 1);
+    const uint64_t g = NP == 64 ? ~0ull : ((1ull << NP) - 1);
+    return ((mask >> sh) & g) != 0;
+}
+
 // ------------------------------------------------------------------ indexing
 
 template <class SH>
@@ -228,7 +237,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         for (int c = 0; c < NC; ++c)
             if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
         inv_rows<SH, NC>(qi, i, badq, L, s);
-        badq = lane_bit(__builtin_amdgcn_ballot_w64(badq));
+        badq = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(badq));
         if (i < NC)
 #pragma unroll
             for (int c = 0; c < NC; ++c) K.Q[s][i][c] = qi[c];
@@ -236,7 +245,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
         for (int c = 0; c < MC; ++c) ri[c] = (c == i) ? (urow ? ri0[c] : 1.0f) : ri0[c];
         inv_rows<SH, MC>(ri, i, badr, L, s);
-        badr = lane_bit(__builtin_amdgcn_ballot_w64(badr));
+        badr = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(badr));
         if (i < MC)
 #pragma unroll
             for (int c = 0; c < MC; ++c) K.R[s][i][c] = ri[c];
@@ -362,7 +371,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         out.sd[c] = rowv ? sd[c] : 0.0f;
     }
     inv_rows<SH, NC>(di, i, bads, L, s);
-    bads = lane_bit(__builtin_amdgcn_ballot_w64(bads));
+    bads = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(bads));
 #pragma unroll
     for (int c = 0; c < NC; ++c) L.xw[s][i][c] = di[c];
     __syncthreads();
