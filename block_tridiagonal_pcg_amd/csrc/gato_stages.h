@@ -691,7 +691,9 @@ struct PcgLds {
 // With four waves per SIMD (VS false) each phase between barriers lowers the
 // wave's priority as it goes (3 for the chain after the barrier, 2 for the
 // product, 1 after it), so the waves of a SIMD that are behind issue first and
-// the four finish their products closer together.
+// the four finish their products closer together; and each wave stores its
+// exchange row before its partial sums, so that the store's latency, which the
+// barrier waits for, overlaps them.
 // The step lengths alpha and beta are formed in vector registers from the
 // totals every lane holds (the same bits in each), so the updates do not wait
 // for a copy to scalar registers.  VS (vector stop): the stop test too, and
@@ -846,9 +848,13 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             for (int c = 0; c < C; ++c) {
                 v[c] = mat_S(M, c, row(c) - 1, pp[c], pv[c], pn[c]);
                 wave_prio<!VS, 1>();
+                if constexpr (!VS) {
+                    L.xv[row(c)][i] = v[c];  // first: the store overlaps the sum
+                    mem_order();
+                }
                 const float t = groupsum<NP>(pv[c] * v[c]);
                 if (lead) L.red0[row(c) - 1] = t;
-                L.xv[row(c)][i] = v[c];
+                if constexpr (VS) L.xv[row(c)][i] = v[c];
             }
             __syncthreads();
             wave_prio<!VS, 3>();
@@ -894,13 +900,17 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             for (int c = 0; c < C; ++c) {
                 if constexpr (!MAT::kPhased) z[c] = M.P(row(c) - 1, rp[c], r[c], rn[c]);
                 wave_prio<!VS, 1>();
+                if constexpr (!VS) {
+                    L.xz[row(c)][i] = z[c];  // first: the store overlaps the sums
+                    mem_order();
+                }
                 const float ta = groupsum<NP>(r[c] * r[c]);
                 const float tb = groupsum<NP>(r[c] * z[c]);
                 if (lead) {
                     L.red1[row(c) - 1] = ta;
                     L.red2[row(c) - 1] = tb;
                 }
-                L.xz[row(c)][i] = z[c];
+                if constexpr (VS) L.xz[row(c)][i] = z[c];
             }
             __syncthreads();
             wave_prio<!VS, 3>();
