@@ -95,8 +95,11 @@ __global__ __launch_bounds__(VS && SH::THREADS > 512 ? 512 : SH::THREADS) void k
     for (int t = threadIdx.x; t < (GATO_MAX_ALPHA + 1) * 64; t += blockDim.x) L.u.mer[t] = 0.0f;
     __syncthreads();
     MeritIn<SH> mi;
+    wave_prio<true, 3>();
     merit_rows<SH>(p, b, k, i, mi);
+    wave_prio<true, 2>();
     merit_knot<SH>(p, k, i, mi, dx, du, dxn, L.u.mer + k, 64);
+    wave_prio<true, 0>();
     __syncthreads();
     int32_t best;
     int lsfail;

@@ -68,8 +68,12 @@ __device__ __forceinline__ void seq_after(double x) { asm volatile("" ::"v"(x) :
 
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// This wave's issue priority (0 lowest .. 3), when ON.
-template <bool ON, int K>
+// This wave's issue priority (0 lowest .. 3), when ON.  The phases between
+// two barriers step it down as they go (3 at the start, lower for later
+// stages), so that the waves of a SIMD that are behind, which are the younger
+// ones when the priorities are equal, issue first and the four reach the
+// barrier closer together, with less of the phase left to one wave alone.
+template <bool ON = true, int K = 0>
 __device__ __forceinline__ void wave_prio()
 {
     if constexpr (ON) __builtin_amdgcn_s_setprio(K);
@@ -227,6 +231,8 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
     const float rv = ld1(p.r, ix.vm(b, k, i), urow);
     const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
 
+    // (wave priorities by stage: wave_prio)
+    wave_prio<true, 3>();
     // Q~_k^-1 (identity rows on lanes/knots outside the problem keep it finite)
     bool badq = false, badr = false, bads = false;
     {
@@ -237,6 +243,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         for (int c = 0; c < NC; ++c)
             if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
         inv_rows<SH, NC>(qi, i, badq, L, s);
+        wave_prio<true, 2>();
         badq = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(badq));
         if (i < NC)
 #pragma unroll
@@ -245,6 +252,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
         for (int c = 0; c < MC; ++c) ri[c] = (c == i) ? (urow ? ri0[c] : 1.0f) : ri0[c];
         inv_rows<SH, MC>(ri, i, badr, L, s);
+        wave_prio<true, 1>();
         badr = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(badr));
         if (i < MC)
 #pragma unroll
@@ -296,6 +304,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
         for (int c = 0; c < NC; ++c) L.xw[s][i][c] = W[c];
     }
+    wave_prio<true, 0>();
     __syncthreads();
 
     // O_k = S_{k,k+1} = -W_k' (transpose through LDS); S_{k,k-1} = -W_{k-1}
@@ -364,6 +373,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
     }
 
     // D_k^-1
+    wave_prio<true, 3>();
     float di[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -371,6 +381,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         out.sd[c] = rowv ? sd[c] : 0.0f;
     }
     inv_rows<SH, NC>(di, i, bads, L, s);
+    wave_prio<true, 0>();
     bads = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(bads));
 #pragma unroll
     for (int c = 0; c < NC; ++c) L.xw[s][i][c] = di[c];
@@ -388,6 +399,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
             Z[c] = 0.0f;
         }
         __syncthreads();
+        wave_prio<true, 3>();
         if constexpr (SH::MMA) {
             // Z = D_k^-1 (O_k D_{k+1}^-1): Y holds the rows of (O_k D_{k+1}^-1)'
             mma_t<NP> acc = {};
@@ -405,6 +417,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
             L.xw[s][i][c] = Z[c];
             out.pup[c] = (rowv && k < N - 1) ? -Z[c] : 0.0f;
         }
+        wave_prio<true, 0>();
     }
     __syncthreads();
 #pragma unroll
@@ -689,9 +702,8 @@ struct PcgLds {
 // lambda is accumulated in fp64: on ill-conditioned solves it sums hundreds of
 // small steps, and in fp32 that sum alone would cost ~1e-3 in dz.
 // With four waves per SIMD (VS false) each phase between barriers lowers the
-// wave's priority as it goes (3 for the chain after the barrier, 2 for the
-// product, 1 after it), so the waves of a SIMD that are behind issue first and
-// the four finish their products closer together; and each wave stores its
+// wave's priority as it goes (wave_prio: 3 for the chain after the barrier, 2
+// for the product, 1 after it); and each wave stores its
 // exchange row before its partial sums, so that the store's latency, which the
 // barrier waits for, overlaps them.
 // The step lengths alpha and beta are formed in vector registers from the
