@@ -58,7 +58,7 @@ __global__ __launch_bounds__(VS && SH::THREADS > 512 ? 512 : SH::THREADS) void k
     float lam = ld1(p.lambda, ix.vn(b, k, i), rowv);
     Rows<SH> rw;
     int fl = 0;
-    form<SH>(p, b, 0, p.N, L.u.form, L.park, rw, fl, [](const float*, const float*) {});
+    form<SH, true, true>(p, b, 0, p.N, L.u.form, L.park, rw, fl, [](const float*, const float*) {});
     if (fl && i == 0) atomicOr(&L.flags, fl);
 
     int it = 0, pfl = 0;

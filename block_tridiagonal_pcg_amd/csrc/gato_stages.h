@@ -203,7 +203,9 @@ struct Park {
 // `fl` gets the Q/R/S_NOT_SPD bits of this knot.  With PRE false the stair
 // preconditioner (D_k^-1 and the Phi^-1 rows) is not formed: the direct solve
 // does not use it, and S_NOT_SPD then comes from the solve's own pivots.
-template <class SH, bool PRE = true, class Sink>
+// PRIO: stage-ordered wave priorities (wave_prio), for one workgroup per CU;
+// with the windowed formation's two workgroups per CU they cost time.
+template <class SH, bool PRE = true, bool PRIO = false, class Sink>
 __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, FormLds<SH>& L, Park<SH>& K,
                                      Rows<SH>& out, int& fl, Sink sink)
 {
@@ -232,7 +234,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
     const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
 
     // (wave priorities by stage: wave_prio)
-    wave_prio<true, 3>();
+    wave_prio<PRIO, 3>();
     // Q~_k^-1 (identity rows on lanes/knots outside the problem keep it finite)
     bool badq = false, badr = false, bads = false;
     {
@@ -243,7 +245,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         for (int c = 0; c < NC; ++c)
             if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
         inv_rows<SH, NC>(qi, i, badq, L, s);
-        wave_prio<true, 2>();
+        wave_prio<PRIO, 2>();
         badq = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(badq));
         if (i < NC)
 #pragma unroll
@@ -252,7 +254,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
         for (int c = 0; c < MC; ++c) ri[c] = (c == i) ? (urow ? ri0[c] : 1.0f) : ri0[c];
         inv_rows<SH, MC>(ri, i, badr, L, s);
-        wave_prio<true, 1>();
+        wave_prio<PRIO, 1>();
         badr = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(badr));
         if (i < MC)
 #pragma unroll
@@ -304,7 +306,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
 #pragma unroll
         for (int c = 0; c < NC; ++c) L.xw[s][i][c] = W[c];
     }
-    wave_prio<true, 0>();
+    wave_prio<PRIO, 0>();
     __syncthreads();
 
     // O_k = S_{k,k+1} = -W_k' (transpose through LDS); S_{k,k-1} = -W_{k-1}
@@ -373,7 +375,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
     }
 
     // D_k^-1
-    wave_prio<true, 3>();
+    wave_prio<PRIO, 3>();
     float di[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -381,7 +383,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         out.sd[c] = rowv ? sd[c] : 0.0f;
     }
     inv_rows<SH, NC>(di, i, bads, L, s);
-    wave_prio<true, 0>();
+    wave_prio<PRIO, 0>();
     bads = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(bads));
 #pragma unroll
     for (int c = 0; c < NC; ++c) L.xw[s][i][c] = di[c];
@@ -399,7 +401,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
             Z[c] = 0.0f;
         }
         __syncthreads();
-        wave_prio<true, 3>();
+        wave_prio<PRIO, 3>();
         if constexpr (SH::MMA) {
             // Z = D_k^-1 (O_k D_{k+1}^-1): Y holds the rows of (O_k D_{k+1}^-1)'
             mma_t<NP> acc = {};
@@ -417,7 +419,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
             L.xw[s][i][c] = Z[c];
             out.pup[c] = (rowv && k < N - 1) ? -Z[c] : 0.0f;
         }
-        wave_prio<true, 0>();
+        wave_prio<PRIO, 0>();
     }
     __syncthreads();
 #pragma unroll
