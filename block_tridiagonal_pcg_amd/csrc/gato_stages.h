@@ -419,7 +419,6 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
             L.xw[s][i][c] = Z[c];
             out.pup[c] = (rowv && k < N - 1) ? -Z[c] : 0.0f;
         }
-        wave_prio<PRIO, 0>();
     }
     __syncthreads();
 #pragma unroll
@@ -430,6 +429,7 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         out.pd[c] = rowv ? di[c] : 0.0f;
     }
     __syncthreads();
+    wave_prio<PRIO, 0>();
     fl = 0;
     if (kv) {
         if (badq) fl |= GATO_F_Q_NOT_SPD;
