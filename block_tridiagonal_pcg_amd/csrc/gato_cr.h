@@ -612,6 +612,8 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
     if (threadIdx.x == 0) sm.flags = 0;
     __syncthreads();  // the flag word is zero before any wave can set a bit in it
     bool bad = false, nonfinite = false;
+    // stage-ordered wave priorities (wave_prio) in level 0 and the recoveries
+    wave_prio<true, 3>();
 
     // level 0, eliminations: the odd knots; their W rows go to LDS, and their C'
     // rows, needed only by the last back-substitution step, to the workspace
@@ -646,6 +648,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
         for (int c = 0; c < NC; ++c) a[c] = hasO ? a[c] : (c == i ? 1.0f : 0.0f);
         if (__builtin_amdgcn_ballot_w64(hasO) != 0) {
             chol_solve<NP, NC, KA>(a, i, bad, hasO);
+            wave_prio<true, 1>();
             if (ld) {
 #pragma unroll
                 for (int c = 0; c < YW; ++c) sm.os[g][i][c] = a[NC + c];
@@ -678,6 +681,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
 #pragma unroll
         for (int c = 0; c < NC; ++c) e[NC + c] = 0.0f;
     }
+    wave_prio<true, 0>();
     __syncthreads();
 
     // Schur update of a kept knot from the W rows of its eliminated neighbours
@@ -947,6 +951,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
             const float lam = rowv ? sm.lam[kk][ii] : 0.0f;
             const float lamn = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
             RecRows<SH> r;
+            wave_prio<true, 3>();
             rec_load<SH>(p, bl, kk, i, ok, r);
             float dx, du;
             {
@@ -956,6 +961,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
                 dotb<NP, NC>(h, Bc<NP>(r.qv), r.qi);
                 recover<SH>(i, rowv, urow, lam, lamn, r.qi, sup, h, r.bc, r.rv, r.ri, dx, du);
             }
+            wave_prio<true, 2>();
             float* const lamb = p.lambda + (size_t)bl * N * NC;  // this solve's lambda and dz
             float* const dzb = p.dz + ix.dx(bl, 0, 0);
             if (rowv) {
@@ -1032,6 +1038,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
             }
             hh[w] = h;
         }
+        wave_prio<true, 0>();
         __syncthreads();
         refresh();
         // gamma'_0 = x0' + h_0, gamma'_{k+1} = (e'_k - t_k) + h_{k+1}, e'_k = e_k + A dx_k + B du_k - dx_{k+1}
@@ -1164,6 +1171,7 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
             const float mu = rowv ? sm.lam[kk][ii] : 0.0f;
             const float mun = (rowv && kk + 1 < N) ? sm.lam[kk + 1 < N ? kk + 1 : kk][ii] : 0.0f;
             float qi[NC], ri[MC], bc[NC], sup[NC];
+            wave_prio<true, 3>();
             ld_row<NC>(p.Qinv, ix.Q(bl, kk, i), rowv, qi);
             ld_row<MC>(p.Rinv, ix.R(bl, kk, i), urow, ri);
             ld_row<NC, MC>(p.Bu, ix.Bu(bl, kk, 0) + i, urow, bc);  // column i of B_k
@@ -1181,7 +1189,9 @@ __device__ __forceinline__ void cr_resident(const Params& p, int b)
                 dzb[(unsigned)(kk * (NC + MC) + i)] += ddx;
             }
             if (urow) dzb[(unsigned)(kk * (NC + MC) + NC + i)] += ddu;
+            wave_prio<true, 1>();
         }
+        wave_prio<true, 0>();
     }
 
     const int fl = (bad ? GATO_F_S_NOT_SPD : 0) | (nonfinite ? GATO_F_NONFINITE : 0);
