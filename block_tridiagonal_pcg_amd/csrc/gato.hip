@@ -477,9 +477,12 @@ __global__ __launch_bounds__(1024) void k_merit(Params p)
         const float du = ld1(p.dz, ix.du(b, k, i), hn && i < MC);
         const float dxn = ld1(p.dz, ix.dx(b, k + 1, i), hn && i < NC);
         MeritIn<SH> mi;
+        wave_prio<true, 3>();
         merit_rows<SH>(p, b, k, i, mi);
+        wave_prio<true, 2>();
         merit_knot<SH>(p, k, i, mi, dx, du, dxn, mer + (kv ? k : 0), P);
     }
+    wave_prio<true, 0>();
     __syncthreads();
     int32_t best;
     int lsfail;
