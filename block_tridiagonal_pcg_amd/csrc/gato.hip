@@ -64,7 +64,7 @@ __global__ __launch_bounds__(VS && SH::THREADS > 512 ? 512 : SH::THREADS) void k
     int it = 0, pfl = 0;
     float rel = 0.0f;
     const RegMat<SH> M{&rw};
-    pcg_robust<SH, 1, RegMat<SH>, VS>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
+    pcg_robust<SH, 1, RegMat<SH>, VS, !VS>(p, M, &rw.gam, &lam, L.u.pcg, it, rel, pfl);
 
     // recovery of dz (exchange rows of the PCG buffers: knot k at row k + 1)
     L.u.pcg.xv[s + 1][i] = lam;

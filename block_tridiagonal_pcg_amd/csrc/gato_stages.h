@@ -720,7 +720,7 @@ struct PcgLds {
 // preconditioner is not positive definite on this solve.
 constexpr int PCG_INDEFINITE = 1 << 16;
 
-template <class SH, int C, class MAT, bool VS = false>
+template <class SH, int C, class MAT, bool VS = false, bool RS = false>
 __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* gam, float* lam, PcgLds<SH, C>& L,
                                     int max_iters, int& iters_out, float& relres, int& flags_out)
 {
@@ -885,8 +885,15 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 pin(vp[c]);
                 pin(vn[c]);
             }
-            int stop = !__builtin_isfinite(pSp) ? GATO_F_NONFINITE : !(pSp > 0.0f) ? GATO_F_PCG_BREAKDOWN : 0;
+            const int stop1 = !__builtin_isfinite(pSp) ? GATO_F_NONFINITE : !(pSp > 0.0f) ? GATO_F_PCG_BREAKDOWN : 0;
+            int stop = stop1;
             const float a = eta * __builtin_amdgcn_rcpf(pSpv);
+            // A breakdown here ends the loop after the second barrier with lambda,
+            // r and r'r as they were.  The updates select the old values; with RS
+            // (for four waves per SIMD, where it pays) only lambda's does, r's are
+            // made regardless, off the scalar stop test's path (r is not used after
+            // the loop), and the old r'r is put back at the exit.
+            const float rrk = rr;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 const double l1 = fma((double)a, (double)pv[c], lamd[c]);
@@ -894,9 +901,15 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 const float rp1 = fmaf(-a, vp[c], rp[c]);
                 const float rn1 = fmaf(-a, vn[c], rn[c]);
                 lamd[c] = stop ? lamd[c] : l1;
-                r[c] = stop ? r[c] : r1;
-                rp[c] = stop ? rp[c] : rp1;
-                rn[c] = stop ? rn[c] : rn1;
+                if constexpr (!RS) {
+                    r[c] = stop ? r[c] : r1;
+                    rp[c] = stop ? rp[c] : rp1;
+                    rn[c] = stop ? rn[c] : rn1;
+                } else {
+                    r[c] = r1;
+                    rp[c] = rp1;
+                    rn[c] = rn1;
+                }
             }
             itv += stop ? 0 : 1;
             // z = Phi^-1 r ; r'r, r'z ; z to neighbours
@@ -956,6 +969,7 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             }
             if (__builtin_expect(stop != 0, 0)) {
                 flags |= stop > 0 ? stop : 0;
+                if (RS && stop1) rr = rrk;
                 break;
             }
             const float be = rzv * __builtin_amdgcn_rcpf(eta);
@@ -987,11 +1001,11 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
 // factored form and restarts from its current lambda with the iterations left;
 // iters counts both runs.  The decision is uniform over the workgroup (one
 // solve), and a solve whose r'z stays positive never takes it.
-template <class SH, int C, class MAT, bool VS = false>
+template <class SH, int C, class MAT, bool VS = false, bool RS = false>
 __device__ __forceinline__ void pcg_robust(const Params& p, const MAT& M, const float* gam, float* lam,
                                            PcgLds<SH, C>& L, int& iters_out, float& relres, int& flags_out)
 {
-    pcg<SH, C, MAT, VS>(p, M, gam, lam, L, p.max_iters, iters_out, relres, flags_out);
+    pcg<SH, C, MAT, VS, RS>(p, M, gam, lam, L, p.max_iters, iters_out, relres, flags_out);
     if constexpr (MAT::kAssembled) {
         static_assert(C == 1, "one knot per lane group");
         if (flags_out == PCG_INDEFINITE) {
@@ -1003,7 +1017,7 @@ __device__ __forceinline__ void pcg_robust(const Params& p, const MAT& M, const 
                 sym_rows<SH>(M.rw->pd, L.xy[threadIdx.x / SH::NP + 1], dsym);
                 const RegMatF<SH> F{{M.rw}, dsym, L.xy};
                 int it2 = 0, fl2 = 0;
-                pcg<SH, C, RegMatF<SH>, VS>(p, F, gam, lam, L, left, it2, relres, fl2);
+                pcg<SH, C, RegMatF<SH>, VS, RS>(p, F, gam, lam, L, left, it2, relres, fl2);
                 iters_out += it2;
                 flags_out = fl2;
             }
