@@ -424,6 +424,24 @@ def test_fused_step_equals_staged_calls():
     np.testing.assert_array_equal(fused["best"], m["best"])
 
 
+def test_fused_step_equals_staged_calls_through_breakdowns():
+    """Indefinite problems (Q_k = -I at one knot, of several sizes), where PCG stops at
+    p'Sp <= 0 or r'z <= 0: the fused kernel, which takes the residual's step before it
+    knows of a breakdown and restores r'r at the exit, gives the bits of the staged
+    calls, which keep r as it was; at least one solve ends in a breakdown."""
+    bt = _batch(3, 16)
+    for b in range(16):
+        bt["Q"][b, 4 + 3 * b] = (-0.05 * (b + 1)) * np.eye(14, dtype=np.float32)
+    fused = gpu_sqp(bt, 1e-6, 200)
+    f = gpu_form(bt)
+    p = gpu_pcg(bt, f, 1e-6, 200)
+    print("flags", fused["flags"].tolist(), "iters", fused["iters"].tolist())
+    assert (fused["flags"] & ops.F_PCG_BREAKDOWN).any()
+    for key in ("lam", "dz", "iters", "relres"):
+        np.testing.assert_array_equal(fused[key], p[key], err_msg=key)
+    np.testing.assert_array_equal(fused["flags"] & ~ops.F_LS_FAILED, (f["flags"] | p["flags"]) & ~ops.F_LS_FAILED)
+
+
 def test_solve_independent_of_batch_position():
     big = _batch(2, 16)
     g = gpu_sqp(big, 1e-6, 200)
