@@ -703,18 +703,20 @@ struct PcgLds {
 // the same arithmetic as their owners, so the products need no more exchange.
 // lambda is accumulated in fp64: on ill-conditioned solves it sums hundreds of
 // small steps, and in fp32 that sum alone would cost ~1e-3 in dz.
-// With four waves per SIMD (VS false) each phase between barriers lowers the
-// wave's priority as it goes (wave_prio: 3 for the chain after the barrier, 2
-// for the product, 1 after it); and each wave stores its
-// exchange row before its partial sums, so that the store's latency, which the
-// barrier waits for, overlaps them.
-// The step lengths alpha and beta are formed in vector registers from the
-// totals every lane holds (the same bits in each), so the updates do not wait
-// for a copy to scalar registers.  VS (vector stop): the stop test too, and
-// one scalar copy of its outcome for the loop's branch.  That suits one or two
-// waves per SIMD, where the scalar round trips of the test sit on the
-// iteration's critical path; with four waves per SIMD the vector unit is the
-// busier one, and the test is cheaper on the scalar unit.
+// Scheduling (the results are the same bits either way):
+// - The step lengths alpha and beta are formed in vector registers from the
+//   totals every lane holds (the same bits in each), so the updates do not wait
+//   for a copy to scalar registers.
+// - VS (vector stop), for one or two waves per SIMD: the stop test runs on the
+//   vector unit too, with one scalar copy of its outcome for the loop's branch,
+//   since there the test's scalar round trips sit on the iteration's critical
+//   path.  With four waves per SIMD the vector unit is the busier one and the
+//   test stays on the scalar unit; then (VS false) each phase between barriers
+//   lowers the wave's priority as it goes (wave_prio: 3 for the chain after the
+//   barrier, 2 for the product, 1 after it), and each wave stores its exchange
+//   row before its partial sums, so that the store's latency, which the barrier
+//   waits for, overlaps them.
+// - RS: the residual's updates do not wait for the breakdown test (below).
 // Internal stop code of pcg() (not a GATO_F_* bit): with the assembled Phi^-1,
 // r'z <= 0 while the residual is above the tolerance, i.e. the fp32
 // preconditioner is not positive definite on this solve.
