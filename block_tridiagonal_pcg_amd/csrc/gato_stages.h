@@ -68,6 +68,15 @@ __device__ __forceinline__ void seq_after(double x) { asm volatile("" ::"v"(x) :
 
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Float tests on the bit patterns, so that for values in scalar registers they
+// are scalar integer instructions (no round trip through the vector unit):
+// finite <=> the exponent is not all ones; for non-negative, non-NaN x and y,
+// x <= y <=> bits(x) <= bits(y); x > 0 <=> bits(x) > 0 as a signed integer
+// (for x not NaN).
+__device__ __forceinline__ bool finite_bits(float x) { return (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u; }
+__device__ __forceinline__ bool le_nonneg_bits(float x, float y) { return __float_as_uint(x) <= __float_as_uint(y); }
+__device__ __forceinline__ bool pos_bits(float x) { return __float_as_int(x) > 0; }
+
 // This wave's issue priority (0 lowest .. 3), when ON.  The phases between
 // two barriers step it down as they go (3 at the start, lower for later
 // stages), so that the waves of a SIMD that are behind, which are the younger
@@ -887,7 +896,11 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
                 pin(vp[c]);
                 pin(vn[c]);
             }
-            const int stop1 = !__builtin_isfinite(pSp) ? GATO_F_NONFINITE : !(pSp > 0.0f) ? GATO_F_PCG_BREAKDOWN : 0;
+            int stop1;
+            if constexpr (VS)
+                stop1 = !__builtin_isfinite(pSp) ? GATO_F_NONFINITE : !(pSp > 0.0f) ? GATO_F_PCG_BREAKDOWN : 0;
+            else
+                stop1 = !finite_bits(pSp) ? GATO_F_NONFINITE : !pos_bits(pSp) ? GATO_F_PCG_BREAKDOWN : 0;
             int stop = stop1;
             const float a = eta * __builtin_amdgcn_rcpf(pSpv);
             // A breakdown here ends the loop after the second barrier with lambda,
@@ -963,10 +976,17 @@ __device__ __forceinline__ void pcg(const Params& p, const MAT& M, const float* 
             // with the assembled Phi^-1, the cap (selects, one branch)
             {
                 int st = itv >= max_iters ? GATO_F_PCG_MAXITER : 0;
-                st = (MAT::kAssembled && !(rz > 0.0f)) ? PCG_INDEFINITE : st;
-                st = !__builtin_isfinite(rz) ? GATO_F_NONFINITE : st;
-                st = rr <= tol2 ? -1 : st;  // converged
-                st = !__builtin_isfinite(rr) ? GATO_F_NONFINITE : st;
+                if constexpr (VS) {
+                    st = (MAT::kAssembled && !(rz > 0.0f)) ? PCG_INDEFINITE : st;
+                    st = !__builtin_isfinite(rz) ? GATO_F_NONFINITE : st;
+                    st = rr <= tol2 ? -1 : st;  // converged
+                    st = !__builtin_isfinite(rr) ? GATO_F_NONFINITE : st;
+                } else {  // the same tests on the bits (rr >= 0 and tol2 > 0)
+                    st = (MAT::kAssembled && !pos_bits(rz)) ? PCG_INDEFINITE : st;
+                    st = !finite_bits(rz) ? GATO_F_NONFINITE : st;
+                    st = le_nonneg_bits(rr, tol2) ? -1 : st;  // converged
+                    st = !finite_bits(rr) ? GATO_F_NONFINITE : st;
+                }
                 stop = uniform_i(stop ? stop : st);
             }
             if (__builtin_expect(stop != 0, 0)) {
