@@ -500,7 +500,7 @@ def step_sweep(a):
 
     def time_step(dims, dev, solver):
         out = ops.alloc_outputs(dims, 8)
-        ws = ops.workspace_for(dims, 8)
+        ws = ops.workspace_for(dims, 8, solver=solver)
         call = ops.prepared_sqp_step(dims, *[dev[f] for f in synth.FIELDS], None, 1e-6, 200, synth.ALPHAS, 1.0,
                                      out["lam"], out["dz"], out["merit"], out["merit0"], out["best"], out["iters"],
                                      out["relres"], out["flags"], workspace=ws, solver=solver)

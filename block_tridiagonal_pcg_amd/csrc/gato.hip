@@ -910,7 +910,9 @@ struct PadLayout {
     size_t Q, q, R, r, A, Bu, e, x0, lam, dz, inner, total;
 };
 
-static PadLayout pad_layout(const gato_dims_t* pd)
+// direct: the inner call runs a direct solve even where the fused path applies
+// (an explicit solver in gato_step_opts_t).
+static PadLayout pad_layout(const gato_dims_t* pd, bool direct)
 {
     const size_t B = pd->B, N = pd->N, n = pd->n, m = pd->m, Nd = N > 1 ? N - 1 : 0;
     PadLayout w;
@@ -931,7 +933,7 @@ static PadLayout pad_layout(const gato_dims_t* pd)
     w.lam = take(B * N * n);
     w.dz = take(B * (N * n + Nd * m));
     w.inner = off;
-    w.total = off + (fused_path(pd) ? 0 : ws_layout(pd).total);
+    w.total = off + ((fused_path(pd) && !direct) ? 0 : ws_layout(pd).total);
     return w;
 }
 
@@ -1065,9 +1067,21 @@ size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha)
     if (!native_shape(dims->n, dims->m)) {
         gato_dims_t pd;
         padded_dims(dims, &pd);
-        return pad_layout(&pd).total;
+        return pad_layout(&pd, false).total;
     }
     if (fused_path(dims)) return 0;
+    return ws_layout(dims).total;
+}
+
+size_t gato_step_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha, const gato_step_opts_t* opts)
+{
+    if (opts == nullptr || opts->solver == GATO_SOLVER_AUTO) return gato_workspace_bytes(dims, n_alpha);
+    if (check_dims_step(dims) != GATO_OK || dims->B == 0) return 0;
+    if (!native_shape(dims->n, dims->m)) {
+        gato_dims_t pd;
+        padded_dims(dims, &pd);
+        return pad_layout(&pd, true).total;
+    }
     return ws_layout(dims).total;
 }
 
@@ -1260,7 +1274,7 @@ int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, 
         if (rc) return rc;
         gato_dims_t pd;
         padded_dims(dims, &pd);
-        const PadLayout pl = pad_layout(&pd);
+        const PadLayout pl = pad_layout(&pd, opts && opts->solver != GATO_SOLVER_AUTO);
         if (workspace == nullptr || workspace_bytes < pl.total) return GATO_E_WORKSPACE;
         if (((uintptr_t)workspace & 255u) != 0) return GATO_E_ALIGN;
         char* ws = static_cast<char*>(workspace);
@@ -1303,7 +1317,8 @@ int gato_sqp_step_opts(const gato_dims_t* dims, const float* Q, const float* q, 
     if (!(eps > 0.0f) || max_iters < 1) return GATO_E_PARAM;
     rc = check_alpha(alphas_host, n_alpha, mu);
     if (rc) return rc;
-    const bool fused = fused_path(dims);
+    // an explicit solver runs its direct solve at any horizon, the fused ones included
+    const bool fused = fused_path(dims) && solver == GATO_SOLVER_AUTO;
     const WsLayout wl = ws_layout(dims);
     if (!fused && dims->B > 0) {
         if (workspace == nullptr || workspace_bytes < wl.total) return GATO_E_WORKSPACE;

@@ -43,6 +43,7 @@ EXPORTS = (
     "gato_sqp_step_opts",
     "gato_sqp_step_noalloc",
     "gato_workspace_bytes",
+    "gato_step_workspace_bytes",
     "gato_step_solver",
     "gato_status_string",
     "gato_shape_supported",
@@ -112,6 +113,8 @@ def load():
             lib.gato_step_solver.restype = ctypes.c_int
             lib.gato_workspace_bytes.argtypes = [P, I]
             lib.gato_workspace_bytes.restype = Z
+            lib.gato_step_workspace_bytes.argtypes = [P, I, P]
+            lib.gato_step_workspace_bytes.restype = Z
             lib.gato_status_string.argtypes = [ctypes.c_int]
             lib.gato_status_string.restype = ctypes.c_char_p
             lib.gato_shape_supported.argtypes = [I, I, I]
@@ -309,6 +312,13 @@ def gato_workspace_bytes(dims, n_alpha=8):
     return int(load().gato_workspace_bytes(ctypes.byref(d), int(n_alpha)))
 
 
+def gato_step_workspace_bytes(dims, n_alpha=8, solver=None, refine=None):
+    """Bytes of workspace gato_sqp_step_opts needs with these choices (None: gato_sqp_step's)."""
+    d = _dims(*dims)
+    o = _opts(solver, refine)
+    return int(load().gato_step_workspace_bytes(ctypes.byref(d), int(n_alpha), ctypes.byref(o) if o else None))
+
+
 def gato_shape_supported(n, m, N):
     """1: the build has kernels for (n, m); 2: gato_sqp_step serves it by padding to a
     compiled shape (the stage calls do not); 0: unsupported."""
@@ -430,8 +440,9 @@ def to_device(batch, device="cuda"):
     return out
 
 
-def workspace_for(dims, n_alpha=8, device="cuda"):
-    nb = gato_workspace_bytes(dims, n_alpha)
+def workspace_for(dims, n_alpha=8, device="cuda", solver=None, refine=None):
+    """The workspace gato_sqp_step (gato_sqp_step_opts with solver/refine) needs, or None."""
+    nb = gato_step_workspace_bytes(dims, n_alpha, solver, refine)
     return torch.empty(nb, dtype=torch.uint8, device=device) if nb > 0 else None
 
 

@@ -329,12 +329,17 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
 
 /* Per-call choices of gato_sqp_step_opts.  They select among kernels and
  * passes; none of them changes the problem solved.
- *   solver: for horizons beyond the fused ones, GATO_SOLVER_AUTO (the
- *           horizon policy), GATO_SOLVER_THOMAS, GATO_SOLVER_CR or
- *           GATO_SOLVER_CR_STREAM; ignored where the fused path applies.
+ *   solver: GATO_SOLVER_AUTO (the horizon policy), or a direct solve that
+ *           then runs at every horizon, the fused ones included:
+ *           GATO_SOLVER_THOMAS, GATO_SOLVER_CR or GATO_SOLVER_CR_STREAM.
+ *           PCG stops at ||r|| <= eps ||gamma||, which bounds dz only to
+ *           about cond(S) * eps; for ill-conditioned problems within the
+ *           fused horizon (cond(S) ~ 1e6) a direct solve with its refinement
+ *           pass gives the step to ~1e-5 instead of ~1e-3.  Such a call
+ *           needs the workspace gato_step_workspace_bytes() gives.
  *   refine: 1 (the default of gato_sqp_step) runs the KKT refinement pass
  *           after a direct solve, 0 leaves the fp32 direct solve's step as
- *           it is; ignored where the fused path applies. */
+ *           it is; ignored on the fused path. */
 typedef struct {
     int32_t solver;
     int32_t refine;
@@ -386,6 +391,12 @@ int gato_step_solver(const gato_dims_t* dims);
  * a shape with kernels of its own; the padded copies otherwise, see
  * gato_shape_supported). */
 size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha);
+
+/* The workspace gato_sqp_step_opts needs with these choices (opts nullable:
+ * then, as with GATO_SOLVER_AUTO, gato_workspace_bytes()); a direct solver
+ * within the fused horizon needs one where the fused path needs none.  0 for
+ * invalid dims, B = 0, or choices that need no workspace. */
+size_t gato_step_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha, const gato_step_opts_t* opts);
 
 /* Static description of a status code. */
 const char* gato_status_string(int code);

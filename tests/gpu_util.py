@@ -93,7 +93,7 @@ def gpu_sqp(batch, eps, max_iters, mu=1.0, alphas=ALPHAS, rho=None, lambda0=None
     if lambda0 is not None:
         out["lam"].copy_(torch.as_tensor(np.asarray(lambda0, np.float32)))
     rh = None if rho is None else torch.as_tensor(np.asarray(rho, np.float32)).cuda()
-    ws = ops.workspace_for(dims, len(alphas))
+    ws = ops.workspace_for(dims, len(alphas), solver=solver, refine=refine)
     if ws is not None:
         ws.fill_(255)  # every float NaN: a read of a row the step did not write shows in the result
     st = ops.gato_sqp_step(dims, *[dev[f] for f in synth.FIELDS], rh, eps, max_iters, alphas, mu, out["lam"],

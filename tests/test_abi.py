@@ -84,7 +84,7 @@ def test_header_declares_the_abi():
         "gato_direct_solve", "gato_direct_workspace_bytes", "gato_form_schur", "gato_merit_eval",
         "gato_merit_eval_shape", "gato_pcg_solve", "gato_shape_supported", "gato_sqp_step",
         "gato_sqp_step_noalloc", "gato_sqp_step_opts", "gato_status_string", "gato_step_solver",
-        "gato_workspace_bytes", "gato_chain_qp", "gato_take_step"])
+        "gato_workspace_bytes", "gato_step_workspace_bytes", "gato_chain_qp", "gato_take_step"])
 
 
 def test_driver_calls_validate_on_the_host(lib):
@@ -238,6 +238,46 @@ def test_shapes_served_by_padding(lib):
     assert h(ctypes.byref(d), *args, ctypes.c_void_p(1 << 20), ctypes.c_size_t(pads - 1), None, None) == \
         ops.E_WORKSPACE
     assert h(ctypes.byref(d), *args, ctypes.c_void_p((1 << 20) + 4), ctypes.c_size_t(pads), None, None) == ops.E_ALIGN
+
+
+def test_step_workspace_for_explicit_solvers(lib):
+    """An explicit direct solver runs at every horizon, the fused ones included, and needs
+    the direct path's workspace there (gato_step_workspace_bytes); without one, or with too
+    little, gato_sqp_step_opts returns GATO_E_WORKSPACE before anything runs."""
+    from block_tridiagonal_pcg_amd import ops
+
+    for dims in ((14, 7, 64, 128), (14, 7, 128, 512), (24, 12, 16, 8), (10, 5, 32, 8), (10, 5, 100, 4), (4, 2, 8, 1)):
+        assert ops.gato_step_workspace_bytes(dims) == ops.gato_workspace_bytes(dims), dims
+        assert ops.gato_step_workspace_bytes(dims, solver=ops.SOLVER_AUTO, refine=0) == \
+            ops.gato_workspace_bytes(dims), dims
+    # beyond the fused horizon every solver uses the same layout
+    for s in (ops.SOLVER_THOMAS, ops.SOLVER_CR, ops.SOLVER_CR_STREAM):
+        assert ops.gato_step_workspace_bytes((14, 7, 128, 512), solver=s) == ops.gato_workspace_bytes((14, 7, 128, 512))
+    # within it, the direct path's layout where the fused path needs none: the one of a
+    # horizon beyond, scaled to these dims (stage-1 rows, the solves' workspace, refinement)
+    fused = (14, 7, 64, 128)
+    need = ops.gato_step_workspace_bytes(fused, solver=ops.SOLVER_CR)
+    assert ops.gato_workspace_bytes(fused) == 0 and need > 0
+    assert need == ops.gato_step_workspace_bytes(fused, solver=ops.SOLVER_THOMAS)
+    assert need >= max(ops.gato_direct_workspace_bytes(fused), ops.gato_cr_workspace_bytes(fused))
+    # a padded shape adds the inner call's direct workspace to its padded copies
+    assert ops.gato_step_workspace_bytes((10, 5, 32, 8), solver=ops.SOLVER_CR) == \
+        ops.gato_workspace_bytes((10, 5, 32, 8)) + ops.gato_step_workspace_bytes((12, 6, 32, 8), solver=ops.SOLVER_CR)
+    assert ops.gato_step_workspace_bytes((29, 7, 64, 8), solver=ops.SOLVER_CR) == 0   # unsupported
+    assert ops.gato_step_workspace_bytes((14, 7, 64, 0), solver=ops.SOLVER_CR) == 0   # empty batch
+    al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
+    P = [ctypes.c_void_p(4096 * (j + 1)) for j in range(17)]
+    args = [*P[:9], 1e-6, 200, al, 8, 1.0, *P[9:17]]
+    h = lib.gato_sqp_step_opts
+    for dims in (fused, (10, 5, 32, 8)):
+        d = ops.Dims(*dims)
+        o = ops.StepOpts(ops.SOLVER_CR, 1)
+        nb = ops.gato_step_workspace_bytes(dims, solver=ops.SOLVER_CR)
+        assert h(ctypes.byref(d), *args, None, ctypes.c_size_t(0), None, ctypes.byref(o), None) == ops.E_WORKSPACE
+        assert h(ctypes.byref(d), *args, ctypes.c_void_p(1 << 20), ctypes.c_size_t(nb - 1), None, ctypes.byref(o),
+                 None) == ops.E_WORKSPACE
+        assert h(ctypes.byref(d), *args, ctypes.c_void_p((1 << 20) + 4), ctypes.c_size_t(nb), None, ctypes.byref(o),
+                 None) == ops.E_ALIGN
 
 
 def _call_form(lib, dims, ptrs):

@@ -209,6 +209,60 @@ def test_sqp_step_refinement_meets_the_bars_when_ill_conditioned(solver):
     assert m.max() <= 1e-4
 
 
+@pytest.mark.parametrize("solver", ["cr", "thomas"])
+def test_explicit_direct_solver_within_the_fused_horizon(solver):
+    """An explicit solver in gato_sqp_step_opts runs its direct solve and refinement pass
+    where gato_sqp_step runs the fused PCG (N = 64).  On workload 5's ill-conditioned
+    generators at that horizon the PCG step, which stops at ||r|| <= 1e-6 ||gamma||, bounds
+    dz only to about cond(S) * 1e-6 (its error is printed); the refined direct step is the
+    oracle's exact step within 2e-5 in dz and 1e-4 in every merit."""
+    from gpu_util import gpu_sqp
+
+    which = {"cr": ops.SOLVER_CR, "thomas": ops.SOLVER_THOMAS}[solver]
+    B, N = 32, 64
+    _ident("explicit direct solver at a fused horizon, workload 5", solver, B, N)
+    bt = synth.make_batch(5, B, N=N)
+    assert ops.gato_step_solver(bt["dims"]) == ops.SOLVER_FUSED_PCG
+    ins = synth.inputs(bt)
+    form = oracle.form_schur(*ins)
+    _, dz = _exact(bt, form)
+    merit = oracle.merit_eval(*ins, dz, synth.ALPHAS, 1.0)["merit"]
+    fused = gpu_sqp(bt, 1e-6, 2000)
+    g = gpu_sqp(bt, 1e-6, 2000, solver=which)
+    ef, e = rel_rows(fused["dz"], dz), rel_rows(g["dz"], dz)
+    m = np.abs(g["merit"] - merit) / np.abs(merit)
+    print("dz rel err vs the exact step: fused PCG max %.3e median %.3e; %s + refinement max %.3e; merit max %.3e" % (
+        ef.max(), np.median(ef), solver, e.max(), m.max()))
+    assert (fused["iters"] > 0).all() and (g["iters"] == 0).all()
+    assert ((g["flags"] & ~ops.F_LS_FAILED) == 0).all()
+    assert e.max() <= 2e-5 and m.max() <= 1e-4
+
+
+@pytest.mark.parametrize("cid,n,m,N,B,solver,refine", [
+    (3, 14, 7, 64, 8, ops.SOLVER_CR, 1), (3, 14, 7, 64, 8, ops.SOLVER_THOMAS, 0), (2, 10, 5, 32, 4, ops.SOLVER_CR, 1),
+    (4, 24, 12, 16, 4, ops.SOLVER_CR_STREAM, 1), (1, 4, 2, 8, 1, ops.SOLVER_THOMAS, 1), (3, 14, 7, 1, 2, ops.SOLVER_CR, 1)])
+def test_explicit_direct_solver_on_fused_dims_keeps_a_well_conditioned_step(cid, n, m, N, B, solver, refine):
+    """The explicit direct solvers on dims the fused path serves (16- and 32-lane groups, a
+    padded shape, one knot), with and without the refinement pass: the oracle's exact step
+    within the well-conditioned bar, merits within 1e-4, no PCG iterations."""
+    from gpu_util import gpu_sqp
+
+    _ident("explicit direct solver at fused dims", cid, n, m, N, B, solver, refine)
+    bt = synth.make_batch(cid, B, n=n, m=m, N=N)
+    assert ops.gato_step_solver(bt["dims"]) == ops.SOLVER_FUSED_PCG
+    ins = synth.inputs(bt)
+    form = oracle.form_schur(*ins)
+    _, dz = _exact(bt, form)
+    merit = oracle.merit_eval(*ins, dz, synth.ALPHAS, 1.0)["merit"]
+    g = gpu_sqp(bt, 1e-6, 200, solver=solver, refine=refine)
+    e = rel_rows(g["dz"], dz)
+    me = np.abs(g["merit"] - merit) / np.maximum(np.abs(merit), 1e-30)
+    print("dz rel err max %.3e; merit rel err max %.3e" % (e.max(), me.max()))
+    assert (g["iters"] == 0).all()
+    assert ((g["flags"] & ~ops.F_LS_FAILED) == 0).all()
+    assert e.max() <= 5e-5 and me.max() <= 1e-4
+
+
 @pytest.mark.parametrize("cid,B,N", [(3, 6, 150), (3, 1, 65), (4, 3, 40), (4, 2, 17)])
 def test_sqp_step_refinement_keeps_a_well_conditioned_step(cid, B, N):
     """The refinement pass leaves a well-conditioned long-horizon step the oracle's
