@@ -37,6 +37,19 @@ MU = 1.0
 CAPS = {1: 200, 2: 200, 3: 200, 4: 200, 5: 2000}
 KERNEL = "k_sqp_fused"
 
+# Timings the GATO pages give for the iiwa14-shaped horizon (n = 14, m = 7, N = 64) on other
+# hardware (GATO docs, "Merit launch timing": the RTX 5090 table, the MPS-limited tables and the
+# Jetson AGX Orin sweep of October 24).  They time whole nonlinear SQP solves with rigid-body
+# dynamics and rollouts, not this LQ step: context printed beside the measurement, never a ratio.
+PAGES_CONTEXT = {
+    "note": "the pages' timings of whole nonlinear SQP solves on other hardware; context, not a target",
+    "rtx5090_merit_launch_us_64_threads": {"B1": 33, "B8": 72, "B16": 119},
+    "rtx5090_two_iteration_solve_ms_64_threads": {"B1": 2.273, "B8": 2.874, "B16": 3.057},
+    "rtx5090_10pct_sms_merit_launch_us_64_threads": {"B1": 63, "B8": 289, "B16": 547},
+    "jetson_orin_40W_linsys_ms_per_solve_B1": {"cold": 12.32, "warm": [15.45, 16.34],
+                                               "note": "plant and N not stated on the page"},
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -765,6 +778,7 @@ def main():
                     "same iterations would need from HBM, not HBM traffic",
         },
         "source_sha": source_digest(),
+        "pages_context": PAGES_CONTEXT if (n, m, N) == (14, 7, 64) else None,
     }
     if not a.no_cpu_baseline:
         rec["cpu_baseline"], o_step = cpu_baseline(batch, n_alpha, a.cpu_seconds)
