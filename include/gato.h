@@ -333,10 +333,11 @@ int gato_sqp_step(const gato_dims_t* dims, const float* Q, const float* q, const
  *           then runs at every horizon, the fused ones included:
  *           GATO_SOLVER_THOMAS, GATO_SOLVER_CR or GATO_SOLVER_CR_STREAM.
  *           PCG stops at ||r|| <= eps ||gamma||, which bounds dz only to
- *           about cond(S) * eps; for ill-conditioned problems within the
- *           fused horizon (cond(S) ~ 1e6) a direct solve with its refinement
- *           pass gives the step to ~1e-5 instead of ~1e-3.  Such a call
- *           needs the workspace gato_step_workspace_bytes() gives.
+ *           about cond(S) * eps; on ill-conditioned problems within the
+ *           fused horizon (cond(S) ~ 1e6, N = 64) the PCG step lies within
+ *           ~5e-4 of the exact step, a direct solve with its refinement pass
+ *           within ~5e-6.  Such a call needs the workspace
+ *           gato_step_workspace_bytes() gives.
  *   refine: 1 (the default of gato_sqp_step) runs the KKT refinement pass
  *           after a direct solve, 0 leaves the fp32 direct solve's step as
  *           it is; ignored on the fused path. */
