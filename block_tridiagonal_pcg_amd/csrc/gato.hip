@@ -1075,6 +1075,10 @@ size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha)
 
 size_t gato_step_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha, const gato_step_opts_t* opts)
 {
+    if (opts && ((opts->solver != GATO_SOLVER_AUTO && opts->solver != GATO_SOLVER_THOMAS &&
+                  opts->solver != GATO_SOLVER_CR && opts->solver != GATO_SOLVER_CR_STREAM) ||
+                 (opts->refine != 0 && opts->refine != 1)))
+        return 0;  // choices gato_sqp_step_opts rejects
     if (opts == nullptr || opts->solver == GATO_SOLVER_AUTO) return gato_workspace_bytes(dims, n_alpha);
     if (check_dims_step(dims) != GATO_OK || dims->B == 0) return 0;
     if (!native_shape(dims->n, dims->m)) {

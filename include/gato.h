@@ -396,7 +396,8 @@ size_t gato_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha);
 /* The workspace gato_sqp_step_opts needs with these choices (opts nullable:
  * then, as with GATO_SOLVER_AUTO, gato_workspace_bytes()); a direct solver
  * within the fused horizon needs one where the fused path needs none.  0 for
- * invalid dims, B = 0, or choices that need no workspace. */
+ * invalid dims, B = 0, choices that need no workspace, or choices
+ * gato_sqp_step_opts rejects (GATO_E_PARAM there). */
 size_t gato_step_workspace_bytes(const gato_dims_t* dims, int32_t n_alpha, const gato_step_opts_t* opts);
 
 /* Static description of a status code. */

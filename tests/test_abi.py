@@ -265,6 +265,9 @@ def test_step_workspace_for_explicit_solvers(lib):
         ops.gato_workspace_bytes((10, 5, 32, 8)) + ops.gato_step_workspace_bytes((12, 6, 32, 8), solver=ops.SOLVER_CR)
     assert ops.gato_step_workspace_bytes((29, 7, 64, 8), solver=ops.SOLVER_CR) == 0   # unsupported
     assert ops.gato_step_workspace_bytes((14, 7, 64, 0), solver=ops.SOLVER_CR) == 0   # empty batch
+    assert ops.gato_step_workspace_bytes(fused, solver=ops.SOLVER_FUSED_PCG) == 0    # rejected choices
+    assert ops.gato_step_workspace_bytes(fused, solver=7) == 0
+    assert ops.gato_step_workspace_bytes(fused, solver=ops.SOLVER_CR, refine=2) == 0
     al = (ctypes.c_float * 8)(*[2.0 ** -i for i in range(8)])
     P = [ctypes.c_void_p(4096 * (j + 1)) for j in range(17)]
     args = [*P[:9], 1e-6, 200, al, 8, 1.0, *P[9:17]]
