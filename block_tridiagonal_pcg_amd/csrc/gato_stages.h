@@ -231,16 +231,13 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
     const int sp = s > 0 ? s - 1 : 0;  // previous slot (clamped)
     const bool has_prev = s >= 1 && k >= 1;
 
-    // Every input row this knot needs, loaded up front so that the loads for
-    // the products overlap the inversions.
+    // The rows the inversions need first; the rows for the products are requested
+    // after the first inversion (below), so that a wave is not held at its start
+    // until all of its loads are accepted, and they arrive during the second.
     float qi0[NC], ri0[MC], ar[NC], br[MC];
+    float qv, rv, ev;
     ld_row<NC>(p.Q, ix.Q(b, k, i), rowv, qi0);
     ld_row<MC>(p.R, ix.R(b, k, i), urow, ri0);
-    ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, ar);
-    ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, br);
-    const float qv = ld1(p.q, ix.vn(b, k, i), rowv);
-    const float rv = ld1(p.r, ix.vm(b, k, i), urow);
-    const float ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
 
     // (wave priorities by stage: wave_prio)
     wave_prio<PRIO, 3>();
@@ -254,6 +251,11 @@ __device__ __forceinline__ void form(const Params& p, int b, int w0, int nslot, 
         for (int c = 0; c < NC; ++c)
             if (c == i) qi[c] = rowv ? qi[c] + rh : 1.0f;
         inv_rows<SH, NC>(qi, i, badq, L, s);
+        ld_row<NC>(p.A, ix.A(b, k, i), hn && i < NC, ar);
+        ld_row<MC>(p.Bu, ix.Bu(b, k, i), hn && i < NC, br);
+        qv = ld1(p.q, ix.vn(b, k, i), rowv);
+        rv = ld1(p.r, ix.vm(b, k, i), urow);
+        ev = ld1(p.e, ix.e(b, k, i), hn && i < NC);
         wave_prio<PRIO, 2>();
         badq = group_any<SH::NP>(__builtin_amdgcn_ballot_w64(badq));
         if (i < NC)
